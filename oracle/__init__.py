@@ -1,0 +1,5 @@
+"""CPU oracle for SparK (test infrastructure only; see spark_oracle's header)."""
+from .spark_oracle import *  # noqa: F401,F403
+from .spark_oracle import (num_kept, chan_energy, saliency_keys, select_top_t, mask_words,  # noqa: F401
+                           mask_from_words, pack_kept, prune, stats, expand_keys, decode_attn,
+                           dense_attn, window_scores, snapkv_evict, window_rows)

@@ -1,0 +1,274 @@
+"""CPU oracle for SparK prefill pruning and decode attention.
+
+TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this module. The GPU library never calls it and
+shares no code with it.
+
+Plain NumPy, written for reading, not speed. Citations name the SparK
+walkthrough page ("KV Cache 还能再砍一刀：SparK 在通道维度上做了一件被忽略多年的事",
+ai-paper-analysis.pages.dev) by section and equation, and the AMD blog page
+(bqwf.cn, "AAAI 2026 AMD论文Spark方法揭秘") by figure/table.
+
+Precision: float64 everywhere except the two steps whose result decides an
+integer (the channel mask). There the method's ranking is defined on fp32
+values computed in a fixed order, so that a GPU can reproduce the mask bit for
+bit:
+  * channel energy A_j: a sequential fp32 sum of fl32(q^2) (exact squares of
+    bf16 values) over the window rows, group head outer, window position inner;
+  * saliency key: fl32(A_j * fl32(k^2)), one IEEE multiply.
+
+Readings of points the pages leave open (each is listed in the design doc):
+  * ||q^j||_2 is the L2 norm of channel j over the stacked window queries of
+    all G query heads that share the KV head ("l2"); the walkthrough's
+    mean-query proxy of section 3.2 is mode "mean" (A_j = m_j^2 with m_j the
+    fp32 sum of the window queries; the 1/(GW)^2 factor does not change any
+    ranking or recovery value and is omitted).
+  * Ranking by w^2 = A_j k^2 instead of w = sqrt(A_j)|k|: same order in exact
+    arithmetic, and needs no square root.
+  * T = floor((1 - lambda) * D + 0.5) with lambda taken as an IEEE fp32 value.
+  * Ties go to the lower channel index; kept values are packed in ascending
+    channel order; mask word w bit b is channel 32w + b.
+  * Recovery F default "mean_retained": per (batch, KV head, channel), the mean
+    of the retained key values over all tokens (0 if none retained). The
+    walkthrough's Degenerate F (section 3.3, F table) is "score_mean_pruned".
+  * Decode: one new query per head attends to all S cached tokens (no causal
+    mask), scale 1/sqrt(D), recovery only in the scores, V dense.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+QAGG_L2 = "l2"
+QAGG_MEAN = "mean"
+
+F_MEAN_RETAINED = "mean_retained"
+F_ZERO = "zero"
+F_CONST = "const"
+F_SCORE_MEAN_PRUNED = "score_mean_pruned"
+
+
+def num_kept(D: int, lam: float) -> int:
+    """T = floor((1 - lambda) D + 0.5): channels kept per token.
+
+    Walkthrough section 3.1 (the reduced objective keeps exactly T channels);
+    lambda is the pruned fraction of key channels (AMD blog, Table 1 caption).
+    lambda is rounded to fp32 first, as the C ABI receives it.
+    """
+    lam32 = float(np.float32(lam))
+    if not (0.0 <= lam32 <= 1.0):
+        raise ValueError("lambda must lie in [0, 1]")
+    return int(math.floor((1.0 - lam32) * D + 0.5))
+
+
+def _f32(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float32)
+
+
+def window_rows(q_win: np.ndarray, n_kv: int) -> np.ndarray:
+    """Stack the window queries of each KV head's query group.
+
+    q_win [B][N_q][W][D] -> [B][N_kv][G*W][D], row index g*W + w, where query
+    head h*G + g reads KV head h.
+    """
+    B, Nq, W, D = q_win.shape
+    G = Nq // n_kv
+    return np.asarray(q_win).reshape(B, n_kv, G * W, D)
+
+
+def chan_energy(q_win: np.ndarray, n_kv: int, qagg: str = QAGG_L2) -> np.ndarray:
+    """A[b,h,j], the squared channel norm of the window queries (fp32, fixed order).
+
+    Walkthrough section 3.1: saliency w = ||q^j||_2 ||k^j||_2; section 3.2 and
+    its display equation: the queries of the last W positions stand in for
+    the future queries.
+    """
+    rows = _f32(window_rows(q_win, n_kv))
+    B, H, R, D = rows.shape
+    acc = np.zeros((B, H, D), dtype=np.float32)
+    if qagg == QAGG_L2:
+        for i in range(R):            # sequential: row g*W + w in increasing order
+            x = rows[:, :, i, :]
+            acc = acc + x * x         # fp32: x*x exact for bf16 x, one rounding per add
+        return acc
+    if qagg == QAGG_MEAN:
+        for i in range(R):
+            acc = acc + rows[:, :, i, :]
+        return acc * acc
+    raise ValueError(qagg)
+
+
+def saliency_keys(A: np.ndarray, k: np.ndarray) -> np.ndarray:
+    """key[b,h,t,j] = fl32(A_j * fl32(k_tj^2)) = w^2 in fp32 (walkthrough section 3.1)."""
+    k = _f32(k)
+    return _f32(A)[:, :, None, :] * (k * k)
+
+
+def select_top_t(keys: np.ndarray, T: int) -> np.ndarray:
+    """Boolean mask of the T largest keys per token, ties to the lower channel.
+
+    Walkthrough section 3.1: with the cross-channel terms dropped, the
+    objective max sum_j w^j z^j subject to sum_j z^j = T is solved greedily
+    by sorting the channels of each token.
+    """
+    order = np.argsort(-keys, axis=-1, kind="stable")
+    mask = np.zeros(keys.shape, dtype=bool)
+    np.put_along_axis(mask, order[..., :T], True, axis=-1)
+    return mask
+
+
+def mask_words(mask: np.ndarray) -> np.ndarray:
+    """bool [..., D] -> uint32 [..., ceil(D/32)]; bit b of word w is channel 32w + b."""
+    D = mask.shape[-1]
+    nw = (D + 31) // 32
+    if D != 32 * nw:
+        mask = np.concatenate([mask, np.zeros(mask.shape[:-1] + (32 * nw - D,), bool)], axis=-1)
+    m = mask.reshape(mask.shape[:-1] + (nw, 32)).astype(np.uint64)
+    return (m << np.arange(32, dtype=np.uint64)).sum(axis=-1).astype(np.uint32)
+
+
+def mask_from_words(words: np.ndarray, D: int) -> np.ndarray:
+    """uint32 [..., ceil(D/32)] -> bool [..., D]."""
+    w = np.asarray(words, dtype=np.uint32)
+    bits = (w[..., :, None] >> np.arange(32, dtype=np.uint32)) & np.uint32(1)
+    return bits.reshape(w.shape[:-1] + (32 * w.shape[-1],))[..., :D].astype(bool)
+
+
+def pack_kept(k: np.ndarray, mask: np.ndarray) -> np.ndarray:
+    """Retained key values per token in ascending channel order: [..., T]."""
+    T = int(mask[(0,) * (mask.ndim - 1)].sum()) if mask.size else 0
+    kept = np.asarray(k)[mask]       # row-major: token by token, channel ascending
+    return kept.reshape(mask.shape[:-1] + (T,))
+
+
+def prune(q_win: np.ndarray, k: np.ndarray, n_kv: int, lam: float, qagg: str = QAGG_L2) -> dict:
+    """Prefill pruning (walkthrough section 3.2, Fig. 3 prefill half).
+
+    Returns A [B][N_kv][D] fp32, mask bool [B][N_kv][S][D], words uint32
+    [B][N_kv][S][D/32] and packed [B][N_kv][S][T] (same dtype as k).
+    """
+    D = k.shape[-1]
+    T = num_kept(D, lam)
+    A = chan_energy(q_win, n_kv, qagg)
+    mask = select_top_t(saliency_keys(A, k), T)
+    return {"T": T, "A": A, "mask": mask, "words": mask_words(mask), "packed": pack_kept(k, mask)}
+
+
+def stats(k: np.ndarray, mask: np.ndarray, A: np.ndarray, mode: str = F_MEAN_RETAINED,
+          f_const: float = 0.01):
+    """Recovery vector r [B][N_kv][D] (fp32) and retained count cnt (int32).
+
+    Walkthrough section 3.3 step 1: prefill caches distribution statistics
+    beside the pruned keys and the mask. ``k`` is the dense key tensor (only
+    the retained entries are read, except by "score_mean_pruned", which needs
+    the pruned ones).
+      mean_retained:     r_j = mean of k_tj over tokens t that keep j (0 if none)
+      zero / const:      the naive fills of section 3.3 (0 and a constant)
+      score_mean_pruned: section 3.3 steps 1-4 with the Degenerate F:
+                         mu = mean over pruned (t, j) of a_j |k_tj|, a_j = sqrt(A_j);
+                         the back-solved key is mu / a_j (0 if a_j = 0).
+    """
+    k64 = np.asarray(k, dtype=np.float64)
+    cnt = mask.sum(axis=2).astype(np.int32)
+    B, H, S, D = k64.shape
+    if mode == F_MEAN_RETAINED:
+        s = np.where(mask, k64, 0.0).sum(axis=2)
+        r = np.where(cnt > 0, s / np.maximum(cnt, 1), 0.0)
+    elif mode == F_ZERO:
+        r = np.zeros((B, H, D))
+    elif mode == F_CONST:
+        r = np.full((B, H, D), float(np.float32(f_const)))
+    elif mode == F_SCORE_MEAN_PRUNED:
+        a = np.sqrt(np.asarray(A, dtype=np.float64))                    # [B][H][D]
+        w = np.abs(k64) * a[:, :, None, :]
+        npruned = (~mask).sum(axis=(2, 3))
+        mu = np.where(npruned > 0, np.where(~mask, w, 0.0).sum(axis=(2, 3)) / np.maximum(npruned, 1), 0.0)
+        r = np.where(a > 0, mu[:, :, None] / np.where(a > 0, a, 1.0), 0.0)
+    else:
+        raise ValueError(mode)
+    return r.astype(np.float32), cnt
+
+
+def expand_keys(packed: np.ndarray, mask: np.ndarray, r: np.ndarray) -> np.ndarray:
+    """K_hat = mask ? stored value : r_j, in float64 (walkthrough section 3.3, Fig. 3 decode half)."""
+    khat = np.broadcast_to(np.asarray(r, dtype=np.float64)[:, :, None, :], mask.shape).copy()
+    khat[mask] = np.asarray(packed, dtype=np.float64).reshape(-1)
+    return khat
+
+
+def _attend(q: np.ndarray, keys: np.ndarray, v: np.ndarray, scale: float) -> np.ndarray:
+    """Softmax attention of one query per head over all cached tokens, float64.
+
+    q [B][N_q][D], keys/v [B][N_kv][S][D]; query head i reads KV head i // G.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, Nq, D = q.shape
+    Nkv = keys.shape[1]
+    G = Nq // Nkv
+    out = np.empty((B, Nq, D), dtype=np.float64)
+    for b in range(B):
+        for i in range(Nq):
+            h = i // G
+            s = (keys[b, h] @ q[b, i]) * scale
+            p = np.exp(s - s.max())
+            p /= p.sum()
+            out[b, i] = p @ v[b, h]
+    return out
+
+
+def decode_attn(q, packed, mask, v, r, scale: float | None = None) -> np.ndarray:
+    """One decode step over the pruned cache: recover, then standard attention.
+
+    Walkthrough section 3.3 and Fig. 3 (decode half); AMD blog Fig. 2.
+    Returns out [B][N_q][D] in float64.
+    """
+    D = mask.shape[-1]
+    scale = 1.0 / math.sqrt(D) if scale is None or scale <= 0 else float(scale)
+    return _attend(q, expand_keys(packed, mask, r), v, scale)
+
+
+def dense_attn(q, k, v, scale: float | None = None) -> np.ndarray:
+    """Unpruned attention (the full KV cache of walkthrough Fig. 2a), float64."""
+    D = k.shape[-1]
+    scale = 1.0 / math.sqrt(D) if scale is None or scale <= 0 else float(scale)
+    return _attend(q, np.asarray(k, dtype=np.float64), v, scale)
+
+
+def window_scores(q_win: np.ndarray, k: np.ndarray) -> np.ndarray:
+    """Window-summed causal softmax score per cached token, float64: [B][N_kv][S].
+
+    The observation-window eviction that SparK is stacked on (walkthrough
+    section 4.1; section 3.2 borrows its window). Query row (g, w) sits at
+    position S - W + w and sees tokens t <= S - W + w; its softmax over those
+    tokens is summed over the G heads of the group and the W window rows.
+    """
+    B, Nq, W, D = q_win.shape
+    Nkv, S = k.shape[1], k.shape[2]
+    rows = np.asarray(window_rows(q_win, Nkv), dtype=np.float64)    # [B][H][G*W][D]
+    k64 = np.asarray(k, dtype=np.float64)
+    pos = np.tile(np.arange(S - W, S), Nq // Nkv)                     # row position
+    visible = np.arange(S)[None, :] <= pos[:, None]                   # [G*W][S]
+    score = np.empty((B, Nkv, S), dtype=np.float64)
+    for b in range(B):
+        for h in range(Nkv):
+            logit = (rows[b, h] @ k64[b, h].T) / math.sqrt(D)
+            logit = np.where(visible, logit, -np.inf)
+            p = np.exp(logit - logit.max(axis=1, keepdims=True))
+            p /= p.sum(axis=1, keepdims=True)
+            score[b, h] = p.sum(axis=0)
+    return score
+
+
+def snapkv_evict(q_win, k, v, keep: int):
+    """Keep the `keep` highest-scoring tokens per (batch, KV head), ties to the lower t.
+
+    Returns idx [B][N_kv][keep] (ascending), k_kept and v_kept [B][N_kv][keep][D].
+    """
+    score = window_scores(q_win, k)
+    order = np.argsort(-score, axis=-1, kind="stable")[..., :keep]
+    idx = np.sort(order, axis=-1)
+    kk = np.take_along_axis(np.asarray(k), idx[..., None], axis=2)
+    vv = np.take_along_axis(np.asarray(v), idx[..., None], axis=2)
+    return idx.astype(np.int32), kk, vv
