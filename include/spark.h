@@ -1,0 +1,147 @@
+/*
+ * spark.h - C ABI of libspark.so: SparK query-aware, recoverable KV-cache
+ * channel pruning (prefill prune, statistics, decode attention) on MI355X.
+ *
+ * Sources. "KV Cache 还能再砍一刀：SparK 在通道维度上做了一件被忽略多年的事"
+ * (ai-paper-analysis.pages.dev walkthrough of arXiv 2508.15212), called "the
+ * walkthrough" below, and the AMD blog page "AAAI 2026 AMD论文Spark方法揭秘"
+ * (bqwf.cn), called "the blog". Problem size symbols follow the walkthrough's
+ * section 1 (B batch, S sequence length, N heads, D head dimension).
+ *
+ * Conventions for every entry point
+ *  - Tensors are dense, row-major, in device memory, and owned by the caller.
+ *    The library never allocates, frees or caches device memory; scratch
+ *    space comes from the caller's workspace `ws` of `ws_bytes` bytes, sized
+ *    by the matching *_workspace_bytes() call. Workspaces must be 256-byte
+ *    aligned; every tensor pointer must be 16-byte aligned.
+ *  - bf16 tensors are passed as `const void*` holding IEEE bfloat16 values.
+ *  - `stream` is a hipStream_t (NULL = the legacy default stream). Calls are
+ *    asynchronous on that stream and never synchronise with the host.
+ *  - Return value: SPARK_OK, or a negative spark_status. Arguments are
+ *    checked on the host before anything is launched; on a check failure
+ *    nothing is launched and no output is touched. A failed kernel launch
+ *    returns SPARK_EHIP. No exception crosses the ABI.
+ *  - Only D = 128 is implemented (SPARK_EUNSUPPORTED otherwise) and
+ *    G = N_q / N_kv must be 1, 2, 4 or 8 (GQA: query head i reads KV head
+ *    i / G). Non-finite inputs give undefined (but memory-safe) results.
+ *  - Two calls that share a workspace must not overlap in time.
+ */
+#ifndef SPARK_H
+#define SPARK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SPARK_OK = 0,
+    SPARK_EINVAL = -1,        /* bad size, ratio, mode or null pointer */
+    SPARK_EUNSUPPORTED = -2,  /* valid but not implemented (D != 128, G not in {1,2,4,8}) */
+    SPARK_EALIGN = -3,        /* pointer misaligned */
+    SPARK_ENOSPACE = -4,      /* workspace too small */
+    SPARK_EHIP = -5           /* HIP runtime error at launch */
+} spark_status;
+
+/* Recovery function F for pruned channels (walkthrough section 3.3, F table,
+ * and the zero / small-constant fills it compares against). */
+typedef enum {
+    SPARK_F_MEAN_RETAINED = 0,     /* r_j = mean of retained k_tj over tokens t keeping channel j */
+    SPARK_F_ZERO = 1,              /* r_j = 0 */
+    SPARK_F_CONST = 2,             /* r_j = f_const */
+    SPARK_F_SCORE_MEAN_PRUNED = 3  /* Degenerate F: mu = mean over pruned (t,j) of a_j |k_tj|,
+                                      a_j = sqrt(A_j); r_j = mu / a_j (0 if a_j = 0) */
+} spark_recovery;
+
+/* How the window queries form the channel energy A_j = ||q^j||_2^2. */
+typedef enum {
+    SPARK_QAGG_L2 = 0,   /* A_j = sum over the G*W stacked window rows of q^2 (fp32, sequential) */
+    SPARK_QAGG_MEAN = 1  /* A_j = m_j^2, m_j = fp32 sequential sum of the rows (walkthrough
+                            section 3.2 mean query; the constant 1/(GW) is dropped) */
+} spark_qagg;
+
+/* T = floor((1 - lambda) * D + 0.5), evaluated in double from the fp32
+ * lambda: the number of key channels each token keeps (walkthrough section
+ * 3.1, the T of the reduced objective; lambda is the pruned fraction, blog
+ * Table 1 caption). Returns -1 if lambda is outside [0, 1] or D < 1. */
+int spark_num_kept(int D, float lambda);
+
+/* Human-readable name of a spark_status. Never NULL. */
+const char* spark_strerror(int status);
+
+/* Workspace sizes in bytes (0 on invalid sizes). */
+size_t spark_prefill_workspace_bytes(int B, int S, int N_kv, int D);
+size_t spark_decode_workspace_bytes(int B, int S, int N_q, int N_kv, int D, int splits);
+
+/*
+ * Prefill pruning: channel energy, saliency, per-token top-T, packing and
+ * recovery statistics in one call (walkthrough sections 3.1-3.3, Fig. 3
+ * prefill half; blog Fig. 2).
+ *
+ *  q_win        bf16 [B][N_q][W][D]  the last W = window prompt queries
+ *  k            bf16 [B][N_kv][S][D] keys
+ *  lambda       pruned fraction of channels, in [0, 1]; T = spark_num_kept(D, lambda)
+ *  window       W, 1 <= W
+ *  qagg         spark_qagg
+ *  recovery     spark_recovery; f_const is used by SPARK_F_CONST only
+ * Outputs (caller-allocated, fully overwritten):
+ *  k_packed     bf16 [B][N_kv][S][T]  retained values, ascending channel order
+ *  mask         uint32 [B][N_kv][S][D/32]  bit b of word w set <=> channel 32w+b kept;
+ *               exactly T bits set per token. Selection order: saliency key
+ *               fl32(A_j * fl32(k_tj^2)) descending, ties to the lower channel.
+ *  chan_energy  fp32 [B][N_kv][D]  A_j
+ *  r            fp32 [B][N_kv][D]  recovery vector per recovery mode
+ *  cnt          int32 [B][N_kv][D] tokens keeping channel j (may be NULL)
+ * k_packed may be NULL only when T = 0.
+ */
+int spark_prefill_prune(const void* q_win, const void* k,
+                        int B, int S, int N_q, int N_kv, int D, float lambda, int window,
+                        int qagg, int recovery, float f_const,
+                        void* k_packed, uint32_t* mask, float* chan_energy, float* r, int32_t* cnt,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Recovery statistics recomputed from a stored pruned cache (walkthrough
+ * section 3.3 step 1), e.g. to switch F without pruning again.
+ *  k_packed, mask, chan_energy   as written by spark_prefill_prune
+ *  k_dense      bf16 [B][N_kv][S][D]; required by SPARK_F_SCORE_MEAN_PRUNED
+ *               (the pruned values are not in the packed store), else ignored
+ *  r, cnt       outputs as in spark_prefill_prune (cnt may be NULL)
+ */
+int spark_stats(const void* k_packed, const uint32_t* mask, const float* chan_energy,
+                const void* k_dense, int B, int S, int N_kv, int D, float lambda,
+                int recovery, float f_const, float* r, int32_t* cnt,
+                void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * One decode step over the pruned cache: each pruned channel of each cached
+ * key takes r_j, then ordinary softmax attention runs over all S tokens with
+ * dense V (walkthrough section 3.3 and Fig. 3 decode half; blog Fig. 2).
+ *  q        bf16 [B][N_q][D]  one new query per head
+ *  k_packed, mask, r         the pruned cache (layouts as above)
+ *  v        bf16 [B][N_kv][S][D]
+ *  scale    softmax scale; <= 0 selects 1/sqrt(D)
+ *  splits   sequence splits per (b, KV head); 0 lets the library choose;
+ *           at most ceil(S / 64)
+ *  out      fp32 [B][N_q][D]
+ * No causal mask: the query attends to every cached token. fp32 arithmetic
+ * on bf16 inputs. The first SPARK_DECODE_COUNTER_BYTES of ws hold completion
+ * counters that must be zero before the first call (spark_decode_ws_init);
+ * every call that completes leaves them zero again.
+ */
+#define SPARK_DECODE_COUNTER_BYTES 4096
+int spark_decode_attn(const void* q, const void* k_packed, const uint32_t* mask, const void* v,
+                      const float* r, int B, int S, int N_q, int N_kv, int D, float lambda,
+                      float scale, int splits, float* out, void* ws, size_t ws_bytes, void* stream);
+
+/* Zero the decode completion counters of a workspace (a fill kernel on
+ * `stream`; safe to record in a HIP graph). */
+int spark_decode_ws_init(void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARK_H */

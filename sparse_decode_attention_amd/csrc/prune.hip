@@ -1,0 +1,256 @@
+// Prefill side of SparK on gfx950: channel energy of the observation window,
+// per-token exact top-T channel selection, packing of the retained keys, and
+// the recovery statistics (walkthrough sections 3.1-3.3, Fig. 3 prefill half).
+//
+// Bit-exactness: the channel energy is an fp32 sum in a fixed order (group
+// head outer, window row inner) of exact bf16 squares, and the saliency key is
+// one IEEE fp32 multiply A_j * k^2. Selection compares the keys' bit patterns
+// as unsigned integers (non-negative floats order like their bits), so masks
+// do not depend on any floating-point reduction order.
+#include "common.h"
+#include "kernels.h"
+
+namespace spark {
+
+// ---------------------------------------------------------------- channel energy
+// One thread per (b, kv head, channel); threads of a block read 256 contiguous
+// bytes of each window row.
+__global__ void __launch_bounds__(128)
+chan_energy_kernel(const uint16_t* __restrict__ q_win, float* __restrict__ A,
+                   int N_q, int N_kv, int W, int qagg) {
+    const int bh = blockIdx.x;
+    const int b = bh / N_kv, h = bh % N_kv;
+    const int G = N_q / N_kv;
+    const int j = threadIdx.x;
+    float acc = 0.f;
+    for (int g = 0; g < G; ++g) {
+        const uint16_t* row = q_win + (((size_t)b * N_q + (size_t)h * G + g) * W) * 128;
+        for (int w = 0; w < W; ++w) {
+            const float x = bf16_to_f32(row[(size_t)w * 128 + j]);
+            acc = (qagg == 0) ? __fadd_rn(acc, __fmul_rn(x, x)) : __fadd_rn(acc, x);
+        }
+    }
+    A[(size_t)bh * 128 + j] = (qagg == 0) ? acc : __fmul_rn(acc, acc);
+}
+
+// ---------------------------------------------------------------- select + pack
+// Block: 4 waves over PRUNE_TOKENS_PER_BLOCK consecutive tokens of one
+// (b, kv head). Each wave takes one token at a time with lane L holding
+// channels L and L + 64, so the two 64-lane ballots of "kept" are the mask
+// words directly (channels 0-63, 64-127).
+//
+// Top-T: find the T-th largest key theta by deciding its bits from the top
+// (bit 30 down; bit 31 is the sign, always 0), counting keys >= candidate
+// with two ballots per step. The search stops early when exactly T keys are
+// >= the candidate: those T are the answer and no tie straddles it.
+// Otherwise theta is exact and the channels equal to theta are taken in
+// ascending channel order until T are kept.
+__global__ void __launch_bounds__(256)
+select_pack_kernel(const uint16_t* __restrict__ k, const float* __restrict__ A,
+                   uint16_t* __restrict__ k_packed, uint32_t* __restrict__ mask,
+                   double* __restrict__ part_sum, int32_t* __restrict__ part_cnt,
+                   double* __restrict__ part_pruned,
+                   int S, int T, int nblk, int recovery) {
+    __shared__ uint4 stage[4][64];            // 4 tokens x 256 B per wave
+    __shared__ double red_sum[4][128];
+    __shared__ int red_cnt[4][128];
+    __shared__ double red_pr[4];
+
+    const int bh = blockIdx.y;
+    const int blk = blockIdx.x;
+    const int wave = threadIdx.x >> 6;
+    const int L = threadIdx.x & 63;
+    const int t_begin = blk * PRUNE_TOKENS_PER_BLOCK;
+    const int t_end = min(S, t_begin + PRUNE_TOKENS_PER_BLOCK);
+
+    const float A0 = A[(size_t)bh * 128 + L];
+    const float A1 = A[(size_t)bh * 128 + 64 + L];
+    const double a0 = sqrt((double)A0), a1 = sqrt((double)A1);
+
+    double sum0 = 0.0, sum1 = 0.0, pruned = 0.0;
+    int cnt0 = 0, cnt1 = 0;
+
+    const uint16_t* kbh = k + (size_t)bh * S * 128;
+    uint16_t* pbh = k_packed ? k_packed + (size_t)bh * S * T : nullptr;
+    uint32_t* mbh = mask + (size_t)bh * S * 4;
+    uint16_t* st = reinterpret_cast<uint16_t*>(&stage[wave][0]);
+
+    // wave w takes tokens t_begin + 4*(w + 4*i) .. +3
+    for (int t4 = t_begin + 4 * wave; t4 < t_end; t4 += 16) {
+        const int n4 = min(4, t_end - t4);
+        {   // coalesced load of up to 4 token rows (16 B per lane)
+            const int tok = L >> 4;
+            uint4 x = make_uint4(0, 0, 0, 0);
+            if (tok < n4) x = *reinterpret_cast<const uint4*>(kbh + (size_t)(t4 + tok) * 128 + (L & 15) * 8);
+            stage[wave][L] = x;
+        }
+        wave_lds_sync();
+        for (int i = 0; i < n4; ++i) {
+            const int t = t4 + i;
+            const uint16_t kb0 = st[i * 128 + L], kb1 = st[i * 128 + 64 + L];
+            const float k0 = bf16_to_f32(kb0), k1 = bf16_to_f32(kb1);
+            const uint32_t key0 = __float_as_uint(__fmul_rn(A0, __fmul_rn(k0, k0)));
+            const uint32_t key1 = __float_as_uint(__fmul_rn(A1, __fmul_rn(k1, k1)));
+            bool kept0, kept1;
+            if (T >= 128) {
+                kept0 = kept1 = true;
+            } else if (T <= 0) {
+                kept0 = kept1 = false;
+            } else {
+                uint32_t v = 0;
+                bool exact = false;
+                for (int bit = 30; bit >= 0; --bit) {
+                    const uint32_t c = v | (1u << bit);
+                    const int n = __popcll(ballot(key0 >= c)) + __popcll(ballot(key1 >= c));
+                    if (n >= T) {
+                        v = c;
+                        if (n == T) { exact = true; break; }
+                    }
+                }
+                if (exact) {
+                    kept0 = key0 >= v;
+                    kept1 = key1 >= v;
+                } else {
+                    const bool gt0 = key0 > v, gt1 = key1 > v;
+                    const int need = T - (__popcll(ballot(gt0)) + __popcll(ballot(gt1)));
+                    const uint64_t eq0 = ballot(key0 == v), eq1 = ballot(key1 == v);
+                    const int r0 = (int)mbcnt(eq0);
+                    const int r1 = __popcll(eq0) + (int)mbcnt(eq1);
+                    kept0 = gt0 || (key0 == v && r0 < need);
+                    kept1 = gt1 || (key1 == v && r1 < need);
+                }
+            }
+            const uint64_t m0 = ballot(kept0), m1 = ballot(kept1);
+            if (L == 0) {
+                *reinterpret_cast<uint4*>(mbh + (size_t)t * 4) =
+                    make_uint4((uint32_t)m0, (uint32_t)(m0 >> 32), (uint32_t)m1, (uint32_t)(m1 >> 32));
+            }
+            if (kept0) pbh[(size_t)t * T + mbcnt(m0)] = kb0;
+            if (kept1) pbh[(size_t)t * T + __popcll(m0) + mbcnt(m1)] = kb1;
+            if (recovery == 0) {
+                if (kept0) { sum0 += (double)k0; ++cnt0; }
+                if (kept1) { sum1 += (double)k1; ++cnt1; }
+            } else {
+                cnt0 += kept0;
+                cnt1 += kept1;
+                if (recovery == 3) {
+                    if (!kept0) pruned += a0 * (double)fabsf(k0);
+                    if (!kept1) pruned += a1 * (double)fabsf(k1);
+                }
+            }
+        }
+        wave_lds_sync();
+    }
+
+    // fixed-order combination of the 4 waves, then one partial per block
+    red_sum[wave][L] = sum0;
+    red_sum[wave][64 + L] = sum1;
+    red_cnt[wave][L] = cnt0;
+    red_cnt[wave][64 + L] = cnt1;
+    if (recovery == 3) {
+        double p = pruned;
+        for (int o = 32; o > 0; o >>= 1) p += __shfl_xor(p, o, 64);
+        if (L == 0) red_pr[wave] = p;
+    }
+    __syncthreads();
+    if (threadIdx.x < 128) {
+        const int j = threadIdx.x;
+        const double s = ((red_sum[0][j] + red_sum[1][j]) + red_sum[2][j]) + red_sum[3][j];
+        const int c = red_cnt[0][j] + red_cnt[1][j] + red_cnt[2][j] + red_cnt[3][j];
+        part_sum[((size_t)bh * nblk + blk) * 128 + j] = s;
+        part_cnt[((size_t)bh * nblk + blk) * 128 + j] = c;
+        if (j == 0) part_pruned[(size_t)bh * nblk + blk] =
+            (recovery == 3) ? ((red_pr[0] + red_pr[1]) + red_pr[2]) + red_pr[3] : 0.0;
+    }
+}
+
+// ---------------------------------------------------------------- stats from a stored cache
+// Same partials as select_pack_kernel, read back from (packed, mask) or, for
+// the pruned-score mean, from the dense keys.
+__global__ void __launch_bounds__(256)
+stats_partial_kernel(const uint16_t* __restrict__ k_packed, const uint32_t* __restrict__ mask,
+                     const uint16_t* __restrict__ k_dense, const float* __restrict__ A,
+                     double* __restrict__ part_sum, int32_t* __restrict__ part_cnt,
+                     double* __restrict__ part_pruned, int S, int T, int nblk, int recovery) {
+    __shared__ double red_sum[4][128];
+    __shared__ int red_cnt[4][128];
+    __shared__ double red_pr[4];
+    const int bh = blockIdx.y, blk = blockIdx.x;
+    const int wave = threadIdx.x >> 6, L = threadIdx.x & 63;
+    const int t_begin = blk * PRUNE_TOKENS_PER_BLOCK;
+    const int t_end = min(S, t_begin + PRUNE_TOKENS_PER_BLOCK);
+    const double a0 = sqrt((double)A[(size_t)bh * 128 + L]);
+    const double a1 = sqrt((double)A[(size_t)bh * 128 + 64 + L]);
+    double sum0 = 0.0, sum1 = 0.0, pruned = 0.0;
+    int cnt0 = 0, cnt1 = 0;
+    for (int t = t_begin + wave; t < t_end; t += 4) {
+        const uint4 mw = *reinterpret_cast<const uint4*>(mask + ((size_t)bh * S + t) * 4);
+        const uint64_t m0 = ((uint64_t)mw.y << 32) | mw.x;
+        const uint64_t m1 = ((uint64_t)mw.w << 32) | mw.z;
+        const bool kept0 = (m0 >> L) & 1, kept1 = (m1 >> L) & 1;
+        cnt0 += kept0;
+        cnt1 += kept1;
+        if (recovery == 0) {
+            // ranks are bounded by T so a mask with extra bits cannot read past the row
+            const uint16_t* row = k_packed + ((size_t)bh * S + t) * T;
+            const int rk0 = (int)mbcnt(m0), rk1 = __popcll(m0) + (int)mbcnt(m1);
+            if (kept0 && rk0 < T) sum0 += (double)bf16_to_f32(row[rk0]);
+            if (kept1 && rk1 < T) sum1 += (double)bf16_to_f32(row[rk1]);
+        } else if (recovery == 3) {
+            const uint16_t* row = k_dense + ((size_t)bh * S + t) * 128;
+            if (!kept0) pruned += a0 * (double)fabsf(bf16_to_f32(row[L]));
+            if (!kept1) pruned += a1 * (double)fabsf(bf16_to_f32(row[64 + L]));
+        }
+    }
+    red_sum[wave][L] = sum0;
+    red_sum[wave][64 + L] = sum1;
+    red_cnt[wave][L] = cnt0;
+    red_cnt[wave][64 + L] = cnt1;
+    if (recovery == 3) {
+        double p = pruned;
+        for (int o = 32; o > 0; o >>= 1) p += __shfl_xor(p, o, 64);
+        if (L == 0) red_pr[wave] = p;
+    }
+    __syncthreads();
+    if (threadIdx.x < 128) {
+        const int j = threadIdx.x;
+        part_sum[((size_t)bh * nblk + blk) * 128 + j] =
+            ((red_sum[0][j] + red_sum[1][j]) + red_sum[2][j]) + red_sum[3][j];
+        part_cnt[((size_t)bh * nblk + blk) * 128 + j] = red_cnt[0][j] + red_cnt[1][j] + red_cnt[2][j] + red_cnt[3][j];
+        if (j == 0) part_pruned[(size_t)bh * nblk + blk] =
+            (recovery == 3) ? ((red_pr[0] + red_pr[1]) + red_pr[2]) + red_pr[3] : 0.0;
+    }
+}
+
+// ---------------------------------------------------------------- partials -> r
+// One thread per (b, kv head, channel); blocks are combined in index order.
+__global__ void __launch_bounds__(128)
+stats_reduce_kernel(const double* __restrict__ part_sum, const int32_t* __restrict__ part_cnt,
+                    const double* __restrict__ part_pruned, const float* __restrict__ A,
+                    float* __restrict__ r, int32_t* __restrict__ cnt,
+                    int S, int T, int nblk, int recovery, float f_const) {
+    const int bh = blockIdx.x, j = threadIdx.x;
+    double s = 0.0;
+    long long c = 0;
+    for (int blk = 0; blk < nblk; ++blk) {
+        s += part_sum[((size_t)bh * nblk + blk) * 128 + j];
+        c += part_cnt[((size_t)bh * nblk + blk) * 128 + j];
+    }
+    float out = 0.f;
+    if (recovery == 0) {
+        out = c > 0 ? (float)(s / (double)c) : 0.f;
+    } else if (recovery == 2) {
+        out = f_const;
+    } else if (recovery == 3) {
+        double p = 0.0;
+        for (int blk = 0; blk < nblk; ++blk) p += part_pruned[(size_t)bh * nblk + blk];
+        const double npruned = (double)S * (double)(128 - T);
+        const double mu = npruned > 0 ? p / npruned : 0.0;
+        const double a = sqrt((double)A[(size_t)bh * 128 + j]);
+        out = a > 0 ? (float)(mu / a) : 0.f;
+    }
+    r[(size_t)bh * 128 + j] = out;
+    if (cnt) cnt[(size_t)bh * 128 + j] = (int32_t)c;
+}
+
+}  // namespace spark

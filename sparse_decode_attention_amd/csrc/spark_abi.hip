@@ -1,0 +1,220 @@
+// C ABI of libspark.so (declared in include/spark.h): host-side argument
+// checks, workspace layout and kernel launches.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/spark.h"
+#include "kernels.h"
+
+using namespace spark;
+
+namespace {
+
+inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int kept_or_neg(int D, float lambda) {
+    if (D < 1 || !(lambda >= 0.0f && lambda <= 1.0f)) return -1;
+    return (int)floor((1.0 - (double)lambda) * (double)D + 0.5);
+}
+
+int check_group(int N_q, int N_kv) {
+    if (N_q < 1 || N_kv < 1 || N_q % N_kv != 0) return SPARK_EINVAL;
+    const int G = N_q / N_kv;
+    if (G != 1 && G != 2 && G != 4 && G != 8) return SPARK_EUNSUPPORTED;
+    return SPARK_OK;
+}
+
+// prefill workspace: part_sum double [BH][nblk][128] | part_cnt int32 [BH][nblk][128] | part_pruned double [BH][nblk]
+struct PrefillWs {
+    double* sum;
+    int32_t* cnt;
+    double* pruned;
+    size_t bytes;
+    int nblk;
+};
+
+PrefillWs prefill_layout(void* ws, int B, int S, int N_kv) {
+    PrefillWs w{};
+    const size_t BH = (size_t)B * N_kv;
+    w.nblk = (S + PRUNE_TOKENS_PER_BLOCK - 1) / PRUNE_TOKENS_PER_BLOCK;
+    const size_t n = BH * (size_t)w.nblk;
+    const size_t s_sum = round_up(n * 128 * sizeof(double), 256);
+    const size_t s_cnt = round_up(n * 128 * sizeof(int32_t), 256);
+    const size_t s_pr = round_up(n * sizeof(double), 256);
+    char* base = static_cast<char*>(ws);
+    w.sum = reinterpret_cast<double*>(base);
+    w.cnt = reinterpret_cast<int32_t*>(base + s_sum);
+    w.pruned = reinterpret_cast<double*>(base + s_sum + s_cnt);
+    w.bytes = s_sum + s_cnt + s_pr;
+    return w;
+}
+
+int auto_splits(int BH, int S) {
+    const int max_splits = (S + DECODE_TILE - 1) / DECODE_TILE;
+    int want = (512 + BH - 1) / BH;           // about two 4-wave blocks per CU
+    if (want < 1) want = 1;
+    if (want > max_splits) want = max_splits;
+    return want;
+}
+
+// decode: the number of splits actually launched and the tokens per split
+void decode_plan(int BH, int S, int splits, int* nsplit, int* chunk) {
+    int n = splits > 0 ? splits : auto_splits(BH, S);
+    const int max_splits = (S + DECODE_TILE - 1) / DECODE_TILE;
+    if (n > max_splits) n = max_splits;
+    int c = (S + n - 1) / n;
+    c = (c + DECODE_TILE - 1) / DECODE_TILE * DECODE_TILE;
+    *chunk = c;
+    *nsplit = (S + c - 1) / c;
+}
+
+size_t decode_ws_bytes(int BH, int G, int nsplit) {
+    return SPARK_DECODE_COUNTER_BYTES + round_up((size_t)BH * nsplit * 2 * G * sizeof(float), 256) +
+           round_up((size_t)BH * nsplit * G * 128 * sizeof(float), 256);
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? SPARK_OK : SPARK_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+int spark_num_kept(int D, float lambda) { return kept_or_neg(D, lambda); }
+
+const char* spark_strerror(int status) {
+    switch (status) {
+        case SPARK_OK: return "ok";
+        case SPARK_EINVAL: return "invalid argument";
+        case SPARK_EUNSUPPORTED: return "unsupported size (D must be 128; N_q/N_kv in {1,2,4,8})";
+        case SPARK_EALIGN: return "misaligned pointer (tensors 16 B, workspace 256 B)";
+        case SPARK_ENOSPACE: return "workspace too small";
+        case SPARK_EHIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+size_t spark_prefill_workspace_bytes(int B, int S, int N_kv, int D) {
+    if (B < 1 || S < 1 || N_kv < 1 || D < 1) return 0;
+    return prefill_layout(nullptr, B, S, N_kv).bytes;
+}
+
+size_t spark_decode_workspace_bytes(int B, int S, int N_q, int N_kv, int D, int splits) {
+    if (B < 1 || S < 1 || N_kv < 1 || N_q < 1 || D < 1 || splits < 0 || N_q % N_kv) return 0;
+    int nsplit, chunk;
+    decode_plan(B * N_kv, S, splits, &nsplit, &chunk);
+    return decode_ws_bytes(B * N_kv, N_q / N_kv, nsplit);
+}
+
+int spark_prefill_prune(const void* q_win, const void* k, int B, int S, int N_q, int N_kv, int D,
+                        float lambda, int window, int qagg, int recovery, float f_const,
+                        void* k_packed, uint32_t* mask, float* chan_energy, float* r, int32_t* cnt,
+                        void* ws, size_t ws_bytes, void* stream) {
+    if (B < 1 || S < 1 || D < 1 || window < 1) return SPARK_EINVAL;
+    const int T = kept_or_neg(D, lambda);
+    if (T < 0) return SPARK_EINVAL;
+    if (qagg != SPARK_QAGG_L2 && qagg != SPARK_QAGG_MEAN) return SPARK_EINVAL;
+    if (recovery < SPARK_F_MEAN_RETAINED || recovery > SPARK_F_SCORE_MEAN_PRUNED) return SPARK_EINVAL;
+    if (int e = check_group(N_q, N_kv)) return e;
+    if (D != 128) return SPARK_EUNSUPPORTED;
+    if (!q_win || !k || !mask || !chan_energy || !r || !ws || (T > 0 && !k_packed)) return SPARK_EINVAL;
+    if (!aligned(q_win, 16) || !aligned(k, 16) || !aligned(mask, 16) || !aligned(chan_energy, 16) ||
+        !aligned(r, 16) || (k_packed && !aligned(k_packed, 16)) || (cnt && !aligned(cnt, 16)) || !aligned(ws, 256))
+        return SPARK_EALIGN;
+    const PrefillWs w = prefill_layout(ws, B, S, N_kv);
+    if (ws_bytes < w.bytes) return SPARK_ENOSPACE;
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int BH = B * N_kv;
+    hipLaunchKernelGGL(chan_energy_kernel, dim3(BH), dim3(128), 0, st,
+                       static_cast<const uint16_t*>(q_win), chan_energy, N_q, N_kv, window, qagg);
+    hipLaunchKernelGGL(select_pack_kernel, dim3(w.nblk, BH), dim3(256), 0, st,
+                       static_cast<const uint16_t*>(k), chan_energy, static_cast<uint16_t*>(k_packed), mask,
+                       w.sum, w.cnt, w.pruned, S, T, w.nblk, recovery);
+    hipLaunchKernelGGL(stats_reduce_kernel, dim3(BH), dim3(128), 0, st,
+                       w.sum, w.cnt, w.pruned, chan_energy, r, cnt, S, T, w.nblk, recovery, f_const);
+    return hip_status(hipGetLastError());
+}
+
+int spark_stats(const void* k_packed, const uint32_t* mask, const float* chan_energy, const void* k_dense,
+                int B, int S, int N_kv, int D, float lambda, int recovery, float f_const,
+                float* r, int32_t* cnt, void* ws, size_t ws_bytes, void* stream) {
+    if (B < 1 || S < 1 || N_kv < 1 || D < 1) return SPARK_EINVAL;
+    const int T = kept_or_neg(D, lambda);
+    if (T < 0) return SPARK_EINVAL;
+    if (recovery < SPARK_F_MEAN_RETAINED || recovery > SPARK_F_SCORE_MEAN_PRUNED) return SPARK_EINVAL;
+    if (D != 128) return SPARK_EUNSUPPORTED;
+    if (!mask || !chan_energy || !r || !ws) return SPARK_EINVAL;
+    if (recovery == SPARK_F_MEAN_RETAINED && T > 0 && !k_packed) return SPARK_EINVAL;
+    if (recovery == SPARK_F_SCORE_MEAN_PRUNED && !k_dense) return SPARK_EINVAL;
+    if (!aligned(mask, 16) || !aligned(chan_energy, 16) || !aligned(r, 16) || (cnt && !aligned(cnt, 16)) ||
+        (k_packed && !aligned(k_packed, 16)) || (k_dense && !aligned(k_dense, 16)) || !aligned(ws, 256))
+        return SPARK_EALIGN;
+    const PrefillWs w = prefill_layout(ws, B, S, N_kv);
+    if (ws_bytes < w.bytes) return SPARK_ENOSPACE;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int BH = B * N_kv;
+    hipLaunchKernelGGL(stats_partial_kernel, dim3(w.nblk, BH), dim3(256), 0, st,
+                       static_cast<const uint16_t*>(k_packed), mask, static_cast<const uint16_t*>(k_dense),
+                       chan_energy, w.sum, w.cnt, w.pruned, S, T, w.nblk, recovery);
+    hipLaunchKernelGGL(stats_reduce_kernel, dim3(BH), dim3(128), 0, st,
+                       w.sum, w.cnt, w.pruned, chan_energy, r, cnt, S, T, w.nblk, recovery, f_const);
+    return hip_status(hipGetLastError());
+}
+
+int spark_decode_attn(const void* q, const void* k_packed, const uint32_t* mask, const void* v, const float* r,
+                      int B, int S, int N_q, int N_kv, int D, float lambda, float scale, int splits,
+                      float* out, void* ws, size_t ws_bytes, void* stream) {
+    if (B < 1 || S < 1 || D < 1 || splits < 0) return SPARK_EINVAL;
+    const int T = kept_or_neg(D, lambda);
+    if (T < 0) return SPARK_EINVAL;
+    if (!(scale == scale)) return SPARK_EINVAL;
+    if (int e = check_group(N_q, N_kv)) return e;
+    if (D != 128) return SPARK_EUNSUPPORTED;
+    const int BH = B * N_kv;
+    if ((size_t)BH > (SPARK_DECODE_COUNTER_BYTES / 4)) return SPARK_EUNSUPPORTED;
+    if (!q || !mask || !v || !r || !out || !ws || (T > 0 && !k_packed)) return SPARK_EINVAL;
+    if (!aligned(q, 16) || !aligned(mask, 16) || !aligned(v, 16) || !aligned(r, 16) || !aligned(out, 16) ||
+        (k_packed && !aligned(k_packed, 16)) || !aligned(ws, 256))
+        return SPARK_EALIGN;
+    const int G = N_q / N_kv;
+    int nsplit, chunk;
+    decode_plan(BH, S, splits, &nsplit, &chunk);
+    if (ws_bytes < decode_ws_bytes(BH, G, nsplit)) return SPARK_ENOSPACE;
+
+    char* base = static_cast<char*>(ws);
+    DecodeArgs a{};
+    a.q = static_cast<const uint16_t*>(q);
+    a.packed = static_cast<const uint16_t*>(k_packed);
+    a.mask = mask;
+    a.v = static_cast<const uint16_t*>(v);
+    a.r = r;
+    a.out = out;
+    a.counters = reinterpret_cast<uint32_t*>(base);
+    a.part_ml = reinterpret_cast<float*>(base + SPARK_DECODE_COUNTER_BYTES);
+    a.part_acc = reinterpret_cast<float*>(base + SPARK_DECODE_COUNTER_BYTES +
+                                          round_up((size_t)BH * nsplit * 2 * G * sizeof(float), 256));
+    a.packed_elems = (size_t)BH * S * T;
+    a.S = S;
+    a.T = T;
+    a.N_q = N_q;
+    a.N_kv = N_kv;
+    a.nsplit = nsplit;
+    a.chunk = chunk;
+    const float sc = scale > 0.f ? scale : (float)(1.0 / sqrt((double)D));
+    a.qscale = sc * 1.4426950408889634f;
+    a.lds_stage_bytes = decode_stage_bytes(T);
+    return hip_status(launch_decode(a, G, BH, static_cast<hipStream_t>(stream)));
+}
+
+int spark_decode_ws_init(void* ws, size_t ws_bytes, void* stream) {
+    if (!ws) return SPARK_EINVAL;
+    if (!aligned(ws, 256)) return SPARK_EALIGN;
+    if (ws_bytes < SPARK_DECODE_COUNTER_BYTES) return SPARK_ENOSPACE;
+    const size_t n = SPARK_DECODE_COUNTER_BYTES / 4;
+    hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), static_cast<uint32_t*>(ws), 0u, n);
+    return hip_status(hipGetLastError());
+}
+
+}  // extern "C"

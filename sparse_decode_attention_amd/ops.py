@@ -1,0 +1,190 @@
+"""ctypes binding of libspark.so over torch device tensors.
+
+Argument marshalling only: every step of prefill pruning, statistics and
+decode attention runs in the HIP kernels of libspark.so. Torch provides device
+memory (outputs and workspaces are torch tensors) and the current HIP stream.
+If the library is missing this module raises; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import threading
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libspark.so")
+HEADER = os.path.join(os.path.dirname(_PKG), "include", "spark.h")
+
+OK, EINVAL, EUNSUPPORTED, EALIGN, ENOSPACE, EHIP = 0, -1, -2, -3, -4, -5
+RECOVERY = {"mean_retained": 0, "zero": 1, "const": 2, "score_mean_pruned": 3}
+QAGG = {"l2": 0, "mean": 1}
+DECODE_COUNTER_BYTES = 4096
+
+_lib = None
+_lock = threading.Lock()
+
+_vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_SIGS = {
+    "spark_num_kept": (_i, [_i, _f]),
+    "spark_strerror": (ctypes.c_char_p, [_i]),
+    "spark_prefill_workspace_bytes": (_sz, [_i, _i, _i, _i]),
+    "spark_decode_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "spark_prefill_prune": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _f, _i, _i, _i, _f,
+                                 _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "spark_stats": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _f, _vp, _vp, _vp, _sz, _vp]),
+    "spark_decode_attn": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _f, _i, _vp, _vp, _sz, _vp]),
+    "spark_decode_ws_init": (_i, [_vp, _sz, _vp]),
+}
+
+
+class SparkError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {status} ({strerror(status)})")
+
+
+def header_symbols() -> list[str]:
+    """Entry points declared in include/spark.h."""
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(spark_\w+)\s*\(", txt, re.M)))
+
+
+def lib() -> ctypes.CDLL:
+    """Load libspark.so (built by sparse_decode_attention_amd.build)."""
+    global _lib
+    if _lib is None:
+        with _lock:
+            if _lib is None:
+                if not os.path.exists(LIB_PATH):
+                    raise RuntimeError(f"{LIB_PATH} is missing: run `python -m sparse_decode_attention_amd.build`")
+                l = ctypes.CDLL(LIB_PATH)
+                for name, (res, args) in _SIGS.items():
+                    fn = getattr(l, name)
+                    fn.restype, fn.argtypes = res, args
+                _lib = l
+    return _lib
+
+
+def strerror(status: int) -> str:
+    return lib().spark_strerror(int(status)).decode()
+
+
+def num_kept(D: int, lam: float) -> int:
+    return int(lib().spark_num_kept(int(D), float(lam)))
+
+
+def _check(fn: str, status: int) -> None:
+    if status != OK:
+        raise SparkError(fn, status)
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(dev) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype, shape=None) -> None:
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous device tensor")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+# workspaces are cached per (device, kind); decode workspaces are zeroed when
+# allocated (the completion counters must start at zero and are left at zero)
+_ws_cache: dict = {}
+
+
+def workspace(dev, kind: str, nbytes: int) -> torch.Tensor:
+    key = (str(dev), kind)
+    ws = _ws_cache.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        _ws_cache[key] = ws
+    return ws
+
+
+def prefill_prune(q_win: torch.Tensor, k: torch.Tensor, n_kv: int, lam: float, qagg: str = "l2",
+                  recovery: str = "mean_retained", f_const: float = 0.01, out: dict | None = None) -> dict:
+    """spark_prefill_prune: q_win bf16 [B][N_q][W][D], k bf16 [B][N_kv][S][D].
+
+    Returns {"T", "k_packed", "mask", "chan_energy", "r", "cnt"} (new tensors
+    unless `out` supplies them).
+    """
+    B, N_q, W, D = q_win.shape
+    S = k.shape[2]
+    _need(q_win, "q_win", torch.bfloat16)
+    _need(k, "k", torch.bfloat16, (B, n_kv, S, D))
+    T = num_kept(D, lam)
+    if T < 0:
+        raise SparkError("spark_num_kept", EINVAL)
+    dev = k.device
+    o = dict(out or {})
+    o.setdefault("k_packed", torch.empty((B, n_kv, S, T), dtype=torch.bfloat16, device=dev))
+    o.setdefault("mask", torch.empty((B, n_kv, S, (D + 31) // 32), dtype=torch.int32, device=dev))
+    o.setdefault("chan_energy", torch.empty((B, n_kv, D), dtype=torch.float32, device=dev))
+    o.setdefault("r", torch.empty((B, n_kv, D), dtype=torch.float32, device=dev))
+    o.setdefault("cnt", torch.empty((B, n_kv, D), dtype=torch.int32, device=dev))
+    nb = lib().spark_prefill_workspace_bytes(B, S, n_kv, D)
+    ws = workspace(dev, "prefill", nb)
+    st = lib().spark_prefill_prune(_ptr(q_win), _ptr(k), B, S, N_q, n_kv, D, float(lam), W,
+                                   QAGG[qagg], RECOVERY[recovery], float(f_const),
+                                   _ptr(o["k_packed"]) if T > 0 else None, _ptr(o["mask"]),
+                                   _ptr(o["chan_energy"]), _ptr(o["r"]), _ptr(o["cnt"]),
+                                   _ptr(ws), ws.numel(), _stream(dev))
+    _check("spark_prefill_prune", st)
+    o["T"] = T
+    return o
+
+
+def stats(k_packed, mask, chan_energy, lam: float, recovery: str = "mean_retained", f_const: float = 0.01,
+          k_dense=None, r=None, cnt=None):
+    """spark_stats: recompute (r, cnt) from a stored pruned cache."""
+    B, n_kv, S, nw = mask.shape
+    D = chan_energy.shape[-1]
+    dev = mask.device
+    r = torch.empty((B, n_kv, D), dtype=torch.float32, device=dev) if r is None else r
+    cnt = torch.empty((B, n_kv, D), dtype=torch.int32, device=dev) if cnt is None else cnt
+    nb = lib().spark_prefill_workspace_bytes(B, S, n_kv, D)
+    ws = workspace(dev, "prefill", nb)
+    T = num_kept(D, lam)
+    st = lib().spark_stats(_ptr(k_packed) if (k_packed is not None and T > 0) else None, _ptr(mask),
+                           _ptr(chan_energy), _ptr(k_dense), B, S, n_kv, D, float(lam), RECOVERY[recovery],
+                           float(f_const), _ptr(r), _ptr(cnt), _ptr(ws), ws.numel(), _stream(dev))
+    _check("spark_stats", st)
+    return r, cnt
+
+
+def decode_ws_bytes(B, S, N_q, N_kv, D=128, splits=0) -> int:
+    return int(lib().spark_decode_workspace_bytes(B, S, N_q, N_kv, D, splits))
+
+
+def decode_attn(q, k_packed, mask, v, r, lam: float, scale: float = 0.0, splits: int = 0, out=None, ws=None):
+    """spark_decode_attn: q bf16 [B][N_q][D] -> out fp32 [B][N_q][D]."""
+    B, N_q, D = q.shape
+    n_kv, S = v.shape[1], v.shape[2]
+    _need(q, "q", torch.bfloat16)
+    _need(v, "v", torch.bfloat16, (B, n_kv, S, D))
+    dev = q.device
+    out = torch.empty((B, N_q, D), dtype=torch.float32, device=dev) if out is None else out
+    nb = decode_ws_bytes(B, S, N_q, n_kv, D, splits)
+    if ws is None:
+        ws = workspace(dev, "decode", nb)
+    T = num_kept(D, lam)
+    st = lib().spark_decode_attn(_ptr(q), _ptr(k_packed) if T > 0 else None, _ptr(mask), _ptr(v), _ptr(r),
+                                 B, S, N_q, n_kv, D, float(lam), float(scale), int(splits), _ptr(out),
+                                 _ptr(ws), ws.numel(), _stream(dev))
+    _check("spark_decode_attn", st)
+    return out
+
+
+def decode_ws_init(ws: torch.Tensor) -> None:
+    _check("spark_decode_ws_init", lib().spark_decode_ws_init(_ptr(ws), ws.numel(), _stream(ws.device)))

@@ -1,0 +1,124 @@
+"""The C ABI without a GPU: the library loads, exports every declared entry
+point, and rejects invalid arguments with the documented status before
+launching anything (no call here reaches a kernel launch)."""
+import ctypes
+
+import numpy as np
+import pytest
+
+import oracle
+from sparse_decode_attention_amd import ops
+
+FAKE = 0x10000          # 256-byte aligned, never dereferenced: every call below fails validation first
+MIS = 0x10008           # 8-byte aligned only
+
+
+def test_library_exports_every_declared_symbol():
+    syms = ops.header_symbols()
+    assert {"spark_prefill_prune", "spark_stats", "spark_decode_attn", "spark_num_kept"} <= set(syms)
+    l = ops.lib()
+    for s in syms:
+        assert hasattr(l, s), s
+        assert ctypes.cast(getattr(l, s), ctypes.c_void_p).value
+
+
+def test_num_kept_matches_oracle_rule():
+    lams = list(np.linspace(0, 1, 1001)) + [0.5, 0.7, 0.8, 0.2, 1 - 63.5 / 128, 1 - 25.5 / 128]
+    for D in (8, 64, 128):
+        for lam in lams:
+            assert ops.num_kept(D, lam) == oracle.num_kept(D, lam), (D, lam)
+    assert ops.num_kept(128, -0.1) == -1 and ops.num_kept(128, 1.5) == -1
+    assert ops.num_kept(128, float("nan")) == -1 and ops.num_kept(0, 0.5) == -1
+
+
+def test_strerror_names_every_status():
+    for st in (0, -1, -2, -3, -4, -5):
+        assert ops.strerror(st) and ops.strerror(st) != "unknown status"
+    assert ops.strerror(7) == "unknown status"
+
+
+def test_workspace_sizes():
+    l = ops.lib()
+    assert l.spark_prefill_workspace_bytes(1, 32768, 8, 128) > 0
+    assert l.spark_prefill_workspace_bytes(0, 32768, 8, 128) == 0
+    n_auto = l.spark_decode_workspace_bytes(1, 32768, 32, 8, 128, 0)
+    n_one = l.spark_decode_workspace_bytes(1, 32768, 32, 8, 128, 1)
+    assert n_auto > n_one >= ops.DECODE_COUNTER_BYTES
+    assert l.spark_decode_workspace_bytes(1, 32768, 30, 8, 128, 0) == 0
+
+
+def _prefill(**kw):
+    a = dict(q_win=FAKE, k=FAKE, B=1, S=64, N_q=32, N_kv=8, D=128, lam=0.5, W=4, qagg=0, rec=0, fc=0.01,
+             kp=FAKE, mask=FAKE, A=FAKE, r=FAKE, cnt=FAKE, ws=FAKE, nws=0, st=None)
+    a.update(kw)
+    return ops.lib().spark_prefill_prune(a["q_win"], a["k"], a["B"], a["S"], a["N_q"], a["N_kv"], a["D"],
+                                         a["lam"], a["W"], a["qagg"], a["rec"], a["fc"], a["kp"], a["mask"],
+                                         a["A"], a["r"], a["cnt"], a["ws"], a["nws"], a["st"])
+
+
+def test_prefill_rejects_bad_arguments():
+    assert _prefill(B=0) == ops.EINVAL
+    assert _prefill(S=0) == ops.EINVAL
+    assert _prefill(W=0) == ops.EINVAL
+    assert _prefill(lam=1.2) == ops.EINVAL
+    assert _prefill(lam=float("nan")) == ops.EINVAL
+    assert _prefill(qagg=5) == ops.EINVAL
+    assert _prefill(rec=9) == ops.EINVAL
+    assert _prefill(N_q=30) == ops.EINVAL
+    assert _prefill(N_q=24) == ops.EUNSUPPORTED          # G = 3
+    assert _prefill(D=64) == ops.EUNSUPPORTED
+    assert _prefill(k=None) == ops.EINVAL
+    assert _prefill(mask=None) == ops.EINVAL
+    assert _prefill(kp=None) == ops.EINVAL               # T > 0 needs the packed store
+    assert _prefill(kp=MIS) == ops.EALIGN
+    assert _prefill(ws=FAKE + 16) == ops.EALIGN
+    assert _prefill(nws=16) == ops.ENOSPACE
+
+
+def _decode(**kw):
+    a = dict(q=FAKE, kp=FAKE, mask=FAKE, v=FAKE, r=FAKE, B=1, S=64, N_q=32, N_kv=8, D=128, lam=0.5,
+             scale=0.0, splits=0, out=FAKE, ws=FAKE, nws=0, st=None)
+    a.update(kw)
+    return ops.lib().spark_decode_attn(a["q"], a["kp"], a["mask"], a["v"], a["r"], a["B"], a["S"], a["N_q"],
+                                       a["N_kv"], a["D"], a["lam"], a["scale"], a["splits"], a["out"], a["ws"],
+                                       a["nws"], a["st"])
+
+
+def test_decode_rejects_bad_arguments():
+    assert _decode(S=0) == ops.EINVAL
+    assert _decode(splits=-1) == ops.EINVAL
+    assert _decode(lam=-0.5) == ops.EINVAL
+    assert _decode(scale=float("nan")) == ops.EINVAL
+    assert _decode(N_kv=5) == ops.EINVAL
+    assert _decode(N_q=16, N_kv=1) == ops.EUNSUPPORTED   # G = 16
+    assert _decode(D=256) == ops.EUNSUPPORTED
+    assert _decode(B=200, N_kv=8) == ops.EUNSUPPORTED    # more (b, kv head) pairs than counters
+    assert _decode(v=None) == ops.EINVAL
+    assert _decode(out=None) == ops.EINVAL
+    assert _decode(q=MIS) == ops.EALIGN
+    assert _decode(ws=FAKE + 64) == ops.EALIGN
+    assert _decode(nws=ops.DECODE_COUNTER_BYTES) == ops.ENOSPACE
+
+
+def test_stats_rejects_bad_arguments():
+    l = ops.lib()
+
+    def call(**kw):
+        a = dict(kp=FAKE, mask=FAKE, A=FAKE, kd=None, B=1, S=64, N_kv=8, D=128, lam=0.5, rec=0, fc=0.0,
+                 r=FAKE, cnt=None, ws=FAKE, nws=0)
+        a.update(kw)
+        return l.spark_stats(a["kp"], a["mask"], a["A"], a["kd"], a["B"], a["S"], a["N_kv"], a["D"], a["lam"],
+                             a["rec"], a["fc"], a["r"], a["cnt"], a["ws"], a["nws"], None)
+    assert call(rec=3) == ops.EINVAL                     # pruned-score mean needs the dense keys
+    assert call(kp=None) == ops.EINVAL
+    assert call(rec=4) == ops.EINVAL
+    assert call(D=96) == ops.EUNSUPPORTED
+    assert call(mask=MIS) == ops.EALIGN
+    assert call() == ops.ENOSPACE
+
+
+def test_decode_ws_init_checks():
+    l = ops.lib()
+    assert l.spark_decode_ws_init(None, 4096, None) == ops.EINVAL
+    assert l.spark_decode_ws_init(FAKE + 4, 4096, None) == ops.EALIGN
+    assert l.spark_decode_ws_init(FAKE, 100, None) == ops.ENOSPACE
