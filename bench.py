@@ -1,0 +1,399 @@
+"""Benchmark: SparK decode attention over the pruned key cache on one MI355X.
+
+One step = the whole hot path on one LLaMA-3.1-8B-shaped layer (B=1,
+S=32768, 32 query heads, 8 KV heads, D=128, window 32, lambda=0.5):
+prefill prune (channel energy, per-token top-T, packing, recovery
+statistics) followed by 64 decode steps. The decode steps rotate over R
+replicas of the pruned cache (packed K, mask, V, r) totalling >= 768 MB, so
+the 256 MB Infinity Cache cannot serve them and the reported bandwidth is
+HBM bandwidth. Decode launches are replayed from a HIP graph (one graph per
+step, 64 kernels); prefill is a second graph.
+
+value = effective decode bytes / decode time, where the effective bytes of a
+decode step are B*N_kv*S*(2T + 16 + 2D): packed K, the 16-byte mask and dense
+V. Inputs are resident in HBM before timing starts.
+
+Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "SparK decode attn effective KV GB/s & %HBM peak, S=32K, λ=0.5/0.8"
+HBM_PEAK_GBS = 8000.0
+MALL_DEFEAT_BYTES = 768e6
+DECODE_SOURCES = ["sparse_decode_attention_amd/csrc/decode.hip", "sparse_decode_attention_amd/csrc/kernels.h",
+                  "sparse_decode_attention_amd/csrc/common.h", "sparse_decode_attention_amd/csrc/spark_abi.hip"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_kernel_llama8b_s32k_traffic.md")
+
+
+def decode_source_sha() -> str:
+    h = hashlib.sha256()
+    for p in DECODE_SOURCES:
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str):
+    """Per-launch HBM bytes of the decode kernel from the committed rocprofv3
+    counter summary, if it was taken on the current kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and line.strip().startswith("- "):
+            k, v = line.strip()[2:].split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != decode_source_sha() or kv.get("workload") != workload:
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def effective_decode_bytes(w, T):
+    return w.B * w.n_kv * w.S * (2 * T + 16 + 2 * w.D)
+
+
+def effective_prefill_bytes(w, T):
+    return w.B * w.n_kv * w.S * (2 * w.D + 2 * T + 16)
+
+
+def run_leg(w, steps, warmup, rotate=True, seed=0, verbose=True):
+    import torch
+    from sparse_decode_attention_amd import gen, ops
+
+    dev = torch.device("cuda:0")
+    T = ops.num_kept(w.D, w.lam)
+    x = gen.torch_layer(w, dev, seed=seed, steps=w.steps)
+    dec_bytes = effective_decode_bytes(w, T)
+    R = max(1, int(-(-MALL_DEFEAT_BYTES // dec_bytes))) if rotate else 1
+    # replica 0 is written by the prefill every step; replicas 1..R-1 hold copies of it
+    reps = []
+    for i in range(R):
+        reps.append({
+            "k_packed": torch.empty((w.B, w.n_kv, w.S, T), dtype=torch.bfloat16, device=dev),
+            "mask": torch.empty((w.B, w.n_kv, w.S, 4), dtype=torch.int32, device=dev),
+            "chan_energy": torch.empty((w.B, w.n_kv, w.D), dtype=torch.float32, device=dev),
+            "r": torch.empty((w.B, w.n_kv, w.D), dtype=torch.float32, device=dev),
+            "cnt": torch.empty((w.B, w.n_kv, w.D), dtype=torch.int32, device=dev),
+            "v": x["v"] if i == 0 else x["v"].clone(),
+        })
+    outs = torch.empty((w.steps, w.B, w.n_q, w.D), dtype=torch.float32, device=dev)
+
+    def prefill():
+        ops.prefill_prune(x["q_win"], x["k"], w.n_kv, w.lam, out=reps[0])
+
+    def decode_all():
+        for s in range(w.steps):
+            rp = reps[s % R]
+            ops.decode_attn(x["q_dec"][s], rp["k_packed"], rp["mask"], rp["v"], rp["r"], w.lam, out=outs[s])
+
+    # eager pass: fills every replica and allocates the cached workspaces
+    prefill()
+    for rp in reps[1:]:
+        for n in ("k_packed", "mask", "chan_energy", "r", "cnt"):
+            rp[n].copy_(reps[0][n])
+    decode_all()
+    torch.cuda.synchronize()
+    eager = outs.clone()
+
+    s_cap = torch.cuda.Stream(dev)
+    s_cap.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(s_cap):
+        g_pre, g_dec = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_pre, stream=s_cap):
+            prefill()
+        with torch.cuda.graph(g_dec, stream=s_cap):
+            decode_all()
+    torch.cuda.current_stream(dev).wait_stream(s_cap)
+    torch.cuda.synchronize()
+
+    # graph replays must reproduce the eager results bit for bit
+    for _ in range(2):
+        g_pre.replay()
+        g_dec.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(outs, eager):
+            raise RuntimeError("graph replay differs from eager decode")
+
+    st = torch.cuda.current_stream(dev)
+    for _ in range(warmup):
+        g_pre.replay()
+        g_dec.replay()
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(st)
+        g_pre.replay()
+        ev[i][1].record(st)
+        g_dec.replay()
+        ev[i][2].record(st)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    if not torch.equal(outs, eager):
+        raise RuntimeError("timed replay differs from eager decode")
+
+    pre_ms = sorted(e[0].elapsed_time(e[1]) for e in ev)
+    dec_ms = sorted(e[1].elapsed_time(e[2]) for e in ev)
+    step_ms = sorted(e[0].elapsed_time(e[2]) for e in ev)
+    med = lambda a: a[len(a) // 2]
+    dec_launch_us = med(dec_ms) * 1e3 / w.steps
+    res = {
+        "T": T, "replicas": R, "replica_bytes": dec_bytes,
+        "decode_bytes_per_step": dec_bytes,
+        "decode_us_per_launch": dec_launch_us,
+        "decode_GBps": dec_bytes / (dec_launch_us * 1e-6) / 1e9,
+        "prefill_us": med(pre_ms) * 1e3,
+        "prefill_GBps": effective_prefill_bytes(w, T) / (med(pre_ms) * 1e-3) / 1e9,
+        "step_ms_median": med(step_ms),
+        "step_ms_mean": sum(step_ms) / len(step_ms),
+        "wall_s": wall,
+        "tokens_heads_per_s": w.B * w.S * w.n_q / (dec_launch_us * 1e-6),
+        "x": x, "reps": reps,
+    }
+    return res
+
+
+def stream_ceiling(nbytes: int, reps: int = 7, blocks: int = 512) -> float:
+    """GB/s of a plain streaming read (spark_read_stream) of `nbytes`, rotated
+    over >= 768 MB of buffers like the decode replicas: the practical HBM read
+    rate at this working-set size, measured on the same device."""
+    import torch
+    from sparse_decode_attention_amd import ops
+    dev = torch.device("cuda:0")
+    n = (nbytes // 16) * 8
+    R = max(2, int(-(-MALL_DEFEAT_BYTES // nbytes)))
+    xs = [torch.zeros(n, dtype=torch.bfloat16, device=dev) for _ in range(R)]
+    sink = torch.zeros(blocks, dtype=torch.int32, device=dev)
+
+    def run():
+        for xx in xs:
+            ops.read_stream(xx, sink, blocks)
+    run()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            run()
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e-3 / R)
+    ts.sort()
+    return n * 2 / ts[len(ts) // 2] / 1e9
+
+
+def cpu_baseline(w, x, reps, T):
+    """The oracle (NumPy, float64) on the host cores: one prefill prune of the
+    layer and 3 decode steps at full shape."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from sparse_decode_attention_amd import gen
+
+    def host(t):
+        return gen.bf16_bits_to_f32(t.view(torch.int16).cpu().numpy().view(np.uint16))
+
+    q_win, k, v = host(x["q_win"]), host(x["k"]), host(x["v"])
+    q_dec = host(x["q_dec"][:3])
+    t0 = time.perf_counter()
+    pr = oracle.prune(q_win, k, w.n_kv, w.lam)
+    r, _ = oracle.stats(k, pr["mask"], pr["A"])
+    t1 = time.perf_counter()
+    n_dec = 3
+    for s in range(n_dec):
+        oracle.decode_attn(q_dec[s], pr["packed"], pr["mask"], v, r)
+    t2 = time.perf_counter()
+    # the oracle's masks must match the GPU's (a cheap end-to-end sanity check)
+    gpu_words = reps[0]["mask"].cpu().numpy().view(np.uint32)
+    if not np.array_equal(gpu_words, pr["words"]):
+        raise RuntimeError("GPU masks differ from the oracle's")
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas = 1
+    dec_s = (t2 - t1) / n_dec
+    return {
+        "value": effective_decode_bytes(w, T) / dec_s / 1e9, "unit": "GB/s", "cores": blas, "kind": "oracle",
+        "sample": f"{w.name}: 1 prefill prune+stats ({t1 - t0:.1f} s) and {n_dec} full-shape decode steps "
+                  f"({dec_s:.2f} s each) in NumPy float64; decode effective bytes / decode time; "
+                  f"BLAS threads {blas}, elementwise NumPy single-threaded, host has {os.cpu_count()} CPUs",
+        "prefill_s": t1 - t0, "decode_s_per_step": dec_s,
+    }
+
+
+def summarize(kt_dir: str, fetch_dir: str, write_dir: str, workload: str, command: str) -> str:
+    """Write profiles/decode_kernel_llama8b_s32k_traffic.md from rocprofv3
+    output: kernel-trace stats (average duration of the decode kernel) and the
+    FETCH_SIZE / WRITE_SIZE passes (KiB per dispatch), scaled by what the same
+    counters read for the plain 256 MiB device copy the run also performs."""
+    import csv
+    import glob
+
+    def rows(d, name):
+        out = []
+        for f in glob.glob(os.path.join(d, "**", name), recursive=True):
+            out += list(csv.DictReader(open(f)))
+        return out
+
+    stats = rows(kt_dir, "*kernel_stats.csv")
+    dec = [r for r in stats if "decode_fast_kernel" in r["Name"] or "decode_kernel" in r["Name"]]
+    dec.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    avg_ns = float(dec[0]["AverageNs"])
+    kname = dec[0]["Name"]
+
+    def per_dispatch(d, counter):
+        vals, calib = [], []
+        for r in rows(d, "*counter_collection.csv"):
+            if r["Counter_Name"] != counter:
+                continue
+            if r["Kernel_Name"] == kname:
+                vals.append(float(r["Counter_Value"]))
+            if "copyBuffer" in r["Kernel_Name"] and int(r["Grid_Size"]) >= 131072:
+                calib.append(float(r["Counter_Value"]))
+        return sum(vals) / len(vals), max(calib)
+
+    f_kib, f_cal = per_dispatch(fetch_dir, "FETCH_SIZE")
+    w_kib, w_cal = per_dispatch(write_dir, "WRITE_SIZE")
+    copy_bytes = 256 << 20
+    f_scale, w_scale = copy_bytes / (f_cal * 1024), copy_bytes / (w_cal * 1024)
+    fetch_b, write_b = f_kib * 1024 * f_scale, w_kib * 1024 * w_scale
+    text = f"""# Decode kernel: time and HBM traffic, {workload}
+
+Command (rocprofv3, three runs; the GPU-side numbers below come from it):
+
+    {command}
+
+- kernel: {kname}
+- workload: {workload}
+- source_sha256: {decode_source_sha()}
+- avg_duration_ns: {avg_ns:.0f}
+- fetch_kib_per_dispatch_raw: {f_kib:.1f}
+- write_kib_per_dispatch_raw: {w_kib:.1f}
+- calibration: a 256 MiB device copy (__amd_rocclr_copyBuffer) reads FETCH_SIZE {f_cal:.0f} KiB and WRITE_SIZE {w_cal:.0f} KiB, so the scale factors are fetch x{f_scale:.3f}, write x{w_scale:.3f}
+- fetch_bytes_per_launch: {fetch_b:.0f}
+- write_bytes_per_launch: {write_b:.0f}
+- hbm_bytes_per_launch: {fetch_b + write_b:.0f}
+"""
+    return text
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama8b_s32k_l05")
+    ap.add_argument("--second", default="llama8b_s32k_l08", help="second reported workload ('' to skip)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--warm", action="store_true", help="also report a run without replica rotation")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="run a plain device copy of this size after the legs (counter calibration)")
+    ap.add_argument("--summarize", nargs=3, metavar=("KT_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="write the rocprofv3 traffic summary under profiles/ and exit")
+    ap.add_argument("--summary-command", default="", help="command line recorded in the summary")
+    args = ap.parse_args()
+    if args.summarize:
+        txt = summarize(*args.summarize, args.workload, args.summary_command)
+        open(TRAFFIC_FILE, "w").write(txt)
+        print(txt)
+        return
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the SparK hot path here is a single-GPU kernel set; "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from sparse_decode_attention_amd import ops
+    from sparse_decode_attention_amd.configs import WORKLOADS
+
+    ops.lib()
+    w = WORKLOADS[args.workload]
+    print(f"bench: {w.name} steps={args.steps} warmup={args.warmup}", file=sys.stderr, flush=True)
+    main_leg = run_leg(w, args.steps, args.warmup)
+    T = main_leg["T"]
+    line = {
+        "metric": METRIC,
+        "value": round(main_leg["decode_GBps"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(main_leg["step_ms_median"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "S": w.S, "N_q": w.n_q, "N_kv": w.n_kv, "D": w.D,
+                   "window": w.window, "lambda": w.lam, "T": T, "decode_steps_per_step": w.steps,
+                   "storage": "bf16 q/k/v/packed, uint32 mask, fp32 r/out", "replicas": main_leg["replicas"]},
+        "pct_hbm_peak": round(100 * main_leg["decode_GBps"] / HBM_PEAK_GBS, 2),
+        "decode_us_per_launch": round(main_leg["decode_us_per_launch"], 3),
+        "tokens_heads_per_s": main_leg["tokens_heads_per_s"],
+        "prefill": {"us": round(main_leg["prefill_us"], 2), "GBps": round(main_leg["prefill_GBps"], 1),
+                    "bytes": effective_prefill_bytes(w, T)},
+    }
+    traffic = read_traffic(w.name)
+    dec_bytes = main_leg["decode_bytes_per_step"]
+    line["roofline"] = {"bound": "hbm", "achieved": round(main_leg["decode_GBps"], 2), "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": round(main_leg["decode_GBps"] / HBM_PEAK_GBS, 4),
+                        "traffic": traffic, "kernel": f"decode_fast_kernel<4, {T}>",
+                        "algorithmic_bytes_per_launch": dec_bytes}
+    ceil = stream_ceiling(dec_bytes)
+    line["stream_ceiling"] = {"GBps": round(ceil, 1), "bytes": dec_bytes,
+                              "frac_of_ceiling": round(main_leg["decode_GBps"] / ceil, 4),
+                              "what": "spark_read_stream of the same bytes, rotated like the decode replicas"}
+    if args.second:
+        w2 = WORKLOADS[args.second]
+        print(f"bench: {w2.name}", file=sys.stderr, flush=True)
+        leg2 = run_leg(w2, args.steps, args.warmup)
+        line["second"] = {"workload": w2.name, "lambda": w2.lam, "T": leg2["T"],
+                          "GBps": round(leg2["decode_GBps"], 2),
+                          "pct_hbm_peak": round(100 * leg2["decode_GBps"] / HBM_PEAK_GBS, 2),
+                          "decode_us_per_launch": round(leg2["decode_us_per_launch"], 3),
+                          "prefill_GBps": round(leg2["prefill_GBps"], 1), "replicas": leg2["replicas"]}
+        del leg2
+    if args.warm:
+        wl = run_leg(w, args.steps, args.warmup, rotate=False)
+        line["warm_single_replica_GBps"] = round(wl["decode_GBps"], 2)
+        del wl
+    if args.calib_copy_mb:
+        n = args.calib_copy_mb * (1 << 20)
+        a = torch.empty(n // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        line["calib_copy_bytes"] = n
+    if not args.no_cpu:
+        print("bench: cpu oracle baseline", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(w, main_leg["x"], main_leg["reps"], T)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -124,7 +124,7 @@ int spark_stats(const void* k_packed, const uint32_t* mask, const float* chan_en
  *  v        bf16 [B][N_kv][S][D]
  *  scale    softmax scale; <= 0 selects 1/sqrt(D)
  *  splits   sequence splits per (b, KV head); 0 lets the library choose;
- *           at most ceil(S / 64)
+ *           larger values are clamped to min(256, ceil(S / 64))
  *  out      fp32 [B][N_q][D]
  * No causal mask: the query attends to every cached token. fp32 arithmetic
  * on bf16 inputs. The first SPARK_DECODE_COUNTER_BYTES of ws hold completion
@@ -139,6 +139,12 @@ int spark_decode_attn(const void* q, const void* k_packed, const uint32_t* mask,
 /* Zero the decode completion counters of a workspace (a fill kernel on
  * `stream`; safe to record in a HIP graph). */
 int spark_decode_ws_init(void* ws, size_t ws_bytes, void* stream);
+
+/* Diagnostic, not part of SparK: read `bytes` (a multiple of 16, 16-byte
+ * aligned) from device memory with `blocks` x 256 threads, folding the data
+ * into sink[0 .. blocks-1] (uint32, XOR-accumulated). Used to measure the
+ * practical HBM read bandwidth that decode is compared with. */
+int spark_read_stream(const void* src, size_t bytes, uint32_t* sink, int blocks, void* stream);
 
 #ifdef __cplusplus
 }

@@ -34,6 +34,29 @@ __device__ __forceinline__ float wave_sum(float x) {
     return x;
 }
 
+// Wave-wide max through DPP (no LDS traffic): butterfly inside each 16-lane
+// row, then the four row results combined from lanes 0, 16, 32, 48.
+__device__ __forceinline__ float dpp_row_max(float x) {
+    int v = __float_as_int(x);
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(v, v, 0xB1, 0xF, 0xF, false)));  // quad_perm 1,0,3,2
+    v = __float_as_int(x);
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(v, v, 0x4E, 0xF, 0xF, false)));  // quad_perm 2,3,0,1
+    v = __float_as_int(x);
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(v, v, 0x141, 0xF, 0xF, false))); // row_half_mirror
+    v = __float_as_int(x);
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(v, v, 0x140, 0xF, 0xF, false))); // row_mirror
+    return x;
+}
+__device__ __forceinline__ float wave_max_dpp(float x) {
+    x = dpp_row_max(x);
+    const int v = __float_as_int(x);
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(v, 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(v, 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(v, 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(v, 48));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
 // LDS written by some lanes of a wave and read by others: order the accesses
 // within the wave (no workgroup barrier needed).
 __device__ __forceinline__ void wave_lds_sync() {

@@ -5,21 +5,29 @@
 //
 // The score is evaluated in its sparse form
 //     q . k_hat_t = q . r + sum over kept j of q^j (k_tj - r_j),
-// so each token costs G*T multiply-adds instead of G*D, and the kept channel
-// indices come straight from the mask bits.
+// so each token costs G*T multiply-adds instead of G*D.
 //
 // Work split (flash-decoding style): grid = (nsplit, B*N_kv). A block of 4
 // waves owns `chunk` consecutive tokens of one (b, KV head) and all G query
 // heads of its group, so every byte of packed K, mask and V is read once per
-// step. Each wave walks 64-token tiles:
-//   * scores with one lane per token; the packed rows of the tile are staged
-//     in LDS with 16-byte loads and read back per lane;
-//   * online softmax (base-2, scale folded into q) with wave-wide max;
-//   * P.V with lane = (token mod 4, 8-channel slice of d): each lane issues
-//     16-byte V loads, 4 tokens per load instruction per wave.
-// Partials (m, l, acc) of the 4 waves are merged in LDS; the last block of a
-// (b, KV head) to finish (device-scope counter) merges all splits and writes
-// the fp32 output, then resets its counter to zero.
+// step. Each wave walks 64-token tiles, one lane per token for the scores:
+//   1. the tile's packed rows (16-byte loads, issued one tile ahead) are
+//      staged in LDS; rows whose dword count would be even are padded by one
+//      dword so that lanes reading "slot rho of their own row" hit distinct
+//      banks;
+//   2. each lane turns its mask into the list of table offsets of its T kept
+//      channels (a store-only loop over the set bits);
+//   3. a uniform loop over the T slots gathers q'_g and r for the slot's
+//      channel from an LDS table and accumulates q'_g (k - r): all lanes run
+//      the same trip count, so the loads of several slots are in flight
+//      together;
+//   4. online softmax (base 2, scale folded into q') with wave-wide max;
+//   5. P.V with lane = (token mod 4, 8-channel slice of d), 16-byte V loads
+//      issued before step 2 so they arrive during the score phase.
+// The 4 waves' (m, l, acc) are merged in LDS; the last block of a (b, KV head)
+// to finish (device-scope counter) merges all splits, writes the fp32 output
+// and resets its counter to zero. Writers never flush their L2: partials go
+// out through device-scope stores, and only the merging block invalidates.
 #include "common.h"
 #include "kernels.h"
 
@@ -30,22 +38,311 @@ namespace {
 template <int G>
 struct QRow { float v[G]; };
 
-}  // namespace
+// One channel of the decode table: q'_g for the G heads of the group, then r.
+// Entries are 16-byte aligned so q' is read with vector LDS loads.
+template <int G>
+struct alignas(16) TabEntry {
+    float q[G];
+    float r;
+};
 
-uint32_t decode_stage_bytes(int T) {
-    // 64 rows of T bf16 plus up to 7 elements of 16-byte misalignment, whole 16-byte chunks
-    const uint32_t elems = (uint32_t)DECODE_TILE * (uint32_t)T + 8u;
-    return ((elems * 2u) + 15u) & ~15u;
+// Split partials cross blocks that may run on different XCDs (separate L2s).
+// They are written with device-scope (sc1) stores, which complete at the
+// device coherence point without writing back the whole L2.
+__device__ __forceinline__ void store_dev(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-size_t decode_lds_bytes(int G, int T) {
-    const size_t tables = (size_t)128 * G * 4 + 128 * 4;
-    const size_t per_wave = (size_t)DECODE_TILE * G * 4 + decode_stage_bytes(T);
-    const size_t waves = DECODE_THREADS / 64;
-    const size_t combine = waves * ((size_t)2 * G + (size_t)G * 128) * 4;
-    const size_t dyn = waves * per_wave > combine + waves * (size_t)DECODE_TILE * G * 4
-                           ? waves * per_wave : combine + waves * (size_t)DECODE_TILE * G * 4;
-    return tables + dyn;
+int tab_stride_for(int G) {
+    switch (G) {
+        case 1: return (int)sizeof(TabEntry<1>);
+        case 2: return (int)sizeof(TabEntry<2>);
+        case 4: return (int)sizeof(TabEntry<4>);
+        default: return (int)sizeof(TabEntry<8>);
+    }
+}
+
+}  // namespace
+
+DecodeLayout decode_layout(int G, int T, int nsplit) {
+    DecodeLayout L{};
+    L.tab_stride = (uint32_t)tab_stride_for(G);
+    L.tab_bytes = 128u * L.tab_stride;
+    L.padded = (T > 0 && T % 2 == 0 && (T / 2) % 2 == 0) ? 1u : 0u;
+    L.half_T = (uint32_t)(T / 2);
+    L.magic = L.padded ? (uint32_t)((0x100000000ull + L.half_T - 1) / L.half_T) : 0u;
+    if (L.padded) {
+        L.row_bytes = (uint32_t)(2 * T + 4);
+        L.stage_bytes = (uint32_t)DECODE_TILE * L.row_bytes;
+    } else {
+        L.row_bytes = (uint32_t)(2 * T);
+        // 64 rows plus up to 7 elements of 16-byte misalignment, in whole 16-byte chunks
+        L.stage_bytes = ((((uint32_t)DECODE_TILE * (uint32_t)T + 8u) * 2u) + 15u) & ~15u;
+    }
+    L.list_bytes = (uint32_t)T * DECODE_TILE * 2u;
+    L.list_bytes = (L.list_bytes + 15u) & ~15u;
+    L.ptab_bytes = (uint32_t)DECODE_TILE * G * 4u;
+    L.wave_bytes = L.list_bytes + L.stage_bytes + L.ptab_bytes;
+    const uint32_t waves = DECODE_THREADS / 64;
+    const uint32_t combine = waves * (2u * G + (uint32_t)G * 128u) * 4u;
+    const uint32_t merge = (((uint32_t)nsplit * 3u * G + G + 3u) & ~3u) * 4u + (uint32_t)DECODE_THREADS * 16u;
+    uint32_t dyn = waves * L.wave_bytes;
+    if (combine > dyn) dyn = combine;
+    if (merge > dyn) dyn = merge;
+    L.lds_bytes = L.tab_bytes + dyn;
+    return L;
+}
+
+// Merge the (m, l, acc) partials of all splits of one (b, KV head) and write
+// out = acc / l. Runs in the block that finished last, after an agent-scope
+// acquire (one L2 invalidate in this block only), so plain vector loads see
+// the partials that other blocks published with device-scope stores. All
+// loads are issued in batches; every reduction has a fixed order, so the
+// output does not depend on which block merges.
+template <int G, int NT>
+__device__ void merge_splits(const DecodeArgs& a, int bh, int b, int h, float* lds) {
+    constexpr int NQ = G * 32;                       // float4 per split partial
+    constexpr int NPH = NT / NQ;                     // threads per float4 column
+    constexpr int NW = NT / 64;
+    constexpr int BATCH = 8;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, L = tid & 63;
+    const int ns = a.nsplit;
+    float* sml = lds;                                // [ns][2][G]
+    float* sf = sml + ns * 2 * G;                    // [ns][G] scale of each split
+    float* sL = sf + ns * G;                         // [G] total l
+    float4* sred = reinterpret_cast<float4*>(lds + ((ns * 3 * G + G + 3) & ~3));  // [NPH][NQ]
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    const float* ml_bh = a.part_ml + (size_t)bh * ns * 2 * G;
+    for (int i = tid; i < ns * 2 * G; i += NT) sml[i] = ml_bh[i];
+    __syncthreads();
+    // per head: M = max over splits, then the split scales and L = sum l * scale
+    for (int g = wave; g < G; g += NW) {
+        float mx = -INFINITY;
+        for (int sp = L; sp < ns; sp += 64) mx = fmaxf(mx, sml[sp * 2 * G + g]);
+        const float M = wave_max_dpp(mx);
+        float ls = 0.f;
+        for (int sp = L; sp < ns; sp += 64) {
+            const float m = sml[sp * 2 * G + g];
+            const float f = (m == -INFINITY) ? 0.f : exp2f(m - M);
+            sf[sp * G + g] = f;
+            ls += sml[sp * 2 * G + G + g] * f;
+        }
+        ls = wave_sum(ls);
+        if (L == 0) sL[g] = ls;
+    }
+    __syncthreads();
+    const int q = tid % NQ, ph = tid / NQ;
+    const int g = q / 32;
+    const float4* acc_bh = reinterpret_cast<const float4*>(a.part_acc + (size_t)bh * ns * G * 128);
+    float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int sp0 = ph; sp0 < ns; sp0 += NPH * BATCH) {
+        float4 v[BATCH];
+#pragma unroll
+        for (int k = 0; k < BATCH; ++k) {
+            const int sp = sp0 + k * NPH;
+            v[k] = sp < ns ? acc_bh[(size_t)sp * NQ + q] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int k = 0; k < BATCH; ++k) {
+            const int sp = sp0 + k * NPH;
+            const float f = sp < ns ? sf[sp * G + g] : 0.f;
+            x.x += v[k].x * f; x.y += v[k].y * f; x.z += v[k].z * f; x.w += v[k].w * f;
+        }
+    }
+    sred[ph * NQ + q] = x;
+    __syncthreads();
+    if (ph == 0) {
+        float4 t = sred[q];
+#pragma unroll
+        for (int p = 1; p < NPH; ++p) {
+            const float4 u = sred[p * NQ + q];
+            t.x += u.x; t.y += u.y; t.z += u.z; t.w += u.w;
+        }
+        const float inv = 1.0f / sL[g];
+        float4* o = reinterpret_cast<float4*>(a.out + ((size_t)b * a.N_q + (size_t)h * G) * 128);
+        o[q] = make_float4(t.x * inv, t.y * inv, t.z * inv, t.w * inv);
+    }
+}
+
+// Packed rows and mask of one tile, loaded one tile ahead into registers.
+struct TileMeta {
+    uint4 pk[8];     // up to 8 16-byte chunks per lane (512 per tile)
+    uint4 mw;        // this lane's token mask
+    size_t ea;       // first loaded element (multiple of 8)
+    int shift;       // elements between ea and the tile's first element
+    int nchunks;     // 16-byte chunks covering the tile
+};
+
+__device__ __forceinline__ uint4 load_chunk(const DecodeArgs& a, size_t ce) {
+    if (ce + 8 <= a.packed_elems) return *reinterpret_cast<const uint4*>(a.packed + ce);
+    uint16_t t[8];
+#pragma unroll
+    for (int x = 0; x < 8; ++x) t[x] = (ce + x < a.packed_elems) ? a.packed[ce + x] : 0;
+    return make_uint4(t[0] | ((uint32_t)t[1] << 16), t[2] | ((uint32_t)t[3] << 16),
+                      t[4] | ((uint32_t)t[5] << 16), t[6] | ((uint32_t)t[7] << 16));
+}
+
+__device__ __forceinline__ void issue_meta(const DecodeArgs& a, int bh, int t0, int nt, int L, TileMeta& m) {
+    const int T = a.T;
+    const size_t e0 = ((size_t)bh * a.S + t0) * (size_t)T;
+    m.ea = e0 & ~(size_t)7;
+    m.shift = (int)(e0 - m.ea);
+    m.nchunks = T > 0 ? (int)((e0 + (size_t)nt * T - m.ea + 7) >> 3) : 0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        const int c = L + 64 * u;
+        m.pk[u] = make_uint4(0, 0, 0, 0);
+        if (c < m.nchunks) m.pk[u] = load_chunk(a, m.ea + (size_t)c * 8);
+    }
+    m.mw = make_uint4(0, 0, 0, 0);
+    if (L < nt) m.mw = *reinterpret_cast<const uint4*>(a.mask + ((size_t)bh * a.S + t0 + L) * 4);
+}
+
+// Write one 16-byte chunk c of the tile into the staged rows.
+__device__ __forceinline__ void stage_chunk(const DecodeLayout& lay, const TileMeta& m, int c, uint4 x,
+                                            unsigned char* stage, int tile_dwords) {
+    if (!lay.padded) {
+        reinterpret_cast<uint4*>(stage)[c] = x;
+        return;
+    }
+    const uint32_t w4[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int u = 4 * c + i - (m.shift >> 1);          // dword index within the tile (T even)
+        if (u >= 0 && u < tile_dwords) {
+            const uint32_t row = __umulhi((uint32_t)u, lay.magic);
+            reinterpret_cast<uint32_t*>(stage)[u + row] = w4[i];
+        }
+    }
+}
+
+// Online softmax over one 64-token tile (base 2): lane L holds the scores of
+// token L for the G heads; p goes to ptab[L][g] and the running (m, l) and
+// the P.V accumulators are rescaled.
+template <int G>
+__device__ __forceinline__ void softmax_tile(const float (&s)[G], float (&m_run)[G], float (&l_run)[G],
+                                             float (&acc)[G][8], float* ptab, int L) {
+    float alpha[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        const float mt = wave_max_dpp(s[g]);
+        const float mn = fmaxf(m_run[g], mt);
+        alpha[g] = exp2f(m_run[g] - mn);
+        const float p = exp2f(s[g] - mn);
+        l_run[g] = l_run[g] * alpha[g] + p;
+        m_run[g] = mn;
+        ptab[L * G + g] = p;
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[g][e] *= alpha[g];
+}
+
+// P.V of one tile: lane (tau, oct) holds V rows 4i+tau, d in [8 oct, 8 oct + 8).
+template <int G>
+__device__ __forceinline__ void pv_tile(const uint4 (&vr)[16], const float* ptab, float (&acc)[G][8], int tau) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int tok = 4 * i + tau;
+        const QRow<G> p = *reinterpret_cast<const QRow<G>*>(ptab + tok * G);
+        const uint32_t w4[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
+        float vf[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            vf[2 * e] = bf16_lo(w4[e]);
+            vf[2 * e + 1] = bf16_hi(w4[e]);
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(p.v[g], vf[e], acc[g][e]);
+    }
+}
+
+// V rows of one tile for the P.V layout (rows past the tile end read as 0).
+__device__ __forceinline__ void load_v_tile(const uint16_t* vbh, int t0, int nt, int tau, int oct, uint4 (&vr)[16]) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int tok = 4 * i + tau;
+        vr[i] = make_uint4(0, 0, 0, 0);
+        if (tok < nt) vr[i] = *reinterpret_cast<const uint4*>(vbh + (size_t)(t0 + tok) * 128 + oct * 8);
+    }
+}
+
+// End of a decode block: reduce each wave's (m, l, acc) over its token phases
+// and lanes, merge the waves in LDS, publish the block's split partial, and,
+// in the last block of the (b, KV head) to finish, merge all splits.
+template <int G, int NT>
+__device__ void finish_block(const DecodeArgs& a, float (&m_run)[G], float (&l_run)[G], float (&acc)[G][8],
+                             unsigned char* wbase, int bh, int b, int h, int split) {
+    constexpr int NW = NT / 64;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int L = tid & 63;
+    const int oct = L & 15;
+    // ---- wave partial: reduce acc over the 4 token phases, l over lanes
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float x = acc[g][e];
+            x += __shfl_xor(x, 16, 64);
+            x += __shfl_xor(x, 32, 64);
+            acc[g][e] = x;
+        }
+        l_run[g] = wave_sum(l_run[g]);
+    }
+    __syncthreads();   // per-wave regions are free now: reuse them for the block merge
+    float* wm = reinterpret_cast<float*>(wbase);               // [NW][G]
+    float* wl = wm + NW * G;                                   // [NW][G]
+    float* wacc = wl + NW * G;                                 // [NW][G][128]
+    if (L < 16) {
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) wacc[(wave * G + g) * 128 + oct * 8 + e] = acc[g][e];
+    }
+    if (L == 0) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) { wm[wave * G + g] = m_run[g]; wl[wave * G + g] = l_run[g]; }
+    }
+    __syncthreads();
+
+    float* pml = a.part_ml + ((size_t)bh * a.nsplit + split) * 2 * G;
+    float* pacc = a.part_acc + ((size_t)bh * a.nsplit + split) * G * 128;
+    for (int i = tid; i < G * 128; i += NT) {
+        const int g = i >> 7, d = i & 127;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, wm[w * G + g]);
+        float x = 0.f, l = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const float f = (wm[w * G + g] == -INFINITY) ? 0.f : exp2f(wm[w * G + g] - M);
+            x += wacc[(w * G + g) * 128 + d] * f;
+            l += wl[w * G + g] * f;
+        }
+        store_dev(pacc + i, x);
+        if (d == 0) { store_dev(pml + g, M); store_dev(pml + G + g, l); }
+    }
+
+    // ---- last block of this (b, KV head) merges all splits.
+    // Every wave waits until its device-scope partial stores have completed,
+    // then the block barrier, then one counter increment: a block that sees
+    // the final count therefore sees every split's partial at device scope.
+    __shared__ int s_last;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) {
+        const uint32_t prev = __hip_atomic_fetch_add(a.counters + bh, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = (prev == (uint32_t)(a.nsplit - 1));
+    }
+    __syncthreads();
+    if (!s_last) return;
+    merge_splits<G, NT>(a, bh, b, h, reinterpret_cast<float*>(wbase));
+    if (tid == 0) __hip_atomic_store(a.counters + bh, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int G>
@@ -53,10 +350,9 @@ __global__ void __launch_bounds__(DECODE_THREADS)
 decode_kernel(const DecodeArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr int NW = DECODE_THREADS / 64;
-    float* qtab = reinterpret_cast<float*>(smem);              // [128][G], scaled by qscale
-    float* rtab = qtab + 128 * G;                              // [128]
-    float* ptab_all = rtab + 128;                              // [NW][64][G]
-    unsigned char* stage_all = reinterpret_cast<unsigned char*>(ptab_all + NW * DECODE_TILE * G);
+    const DecodeLayout& lay = a.lay;
+    unsigned char* tab = smem;                                 // [128] x tab_stride: q'_0..q'_{G-1}, r
+    unsigned char* wbase = smem + lay.tab_bytes;
 
     const int bh = blockIdx.y;
     const int split = blockIdx.x;
@@ -66,25 +362,31 @@ decode_kernel(const DecodeArgs a) {
     const int wave = tid >> 6;
     const int L = tid & 63;
     const int S = a.S, T = a.T;
+    constexpr uint32_t TAB = (uint32_t)sizeof(TabEntry<G>);
+    const bool even_T = (T % 2) == 0;
 
-    // ---- tables: q of the G heads (scaled) and r
+    // ---- table of q' (q * scale * log2 e) and r per channel
     for (int i = tid; i < 128 * G; i += DECODE_THREADS) {
         const int g = i >> 7, j = i & 127;
         const uint16_t qb = a.q[((size_t)b * a.N_q + (size_t)h * G + g) * 128 + j];
-        qtab[j * G + g] = bf16_to_f32(qb) * a.qscale;
+        reinterpret_cast<TabEntry<G>*>(tab)[j].q[g] = bf16_to_f32(qb) * a.qscale;
     }
-    if (tid < 128) rtab[tid] = a.r[(size_t)bh * 128 + tid];
+    if (tid < 128) reinterpret_cast<TabEntry<G>*>(tab)[tid].r = a.r[(size_t)bh * 128 + tid];
+
+    uint16_t* lst = reinterpret_cast<uint16_t*>(wbase + (size_t)wave * lay.wave_bytes);     // [T][64]
+    unsigned char* stage = wbase + (size_t)wave * lay.wave_bytes + lay.list_bytes;
+    float* ptab = reinterpret_cast<float*>(stage + lay.stage_bytes);                      // [64][G]
+    // every list entry holds a valid table offset from the start
+    for (int rho = 0; rho < T; ++rho) lst[rho * 64 + L] = 0;
     __syncthreads();
 
-    // c_g = q'_g . r (the score of an all-pruned key)
+    // c_g = q'_g . r: the score of a key whose channels are all pruned
     float cq[G];
 #pragma unroll
-    for (int g = 0; g < G; ++g)
-        cq[g] = wave_sum(qtab[L * G + g] * rtab[L] + qtab[(L + 64) * G + g] * rtab[L + 64]);
-
-    float* ptab = ptab_all + wave * DECODE_TILE * G;
-    unsigned char* stage = stage_all + (size_t)wave * a.lds_stage_bytes;
-    const uint16_t* stage16 = reinterpret_cast<const uint16_t*>(stage);
+    for (int g = 0; g < G; ++g) {
+        const TabEntry<G>* te = reinterpret_cast<const TabEntry<G>*>(tab);
+        cq[g] = wave_sum(te[L].q[g] * te[L].r + te[L + 64].q[g] * te[L + 64].r);
+    }
 
     const int blk_begin = split * a.chunk;
     const int blk_end = min(S, blk_begin + a.chunk);
@@ -103,216 +405,352 @@ decode_kernel(const DecodeArgs a) {
     }
 
     const uint16_t* vbh = a.v + (size_t)bh * S * 128;
-    const uint32_t* mbh = a.mask + (size_t)bh * S * 4;
+
+    TileMeta meta;
+    if (wave < ntiles) {
+        const int t0 = blk_begin + wave * DECODE_TILE;
+        issue_meta(a, bh, t0, min(DECODE_TILE, blk_end - t0), L, meta);
+    }
 
     for (int tile = wave; tile < ntiles; tile += NW) {
         const int t0 = blk_begin + tile * DECODE_TILE;
         const int nt = min(DECODE_TILE, blk_end - t0);
 
-        // -- loads: packed rows (to LDS), masks, V
-        const size_t e0 = ((size_t)bh * S + t0) * (size_t)T;
-        const size_t ea = e0 & ~(size_t)7;
-        const int shift = (int)(e0 - ea);
-        const size_t e1 = e0 + (size_t)nt * T;
-        const int nchunks = (int)((e1 - ea + 7) >> 3);
-        uint4 pk[4];
-        int npk = 0;
+        // -- 1. stage this tile's packed rows (loaded one tile ahead)
         if (T > 0) {
+            const int tile_dwords = (nt * T) >> 1;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
+            for (int u = 0; u < 8; ++u) {
                 const int c = L + 64 * u;
-                pk[u] = make_uint4(0, 0, 0, 0);
-                if (c < nchunks) {
-                    const size_t ce = ea + (size_t)c * 8;
-                    if (ce + 8 <= a.packed_elems) {
-                        pk[u] = *reinterpret_cast<const uint4*>(a.packed + ce);
-                    } else {
-                        uint16_t tmp[8];
-#pragma unroll
-                        for (int x = 0; x < 8; ++x) tmp[x] = (ce + x < a.packed_elems) ? a.packed[ce + x] : 0;
-                        pk[u] = make_uint4(tmp[0] | ((uint32_t)tmp[1] << 16), tmp[2] | ((uint32_t)tmp[3] << 16),
-                                           tmp[4] | ((uint32_t)tmp[5] << 16), tmp[6] | ((uint32_t)tmp[7] << 16));
-                    }
-                }
+                if (c < meta.nchunks) stage_chunk(lay, meta, c, meta.pk[u], stage, tile_dwords);
             }
-            npk = 4;
+            for (int c = L + 512; c < meta.nchunks; c += 64)      // rows longer than 64 elements
+                stage_chunk(lay, meta, c, load_chunk(a, meta.ea + (size_t)c * 8), stage, tile_dwords);
         }
-        uint4 mw = make_uint4(0, 0, 0, 0);
-        if (L < nt) mw = *reinterpret_cast<const uint4*>(mbh + (size_t)(t0 + L) * 4);
+        const uint4 mw = meta.mw;
+        const int row_base = (lay.padded ? 0 : 2 * meta.shift) + L * (int)lay.row_bytes;
+
+        // -- V of this tile, then the next tile's packed rows and mask
         uint4 vr[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int tok = 4 * i + tau;
-            vr[i] = make_uint4(0, 0, 0, 0);
-            if (tok < nt) vr[i] = *reinterpret_cast<const uint4*>(vbh + (size_t)(t0 + tok) * 128 + oct * 8);
+        load_v_tile(vbh, t0, nt, tau, oct, vr);
+        if (tile + NW < ntiles) {
+            const int t1 = t0 + NW * DECODE_TILE;
+            issue_meta(a, bh, t1, min(DECODE_TILE, blk_end - t1), L, meta);
         }
 
-        // -- packed rows into LDS (chunks beyond the first 256 loaded in a loop)
-        if (npk) {
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int c = L + 64 * u;
-                if (c < nchunks) reinterpret_cast<uint4*>(stage)[c] = pk[u];
-            }
-            for (int c = L + 256; c < nchunks; c += 64) {
-                const size_t ce = ea + (size_t)c * 8;
-                uint4 x;
-                if (ce + 8 <= a.packed_elems) {
-                    x = *reinterpret_cast<const uint4*>(a.packed + ce);
-                } else {
-                    uint16_t tmp[8];
-                    for (int y = 0; y < 8; ++y) tmp[y] = (ce + y < a.packed_elems) ? a.packed[ce + y] : 0;
-                    x = make_uint4(tmp[0] | ((uint32_t)tmp[1] << 16), tmp[2] | ((uint32_t)tmp[3] << 16),
-                                   tmp[4] | ((uint32_t)tmp[5] << 16), tmp[6] | ((uint32_t)tmp[7] << 16));
-                }
-                reinterpret_cast<uint4*>(stage)[c] = x;
-            }
-        }
-        wave_lds_sync();
-
-        // -- scores, one lane per token
-        float s[G];
-#pragma unroll
-        for (int g = 0; g < G; ++g) s[g] = 0.f;
-        if (L < nt) {
-            const uint16_t* row = stage16 + shift + L * T;
-            int rho = 0;
+        // -- 2. list of kept channels (table byte offsets), slot-major [rho][lane]
+        {
+            int cnt = 0;
             const uint32_t words[4] = {mw.x, mw.y, mw.z, mw.w};
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
                 uint32_t m = words[w];
                 while (m) {
-                    const int j = 32 * w + __builtin_ctz(m);
+                    const uint32_t j = 32u * w + (uint32_t)__builtin_ctz(m);
                     m &= m - 1;
-                    const float e = bf16_to_f32(row[rho++]) - rtab[j];
-                    const QRow<G> qv = *reinterpret_cast<const QRow<G>*>(qtab + j * G);
-#pragma unroll
-                    for (int g = 0; g < G; ++g) s[g] = fmaf(qv.v[g], e, s[g]);
+                    lst[cnt * 64 + L] = (uint16_t)(j * TAB);
+                    ++cnt;
                 }
             }
-#pragma unroll
-            for (int g = 0; g < G; ++g) s[g] += cq[g];
-        } else {
-#pragma unroll
-            for (int g = 0; g < G; ++g) s[g] = -INFINITY;
         }
+        wave_lds_sync();
 
-        // -- online softmax (base 2)
-        float alpha[G];
+        // -- 3. scores, one lane per token, 8 slots per batch: the 8 list
+        //       entries, then the 8 table rows and packed values, are each
+        //       requested together before any of them is used
+        float s[G];
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            const float mt = wave_max(s[g]);
-            const float mn = fmaxf(m_run[g], mt);
-            alpha[g] = exp2f(m_run[g] - mn);
-            const float p = exp2f(s[g] - mn);
-            l_run[g] = l_run[g] * alpha[g] + p;
-            m_run[g] = mn;
-            ptab[L * G + g] = p;
+        for (int g = 0; g < G; ++g) s[g] = 0.f;
+        {
+            const uint16_t* lrow = lst + L;
+            const unsigned char* krow = stage + row_base;
+            const int T8 = T & ~7;
+            for (int rho = 0; rho < T8; rho += 8) {
+                uint32_t off[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) off[k] = lrow[(rho + k) * 64];
+                float kv[8];
+                if (even_T) {
+                    // rows start 4-byte aligned when T is even: two bf16 per dword read
+                    const uint32_t* k32 = reinterpret_cast<const uint32_t*>(krow + 2 * rho);
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const uint32_t two = k32[k];
+                        kv[2 * k] = bf16_lo(two);
+                        kv[2 * k + 1] = bf16_hi(two);
+                    }
+                } else {
+                    const uint16_t* k16 = reinterpret_cast<const uint16_t*>(krow + 2 * rho);
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) kv[k] = bf16_to_f32(k16[k]);
+                }
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const TabEntry<G>& te = *reinterpret_cast<const TabEntry<G>*>(
+                        __builtin_assume_aligned(tab + off[k], 16));
+                    const float e = kv[k] - te.r;
+#pragma unroll
+                    for (int g = 0; g < G; ++g) s[g] = fmaf(te.q[g], e, s[g]);
+                }
+            }
+            for (int rho = T8; rho < T; ++rho) {
+                const TabEntry<G>& te = *reinterpret_cast<const TabEntry<G>*>(
+                    __builtin_assume_aligned(tab + lrow[rho * 64], 16));
+                const float e = bf16_to_f32(*reinterpret_cast<const uint16_t*>(krow + 2 * rho)) - te.r;
+#pragma unroll
+                for (int g = 0; g < G; ++g) s[g] = fmaf(te.q[g], e, s[g]);
+            }
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g) s[g] = (L < nt) ? s[g] + cq[g] : -INFINITY;
+
+        // -- 4. online softmax (base 2)
+        softmax_tile<G>(s, m_run, l_run, acc, ptab, L);
+        wave_lds_sync();
+
+        // -- 5. P.V
+        pv_tile<G>(vr, ptab, acc, tau);
+        wave_lds_sync();
+    }
+
+    finish_block<G, DECODE_THREADS>(a, m_run, l_run, acc, wbase, bh, b, h, split);
+}
+
+// Mask and packed row of token t0 + min(L, nt - 1): lanes past the end of a
+// partial tile re-read the last valid row (their scores are discarded).
+template <int T>
+__device__ __forceinline__ void load_row(const DecodeArgs& a, int bh, int t0, int nt, int L,
+                                         uint4& mw, uint32_t (&kr)[(T + 1) / 2]) {
+    constexpr int NDW = (T + 1) / 2;
+    const size_t row = (size_t)bh * a.S + t0 + min(L, nt - 1);
+    mw = *reinterpret_cast<const uint4*>(a.mask + row * 4);
+    if constexpr (T % 8 == 0) {
+        const uint4* src = reinterpret_cast<const uint4*>(a.packed + row * T);   // 16-byte aligned rows
+#pragma unroll
+        for (int i = 0; i < NDW / 4; ++i) {
+            const uint4 x = src[i];
+            kr[4 * i] = x.x; kr[4 * i + 1] = x.y; kr[4 * i + 2] = x.z; kr[4 * i + 3] = x.w;
+        }
+    } else {
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(a.packed + row * T);  // 4-byte aligned rows
+#pragma unroll
+        for (int i = 0; i < NDW; ++i) kr[i] = src[i];
+    }
+}
+
+// Half of a tile's V rows for the P.V layout: lane (tau, oct) takes rows
+// 4i + tau for i in [8 half, 8 half + 8), d in [8 oct, 8 oct + 8). Rows past
+// the end of a partial tile re-read the last valid row; their p is 0.
+__device__ __forceinline__ void load_v_half(const uint16_t* vbh, int t0, int nt, int half, int tau, int oct,
+                                            uint4 (&vr)[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int tok = min(4 * (8 * half + i) + tau, nt - 1);
+        vr[i] = *reinterpret_cast<const uint4*>(vbh + (size_t)(t0 + tok) * 128 + oct * 8);
+    }
+}
+
+template <int G>
+__device__ __forceinline__ void pv_half(const uint4 (&vr)[8], const float* ptab, float (&acc)[G][8], int half, int tau) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int tok = 4 * (8 * half + i) + tau;
+        const QRow<G> p = *reinterpret_cast<const QRow<G>*>(ptab + tok * G);
+        const uint32_t w4[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
+        float vf[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            vf[2 * e] = bf16_lo(w4[e]);
+            vf[2 * e + 1] = bf16_hi(w4[e]);
         }
 #pragma unroll
         for (int g = 0; g < G; ++g)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[g][e] *= alpha[g];
-        wave_lds_sync();
+            for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(p.v[g], vf[e], acc[g][e]);
+    }
+}
 
-        // -- P.V
+// One 64-token tile of the fast kernel: list of kept channels, scores with
+// the packed values in registers, online softmax, P.V in two halves.
+template <int G, int T>
+__device__ __forceinline__ void fast_tile(const DecodeArgs& a, const unsigned char* tab, uint8_t* lst, float* ptab,
+                                          const uint16_t* vbh, const float (&cq)[G], int t0, int nt, int L,
+                                          const uint4 mw, const uint32_t (&kr)[(T + 1) / 2],
+                                          float (&m_run)[G], float (&l_run)[G], float (&acc)[G][8]) {
+    constexpr uint32_t TAB = (uint32_t)sizeof(TabEntry<G>);
+    const int tau = L >> 4, oct = L & 15;
+    // list of kept channels, slot-major bytes [rho][lane]
+    {
+        int cnt = 0;
+        const uint32_t words[4] = {mw.x, mw.y, mw.z, mw.w};
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int tok = 4 * i + tau;
-            const QRow<G> p = *reinterpret_cast<const QRow<G>*>(ptab + tok * G);
-            const uint32_t w4[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
-            float vf[8];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                vf[2 * e] = bf16_lo(w4[e]);
-                vf[2 * e + 1] = bf16_hi(w4[e]);
+        for (int w = 0; w < 4; ++w) {
+            uint32_t m = words[w];
+            while (m) {
+                lst[cnt * 64 + L] = (uint8_t)(32 * w + __builtin_ctz(m));
+                m &= m - 1;
+                ++cnt;
             }
-#pragma unroll
-            for (int g = 0; g < G; ++g)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(p.v[g], vf[e], acc[g][e]);
         }
-        wave_lds_sync();
+    }
+    wave_lds_sync();
+    // scores: slots in groups of 4, table rows requested before use
+    float s[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) s[g] = cq[g];
+#pragma unroll
+    for (int r0 = 0; r0 < T; r0 += 4) {
+        constexpr int NB = 4;
+        // keep each batch's loads inside the batch: unbounded hoisting across
+        // the fully unrolled slot loop would need registers for every slot
+        __builtin_amdgcn_sched_barrier(0);
+        uint32_t off[NB];
+#pragma unroll
+        for (int k = 0; k < NB; ++k)
+            if (r0 + k < T) off[k] = (uint32_t)lst[(r0 + k) * 64 + L] * TAB;
+        TabEntry<G> te[NB];
+#pragma unroll
+        for (int k = 0; k < NB; ++k)
+            if (r0 + k < T) te[k] = *reinterpret_cast<const TabEntry<G>*>(__builtin_assume_aligned(tab + off[k], 16));
+#pragma unroll
+        for (int k = 0; k < NB; ++k) {
+            if (r0 + k < T) {
+                const int rho = r0 + k;
+                const float kv = (rho & 1) ? bf16_hi(kr[rho >> 1]) : bf16_lo(kr[rho >> 1]);
+                const float e = kv - te[k].r;
+#pragma unroll
+                for (int g = 0; g < G; ++g) s[g] = fmaf(te[k].q[g], e, s[g]);
+            }
+        }
+        // consume the partial sums here: otherwise the compiler sinks the
+        // FMAs of every batch to the end and keeps all gathered rows live
+#pragma unroll
+        for (int g = 0; g < G; ++g) asm volatile("" : "+v"(s[g]));
+    }
+    if (L >= nt) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) s[g] = -INFINITY;
+    }
+    uint4 vr[8];
+    load_v_half(vbh, t0, nt, 0, tau, oct, vr);
+    softmax_tile<G>(s, m_run, l_run, acc, ptab, L);
+    wave_lds_sync();
+    pv_half<G>(vr, ptab, acc, 0, tau);
+    __builtin_amdgcn_sched_barrier(0);
+    load_v_half(vbh, t0, nt, 1, tau, oct, vr);
+    pv_half<G>(vr, ptab, acc, 1, tau);
+    wave_lds_sync();
+}
+
+// Decode block specialised for a compile-time T (the pruning ratios in use):
+// DECODE_FAST_THREADS threads (8 waves) per block, one block per CU. Each
+// lane loads its token's packed row straight into registers (T/2 dwords, no
+// LDS staging) and builds the list of its kept channels in LDS as bytes; the
+// score loop then knows each slot's register at compile time.
+template <int G, int T>
+__global__ void __launch_bounds__(DECODE_FAST_THREADS)
+decode_fast_kernel(const DecodeArgs a) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    constexpr uint32_t TAB = (uint32_t)sizeof(TabEntry<G>);
+    constexpr uint32_t LIST = ((uint32_t)T * 64u + 15u) & ~15u;       // u8 [T][64]
+    constexpr uint32_t WAVE = LIST + 64u * G * 4u;                    // list + ptab
+    constexpr int NW = DECODE_FAST_THREADS / 64;
+    static_assert(T % 2 == 0 && T > 0 && T < 128, "fast path needs an even 0 < T < 128");
+    unsigned char* tab = smem;
+    unsigned char* wbase = smem + 128 * TAB;
+
+    const int bh = blockIdx.y;
+    const int split = blockIdx.x;
+    const int b = bh / a.N_kv, h = bh % a.N_kv;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int L = tid & 63;
+    const int S = a.S;
+    const int blk_begin = split * a.chunk;
+    const int blk_end = min(S, blk_begin + a.chunk);
+    const int ntiles = (blk_end - blk_begin + DECODE_TILE - 1) / DECODE_TILE;
+
+    // the first tile's row is requested before the block setup
+    uint4 mw;
+    uint32_t kr[(T + 1) / 2];
+    if (wave < ntiles) {
+        const int t0 = blk_begin + wave * DECODE_TILE;
+        load_row<T>(a, bh, t0, min(DECODE_TILE, blk_end - t0), L, mw, kr);
     }
 
-    // ---- wave partial: reduce acc over the 4 token phases, l over lanes
+    for (int i = tid; i < 128 * G; i += DECODE_FAST_THREADS) {
+        const int g = i >> 7, j = i & 127;
+        const uint16_t qb = a.q[((size_t)b * a.N_q + (size_t)h * G + g) * 128 + j];
+        reinterpret_cast<TabEntry<G>*>(tab)[j].q[g] = bf16_to_f32(qb) * a.qscale;
+    }
+    if (tid < 128) reinterpret_cast<TabEntry<G>*>(tab)[tid].r = a.r[(size_t)bh * 128 + tid];
+    uint8_t* lst = wbase + (size_t)wave * WAVE;
+    float* ptab = reinterpret_cast<float*>(wbase + (size_t)wave * WAVE + LIST);
+    __syncthreads();
+
+    float cq[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float x = acc[g][e];
-            x += __shfl_xor(x, 16, 64);
-            x += __shfl_xor(x, 32, 64);
-            acc[g][e] = x;
-        }
-        l_run[g] = wave_sum(l_run[g]);
-    }
-    __syncthreads();   // staging no longer needed: reuse it for the block merge
-    float* wm = reinterpret_cast<float*>(stage_all);           // [NW][G]
-    float* wl = wm + NW * G;                                   // [NW][G]
-    float* wacc = wl + NW * G;                                 // [NW][G][128]
-    if (L < 16) {
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) wacc[(wave * G + g) * 128 + oct * 8 + e] = acc[g][e];
-    }
-    if (L == 0) {
-#pragma unroll
-        for (int g = 0; g < G; ++g) { wm[wave * G + g] = m_run[g]; wl[wave * G + g] = l_run[g]; }
-    }
-    __syncthreads();
-
-    float* pml = a.part_ml + ((size_t)bh * a.nsplit + split) * 2 * G;
-    float* pacc = a.part_acc + ((size_t)bh * a.nsplit + split) * G * 128;
-    for (int i = tid; i < G * 128; i += DECODE_THREADS) {
-        const int g = i >> 7, d = i & 127;
-        float M = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) M = fmaxf(M, wm[w * G + g]);
-        float x = 0.f, l = 0.f;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) {
-            const float f = (wm[w * G + g] == -INFINITY) ? 0.f : exp2f(wm[w * G + g] - M);
-            x += wacc[(w * G + g) * 128 + d] * f;
-            l += wl[w * G + g] * f;
-        }
-        pacc[i] = x;
-        if (d == 0) { pml[g] = M; pml[G + g] = l; }
+        const TabEntry<G>* te = reinterpret_cast<const TabEntry<G>*>(tab);
+        cq[g] = wave_sum(te[L].q[g] * te[L].r + te[L + 64].q[g] * te[L + 64].r);
     }
 
-    // ---- last block of this (b, KV head) merges all splits
-    __shared__ int s_last;
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-        const uint32_t prev = __hip_atomic_fetch_add(a.counters + bh, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = (prev == (uint32_t)(a.nsplit - 1));
+    float m_run[G], l_run[G], acc[G][8];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        m_run[g] = -INFINITY;
+        l_run[g] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
     }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    const float* ml_bh = a.part_ml + (size_t)bh * a.nsplit * 2 * G;
-    const float* acc_bh = a.part_acc + (size_t)bh * a.nsplit * G * 128;
-    for (int i = tid; i < G * 128; i += DECODE_THREADS) {
-        const int g = i >> 7, d = i & 127;
-        float M = -INFINITY;
-        for (int sp = 0; sp < a.nsplit; ++sp) M = fmaxf(M, ml_bh[sp * 2 * G + g]);
-        float x = 0.f, l = 0.f;
-        for (int sp = 0; sp < a.nsplit; ++sp) {
-            const float ms = ml_bh[sp * 2 * G + g];
-            const float f = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
-            x += acc_bh[(size_t)sp * G * 128 + i] * f;
-            l += ml_bh[sp * 2 * G + G + g] * f;
-        }
-        a.out[((size_t)b * a.N_q + (size_t)h * G + g) * 128 + d] = x / l;
+    const uint16_t* vbh = a.v + (size_t)bh * S * 128;
+
+    for (int tile = wave; tile < ntiles; tile += NW) {
+        const int t0 = blk_begin + tile * DECODE_TILE;
+        const int nt = min(DECODE_TILE, blk_end - t0);
+        if (tile != wave) load_row<T>(a, bh, t0, nt, L, mw, kr);
+        fast_tile<G, T>(a, tab, lst, ptab, vbh, cq, t0, nt, L, mw, kr, m_run, l_run, acc);
     }
-    if (tid == 0) __hip_atomic_store(a.counters + bh, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+    finish_block<G, DECODE_FAST_THREADS>(a, m_run, l_run, acc, wbase, bh, b, h, split);
 }
+
+// LDS bytes of the fast kernel: table, then per wave the list and p, or the
+// block / split merge scratch (reused after the tile loop).
+uint32_t decode_fast_lds_bytes(int G, int T, int nsplit) {
+    const uint32_t tab = 128u * (uint32_t)tab_stride_for(G);
+    const uint32_t list = ((uint32_t)T * 64u + 15u) & ~15u;
+    const uint32_t waves = DECODE_FAST_THREADS / 64;
+    uint32_t dyn = waves * (list + 64u * (uint32_t)G * 4u);
+    const uint32_t combine = waves * (2u * G + (uint32_t)G * 128u) * 4u;
+    const uint32_t merge = (((uint32_t)nsplit * 3u * G + G + 3u) & ~3u) * 4u + (uint32_t)DECODE_FAST_THREADS * 16u;
+    if (combine > dyn) dyn = combine;
+    if (merge > dyn) dyn = merge;
+    return tab + dyn;
+}
+
+bool decode_fast_supported(int G, int T) { return G == 4 && (T == 26 || T == 38 || T == 64); }
 
 hipError_t launch_decode(const DecodeArgs& a, int G, int BH, hipStream_t stream) {
     const dim3 grid(a.nsplit, BH), block(DECODE_THREADS);
-    const size_t lds = decode_lds_bytes(G, a.T);
+    if (decode_fast_supported(G, a.T)) {
+        const dim3 fblock(DECODE_FAST_THREADS);
+        const size_t lds = decode_fast_lds_bytes(G, a.T, a.nsplit);
+        const void* fn = a.T == 26 ? reinterpret_cast<const void*>(&decode_fast_kernel<4, 26>)
+                       : a.T == 38 ? reinterpret_cast<const void*>(&decode_fast_kernel<4, 38>)
+                                   : reinterpret_cast<const void*>(&decode_fast_kernel<4, 64>);
+        if (lds > 65536) {
+            const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            if (e != hipSuccess) return e;
+        }
+        switch (a.T) {
+            case 26: hipLaunchKernelGGL((decode_fast_kernel<4, 26>), grid, fblock, lds, stream, a); break;
+            case 38: hipLaunchKernelGGL((decode_fast_kernel<4, 38>), grid, fblock, lds, stream, a); break;
+            default: hipLaunchKernelGGL((decode_fast_kernel<4, 64>), grid, fblock, lds, stream, a); break;
+        }
+        return hipGetLastError();
+    }
+    const size_t lds = a.lay.lds_bytes;
     const void* fn = nullptr;
     switch (G) {
         case 1: fn = reinterpret_cast<const void*>(&decode_kernel<1>); break;

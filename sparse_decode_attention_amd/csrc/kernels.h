@@ -4,8 +4,12 @@
 #include <stdint.h>
 
 #define PRUNE_TOKENS_PER_BLOCK 256
+#define CHAN_ENERGY_ROWS 128
+#define STATS_PARTS 8
 #define DECODE_THREADS 256
+#define DECODE_FAST_THREADS 512
 #define DECODE_TILE 64
+#define DECODE_MAX_SPLITS 256
 
 namespace spark {
 
@@ -21,6 +25,21 @@ __global__ void stats_reduce_kernel(const double* part_sum, const int32_t* part_
                                     int recovery, float f_const);
 __global__ void fill_u32_kernel(uint32_t* p, uint32_t value, size_t n);
 
+// LDS layout of the decode kernel (computed on the host for T and G).
+struct DecodeLayout {
+    uint32_t tab_stride;   // bytes per channel entry of the q'/r table: G floats of q', then r
+    uint32_t row_bytes;    // LDS bytes between staged packed rows of consecutive tokens
+    uint32_t padded;       // 1: rows padded to an odd dword count (T/2 even), staged dword by dword
+    uint32_t half_T;       // T / 2 (padded rows)
+    uint32_t magic;        // ceil(2^32 / half_T): u / half_T == umulhi(u, magic) for u < 2^16
+    uint32_t list_bytes;   // per wave: kept-channel table offsets, u16 [T][64]
+    uint32_t stage_bytes;  // per wave: staged packed rows of one 64-token tile
+    uint32_t ptab_bytes;   // per wave: p of the tile, [64][G] fp32
+    uint32_t wave_bytes;   // list + stage + ptab
+    uint32_t tab_bytes;    // 128 * tab_stride
+    uint32_t lds_bytes;    // whole block (dynamic LDS)
+};
+
 struct DecodeArgs {
     const uint16_t* q;        // [B][N_q][128]
     const uint16_t* packed;   // [B][N_kv][S][T]
@@ -34,12 +53,13 @@ struct DecodeArgs {
     size_t packed_elems;      // B*N_kv*S*T
     int S, T, N_q, N_kv, nsplit, chunk;
     float qscale;             // softmax scale * log2(e)
-    uint32_t lds_stage_bytes; // per-wave packed staging
+    DecodeLayout lay;
 };
+
+hipError_t launch_read_stream(const void* src, size_t bytes, uint32_t* sink, int blocks, hipStream_t stream);
 
 // Launch the decode kernel for group size G; returns a hipError_t.
 hipError_t launch_decode(const DecodeArgs& a, int G, int BH, hipStream_t stream);
-size_t decode_lds_bytes(int G, int T);
-uint32_t decode_stage_bytes(int T);
+DecodeLayout decode_layout(int G, int T, int nsplit);
 
 }  // namespace spark

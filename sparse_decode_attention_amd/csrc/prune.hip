@@ -13,24 +13,35 @@
 namespace spark {
 
 // ---------------------------------------------------------------- channel energy
-// One thread per (b, kv head, channel); threads of a block read 256 contiguous
-// bytes of each window row.
-__global__ void __launch_bounds__(128)
+// One block per (b, kv head), one thread per channel. The G*W window rows are
+// first staged in LDS with all loads in flight, then each thread sums its
+// channel sequentially (row g*W + w in increasing order).
+__global__ void __launch_bounds__(256)
 chan_energy_kernel(const uint16_t* __restrict__ q_win, float* __restrict__ A,
                    int N_q, int N_kv, int W, int qagg) {
+    __shared__ uint4 rows[CHAN_ENERGY_ROWS * 16];       // up to CHAN_ENERGY_ROWS rows of 256 B
     const int bh = blockIdx.x;
     const int b = bh / N_kv, h = bh % N_kv;
     const int G = N_q / N_kv;
+    const int R = G * W;                                // stacked rows (g outer, w inner)
+    // the G heads of the group are adjacent in q_win, so their W rows are contiguous
+    const uint4* src = reinterpret_cast<const uint4*>(q_win + ((size_t)b * N_q + (size_t)h * G) * W * 128);
     const int j = threadIdx.x;
     float acc = 0.f;
-    for (int g = 0; g < G; ++g) {
-        const uint16_t* row = q_win + (((size_t)b * N_q + (size_t)h * G + g) * W) * 128;
-        for (int w = 0; w < W; ++w) {
-            const float x = bf16_to_f32(row[(size_t)w * 128 + j]);
-            acc = (qagg == 0) ? __fadd_rn(acc, __fmul_rn(x, x)) : __fadd_rn(acc, x);
+    for (int r0 = 0; r0 < R; r0 += CHAN_ENERGY_ROWS) {
+        const int nr = min(CHAN_ENERGY_ROWS, R - r0);
+        __syncthreads();
+        for (int i = threadIdx.x; i < nr * 16; i += blockDim.x) rows[i] = src[(size_t)r0 * 16 + i];
+        __syncthreads();
+        if (j < 128) {
+            const uint16_t* rr = reinterpret_cast<const uint16_t*>(rows);
+            for (int i = 0; i < nr; ++i) {
+                const float x = bf16_to_f32(rr[i * 128 + j]);
+                acc = (qagg == 0) ? __fadd_rn(acc, __fmul_rn(x, x)) : __fadd_rn(acc, x);
+            }
         }
     }
-    A[(size_t)bh * 128 + j] = (qagg == 0) ? acc : __fmul_rn(acc, acc);
+    if (j < 128) A[(size_t)bh * 128 + j] = (qagg == 0) ? acc : __fmul_rn(acc, acc);
 }
 
 // ---------------------------------------------------------------- select + pack
@@ -223,27 +234,46 @@ stats_partial_kernel(const uint16_t* __restrict__ k_packed, const uint32_t* __re
 }
 
 // ---------------------------------------------------------------- partials -> r
-// One thread per (b, kv head, channel); blocks are combined in index order.
-__global__ void __launch_bounds__(128)
+// One block per (b, kv head): thread (part, j) sums a contiguous range of the
+// block partials of channel j, then the STATS_PARTS ranges are added in
+// order, so the result is the same on every run.
+__global__ void __launch_bounds__(128 * STATS_PARTS)
 stats_reduce_kernel(const double* __restrict__ part_sum, const int32_t* __restrict__ part_cnt,
                     const double* __restrict__ part_pruned, const float* __restrict__ A,
                     float* __restrict__ r, int32_t* __restrict__ cnt,
                     int S, int T, int nblk, int recovery, float f_const) {
-    const int bh = blockIdx.x, j = threadIdx.x;
-    double s = 0.0;
+    __shared__ double sh_s[STATS_PARTS][128];
+    __shared__ long long sh_c[STATS_PARTS][128];
+    __shared__ double sh_p[STATS_PARTS];
+    const int bh = blockIdx.x, j = threadIdx.x & 127, part = threadIdx.x >> 7;
+    const int per = (nblk + STATS_PARTS - 1) / STATS_PARTS;
+    const int lo = part * per, hi = min(nblk, lo + per);
+    double s = 0.0, p = 0.0;
     long long c = 0;
-    for (int blk = 0; blk < nblk; ++blk) {
+#pragma unroll 8
+    for (int blk = lo; blk < hi; ++blk) {
         s += part_sum[((size_t)bh * nblk + blk) * 128 + j];
         c += part_cnt[((size_t)bh * nblk + blk) * 128 + j];
     }
+    if (recovery == 3 && j == 0) {
+        for (int blk = lo; blk < hi; ++blk) p += part_pruned[(size_t)bh * nblk + blk];
+        sh_p[part] = p;
+    }
+    sh_s[part][j] = s;
+    sh_c[part][j] = c;
+    __syncthreads();
+    if (part != 0) return;
+    s = 0.0;
+    c = 0;
+    for (int q = 0; q < STATS_PARTS; ++q) { s += sh_s[q][j]; c += sh_c[q][j]; }
     float out = 0.f;
     if (recovery == 0) {
         out = c > 0 ? (float)(s / (double)c) : 0.f;
     } else if (recovery == 2) {
         out = f_const;
     } else if (recovery == 3) {
-        double p = 0.0;
-        for (int blk = 0; blk < nblk; ++blk) p += part_pruned[(size_t)bh * nblk + blk];
+        p = 0.0;
+        for (int q = 0; q < STATS_PARTS; ++q) p += sh_p[q];
         const double npruned = (double)S * (double)(128 - T);
         const double mu = npruned > 0 ? p / npruned : 0.0;
         const double a = sqrt((double)A[(size_t)bh * 128 + j]);

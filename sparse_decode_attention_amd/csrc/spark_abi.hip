@@ -50,9 +50,10 @@ PrefillWs prefill_layout(void* ws, int B, int S, int N_kv) {
     return w;
 }
 
+// About 256 blocks in all (one 8-wave block per CU for the fast kernel).
 int auto_splits(int BH, int S) {
     const int max_splits = (S + DECODE_TILE - 1) / DECODE_TILE;
-    int want = (512 + BH - 1) / BH;           // about two 4-wave blocks per CU
+    int want = (256 + BH - 1) / BH;
     if (want < 1) want = 1;
     if (want > max_splits) want = max_splits;
     return want;
@@ -63,6 +64,7 @@ void decode_plan(int BH, int S, int splits, int* nsplit, int* chunk) {
     int n = splits > 0 ? splits : auto_splits(BH, S);
     const int max_splits = (S + DECODE_TILE - 1) / DECODE_TILE;
     if (n > max_splits) n = max_splits;
+    if (n > DECODE_MAX_SPLITS) n = DECODE_MAX_SPLITS;
     int c = (S + n - 1) / n;
     c = (c + DECODE_TILE - 1) / DECODE_TILE * DECODE_TILE;
     *chunk = c;
@@ -126,12 +128,12 @@ int spark_prefill_prune(const void* q_win, const void* k, int B, int S, int N_q,
 
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int BH = B * N_kv;
-    hipLaunchKernelGGL(chan_energy_kernel, dim3(BH), dim3(128), 0, st,
+    hipLaunchKernelGGL(chan_energy_kernel, dim3(BH), dim3(256), 0, st,
                        static_cast<const uint16_t*>(q_win), chan_energy, N_q, N_kv, window, qagg);
     hipLaunchKernelGGL(select_pack_kernel, dim3(w.nblk, BH), dim3(256), 0, st,
                        static_cast<const uint16_t*>(k), chan_energy, static_cast<uint16_t*>(k_packed), mask,
                        w.sum, w.cnt, w.pruned, S, T, w.nblk, recovery);
-    hipLaunchKernelGGL(stats_reduce_kernel, dim3(BH), dim3(128), 0, st,
+    hipLaunchKernelGGL(stats_reduce_kernel, dim3(BH), dim3(128 * STATS_PARTS), 0, st,
                        w.sum, w.cnt, w.pruned, chan_energy, r, cnt, S, T, w.nblk, recovery, f_const);
     return hip_status(hipGetLastError());
 }
@@ -157,7 +159,7 @@ int spark_stats(const void* k_packed, const uint32_t* mask, const float* chan_en
     hipLaunchKernelGGL(stats_partial_kernel, dim3(w.nblk, BH), dim3(256), 0, st,
                        static_cast<const uint16_t*>(k_packed), mask, static_cast<const uint16_t*>(k_dense),
                        chan_energy, w.sum, w.cnt, w.pruned, S, T, w.nblk, recovery);
-    hipLaunchKernelGGL(stats_reduce_kernel, dim3(BH), dim3(128), 0, st,
+    hipLaunchKernelGGL(stats_reduce_kernel, dim3(BH), dim3(128 * STATS_PARTS), 0, st,
                        w.sum, w.cnt, w.pruned, chan_energy, r, cnt, S, T, w.nblk, recovery, f_const);
     return hip_status(hipGetLastError());
 }
@@ -203,7 +205,7 @@ int spark_decode_attn(const void* q, const void* k_packed, const uint32_t* mask,
     a.chunk = chunk;
     const float sc = scale > 0.f ? scale : (float)(1.0 / sqrt((double)D));
     a.qscale = sc * 1.4426950408889634f;
-    a.lds_stage_bytes = decode_stage_bytes(T);
+    a.lay = decode_layout(G, T, nsplit);
     return hip_status(launch_decode(a, G, BH, static_cast<hipStream_t>(stream)));
 }
 
@@ -215,6 +217,12 @@ int spark_decode_ws_init(void* ws, size_t ws_bytes, void* stream) {
     hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
                        static_cast<hipStream_t>(stream), static_cast<uint32_t*>(ws), 0u, n);
     return hip_status(hipGetLastError());
+}
+
+int spark_read_stream(const void* src, size_t bytes, uint32_t* sink, int blocks, void* stream) {
+    if (!src || !sink || blocks < 1 || blocks > 65535) return SPARK_EINVAL;
+    if (!aligned(src, 16) || (bytes & 15)) return SPARK_EALIGN;
+    return hip_status(launch_read_stream(src, bytes, sink, blocks, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

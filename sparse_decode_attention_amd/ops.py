@@ -37,6 +37,7 @@ _SIGS = {
     "spark_stats": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _f, _vp, _vp, _vp, _sz, _vp]),
     "spark_decode_attn": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _f, _i, _vp, _vp, _sz, _vp]),
     "spark_decode_ws_init": (_i, [_vp, _sz, _vp]),
+    "spark_read_stream": (_i, [_vp, _sz, _vp, _i, _vp]),
 }
 
 
@@ -188,3 +189,9 @@ def decode_attn(q, k_packed, mask, v, r, lam: float, scale: float = 0.0, splits:
 
 def decode_ws_init(ws: torch.Tensor) -> None:
     _check("spark_decode_ws_init", lib().spark_decode_ws_init(_ptr(ws), ws.numel(), _stream(ws.device)))
+
+
+def read_stream(src: torch.Tensor, sink: torch.Tensor, blocks: int = 2048) -> None:
+    """Diagnostic streaming read of `src` (measures the practical HBM read rate)."""
+    _check("spark_read_stream", lib().spark_read_stream(_ptr(src), src.numel() * src.element_size(),
+                                                        _ptr(sink), int(blocks), _stream(src.device)))

@@ -122,3 +122,11 @@ def test_decode_ws_init_checks():
     assert l.spark_decode_ws_init(None, 4096, None) == ops.EINVAL
     assert l.spark_decode_ws_init(FAKE + 4, 4096, None) == ops.EALIGN
     assert l.spark_decode_ws_init(FAKE, 100, None) == ops.ENOSPACE
+
+
+def test_read_stream_checks():
+    l = ops.lib()
+    assert l.spark_read_stream(None, 16, FAKE, 4, None) == ops.EINVAL
+    assert l.spark_read_stream(FAKE, 16, FAKE, 0, None) == ops.EINVAL
+    assert l.spark_read_stream(FAKE + 8, 16, FAKE, 4, None) == ops.EALIGN
+    assert l.spark_read_stream(FAKE, 24, FAKE, 4, None) == ops.EALIGN

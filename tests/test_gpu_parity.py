@@ -242,3 +242,68 @@ def test_errors_on_device():
     with pytest.raises(ops.SparkError) as e:
         ops.decode_attn(dev_bf16(x["q_dec"][0]), g["k_packed"], g["mask"], dev_bf16(x["v"]), g["r"], 0.5, ws=small)
     assert e.value.status == ops.ENOSPACE
+
+
+def test_graph_replays_match_eager():
+    """Prefill and decode captured in HIP graphs (no memset nodes: counters
+    are reset by the kernel itself) give the eager results on every replay,
+    with eager work and synchronisations between replays."""
+    w = WORKLOADS["tiny_s1k"].with_(S=3000)
+    x = gen.numpy_layer(w, seed=11, steps=3)
+    q_win, k, v = dev_bf16(x["q_win"]), dev_bf16(x["k"]), dev_bf16(x["v"])
+    qs = [dev_bf16(x["q_dec"][s]) for s in range(3)]
+    g = run_prefill(x, w.n_kv, 0.8)
+    outs = [torch.empty((w.B, w.n_q, 128), dtype=torch.float32, device=DEV) for _ in range(3)]
+
+    def work():
+        ops.prefill_prune(q_win, k, w.n_kv, 0.8, out=g)
+        for s in range(3):
+            ops.decode_attn(qs[s], g["k_packed"], g["mask"], v, g["r"], 0.8, out=outs[s])
+
+    work()
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs] + [g["mask"].clone(), g["r"].clone()]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            work()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for o in outs:
+            o.fill_(float("nan"))
+        g["mask"].zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [o.clone() for o in outs] + [g["mask"].clone(), g["r"].clone()]
+        for a_, b_ in zip(got, eager):
+            assert torch.equal(a_, b_), f"replay {rep}"
+        work()          # eager work between replays
+        torch.cuda.synchronize()
+
+
+def test_decode_many_splits_s128k():
+    """Auto and maximal split counts at S=131072 agree within tolerance."""
+    w = WORKLOADS["llama8b_s128k_l08"].with_(n_q=8, n_kv=2)
+    x = gen.numpy_layer(w, seed=12, steps=1)
+    g = run_prefill(x, w.n_kv, w.lam)
+    q, v = dev_bf16(x["q_dec"][0]), dev_bf16(x["v"])
+    o_auto = ops.decode_attn(q, g["k_packed"], g["mask"], v, g["r"], w.lam).cpu().numpy()
+    o_max = ops.decode_attn(q, g["k_packed"], g["mask"], v, g["r"], w.lam, splits=100000).cpu().numpy()
+    o_one = ops.decode_attn(q, g["k_packed"], g["mask"], v, g["r"], w.lam, splits=1).cpu().numpy()
+    assert_tol(o_max, o_auto, "max splits")
+    assert_tol(o_one, o_auto, "one split")
+
+
+def test_read_stream_diagnostic_reads_every_word():
+    """The bandwidth-ceiling diagnostic folds every 32-bit word exactly once."""
+    x = torch.randint(-2**31, 2**31 - 1, (3 * 1024 * 1024 + 4,), dtype=torch.int32, device=DEV)
+    for blocks in (1, 7, 512):
+        sink = torch.zeros(blocks, dtype=torch.int32, device=DEV)
+        ops.read_stream(x, sink, blocks)
+        torch.cuda.synchronize()
+        want = np.bitwise_xor.reduce(x.cpu().numpy().view(np.uint32))
+        assert np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32)) == want
