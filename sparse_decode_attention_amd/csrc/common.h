@@ -57,6 +57,31 @@ __device__ __forceinline__ float wave_max_dpp(float x) {
     return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
+// Sum of x over lanes L and L^16 (then L^32): the two outputs of a gfx950
+// permlane swap hold this lane's value and its partner's, in either order.
+__device__ __forceinline__ float xor16_sum(float x) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+// Wave-wide sum without LDS: DPP butterfly inside each 16-lane row, then the
+// rows combined with permlane swaps. Every lane gets the total.
+__device__ __forceinline__ float wave_sum_dpp(float x) {
+    int v = __float_as_int(x);
+    x += __int_as_float(__builtin_amdgcn_update_dpp(v, v, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+    v = __float_as_int(x);
+    x += __int_as_float(__builtin_amdgcn_update_dpp(v, v, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+    v = __float_as_int(x);
+    x += __int_as_float(__builtin_amdgcn_update_dpp(v, v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+    v = __float_as_int(x);
+    x += __int_as_float(__builtin_amdgcn_update_dpp(v, v, 0x140, 0xF, 0xF, false));  // row_mirror
+    return xor32_sum(xor16_sum(x));
+}
+
 // LDS written by some lanes of a wave and read by others: order the accesses
 // within the wave (no workgroup barrier needed).
 __device__ __forceinline__ void wave_lds_sync() {

@@ -53,6 +53,20 @@ __device__ __forceinline__ void store_dev(float* p, float v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Device-scope loads of values written by store_dev in other blocks (which
+// may run on another XCD, behind another L2): each load is itself coherent at
+// device scope, so the reader needs no L2 invalidation.
+__device__ __forceinline__ float load_dev(const float* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float4 load_dev4(const float* p) {
+    const unsigned long long* q = reinterpret_cast<const unsigned long long*>(p);
+    const unsigned long long lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned long long hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return make_float4(__uint_as_float((uint32_t)lo), __uint_as_float((uint32_t)(lo >> 32)),
+                       __uint_as_float((uint32_t)hi), __uint_as_float((uint32_t)(hi >> 32)));
+}
+
 int tab_stride_for(int G) {
     switch (G) {
         case 1: return (int)sizeof(TabEntry<1>);
@@ -112,36 +126,45 @@ __device__ void merge_splits(const DecodeArgs& a, int bh, int b, int h, float* l
     float* sf = sml + ns * 2 * G;                    // [ns][G] scale of each split
     float* sL = sf + ns * G;                         // [G] total l
     float4* sred = reinterpret_cast<float4*>(lds + ((ns * 3 * G + G + 3) & ~3));  // [NPH][NQ]
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    // partials are read with device-scope loads (no acquire fence, which
+    // would invalidate this XCD's L2 under the blocks still streaming)
     const float* ml_bh = a.part_ml + (size_t)bh * ns * 2 * G;
-    for (int i = tid; i < ns * 2 * G; i += NT) sml[i] = ml_bh[i];
+    // the first batch of acc partials is requested together with m and l
+    const int q = tid % NQ, ph = tid / NQ;
+    const int g = q / 32;
+    const float* acc_bh = a.part_acc + (size_t)bh * ns * G * 128;
+    float4 v0[BATCH];
+#pragma unroll
+    for (int k = 0; k < BATCH; ++k) {
+        const int sp = ph + k * NPH;
+        v0[k] = sp < ns ? load_dev4(acc_bh + ((size_t)sp * NQ + q) * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    for (int i = tid; i < ns * 2 * G; i += NT) sml[i] = load_dev(ml_bh + i);
     __syncthreads();
     // per head: M = max over splits, then the split scales and L = sum l * scale
-    for (int g = wave; g < G; g += NW) {
+    for (int hd = wave; hd < G; hd += NW) {
         float mx = -INFINITY;
-        for (int sp = L; sp < ns; sp += 64) mx = fmaxf(mx, sml[sp * 2 * G + g]);
+        for (int sp = L; sp < ns; sp += 64) mx = fmaxf(mx, sml[sp * 2 * G + hd]);
         const float M = wave_max_dpp(mx);
         float ls = 0.f;
         for (int sp = L; sp < ns; sp += 64) {
-            const float m = sml[sp * 2 * G + g];
+            const float m = sml[sp * 2 * G + hd];
             const float f = (m == -INFINITY) ? 0.f : exp2f(m - M);
-            sf[sp * G + g] = f;
-            ls += sml[sp * 2 * G + G + g] * f;
+            sf[sp * G + hd] = f;
+            ls += sml[sp * 2 * G + G + hd] * f;
         }
-        ls = wave_sum(ls);
-        if (L == 0) sL[g] = ls;
+        ls = wave_sum_dpp(ls);
+        if (L == 0) sL[hd] = ls;
     }
     __syncthreads();
-    const int q = tid % NQ, ph = tid / NQ;
-    const int g = q / 32;
-    const float4* acc_bh = reinterpret_cast<const float4*>(a.part_acc + (size_t)bh * ns * G * 128);
     float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int sp0 = ph; sp0 < ns; sp0 += NPH * BATCH) {
         float4 v[BATCH];
 #pragma unroll
         for (int k = 0; k < BATCH; ++k) {
             const int sp = sp0 + k * NPH;
-            v[k] = sp < ns ? acc_bh[(size_t)sp * NQ + q] : make_float4(0.f, 0.f, 0.f, 0.f);
+            if (sp0 == ph) v[k] = v0[k];
+            else v[k] = sp < ns ? load_dev4(acc_bh + ((size_t)sp * NQ + q) * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
         }
 #pragma unroll
         for (int k = 0; k < BATCH; ++k) {
@@ -245,6 +268,9 @@ template <int G>
 __device__ __forceinline__ void pv_tile(const uint4 (&vr)[16], const float* ptab, float (&acc)[G][8], int tau) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
+        // p rows are read four at a time: reading all 16 ahead would hold
+        // 16 * G registers on top of the V tile
+        if ((i & 3) == 0) __builtin_amdgcn_sched_barrier(0);
         const int tok = 4 * i + tau;
         const QRow<G> p = *reinterpret_cast<const QRow<G>*>(ptab + tok * G);
         const uint32_t w4[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
@@ -261,20 +287,27 @@ __device__ __forceinline__ void pv_tile(const uint4 (&vr)[16], const float* ptab
     }
 }
 
-// V rows of one tile for the P.V layout (rows past the tile end read as 0).
+// V rows of one tile for the P.V layout: lane (tau, oct) takes rows 4i + tau,
+// d in [8 oct, 8 oct + 8). Rows past the end of a partial tile re-read the
+// last valid row; their p is 0.
 __device__ __forceinline__ void load_v_tile(const uint16_t* vbh, int t0, int nt, int tau, int oct, uint4 (&vr)[16]) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-        const int tok = 4 * i + tau;
-        vr[i] = make_uint4(0, 0, 0, 0);
-        if (tok < nt) vr[i] = *reinterpret_cast<const uint4*>(vbh + (size_t)(t0 + tok) * 128 + oct * 8);
+        const int tok = min(4 * i + tau, nt - 1);
+        vr[i] = *reinterpret_cast<const uint4*>(vbh + (size_t)(t0 + tok) * 128 + oct * 8);
     }
 }
 
 // End of a decode block: reduce each wave's (m, l, acc) over its token phases
 // and lanes, merge the waves in LDS, publish the block's split partial, and,
 // in the last block of the (b, KV head) to finish, merge all splits.
-template <int G, int NT>
+//
+// Two accumulator layouts: the VALU one (MF false), where lane (tau, oct)
+// holds acc[g][e] for d = 8 oct + e summed over tokens 4i + tau; and the
+// matrix-core one (MF true), where acc[g][nb] is row g (lanes 0-15: hi part of
+// p) or row 4 + g (lanes 16-31: lo part) of the 16x16 tile nb, column
+// d = 16 nb + (lane & 15); lanes 32-63 hold zero rows.
+template <int G, int NT, bool MF>
 __device__ void finish_block(const DecodeArgs& a, float (&m_run)[G], float (&l_run)[G], float (&acc)[G][8],
                              unsigned char* wbase, int bh, int b, int h, int split) {
     constexpr int NW = NT / 64;
@@ -282,17 +315,13 @@ __device__ void finish_block(const DecodeArgs& a, float (&m_run)[G], float (&l_r
     const int wave = tid >> 6;
     const int L = tid & 63;
     const int oct = L & 15;
-    // ---- wave partial: reduce acc over the 4 token phases, l over lanes
+    // ---- wave partial: reduce acc over the 4 token phases (or add the hi
+    // and lo rows), l over lanes
 #pragma unroll
     for (int g = 0; g < G; ++g) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float x = acc[g][e];
-            x += __shfl_xor(x, 16, 64);
-            x += __shfl_xor(x, 32, 64);
-            acc[g][e] = x;
-        }
-        l_run[g] = wave_sum(l_run[g]);
+        for (int e = 0; e < 8; ++e) acc[g][e] = MF ? xor16_sum(acc[g][e]) : xor32_sum(xor16_sum(acc[g][e]));
+        l_run[g] = wave_sum_dpp(l_run[g]);
     }
     __syncthreads();   // per-wave regions are free now: reuse them for the block merge
     float* wm = reinterpret_cast<float*>(wbase);               // [NW][G]
@@ -302,7 +331,7 @@ __device__ void finish_block(const DecodeArgs& a, float (&m_run)[G], float (&l_r
 #pragma unroll
         for (int g = 0; g < G; ++g)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) wacc[(wave * G + g) * 128 + oct * 8 + e] = acc[g][e];
+            for (int e = 0; e < 8; ++e) wacc[(wave * G + g) * 128 + (MF ? 16 * e + oct : oct * 8 + e)] = acc[g][e];
     }
     if (L == 0) {
 #pragma unroll
@@ -324,6 +353,13 @@ __device__ void finish_block(const DecodeArgs& a, float (&m_run)[G], float (&l_r
             x += wacc[(w * G + g) * 128 + d] * f;
             l += wl[w * G + g] * f;
         }
+#if DECODE_SEPARATE_MERGE
+        pacc[i] = x;
+        if (d == 0) { pml[g] = M; pml[G + g] = l; }
+    }
+    (void)b; (void)h;
+}
+#else
         store_dev(pacc + i, x);
         if (d == 0) { store_dev(pml + g, M); store_dev(pml + G + g, l); }
     }
@@ -343,6 +379,55 @@ __device__ void finish_block(const DecodeArgs& a, float (&m_run)[G], float (&l_r
     if (!s_last) return;
     merge_splits<G, NT>(a, bh, b, h, reinterpret_cast<float*>(wbase));
     if (tid == 0) __hip_atomic_store(a.counters + bh, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+#endif
+
+// Split merge as its own kernel (launched after the split kernel on the same
+// stream, so every partial is visible): grid (B*N_kv, G), one thread per d.
+template <int G>
+__global__ void __launch_bounds__(128)
+merge_kernel(const DecodeArgs a) {
+    __shared__ float sml[DECODE_MAX_SPLITS * 2 * G];
+    __shared__ float sf[DECODE_MAX_SPLITS];
+    __shared__ float sL;
+    const int bh = blockIdx.x, g = blockIdx.y, d = threadIdx.x;
+    const int b = bh / a.N_kv, h = bh % a.N_kv;
+    const int ns = a.nsplit;
+    const float* ml_bh = a.part_ml + (size_t)bh * ns * 2 * G;
+    const float* acc_bh = a.part_acc + (size_t)bh * ns * G * 128 + g * 128 + d;
+    constexpr int BATCH = 8;
+    float v0[BATCH];
+#pragma unroll
+    for (int k = 0; k < BATCH; ++k) v0[k] = k < ns ? acc_bh[(size_t)k * G * 128] : 0.f;
+    for (int i = d; i < ns * 2 * G; i += 128) sml[i] = ml_bh[i];
+    __syncthreads();
+    if (d < 64) {
+        float mx = -INFINITY;
+        for (int sp = d; sp < ns; sp += 64) mx = fmaxf(mx, sml[sp * 2 * G + g]);
+        const float M = wave_max_dpp(mx);
+        float ls = 0.f;
+        for (int sp = d; sp < ns; sp += 64) {
+            const float m = sml[sp * 2 * G + g];
+            const float f = (m == -INFINITY) ? 0.f : exp2f(m - M);
+            sf[sp] = f;
+            ls += sml[sp * 2 * G + G + g] * f;
+        }
+        ls = wave_sum_dpp(ls);
+        if (d == 0) sL = ls;
+    }
+    __syncthreads();
+    float x = 0.f;
+    for (int sp0 = 0; sp0 < ns; sp0 += BATCH) {
+        float v[BATCH];
+#pragma unroll
+        for (int k = 0; k < BATCH; ++k) {
+            const int sp = sp0 + k;
+            v[k] = sp0 == 0 ? v0[k] : (sp < ns ? acc_bh[(size_t)sp * G * 128] : 0.f);
+        }
+#pragma unroll
+        for (int k = 0; k < BATCH; ++k) x += (sp0 + k < ns) ? v[k] * sf[sp0 + k] : 0.f;
+    }
+    a.out[((size_t)b * a.N_q + (size_t)h * G + g) * 128 + d] = x / sL;
 }
 
 template <int G>
@@ -513,11 +598,101 @@ decode_kernel(const DecodeArgs a) {
         wave_lds_sync();
     }
 
-    finish_block<G, DECODE_THREADS>(a, m_run, l_run, acc, wbase, bh, b, h, split);
+    finish_block<G, DECODE_THREADS, false>(a, m_run, l_run, acc, wbase, bh, b, h, split);
 }
 
 // Mask and packed row of token t0 + min(L, nt - 1): lanes past the end of a
 // partial tile re-read the last valid row (their scores are discarded).
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// V tile of one wave in LDS for the matrix-core P.V: 64 rows of 256 bytes;
+// the eight 32-byte column blocks of row t are stored in the order
+// block ^ vt_swz(t), so that each transposing read below spreads its 16 rows
+// over all bank groups (two rows per group, the minimum for 512 bytes).
+__device__ __forceinline__ uint32_t vt_swz(uint32_t t) { return (t & 3u) | (((t >> 3) & 1u) << 2); }
+__device__ __forceinline__ uint32_t vt_off(uint32_t t, uint32_t blk, uint32_t byte) {
+    return t * 256u + ((blk ^ vt_swz(t)) << 5) + byte;
+}
+
+// Two fp32 -> packed bf16 pair (round to nearest even).
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
+
+// Online softmax of one tile for the matrix-core P.V: p goes to ptab as
+// [g][64 tokens] fp32; accm[nb][g] (the rows of head g) are rescaled.
+template <int G>
+__device__ __forceinline__ void softmax_tile_mf(const float (&s)[G], float (&m_run)[G], float (&l_run)[G],
+                                                f32x4 (&accm)[8], float* ptab, int L) {
+    static_assert(G == 4, "one accumulator row per head");
+    f32x4 alpha;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        const float mt = wave_max_dpp(s[g]);
+        const float mn = fmaxf(m_run[g], mt);
+        alpha[g] = exp2f(m_run[g] - mn);
+        const float p = exp2f(s[g] - mn);
+        l_run[g] = l_run[g] * alpha[g] + p;
+        m_run[g] = mn;
+        ptab[g * 64 + L] = p;
+    }
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) accm[nb] *= alpha;
+}
+
+// P.V of one 64-token tile on the matrix cores (v_mfma_f32_16x16x32_bf16,
+// four heads). Per 32-token block kb and 16-column block nb:
+//   A (16 x 32): row g < 4 is bf16(p_g), row 4 + g is bf16(p_g - bf16(p_g)),
+//                rows 8-15 are zero, so the hi and lo rows carry p to ~2^-16;
+//   B (32 x 16): V rows of the 32 tokens, columns 16 nb .. 16 nb + 15, read
+//                from the LDS V tile with ds_read_b64_tr_b16 (two reads of
+//                four rows each per lane);
+//   D (16 x 16): accm[nb]; lane l holds rows 4 (l >> 4) + e, column l & 15.
+// vr holds the tile's V rows in the load layout (lane (tau, oct): rows
+// 4i + tau, d in [8 oct, 8 oct + 8)); they are written to the swizzled tile
+// vt first.
+__device__ __forceinline__ void pv_tile_mf(const uint4 (&vr)[16], unsigned char* vt, const float* ptab,
+                                           f32x4 (&accm)[8], int L) {
+    const uint32_t tau = (uint32_t)L >> 4, oct = (uint32_t)L & 15u;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)   // component-wise: keeps vr in registers
+        *reinterpret_cast<u32x4*>(vt + vt_off(4u * i + tau, oct >> 1, (oct & 1u) << 4)) =
+            (u32x4){vr[i].x, vr[i].y, vr[i].z, vr[i].w};
+    wave_lds_sync();
+    const uint32_t m = (uint32_t)L & 15u, q = (uint32_t)L >> 4;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        const float4* pp = reinterpret_cast<const float4*>(ptab + (m & 3u) * 64u + 32u * kb + 8u * q);
+        const float4 p0 = pp[0], p1 = pp[1];
+        const float x[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+        uint32_t aw[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t hi = pack_bf16(x[2 * j], x[2 * j + 1]);
+            const uint32_t lo = pack_bf16(x[2 * j] - bf16_lo(hi), x[2 * j + 1] - bf16_hi(hi));
+            aw[j] = m < 4u ? hi : (m < 8u ? lo : 0u);
+        }
+        const bf16x8 av = __builtin_bit_cast(bf16x8, make_uint4(aw[0], aw[1], aw[2], aw[3]));
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) {
+            const uint32_t t0 = 32u * kb + 8u * q + (m >> 2);
+            const uint32_t byte = (m & 3u) << 3;
+            const i16x4 w0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (i16x4 __attribute__((address_space(3)))*)(vt + vt_off(t0, nb, byte)));
+            const i16x4 w1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (i16x4 __attribute__((address_space(3)))*)(vt + vt_off(t0 + 4u, nb, byte)));
+            const bf16x8 bv = __builtin_bit_cast(bf16x8, __builtin_shufflevector(w0, w1, 0, 1, 2, 3, 4, 5, 6, 7));
+            accm[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, accm[nb], 0, 0, 0);
+        }
+    }
+}
+
 template <int T>
 __device__ __forceinline__ void load_row(const DecodeArgs& a, int bh, int t0, int nt, int L,
                                          uint4& mw, uint32_t (&kr)[(T + 1) / 2]) {
@@ -538,61 +713,45 @@ __device__ __forceinline__ void load_row(const DecodeArgs& a, int bh, int t0, in
     }
 }
 
-// Half of a tile's V rows for the P.V layout: lane (tau, oct) takes rows
-// 4i + tau for i in [8 half, 8 half + 8), d in [8 oct, 8 oct + 8). Rows past
-// the end of a partial tile re-read the last valid row; their p is 0.
-__device__ __forceinline__ void load_v_half(const uint16_t* vbh, int t0, int nt, int half, int tau, int oct,
-                                            uint4 (&vr)[8]) {
+// One 64-token tile of the fast kernel. The tile's V rows (already in flight
+// unless LOAD_V) and the next tile's packed rows are requested first, so they
+// arrive during the list build, the score loop and the softmax; then P.V.
+// Slot list of one tile: lst[rho * 64 + lane] = channel of the lane's
+// rho-th kept channel (ascending), from the lane's 128-bit mask.
+__device__ __forceinline__ void build_list(const uint4& mw, uint8_t* lst, int L) {
+    int cnt = 0;
+    const uint32_t words[4] = {mw.x, mw.y, mw.z, mw.w};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int tok = min(4 * (8 * half + i) + tau, nt - 1);
-        vr[i] = *reinterpret_cast<const uint4*>(vbh + (size_t)(t0 + tok) * 128 + oct * 8);
-    }
-}
-
-template <int G>
-__device__ __forceinline__ void pv_half(const uint4 (&vr)[8], const float* ptab, float (&acc)[G][8], int half, int tau) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int tok = 4 * (8 * half + i) + tau;
-        const QRow<G> p = *reinterpret_cast<const QRow<G>*>(ptab + tok * G);
-        const uint32_t w4[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
-        float vf[8];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            vf[2 * e] = bf16_lo(w4[e]);
-            vf[2 * e + 1] = bf16_hi(w4[e]);
+    for (int w = 0; w < 4; ++w) {
+        uint32_t m = words[w];
+        while (m) {
+            lst[cnt * 64 + L] = (uint8_t)(32 * w + __builtin_ctz(m));
+            m &= m - 1;
+            ++cnt;
         }
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(p.v[g], vf[e], acc[g][e]);
     }
 }
 
-// One 64-token tile of the fast kernel: list of kept channels, scores with
-// the packed values in registers, online softmax, P.V in two halves.
-template <int G, int T>
-__device__ __forceinline__ void fast_tile(const DecodeArgs& a, const unsigned char* tab, uint8_t* lst, float* ptab,
-                                          const uint16_t* vbh, const float (&cq)[G], int t0, int nt, int L,
-                                          const uint4 mw, const uint32_t (&kr)[(T + 1) / 2],
-                                          float (&m_run)[G], float (&l_run)[G], float (&acc)[G][8]) {
+// One 64-token tile of the fast kernel. The tile's V rows (already in flight
+// unless LOAD_V) and the next tile's packed rows are requested first, so they
+// arrive during the list build, the score loop and the softmax; then P.V.
+// With LIST_READY the slot list was built before the call.
+template <int G, int T, bool LOAD_V, bool LIST_READY>
+__device__ __forceinline__ void fast_tile(const DecodeArgs& a, int bh, const unsigned char* tab, uint8_t* lst,
+                                          float* ptab, const uint16_t* vbh, const float (&cq)[G], int t0, int nt,
+                                          int nt_next, int L, uint4& mw, uint32_t (&kr)[(T + 1) / 2],
+                                          uint4 (&vr)[16], float (&m_run)[G], float (&l_run)[G],
+                                          f32x4 (&accm)[8]) {
     constexpr uint32_t TAB = (uint32_t)sizeof(TabEntry<G>);
     const int tau = L >> 4, oct = L & 15;
-    // list of kept channels, slot-major bytes [rho][lane]
-    {
-        int cnt = 0;
-        const uint32_t words[4] = {mw.x, mw.y, mw.z, mw.w};
+    const int t1 = t0 + (DECODE_FAST_THREADS / 64) * DECODE_TILE;
+    if constexpr (LOAD_V) load_v_tile(vbh, t0, nt, tau, oct, vr);
+    const uint4 mw_cur = mw;
+    uint32_t kc[(T + 1) / 2];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            uint32_t m = words[w];
-            while (m) {
-                lst[cnt * 64 + L] = (uint8_t)(32 * w + __builtin_ctz(m));
-                m &= m - 1;
-                ++cnt;
-            }
-        }
-    }
+    for (int i = 0; i < (T + 1) / 2; ++i) kc[i] = kr[i];
+    if (nt_next > 0) load_row<T>(a, bh, t1, nt_next, L, mw, kr);
+    if constexpr (!LIST_READY) build_list(mw_cur, lst, L);
     wave_lds_sync();
     // scores: slots in groups of 4, table rows requested before use
     float s[G];
@@ -616,7 +775,7 @@ __device__ __forceinline__ void fast_tile(const DecodeArgs& a, const unsigned ch
         for (int k = 0; k < NB; ++k) {
             if (r0 + k < T) {
                 const int rho = r0 + k;
-                const float kv = (rho & 1) ? bf16_hi(kr[rho >> 1]) : bf16_lo(kr[rho >> 1]);
+                const float kv = (rho & 1) ? bf16_hi(kc[rho >> 1]) : bf16_lo(kc[rho >> 1]);
                 const float e = kv - te[k].r;
 #pragma unroll
                 for (int g = 0; g < G; ++g) s[g] = fmaf(te[k].q[g], e, s[g]);
@@ -631,14 +790,10 @@ __device__ __forceinline__ void fast_tile(const DecodeArgs& a, const unsigned ch
 #pragma unroll
         for (int g = 0; g < G; ++g) s[g] = -INFINITY;
     }
-    uint4 vr[8];
-    load_v_half(vbh, t0, nt, 0, tau, oct, vr);
-    softmax_tile<G>(s, m_run, l_run, acc, ptab, L);
+    softmax_tile_mf<G>(s, m_run, l_run, accm, ptab, L);
     wave_lds_sync();
-    pv_half<G>(vr, ptab, acc, 0, tau);
-    __builtin_amdgcn_sched_barrier(0);
-    load_v_half(vbh, t0, nt, 1, tau, oct, vr);
-    pv_half<G>(vr, ptab, acc, 1, tau);
+    // the list is dead: the same LDS region takes the V tile
+    pv_tile_mf(vr, lst, ptab, accm, L);
     wave_lds_sync();
 }
 
@@ -652,8 +807,11 @@ __global__ void __launch_bounds__(DECODE_FAST_THREADS)
 decode_fast_kernel(const DecodeArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr uint32_t TAB = (uint32_t)sizeof(TabEntry<G>);
-    constexpr uint32_t LIST = ((uint32_t)T * 64u + 15u) & ~15u;       // u8 [T][64]
-    constexpr uint32_t WAVE = LIST + 64u * G * 4u;                    // list + ptab
+    // per wave: the slot list (u8 [T][64]) during the scores, then the V
+    // tile (64 x 256 bytes) during P.V, in one region; then p as [G][64] fp32
+    constexpr uint32_t LIST = 64u * 256u;
+    static_assert((uint32_t)T * 64u <= LIST, "list fits the V tile region");
+    constexpr uint32_t WAVE = LIST + 64u * G * 4u;
     constexpr int NW = DECODE_FAST_THREADS / 64;
     static_assert(T % 2 == 0 && T > 0 && T < 128, "fast path needs an even 0 < T < 128");
     unsigned char* tab = smem;
@@ -670,56 +828,87 @@ decode_fast_kernel(const DecodeArgs a) {
     const int blk_end = min(S, blk_begin + a.chunk);
     const int ntiles = (blk_end - blk_begin + DECODE_TILE - 1) / DECODE_TILE;
 
-    // the first tile's row is requested before the block setup
+    // Request order and timing matter. With the whole first tile of every
+    // wave requested at once (about 200 KB per CU), any single request takes
+    // as long as that flood takes to drain. So: q and r first; then (after a
+    // barrier, so that every wave has requested q and r) the packed rows and
+    // masks of the first tile; the V rows only once this wave's masks have
+    // arrived. The slot list and the table are built while the packed rows
+    // and V rows stream in. The loads are unconditional (indices clamped into
+    // the head) so that no register copy makes a wave wait early.
+    static_assert(128 * G == DECODE_FAST_THREADS, "one q value per thread");
+    const uint16_t qb = a.q[((size_t)b * a.N_q + (size_t)h * G + (tid >> 7)) * 128 + (tid & 127)];
+    const float rv = a.r[(size_t)bh * 128 + (tid & 127)];
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
     uint4 mw;
     uint32_t kr[(T + 1) / 2];
-    if (wave < ntiles) {
-        const int t0 = blk_begin + wave * DECODE_TILE;
-        load_row<T>(a, bh, t0, min(DECODE_TILE, blk_end - t0), L, mw, kr);
-    }
-
-    for (int i = tid; i < 128 * G; i += DECODE_FAST_THREADS) {
-        const int g = i >> 7, j = i & 127;
-        const uint16_t qb = a.q[((size_t)b * a.N_q + (size_t)h * G + g) * 128 + j];
-        reinterpret_cast<TabEntry<G>*>(tab)[j].q[g] = bf16_to_f32(qb) * a.qscale;
-    }
-    if (tid < 128) reinterpret_cast<TabEntry<G>*>(tab)[tid].r = a.r[(size_t)bh * 128 + tid];
+    uint4 vr[16];
+    const uint16_t* vbh = a.v + (size_t)bh * S * 128;
+    // a wave without a tile (or an empty block) reads row min(t0, S-1)
+    const int tf0 = min(blk_begin + wave * DECODE_TILE, S - 1);
+    const int ntf0 = max(1, min(DECODE_TILE, blk_end - tf0));
+    load_row<T>(a, bh, tf0, ntf0, L, mw, kr);
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::"v"(mw.x), "v"(mw.y), "v"(mw.z), "v"(mw.w));   // wait for the masks only
+    load_v_tile(vbh, tf0, ntf0, L >> 4, L & 15, vr);
+    __builtin_amdgcn_sched_barrier(0);
     uint8_t* lst = wbase + (size_t)wave * WAVE;
     float* ptab = reinterpret_cast<float*>(wbase + (size_t)wave * WAVE + LIST);
+    // the first tile's slot list needs only its masks: build it before
+    // waiting for the table
+    build_list(mw, lst, L);
+    reinterpret_cast<TabEntry<G>*>(tab)[tid & 127].q[tid >> 7] = bf16_to_f32(qb) * a.qscale;
+    if (tid < 128) reinterpret_cast<TabEntry<G>*>(tab)[tid].r = rv;
     __syncthreads();
 
     float cq[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
         const TabEntry<G>* te = reinterpret_cast<const TabEntry<G>*>(tab);
-        cq[g] = wave_sum(te[L].q[g] * te[L].r + te[L + 64].q[g] * te[L + 64].r);
+        cq[g] = wave_sum_dpp(te[L].q[g] * te[L].r + te[L + 64].q[g] * te[L + 64].r);
     }
 
-    float m_run[G], l_run[G], acc[G][8];
+    float m_run[G], l_run[G];
+    f32x4 accm[8];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
         m_run[g] = -INFINITY;
         l_run[g] = 0.f;
+    }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
-    }
-    const uint16_t* vbh = a.v + (size_t)bh * S * 128;
+    for (int nb = 0; nb < 8; ++nb) accm[nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-    for (int tile = wave; tile < ntiles; tile += NW) {
+    // the first tile's V rows were requested before the table set-up; later
+    // tiles request theirs at the start of the tile
+    if (wave < ntiles) {
+        const int t0 = blk_begin + wave * DECODE_TILE;
+        const int t1 = t0 + NW * DECODE_TILE;
+        fast_tile<G, T, false, true>(a, bh, tab, lst, ptab, vbh, cq, t0, min(DECODE_TILE, blk_end - t0),
+                               t1 < blk_end ? min(DECODE_TILE, blk_end - t1) : 0, L, mw, kr, vr, m_run, l_run, accm);
+    }
+    for (int tile = wave + NW; tile < ntiles; tile += NW) {
         const int t0 = blk_begin + tile * DECODE_TILE;
-        const int nt = min(DECODE_TILE, blk_end - t0);
-        if (tile != wave) load_row<T>(a, bh, t0, nt, L, mw, kr);
-        fast_tile<G, T>(a, tab, lst, ptab, vbh, cq, t0, nt, L, mw, kr, m_run, l_run, acc);
+        const int t1 = t0 + NW * DECODE_TILE;     // this wave's next tile, if any
+        uint4 vt[16];
+        fast_tile<G, T, true, false>(a, bh, tab, lst, ptab, vbh, cq, t0, min(DECODE_TILE, blk_end - t0),
+                              t1 < blk_end ? min(DECODE_TILE, blk_end - t1) : 0, L, mw, kr, vt, m_run, l_run, accm);
     }
 
-    finish_block<G, DECODE_FAST_THREADS>(a, m_run, l_run, acc, wbase, bh, b, h, split);
+    float acc[G][8];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) acc[g][nb] = accm[nb][g];
+    finish_block<G, DECODE_FAST_THREADS, true>(a, m_run, l_run, acc, wbase, bh, b, h, split);
 }
 
 // LDS bytes of the fast kernel: table, then per wave the list and p, or the
 // block / split merge scratch (reused after the tile loop).
 uint32_t decode_fast_lds_bytes(int G, int T, int nsplit) {
     const uint32_t tab = 128u * (uint32_t)tab_stride_for(G);
-    const uint32_t list = ((uint32_t)T * 64u + 15u) & ~15u;
+    const uint32_t list = 64u * 256u;     // slot list, then the V tile
+    (void)T;
     const uint32_t waves = DECODE_FAST_THREADS / 64;
     uint32_t dyn = waves * (list + 64u * (uint32_t)G * 4u);
     const uint32_t combine = waves * (2u * G + (uint32_t)G * 128u) * 4u;
@@ -731,7 +920,31 @@ uint32_t decode_fast_lds_bytes(int G, int T, int nsplit) {
 
 bool decode_fast_supported(int G, int T) { return G == 4 && (T == 26 || T == 38 || T == 64); }
 
+static hipError_t launch_merge(const DecodeArgs& a, int G, int BH, hipStream_t stream) {
+#if DECODE_SEPARATE_MERGE
+    const dim3 grid(BH, G), block(128);
+    switch (G) {
+        case 1: hipLaunchKernelGGL(merge_kernel<1>, grid, block, 0, stream, a); break;
+        case 2: hipLaunchKernelGGL(merge_kernel<2>, grid, block, 0, stream, a); break;
+        case 4: hipLaunchKernelGGL(merge_kernel<4>, grid, block, 0, stream, a); break;
+        default: hipLaunchKernelGGL(merge_kernel<8>, grid, block, 0, stream, a); break;
+    }
+    return hipGetLastError();
+#else
+    (void)a; (void)G; (void)BH; (void)stream;
+    return hipSuccess;
+#endif
+}
+
+static hipError_t launch_split(const DecodeArgs& a, int G, int BH, hipStream_t stream);
+
 hipError_t launch_decode(const DecodeArgs& a, int G, int BH, hipStream_t stream) {
+    const hipError_t e = launch_split(a, G, BH, stream);
+    if (e != hipSuccess) return e;
+    return launch_merge(a, G, BH, stream);
+}
+
+static hipError_t launch_split(const DecodeArgs& a, int G, int BH, hipStream_t stream) {
     const dim3 grid(a.nsplit, BH), block(DECODE_THREADS);
     if (decode_fast_supported(G, a.T)) {
         const dim3 fblock(DECODE_FAST_THREADS);

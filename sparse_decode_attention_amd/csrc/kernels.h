@@ -10,6 +10,9 @@
 #define DECODE_FAST_THREADS 512
 #define DECODE_TILE 64
 #define DECODE_MAX_SPLITS 256
+#ifndef DECODE_SEPARATE_MERGE
+#define DECODE_SEPARATE_MERGE 0
+#endif
 
 namespace spark {
 
