@@ -78,6 +78,19 @@ int tab_stride_for(int G) {
 
 }  // namespace
 
+// Byte offset, from the block's finish scratch, of its own split partial
+// ((m, l) then acc, fp32): past both the block combine area and the split
+// merge scratch, so it survives from the combine into the merge.
+__host__ __device__ inline uint32_t finish_own_offset(int G, int NT, int nsplit) {
+    const uint32_t combine = (uint32_t)(NT / 64) * (2u * G + (uint32_t)G * 128u) * 4u;
+    const uint32_t merge = ((((uint32_t)nsplit * 3u * G + G + 3u) & ~3u) * 4u) + (uint32_t)NT * 16u;
+    const uint32_t m = combine > merge ? combine : merge;
+    return (m + 15u) & ~15u;
+}
+__host__ __device__ inline uint32_t finish_scratch_bytes(int G, int NT, int nsplit) {
+    return finish_own_offset(G, NT, nsplit) + (2u * G + (uint32_t)G * 128u) * 4u;
+}
+
 DecodeLayout decode_layout(int G, int T, int nsplit) {
     DecodeLayout L{};
     L.tab_stride = (uint32_t)tab_stride_for(G);
@@ -98,23 +111,22 @@ DecodeLayout decode_layout(int G, int T, int nsplit) {
     L.ptab_bytes = (uint32_t)DECODE_TILE * G * 4u;
     L.wave_bytes = L.list_bytes + L.stage_bytes + L.ptab_bytes;
     const uint32_t waves = DECODE_THREADS / 64;
-    const uint32_t combine = waves * (2u * G + (uint32_t)G * 128u) * 4u;
-    const uint32_t merge = (((uint32_t)nsplit * 3u * G + G + 3u) & ~3u) * 4u + (uint32_t)DECODE_THREADS * 16u;
     uint32_t dyn = waves * L.wave_bytes;
-    if (combine > dyn) dyn = combine;
-    if (merge > dyn) dyn = merge;
+    const uint32_t fin = finish_scratch_bytes(G, DECODE_THREADS, nsplit);
+    if (fin > dyn) dyn = fin;
     L.lds_bytes = L.tab_bytes + dyn;
     return L;
 }
 
 // Merge the (m, l, acc) partials of all splits of one (b, KV head) and write
-// out = acc / l. Runs in the block that finished last, after an agent-scope
-// acquire (one L2 invalidate in this block only), so plain vector loads see
-// the partials that other blocks published with device-scope stores. All
-// loads are issued in batches; every reduction has a fixed order, so the
-// output does not depend on which block merges.
+// out = acc / l. Runs in the block that took the last ticket, once every
+// other split has published its partial with device-scope stores; those are
+// read with device-scope loads, the merging block's own partial (split `own`)
+// from LDS. All loads are issued in batches; every reduction has a fixed
+// order, so the output does not depend on which block merges.
 template <int G, int NT>
-__device__ void merge_splits(const DecodeArgs& a, int bh, int b, int h, float* lds) {
+__device__ void merge_splits(const DecodeArgs& a, int bh, int b, int h, float* lds, int own,
+                             const float* own_ml, const float* own_acc) {
     constexpr int NQ = G * 32;                       // float4 per split partial
     constexpr int NPH = NT / NQ;                     // threads per float4 column
     constexpr int NW = NT / 64;
@@ -137,9 +149,12 @@ __device__ void merge_splits(const DecodeArgs& a, int bh, int b, int h, float* l
 #pragma unroll
     for (int k = 0; k < BATCH; ++k) {
         const int sp = ph + k * NPH;
-        v0[k] = sp < ns ? load_dev4(acc_bh + ((size_t)sp * NQ + q) * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+        v0[k] = sp == own ? reinterpret_cast<const float4*>(own_acc)[q]
+              : sp < ns   ? load_dev4(acc_bh + ((size_t)sp * NQ + q) * 4)
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    for (int i = tid; i < ns * 2 * G; i += NT) sml[i] = load_dev(ml_bh + i);
+    for (int i = tid; i < ns * 2 * G; i += NT)
+        sml[i] = (i / (2 * G) == own) ? own_ml[i % (2 * G)] : load_dev(ml_bh + i);
     __syncthreads();
     // per head: M = max over splits, then the split scales and L = sum l * scale
     for (int hd = wave; hd < G; hd += NW) {
@@ -164,7 +179,9 @@ __device__ void merge_splits(const DecodeArgs& a, int bh, int b, int h, float* l
         for (int k = 0; k < BATCH; ++k) {
             const int sp = sp0 + k * NPH;
             if (sp0 == ph) v[k] = v0[k];
-            else v[k] = sp < ns ? load_dev4(acc_bh + ((size_t)sp * NQ + q) * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+            else v[k] = sp == own ? reinterpret_cast<const float4*>(own_acc)[q]
+                      : sp < ns   ? load_dev4(acc_bh + ((size_t)sp * NQ + q) * 4)
+                                  : make_float4(0.f, 0.f, 0.f, 0.f);
         }
 #pragma unroll
         for (int k = 0; k < BATCH; ++k) {
@@ -309,7 +326,7 @@ __device__ __forceinline__ void load_v_tile(const uint16_t* vbh, int t0, int nt,
 // d = 16 nb + (lane & 15); lanes 32-63 hold zero rows.
 template <int G, int NT, bool MF>
 __device__ void finish_block(const DecodeArgs& a, float (&m_run)[G], float (&l_run)[G], float (&acc)[G][8],
-                             unsigned char* wbase, int bh, int b, int h, int split) {
+                             unsigned char* wbase, int* s_last, int bh, int b, int h, int split) {
     constexpr int NW = NT / 64;
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -339,9 +356,15 @@ __device__ void finish_block(const DecodeArgs& a, float (&m_run)[G], float (&l_r
     }
     __syncthreads();
 
-    float* pml = a.part_ml + ((size_t)bh * a.nsplit + split) * 2 * G;
-    float* pacc = a.part_acc + ((size_t)bh * a.nsplit + split) * G * 128;
-    for (int i = tid; i < G * 128; i += NT) {
+    // the block's own partial is kept in LDS past the merge scratch
+    float* own_ml = reinterpret_cast<float*>(wbase + finish_own_offset(G, NT, a.nsplit));
+    float* own_acc = own_ml + 2 * G;
+    constexpr int EPT = (G * 128 + NT - 1) / NT;       // acc elements per thread
+    float xs[EPT];
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+        const int i = tid + e * NT;
+        if (i >= G * 128) break;
         const int g = i >> 7, d = i & 127;
         float M = -INFINITY;
 #pragma unroll
@@ -353,81 +376,35 @@ __device__ void finish_block(const DecodeArgs& a, float (&m_run)[G], float (&l_r
             x += wacc[(w * G + g) * 128 + d] * f;
             l += wl[w * G + g] * f;
         }
-#if DECODE_SEPARATE_MERGE
-        pacc[i] = x;
-        if (d == 0) { pml[g] = M; pml[G + g] = l; }
-    }
-    (void)b; (void)h;
-}
-#else
-        store_dev(pacc + i, x);
-        if (d == 0) { store_dev(pml + g, M); store_dev(pml + G + g, l); }
+        xs[e] = x;
+        own_acc[i] = x;
+        if (d == 0) { own_ml[g] = M; own_ml[G + g] = l; }
     }
 
-    // ---- last block of this (b, KV head) merges all splits.
-    // Every wave waits until its device-scope partial stores have completed,
-    // then the block barrier, then one counter increment: a block that sees
-    // the final count therefore sees every split's partial at device scope.
-    __shared__ int s_last;
+    // ---- split merge: every block publishes its partial (device-scope
+    // stores), waits until they have completed, then counts itself in; the
+    // block that counts last merges all splits (its own partial from LDS).
+    {
+        float* pml = a.part_ml + ((size_t)bh * a.nsplit + split) * 2 * G;
+        float* pacc = a.part_acc + ((size_t)bh * a.nsplit + split) * G * 128;
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            const int i = tid + e * NT;
+            if (i >= G * 128) break;
+            store_dev(pacc + i, xs[e]);
+            if ((i & 127) == 0) { store_dev(pml + (i >> 7), own_ml[i >> 7]); store_dev(pml + G + (i >> 7), own_ml[G + (i >> 7)]); }
+        }
+    }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tid == 0) {
         const uint32_t prev = __hip_atomic_fetch_add(a.counters + bh, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = (prev == (uint32_t)(a.nsplit - 1));
+        *s_last = (prev == (uint32_t)(a.nsplit - 1));
     }
     __syncthreads();
-    if (!s_last) return;
-    merge_splits<G, NT>(a, bh, b, h, reinterpret_cast<float*>(wbase));
+    if (!*s_last) return;
+    merge_splits<G, NT>(a, bh, b, h, reinterpret_cast<float*>(wbase), split, own_ml, own_acc);
     if (tid == 0) __hip_atomic_store(a.counters + bh, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-#endif
-
-// Split merge as its own kernel (launched after the split kernel on the same
-// stream, so every partial is visible): grid (B*N_kv, G), one thread per d.
-template <int G>
-__global__ void __launch_bounds__(128)
-merge_kernel(const DecodeArgs a) {
-    __shared__ float sml[DECODE_MAX_SPLITS * 2 * G];
-    __shared__ float sf[DECODE_MAX_SPLITS];
-    __shared__ float sL;
-    const int bh = blockIdx.x, g = blockIdx.y, d = threadIdx.x;
-    const int b = bh / a.N_kv, h = bh % a.N_kv;
-    const int ns = a.nsplit;
-    const float* ml_bh = a.part_ml + (size_t)bh * ns * 2 * G;
-    const float* acc_bh = a.part_acc + (size_t)bh * ns * G * 128 + g * 128 + d;
-    constexpr int BATCH = 8;
-    float v0[BATCH];
-#pragma unroll
-    for (int k = 0; k < BATCH; ++k) v0[k] = k < ns ? acc_bh[(size_t)k * G * 128] : 0.f;
-    for (int i = d; i < ns * 2 * G; i += 128) sml[i] = ml_bh[i];
-    __syncthreads();
-    if (d < 64) {
-        float mx = -INFINITY;
-        for (int sp = d; sp < ns; sp += 64) mx = fmaxf(mx, sml[sp * 2 * G + g]);
-        const float M = wave_max_dpp(mx);
-        float ls = 0.f;
-        for (int sp = d; sp < ns; sp += 64) {
-            const float m = sml[sp * 2 * G + g];
-            const float f = (m == -INFINITY) ? 0.f : exp2f(m - M);
-            sf[sp] = f;
-            ls += sml[sp * 2 * G + G + g] * f;
-        }
-        ls = wave_sum_dpp(ls);
-        if (d == 0) sL = ls;
-    }
-    __syncthreads();
-    float x = 0.f;
-    for (int sp0 = 0; sp0 < ns; sp0 += BATCH) {
-        float v[BATCH];
-#pragma unroll
-        for (int k = 0; k < BATCH; ++k) {
-            const int sp = sp0 + k;
-            v[k] = sp0 == 0 ? v0[k] : (sp < ns ? acc_bh[(size_t)sp * G * 128] : 0.f);
-        }
-#pragma unroll
-        for (int k = 0; k < BATCH; ++k) x += (sp0 + k < ns) ? v[k] * sf[sp0 + k] : 0.f;
-    }
-    a.out[((size_t)b * a.N_q + (size_t)h * G + g) * 128 + d] = x / sL;
 }
 
 template <int G>
@@ -598,7 +575,8 @@ decode_kernel(const DecodeArgs a) {
         wave_lds_sync();
     }
 
-    finish_block<G, DECODE_THREADS, false>(a, m_run, l_run, acc, wbase, bh, b, h, split);
+    __shared__ int s_last;
+    finish_block<G, DECODE_THREADS, false>(a, m_run, l_run, acc, wbase, &s_last, bh, b, h, split);
 }
 
 // Mask and packed row of token t0 + min(L, nt - 1): lanes past the end of a
@@ -713,22 +691,38 @@ __device__ __forceinline__ void load_row(const DecodeArgs& a, int bh, int t0, in
     }
 }
 
-// One 64-token tile of the fast kernel. The tile's V rows (already in flight
-// unless LOAD_V) and the next tile's packed rows are requested first, so they
-// arrive during the list build, the score loop and the softmax; then P.V.
-// Slot list of one tile: lst[rho * 64 + lane] = channel of the lane's
-// rho-th kept channel (ascending), from the lane's 128-bit mask.
+// Row stride (u16 elements) of the lane-major slot list: room for T slots and
+// a spare one, rounded so that the stride in dwords is odd, which puts the 64
+// lanes of a dword read on distinct bank pairs.
+template <int T>
+constexpr uint32_t list_stride() { return ((T / 2) % 2 == 1) ? (uint32_t)T + 2u : (uint32_t)T + 4u; }
+
+// Slot list of one tile, lane-major: lst[lane * stride + rho] = 4 * c for the
+// lane's rho-th kept channel c (ascending), i.e. the byte offset of c's r in
+// the fast kernel's r table (a quarter of the offset of its q' row). One
+// bit-clearing loop per mask word; lanes leave it as their word empties.
+template <int T>
 __device__ __forceinline__ void build_list(const uint4& mw, uint8_t* lst, int L) {
-    int cnt = 0;
+    uint16_t* p = reinterpret_cast<uint16_t*>(lst) + (uint32_t)L * list_stride<T>();
     const uint32_t words[4] = {mw.x, mw.y, mw.z, mw.w};
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
         uint32_t m = words[w];
-        while (m) {
-            lst[cnt * 64 + L] = (uint8_t)(32 * w + __builtin_ctz(m));
-            m &= m - 1;
-            ++cnt;
+        const int pc = __builtin_popcount(m);
+        int i = 0;
+        // four bits per trip while at least four remain, then one at a time
+        for (; i + 4 <= pc; i += 4) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                p[i + u] = (uint16_t)(((uint32_t)__builtin_ctz(m) << 2) | (128u * w));
+                m &= m - 1;
+            }
         }
+        for (; i < pc; ++i) {
+            p[i] = (uint16_t)(((uint32_t)__builtin_ctz(m) << 2) | (128u * w));
+            m &= m - 1;
+        }
+        p += pc;
     }
 }
 
@@ -742,8 +736,7 @@ __device__ __forceinline__ void fast_tile(const DecodeArgs& a, int bh, const uns
                                           int nt_next, int L, uint4& mw, uint32_t (&kr)[(T + 1) / 2],
                                           uint4 (&vr)[16], float (&m_run)[G], float (&l_run)[G],
                                           f32x4 (&accm)[8]) {
-    constexpr uint32_t TAB = (uint32_t)sizeof(TabEntry<G>);
-    const int tau = L >> 4, oct = L & 15;
+        const int tau = L >> 4, oct = L & 15;
     const int t1 = t0 + (DECODE_FAST_THREADS / 64) * DECODE_TILE;
     if constexpr (LOAD_V) load_v_tile(vbh, t0, nt, tau, oct, vr);
     const uint4 mw_cur = mw;
@@ -751,9 +744,15 @@ __device__ __forceinline__ void fast_tile(const DecodeArgs& a, int bh, const uns
 #pragma unroll
     for (int i = 0; i < (T + 1) / 2; ++i) kc[i] = kr[i];
     if (nt_next > 0) load_row<T>(a, bh, t1, nt_next, L, mw, kr);
-    if constexpr (!LIST_READY) build_list(mw_cur, lst, L);
+    if constexpr (!LIST_READY) build_list<T>(mw_cur, lst, L);
     wave_lds_sync();
-    // scores: slots in groups of 4, table rows requested before use
+    // scores: s_g = q'_g . r + sum over kept c of q'_g(c) (k_c - r_c), with
+    // q' = q * scale * log2(e) as fp32 float4 per channel (tab) and r as fp32
+    // per channel (rtab, 2 KiB after tab); slots in groups of 4: four list
+    // entries, then four q' rows and four r values
+    static_assert(G == 4, "table row holds four heads");
+    const uint16_t* lrow16 = reinterpret_cast<const uint16_t*>(lst) + (uint32_t)L * list_stride<T>();
+    const unsigned char* rtab = tab + 128 * 16;
     float s[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) s[g] = cq[g];
@@ -766,19 +765,26 @@ __device__ __forceinline__ void fast_tile(const DecodeArgs& a, int bh, const uns
         uint32_t off[NB];
 #pragma unroll
         for (int k = 0; k < NB; ++k)
-            if (r0 + k < T) off[k] = (uint32_t)lst[(r0 + k) * 64 + L] * TAB;
-        TabEntry<G> te[NB];
+            if (r0 + k < T) off[k] = lrow16[r0 + k];
+        float4 qv[NB];
+        float rv[NB];
 #pragma unroll
-        for (int k = 0; k < NB; ++k)
-            if (r0 + k < T) te[k] = *reinterpret_cast<const TabEntry<G>*>(__builtin_assume_aligned(tab + off[k], 16));
+        for (int k = 0; k < NB; ++k) {
+            if (r0 + k < T) {
+                qv[k] = *reinterpret_cast<const float4*>(__builtin_assume_aligned(tab + 4u * off[k], 16));
+                rv[k] = *reinterpret_cast<const float*>(rtab + off[k]);
+            }
+        }
 #pragma unroll
         for (int k = 0; k < NB; ++k) {
             if (r0 + k < T) {
                 const int rho = r0 + k;
                 const float kv = (rho & 1) ? bf16_hi(kc[rho >> 1]) : bf16_lo(kc[rho >> 1]);
-                const float e = kv - te[k].r;
-#pragma unroll
-                for (int g = 0; g < G; ++g) s[g] = fmaf(te[k].q[g], e, s[g]);
+                const float e = kv - rv[k];
+                s[0] = fmaf(qv[k].x, e, s[0]);
+                s[1] = fmaf(qv[k].y, e, s[1]);
+                s[2] = fmaf(qv[k].z, e, s[2]);
+                s[3] = fmaf(qv[k].w, e, s[3]);
             }
         }
         // consume the partial sums here: otherwise the compiler sinks the
@@ -805,17 +811,22 @@ __device__ __forceinline__ void fast_tile(const DecodeArgs& a, int bh, const uns
 template <int G, int T>
 __global__ void __launch_bounds__(DECODE_FAST_THREADS)
 decode_fast_kernel(const DecodeArgs a) {
-    extern __shared__ __align__(16) unsigned char smem[];
-    constexpr uint32_t TAB = (uint32_t)sizeof(TabEntry<G>);
-    // per wave: the slot list (u8 [T][64]) during the scores, then the V
+    // statically sized LDS: its base address is a compile-time constant, so
+    // table offsets fold into the LDS instructions' offset fields
+    __shared__ __align__(16) unsigned char smem[DECODE_FAST_LDS_BYTES];
+    // tables: q'_0..q'_3 of the group as a float4 per channel (2 KiB), then
+    // r as one float per channel (512 bytes)
+    constexpr uint32_t TAB = 16u;
+    constexpr uint32_t TABLES = 128u * 16u + 128u * 4u;     // then a 16-byte flag slot
+    // per wave: the slot list (u16, lane-major) during the scores, then the V
     // tile (64 x 256 bytes) during P.V, in one region; then p as [G][64] fp32
     constexpr uint32_t LIST = 64u * 256u;
-    static_assert((uint32_t)T * 64u <= LIST, "list fits the V tile region");
+    static_assert(64u * list_stride<T>() * 2u <= LIST, "list fits the V tile region");
     constexpr uint32_t WAVE = LIST + 64u * G * 4u;
     constexpr int NW = DECODE_FAST_THREADS / 64;
     static_assert(T % 2 == 0 && T > 0 && T < 128, "fast path needs an even 0 < T < 128");
     unsigned char* tab = smem;
-    unsigned char* wbase = smem + 128 * TAB;
+    unsigned char* wbase = smem + TABLES + 16;
 
     const int bh = blockIdx.y;
     const int split = blockIdx.x;
@@ -836,8 +847,14 @@ decode_fast_kernel(const DecodeArgs a) {
     // arrived. The slot list and the table are built while the packed rows
     // and V rows stream in. The loads are unconditional (indices clamped into
     // the head) so that no register copy makes a wave wait early.
-    static_assert(128 * G == DECODE_FAST_THREADS, "one q value per thread");
-    const uint16_t qb = a.q[((size_t)b * a.N_q + (size_t)h * G + (tid >> 7)) * 128 + (tid & 127)];
+    static_assert((128 * G) % DECODE_FAST_THREADS == 0, "q values per thread");
+    constexpr int QPT = 128 * G / DECODE_FAST_THREADS;
+    uint16_t qb[QPT];
+#pragma unroll
+    for (int i = 0; i < QPT; ++i) {
+        const int j = tid + i * DECODE_FAST_THREADS;
+        qb[i] = a.q[((size_t)b * a.N_q + (size_t)h * G + (j >> 7)) * 128 + (j & 127)];
+    }
     const float rv = a.r[(size_t)bh * 128 + (tid & 127)];
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
@@ -850,23 +867,34 @@ decode_fast_kernel(const DecodeArgs a) {
     const int ntf0 = max(1, min(DECODE_TILE, blk_end - tf0));
     load_row<T>(a, bh, tf0, ntf0, L, mw, kr);
     __builtin_amdgcn_sched_barrier(0);
-    asm volatile("" ::"v"(mw.x), "v"(mw.y), "v"(mw.z), "v"(mw.w));   // wait for the masks only
-    load_v_tile(vbh, tf0, ntf0, L >> 4, L & 15, vr);
     __builtin_amdgcn_sched_barrier(0);
     uint8_t* lst = wbase + (size_t)wave * WAVE;
     float* ptab = reinterpret_cast<float*>(wbase + (size_t)wave * WAVE + LIST);
     // the first tile's slot list needs only its masks: build it before
-    // waiting for the table
-    build_list(mw, lst, L);
-    reinterpret_cast<TabEntry<G>*>(tab)[tid & 127].q[tid >> 7] = bf16_to_f32(qb) * a.qscale;
-    if (tid < 128) reinterpret_cast<TabEntry<G>*>(tab)[tid].r = rv;
+    // waiting for the table, then request the tile's V rows
+    build_list<T>(mw, lst, L);
+    __builtin_amdgcn_sched_barrier(0);
+    load_v_tile(vbh, tf0, ntf0, L >> 4, L & 15, vr);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < QPT; ++i) {
+        const int j = tid + i * DECODE_FAST_THREADS;
+        reinterpret_cast<float*>(tab + (j & 127) * TAB)[j >> 7] = bf16_to_f32(qb[i]) * a.qscale;
+    }
+    if (tid < 128) reinterpret_cast<float*>(tab + 128 * TAB)[tid] = rv;
     __syncthreads();
 
+    // q' . r per head
     float cq[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        const TabEntry<G>* te = reinterpret_cast<const TabEntry<G>*>(tab);
-        cq[g] = wave_sum_dpp(te[L].q[g] * te[L].r + te[L + 64].q[g] * te[L + 64].r);
+    {
+        const float4 e0 = *reinterpret_cast<const float4*>(tab + L * TAB);
+        const float4 e1 = *reinterpret_cast<const float4*>(tab + (L + 64) * TAB);
+        const float r0 = reinterpret_cast<const float*>(tab + 128 * TAB)[L];
+        const float r1 = reinterpret_cast<const float*>(tab + 128 * TAB)[L + 64];
+        cq[0] = wave_sum_dpp(e0.x * r0 + e1.x * r1);
+        cq[1] = wave_sum_dpp(e0.y * r0 + e1.y * r1);
+        cq[2] = wave_sum_dpp(e0.z * r0 + e1.z * r1);
+        cq[3] = wave_sum_dpp(e0.w * r0 + e1.w * r1);
     }
 
     float m_run[G], l_run[G];
@@ -900,66 +928,38 @@ decode_fast_kernel(const DecodeArgs a) {
     for (int g = 0; g < G; ++g)
 #pragma unroll
         for (int nb = 0; nb < 8; ++nb) acc[g][nb] = accm[nb][g];
-    finish_block<G, DECODE_FAST_THREADS, true>(a, m_run, l_run, acc, wbase, bh, b, h, split);
+    finish_block<G, DECODE_FAST_THREADS, true>(a, m_run, l_run, acc, wbase,
+                                               reinterpret_cast<int*>(smem + TABLES), bh, b, h, split);
 }
 
-// LDS bytes of the fast kernel: table, then per wave the list and p, or the
-// block / split merge scratch (reused after the tile loop).
+// LDS bytes the fast kernel needs: tables and flag, then per wave the list /
+// V tile region and p, or the block / split merge scratch (reused after the
+// tile loop). Must not exceed its static DECODE_FAST_LDS_BYTES.
 uint32_t decode_fast_lds_bytes(int G, int T, int nsplit) {
-    const uint32_t tab = 128u * (uint32_t)tab_stride_for(G);
+    const uint32_t tab = 128u * 16u + 128u * 4u + 16u;   // q' float4 and r per channel, flag
     const uint32_t list = 64u * 256u;     // slot list, then the V tile
     (void)T;
     const uint32_t waves = DECODE_FAST_THREADS / 64;
     uint32_t dyn = waves * (list + 64u * (uint32_t)G * 4u);
-    const uint32_t combine = waves * (2u * G + (uint32_t)G * 128u) * 4u;
-    const uint32_t merge = (((uint32_t)nsplit * 3u * G + G + 3u) & ~3u) * 4u + (uint32_t)DECODE_FAST_THREADS * 16u;
-    if (combine > dyn) dyn = combine;
-    if (merge > dyn) dyn = merge;
+    const uint32_t fin = finish_scratch_bytes(G, DECODE_FAST_THREADS, nsplit);
+    if (fin > dyn) dyn = fin;
     return tab + dyn;
 }
 
 bool decode_fast_supported(int G, int T) { return G == 4 && (T == 26 || T == 38 || T == 64); }
 
-static hipError_t launch_merge(const DecodeArgs& a, int G, int BH, hipStream_t stream) {
-#if DECODE_SEPARATE_MERGE
-    const dim3 grid(BH, G), block(128);
-    switch (G) {
-        case 1: hipLaunchKernelGGL(merge_kernel<1>, grid, block, 0, stream, a); break;
-        case 2: hipLaunchKernelGGL(merge_kernel<2>, grid, block, 0, stream, a); break;
-        case 4: hipLaunchKernelGGL(merge_kernel<4>, grid, block, 0, stream, a); break;
-        default: hipLaunchKernelGGL(merge_kernel<8>, grid, block, 0, stream, a); break;
-    }
-    return hipGetLastError();
-#else
-    (void)a; (void)G; (void)BH; (void)stream;
-    return hipSuccess;
-#endif
-}
 
-static hipError_t launch_split(const DecodeArgs& a, int G, int BH, hipStream_t stream);
-
+// One launch: the split blocks, the last of which per (b, KV head) merges.
 hipError_t launch_decode(const DecodeArgs& a, int G, int BH, hipStream_t stream) {
-    const hipError_t e = launch_split(a, G, BH, stream);
-    if (e != hipSuccess) return e;
-    return launch_merge(a, G, BH, stream);
-}
-
-static hipError_t launch_split(const DecodeArgs& a, int G, int BH, hipStream_t stream) {
     const dim3 grid(a.nsplit, BH), block(DECODE_THREADS);
     if (decode_fast_supported(G, a.T)) {
         const dim3 fblock(DECODE_FAST_THREADS);
-        const size_t lds = decode_fast_lds_bytes(G, a.T, a.nsplit);
-        const void* fn = a.T == 26 ? reinterpret_cast<const void*>(&decode_fast_kernel<4, 26>)
-                       : a.T == 38 ? reinterpret_cast<const void*>(&decode_fast_kernel<4, 38>)
-                                   : reinterpret_cast<const void*>(&decode_fast_kernel<4, 64>);
-        if (lds > 65536) {
-            const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-            if (e != hipSuccess) return e;
-        }
+        // the fast kernel's LDS is static (DECODE_FAST_LDS_BYTES)
+        if (decode_fast_lds_bytes(G, a.T, a.nsplit) > (uint32_t)DECODE_FAST_LDS_BYTES) return hipErrorInvalidValue;
         switch (a.T) {
-            case 26: hipLaunchKernelGGL((decode_fast_kernel<4, 26>), grid, fblock, lds, stream, a); break;
-            case 38: hipLaunchKernelGGL((decode_fast_kernel<4, 38>), grid, fblock, lds, stream, a); break;
-            default: hipLaunchKernelGGL((decode_fast_kernel<4, 64>), grid, fblock, lds, stream, a); break;
+            case 26: hipLaunchKernelGGL((decode_fast_kernel<4, 26>), grid, fblock, 0, stream, a); break;
+            case 38: hipLaunchKernelGGL((decode_fast_kernel<4, 38>), grid, fblock, 0, stream, a); break;
+            default: hipLaunchKernelGGL((decode_fast_kernel<4, 64>), grid, fblock, 0, stream, a); break;
         }
         return hipGetLastError();
     }
