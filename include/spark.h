@@ -140,6 +140,32 @@ int spark_decode_attn(const void* q, const void* k_packed, const uint32_t* mask,
  * `stream`; safe to record in a HIP graph). */
 int spark_decode_ws_init(void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Observation-window token eviction (SnapKV style), the stage SparK is
+ * stacked on in the pages' combination with eviction (walkthrough section
+ * 4.1; section 3.2 borrows the observation window). Not SparK itself.
+ * Per (b, KV head h): the G*W window queries q_win[b][hG+g][w] sit at
+ * positions S-W+w and see tokens t <= S-W+w; each row's softmax of
+ * q.k_t / sqrt(D) over those tokens is summed over the G*W rows into
+ * score[t]; the `keep` highest-scoring tokens (ties to the lower t) are kept.
+ *  q_win    bf16 [B][N_q][W][D]
+ *  k, v     bf16 [B][N_kv][S][D]
+ *  idx      int32 [B][N_kv][keep]  kept token indices, ascending
+ *  k_out, v_out  bf16 [B][N_kv][keep][D]  gathered rows; both NULL skips
+ *           the gather
+ *  scores   fp32 [B][N_kv][S]  window-summed scores (NULL: kept in ws)
+ * Logits run on the matrix cores (bf16 inputs, fp32 accumulation); two
+ * passes over K. Requires D = 128, G*W <= 128 and S <= 65536 (else
+ * SPARK_EUNSUPPORTED),
+ * 1 <= W <= S, 1 <= keep <= S (else SPARK_EINVAL). Scores that tie exactly in
+ * fp32 are broken by the lower t; scores are fp32, so tokens whose scores
+ * differ by less than their rounding error may be ordered either way.
+ */
+size_t spark_window_evict_workspace_bytes(int B, int S, int N_q, int N_kv, int D, int window);
+int spark_window_evict(const void* q_win, const void* k, const void* v, int B, int S, int N_q, int N_kv,
+                       int D, int window, int keep, int32_t* idx, void* k_out, void* v_out, float* scores,
+                       void* ws, size_t ws_bytes, void* stream);
+
 /* Diagnostic, not part of SparK: read `bytes` (a multiple of 16, 16-byte
  * aligned) from device memory with `blocks` x 256 threads, folding the data
  * into sink[0 .. blocks-1] (uint32, XOR-accumulated). Used to measure the

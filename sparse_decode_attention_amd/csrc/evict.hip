@@ -1,0 +1,342 @@
+// Observation-window token eviction (SnapKV style) on gfx950: the eviction
+// stage that SparK's channel pruning is stacked on in the compacted-cache
+// workload (SparK walkthrough section 4.1, where the method is combined with
+// SnapKV; section 3.2 takes its observation window from the same idea).
+//
+// Per (b, KV head h), the R = G*W window query rows (head hG+g, position
+// S-W+w, stacked in (g, w) order) score every cached token t <= S-W+w:
+//     logit[r][t] = q_r . k_t / sqrt(D),   p[r][t] = softmax over t of logit[r]
+//     score[t]    = sum over r of p[r][t]
+// and the `keep` highest-scoring tokens (ties to the lower t) are kept in
+// ascending t order, with their K and V rows gathered.
+//
+// The logits are a dense contraction (R x D times D x S), so they run on the
+// matrix cores (v_mfma_f32_16x16x32_bf16) with q and k as exact bf16 and fp32
+// accumulation. Two passes over K: (1) each row's max and sum of exp over its
+// visible tokens (per chunk, then combined), (2) the normalised sum over rows.
+// Then a radix select on the fp32 score bits and a gather.
+#include "common.h"
+#include "kernels.h"
+
+namespace spark {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Each wave owns EVICT_WAVE_ROWS window rows (two 16-row blocks); a block has
+// one wave per 32 rows and all its waves walk the same tokens.
+constexpr int MBW = EVICT_WAVE_ROWS / 16;
+
+// The wave's window rows as MFMA A operands: q[mb][kb] holds rows
+// r0 + 16 mb + (lane & 15), dims 32 kb + 8 (lane >> 4) .. +8 (rows past R
+// are zero).
+__device__ __forceinline__ void load_rows(const EvictArgs& a, int b, int h, int r0, int L, bf16x8 (&q)[MBW][4]) {
+    const int G = a.N_q / a.N_kv;
+#pragma unroll
+    for (int mb = 0; mb < MBW; ++mb) {
+        const int r = r0 + 16 * mb + (L & 15);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (r < a.R) {
+                const int g = r / a.W, w = r % a.W;
+                const uint16_t* src = a.q_win + (((size_t)b * a.N_q + (size_t)h * G + g) * a.W + w) * 128 + 32 * kb +
+                                      8 * (L >> 4);
+                v = *reinterpret_cast<const uint4*>(src);
+            }
+            q[mb][kb] = __builtin_bit_cast(bf16x8, v);
+        }
+    }
+}
+
+// B operands of 16 tokens t0 .. t0+15: lane holds token t0 + (lane & 15),
+// dims 32 kb + 8 (lane >> 4) .. +8 (tokens past S read row S-1).
+__device__ __forceinline__ void load_keys(const EvictArgs& a, const uint16_t* kbh, int t0, int L, uint4 (&kv)[4]) {
+    const int tc = min(t0 + (L & 15), a.S - 1);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) kv[kb] = *reinterpret_cast<const uint4*>(kbh + (size_t)tc * 128 + 32 * kb + 8 * (L >> 4));
+}
+
+// Logits times log2(e)/sqrt(D): s[mb][e] is row r0 + 16 mb + 4 (lane >> 4) + e,
+// token t0 + (lane & 15); tokens past S or not visible to the row are -inf.
+__device__ __forceinline__ void logits16(const EvictArgs& a, const bf16x8 (&q)[MBW][4], const uint4 (&kv)[4], int r0,
+                                         int t0, int L, f32x4 (&s)[MBW]) {
+#pragma unroll
+    for (int mb = 0; mb < MBW; ++mb) {
+        f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q[mb][kb], __builtin_bit_cast(bf16x8, kv[kb]), c, 0, 0, 0);
+        s[mb] = c * a.scale_log2;
+    }
+    // visibility: row r (window position w = r % W) sees t <= S - W + w
+    if (t0 + 15 > a.S - a.W) {
+        const int t = t0 + (L & 15);
+#pragma unroll
+        for (int mb = 0; mb < MBW; ++mb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = r0 + 16 * mb + 4 * (L >> 4) + e;
+                if (t >= a.S || r >= a.R || t > a.S - a.W + r % a.W) s[mb][e] = -INFINITY;
+            }
+    }
+}
+
+// (m, l) of two partial softmax sums over disjoint token sets, base 2.
+__device__ __forceinline__ void ml_merge(float& m, float& l, float mo, float lo) {
+    const float mn = fmaxf(m, mo);
+    l = l * exp2f(m - mn) + lo * exp2f(mo - mn);
+    m = mn;
+}
+
+}  // namespace
+
+// Pass 1: per (b*N_kv + h, chunk of EVICT_CHUNK tokens), each row's max and
+// sum of exp2 over the chunk's visible tokens. The next 16 tokens' keys are
+// requested before the current ones are used.
+__global__ void __launch_bounds__(EVICT_MAX_ROWS / EVICT_WAVE_ROWS * 64) evict_stats_kernel(const EvictArgs a) {
+    const int bh = blockIdx.y, chunk = blockIdx.x;
+    const int b = bh / a.N_kv, h = bh % a.N_kv;
+    const int L = threadIdx.x & 63;
+    const int r0 = (threadIdx.x >> 6) * EVICT_WAVE_ROWS;
+    bf16x8 q[MBW][4];
+    load_rows(a, b, h, r0, L, q);
+    const uint16_t* kbh = a.k + (size_t)bh * a.S * 128;
+    // running (m, l) per lane for its rows and its token column; a finite
+    // start keeps fully masked columns free of inf - inf
+    float m[MBW][4], l[MBW][4];
+#pragma unroll
+    for (int mb = 0; mb < MBW; ++mb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { m[mb][e] = -1e30f; l[mb][e] = 0.f; }
+    const int tb = chunk * EVICT_CHUNK, te = min(a.S, tb + EVICT_CHUNK);
+    uint4 kv[4], kn[4];
+    load_keys(a, kbh, tb, L, kv);
+    for (int t0 = tb; t0 < te; t0 += 16) {
+        if (t0 + 16 < te) load_keys(a, kbh, t0 + 16, L, kn);
+        f32x4 s[MBW];
+        logits16(a, q, kv, r0, t0, L, s);
+#pragma unroll
+        for (int mb = 0; mb < MBW; ++mb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float mn = fmaxf(m[mb][e], s[mb][e]);
+                l[mb][e] = l[mb][e] * exp2f(m[mb][e] - mn) + exp2f(s[mb][e] - mn);
+                m[mb][e] = mn;
+            }
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) kv[kb] = kn[kb];
+    }
+    // combine the 16 token columns (lanes with the same lane >> 4)
+#pragma unroll
+    for (int mb = 0; mb < MBW; ++mb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+#pragma unroll
+            for (int o = 1; o < 16; o <<= 1) {
+                const float mo = __shfl_xor(m[mb][e], o, 64);
+                const float lo = __shfl_xor(l[mb][e], o, 64);
+                ml_merge(m[mb][e], l[mb][e], mo, lo);
+            }
+        }
+    if ((L & 15) == 0) {
+        float* out = a.part + ((size_t)bh * gridDim.x + chunk) * EVICT_MAX_ROWS * 2;
+#pragma unroll
+        for (int mb = 0; mb < MBW; ++mb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = r0 + 16 * mb + 4 * (L >> 4) + e;
+                out[2 * r] = m[mb][e];
+                out[2 * r + 1] = l[mb][e];
+            }
+    }
+}
+
+// Per (b*N_kv + h, row): combine the chunks' (m, l) in chunk order; store
+// (M, 1 / L). Loads are issued eight chunks at a time.
+__global__ void evict_combine_kernel(const EvictArgs a, int nchunk) {
+    const int bh = blockIdx.x, r = threadIdx.x;
+    if (r >= EVICT_MAX_ROWS) return;
+    const float2* p = reinterpret_cast<const float2*>(a.part + (size_t)bh * nchunk * EVICT_MAX_ROWS * 2) + r;
+    float m = -1e30f, l = 0.f;
+    for (int c0 = 0; c0 < nchunk; c0 += 8) {
+        float2 v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = c0 + i < nchunk ? p[(size_t)(c0 + i) * EVICT_MAX_ROWS] : make_float2(-1e30f, 0.f);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ml_merge(m, l, v[i].x, v[i].y);
+    }
+    a.rowstat[((size_t)bh * EVICT_MAX_ROWS + r) * 2] = m;
+    a.rowstat[((size_t)bh * EVICT_MAX_ROWS + r) * 2 + 1] = l > 0.f ? 1.0f / l : 0.f;
+}
+
+// Pass 2: score[t] = sum over rows of exp2(s - M) / L for the chunk's tokens;
+// each wave sums its rows, the waves' sums meet in LDS.
+__global__ void __launch_bounds__(EVICT_MAX_ROWS / EVICT_WAVE_ROWS * 64) evict_score_kernel(const EvictArgs a) {
+    constexpr int NWV = EVICT_MAX_ROWS / EVICT_WAVE_ROWS;
+    __shared__ float part[NWV][EVICT_CHUNK];
+    const int bh = blockIdx.y, chunk = blockIdx.x;
+    const int b = bh / a.N_kv, h = bh % a.N_kv;
+    const int L = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r0 = wave * EVICT_WAVE_ROWS;
+    bf16x8 q[MBW][4];
+    load_rows(a, b, h, r0, L, q);
+    float M[MBW][4], iL[MBW][4];
+#pragma unroll
+    for (int mb = 0; mb < MBW; ++mb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = r0 + 16 * mb + 4 * (L >> 4) + e;
+            M[mb][e] = a.rowstat[((size_t)bh * EVICT_MAX_ROWS + r) * 2];
+            iL[mb][e] = r < a.R ? a.rowstat[((size_t)bh * EVICT_MAX_ROWS + r) * 2 + 1] : 0.f;
+        }
+    const uint16_t* kbh = a.k + (size_t)bh * a.S * 128;
+    const int tb = chunk * EVICT_CHUNK, te = min(a.S, tb + EVICT_CHUNK);
+    uint4 kv[4], kn[4];
+    load_keys(a, kbh, tb, L, kv);
+    for (int t0 = tb; t0 < te; t0 += 16) {
+        if (t0 + 16 < te) load_keys(a, kbh, t0 + 16, L, kn);
+        f32x4 s[MBW];
+        logits16(a, q, kv, r0, t0, L, s);
+        float acc = 0.f;
+#pragma unroll
+        for (int mb = 0; mb < MBW; ++mb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc = fmaf(exp2f(s[mb][e] - M[mb][e]), iL[mb][e], acc);
+        // rows 4 (lane >> 4) + e of every block: add the four lane quarters
+        acc = xor32_sum(xor16_sum(acc));
+        if (L < 16) part[wave][t0 - tb + L] = acc;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) kv[kb] = kn[kb];
+    }
+    __syncthreads();
+    float* sc = a.scores + (size_t)bh * a.S;
+    for (int i = threadIdx.x; i < te - tb; i += blockDim.x) {
+        float v = 0.f;
+#pragma unroll
+        for (int w = 0; w < NWV; ++w) v += part[w][i];
+        sc[tb + i] = v;
+    }
+}
+
+// Per (b*N_kv + h): the `keep` largest scores (fp32 >= 0, compared as their
+// uint32 bits), ties to the lower t, written to idx in ascending t. Bitwise
+// radix select from the top bit (counts by wave sums, no atomics), then an
+// ordered compaction. Each thread owns a contiguous run of at most PER tokens,
+// held in registers.
+template <int PER>
+__global__ void __launch_bounds__(EVICT_SELECT_THREADS) evict_select_kernel(const EvictArgs a) {
+    constexpr int NWV = EVICT_SELECT_THREADS / 64;
+    __shared__ uint32_t wsum[2][NWV];
+    __shared__ uint32_t scan[EVICT_SELECT_THREADS];
+    const int bh = blockIdx.x;
+    const int tid = threadIdx.x, L = tid & 63, wave = tid >> 6;
+    const uint32_t* u = reinterpret_cast<const uint32_t*>(a.scores) + (size_t)bh * a.S;
+    const int S = a.S;
+    const int t_begin = min(S, tid * PER), n = min(S, t_begin + PER) - t_begin;
+    uint32_t x[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) x[i] = i < n ? u[t_begin + i] : 0u;
+    // prefix of the keep-th largest value, found bit by bit: among values
+    // whose higher bits equal the prefix, count those with this bit set
+    uint32_t prefix = 0, krem = (uint32_t)a.keep;
+    for (int bit = 31; bit >= 0; --bit) {
+        uint32_t c = 0;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) c += (i < n) && (((x[i] ^ prefix) >> bit) == 1u);
+        const float cw = wave_sum_dpp((float)c);                   // exact: counts < 2^24
+        if (L == 0) wsum[bit & 1][wave] = (uint32_t)cw;
+        __syncthreads();
+        uint32_t total = 0;
+#pragma unroll
+        for (int w = 0; w < NWV; ++w) total += wsum[bit & 1][w];
+        if (total >= krem) prefix |= 1u << bit;
+        else krem -= total;
+    }
+    // keep every x > prefix and the first krem tokens with x == prefix
+    uint32_t n_eq = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) n_eq += (i < n) && (x[i] == prefix);
+    scan[tid] = n_eq;
+    __syncthreads();
+    for (int o = 1; o < EVICT_SELECT_THREADS; o <<= 1) {
+        const uint32_t v = tid >= o ? scan[tid - o] : 0u;
+        __syncthreads();
+        scan[tid] += v;
+        __syncthreads();
+    }
+    const uint32_t eq_before = scan[tid] - n_eq;
+    __syncthreads();
+    uint32_t n_keep = 0;
+    {
+        uint32_t e = eq_before;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            if (i < n) {
+                if (x[i] > prefix) ++n_keep;
+                else if (x[i] == prefix) { if (e < krem) ++n_keep; ++e; }
+            }
+        }
+    }
+    scan[tid] = n_keep;
+    __syncthreads();
+    for (int o = 1; o < EVICT_SELECT_THREADS; o <<= 1) {
+        const uint32_t v = tid >= o ? scan[tid - o] : 0u;
+        __syncthreads();
+        scan[tid] += v;
+        __syncthreads();
+    }
+    uint32_t pos = scan[tid] - n_keep;
+    int32_t* idx = a.idx + (size_t)bh * a.keep;
+    uint32_t e = eq_before;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        if (i < n) {
+            bool k = x[i] > prefix;
+            if (x[i] == prefix) { k = e < krem; ++e; }
+            if (k && pos < (uint32_t)a.keep) idx[pos++] = t_begin + i;
+        }
+    }
+}
+
+// K and V rows of the kept tokens: one 16-byte chunk per thread.
+__global__ void evict_gather_kernel(const EvictArgs a) {
+    const size_t n = (size_t)a.BH * a.keep * 16;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
+        const size_t row = i >> 4;                  // bh * keep + j
+        const int c = (int)(i & 15);
+        const size_t bh = row / a.keep;
+        const int t = min(max(a.idx[row], 0), a.S - 1);   // indices come from the select kernel
+        const size_t src = ((size_t)bh * a.S + t) * 128 + 8 * c;
+        reinterpret_cast<uint4*>(a.k_out)[row * 16 + c] = *reinterpret_cast<const uint4*>(a.k + src);
+        reinterpret_cast<uint4*>(a.v_out)[row * 16 + c] = *reinterpret_cast<const uint4*>(a.v + src);
+    }
+}
+
+hipError_t launch_evict(const EvictArgs& a, hipStream_t stream) {
+    const int nchunk = (a.S + EVICT_CHUNK - 1) / EVICT_CHUNK;
+    const dim3 blk(EVICT_MAX_ROWS / EVICT_WAVE_ROWS * 64);
+    hipLaunchKernelGGL(evict_stats_kernel, dim3(nchunk, a.BH), blk, 0, stream, a);
+    hipLaunchKernelGGL(evict_combine_kernel, dim3(a.BH), dim3(EVICT_MAX_ROWS), 0, stream, a, nchunk);
+    hipLaunchKernelGGL(evict_score_kernel, dim3(nchunk, a.BH), blk, 0, stream, a);
+    const int per = (a.S + EVICT_SELECT_THREADS - 1) / EVICT_SELECT_THREADS;
+    if (per <= 8) hipLaunchKernelGGL(evict_select_kernel<8>, dim3(a.BH), dim3(EVICT_SELECT_THREADS), 0, stream, a);
+    else if (per <= 32) hipLaunchKernelGGL(evict_select_kernel<32>, dim3(a.BH), dim3(EVICT_SELECT_THREADS), 0, stream, a);
+    else if (per <= 64) hipLaunchKernelGGL(evict_select_kernel<64>, dim3(a.BH), dim3(EVICT_SELECT_THREADS), 0, stream, a);
+    else return hipErrorInvalidValue;
+    if (a.k_out != nullptr) {
+        const size_t n = (size_t)a.BH * a.keep * 16;
+        const int blocks = (int)((n + 255) / 256 < 65535 ? (n + 255) / 256 : 65535);
+        hipLaunchKernelGGL(evict_gather_kernel, dim3(blocks), dim3(256), 0, stream, a);
+    }
+    return hipGetLastError();
+}
+
+size_t evict_part_floats(int BH, int S) {
+    const size_t nchunk = (size_t)(S + EVICT_CHUNK - 1) / EVICT_CHUNK;
+    return (size_t)BH * nchunk * EVICT_MAX_ROWS * 2;
+}
+
+}  // namespace spark

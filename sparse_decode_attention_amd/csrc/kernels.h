@@ -13,6 +13,12 @@
 #define DECODE_FAST_LDS_BYTES (2576 + (DECODE_FAST_THREADS / 64) * (16384 + 1024))
 #define DECODE_TILE 64
 #define DECODE_MAX_SPLITS 256
+// window eviction: at most 128 stacked window rows (G * W), tokens per block
+#define EVICT_MAX_ROWS 128
+#define EVICT_WAVE_ROWS 32
+#define EVICT_CHUNK 512
+#define EVICT_SELECT_THREADS 1024
+#define EVICT_MAX_S (EVICT_SELECT_THREADS * 64)   // tokens per (b, KV head) the select handles
 
 namespace spark {
 
@@ -58,6 +64,23 @@ struct DecodeArgs {
     float qscale;             // softmax scale * log2(e)
     DecodeLayout lay;
 };
+
+struct EvictArgs {
+    const uint16_t* q_win;    // [B][N_q][W][128]
+    const uint16_t* k;        // [B][N_kv][S][128]
+    const uint16_t* v;        // [B][N_kv][S][128]
+    int32_t* idx;             // [B][N_kv][keep]
+    uint16_t* k_out;          // [B][N_kv][keep][128] or null (then v_out too: no gather)
+    uint16_t* v_out;
+    float* scores;            // [B][N_kv][S]
+    float* part;              // [B*N_kv][nchunk][EVICT_MAX_ROWS][2]
+    float* rowstat;           // [B*N_kv][EVICT_MAX_ROWS][2]
+    int BH, S, N_q, N_kv, W, R, keep;
+    float scale_log2;         // log2(e) / sqrt(D)
+};
+
+hipError_t launch_evict(const EvictArgs& a, hipStream_t stream);
+size_t evict_part_floats(int BH, int S);
 
 hipError_t launch_read_stream(const void* src, size_t bytes, uint32_t* sink, int blocks, hipStream_t stream);
 

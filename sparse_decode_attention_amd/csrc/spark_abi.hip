@@ -219,6 +219,55 @@ int spark_decode_ws_init(void* ws, size_t ws_bytes, void* stream) {
     return hip_status(hipGetLastError());
 }
 
+// window eviction workspace: chunk (m, l) partials, per-row (M, 1/L), scores
+static size_t evict_ws_bytes(int BH, int S) {
+    return round_up(evict_part_floats(BH, S) * sizeof(float), 256) +
+           round_up((size_t)BH * EVICT_MAX_ROWS * 2 * sizeof(float), 256) + round_up((size_t)BH * S * sizeof(float), 256);
+}
+
+size_t spark_window_evict_workspace_bytes(int B, int S, int N_q, int N_kv, int D, int window) {
+    if (B < 1 || S < 1 || N_kv < 1 || N_q < 1 || D < 1 || window < 1 || N_q % N_kv) return 0;
+    return evict_ws_bytes(B * N_kv, S);
+}
+
+int spark_window_evict(const void* q_win, const void* k, const void* v, int B, int S, int N_q, int N_kv, int D,
+                       int window, int keep, int32_t* idx, void* k_out, void* v_out, float* scores, void* ws,
+                       size_t ws_bytes, void* stream) {
+    if (B < 1 || S < 1 || D < 1 || window < 1 || window > S || keep < 1 || keep > S) return SPARK_EINVAL;
+    if (int e = check_group(N_q, N_kv)) return e;
+    if (D != 128) return SPARK_EUNSUPPORTED;
+    const int G = N_q / N_kv;
+    if ((long)G * window > EVICT_MAX_ROWS || S > EVICT_MAX_S) return SPARK_EUNSUPPORTED;
+    if (!q_win || !k || !idx || !ws || ((k_out == nullptr) != (v_out == nullptr)) || (k_out && !v)) return SPARK_EINVAL;
+    if (!aligned(q_win, 16) || !aligned(k, 16) || (v && !aligned(v, 16)) || !aligned(idx, 4) ||
+        (k_out && (!aligned(k_out, 16) || !aligned(v_out, 16))) || (scores && !aligned(scores, 4)) || !aligned(ws, 256))
+        return SPARK_EALIGN;
+    const int BH = B * N_kv;
+    if (ws_bytes < evict_ws_bytes(BH, S)) return SPARK_ENOSPACE;
+    char* base = static_cast<char*>(ws);
+    EvictArgs a{};
+    a.q_win = static_cast<const uint16_t*>(q_win);
+    a.k = static_cast<const uint16_t*>(k);
+    a.v = static_cast<const uint16_t*>(v);
+    a.idx = idx;
+    a.k_out = static_cast<uint16_t*>(k_out);
+    a.v_out = static_cast<uint16_t*>(v_out);
+    a.part = reinterpret_cast<float*>(base);
+    base += round_up(evict_part_floats(BH, S) * sizeof(float), 256);
+    a.rowstat = reinterpret_cast<float*>(base);
+    base += round_up((size_t)BH * EVICT_MAX_ROWS * 2 * sizeof(float), 256);
+    a.scores = scores ? scores : reinterpret_cast<float*>(base);
+    a.BH = BH;
+    a.S = S;
+    a.N_q = N_q;
+    a.N_kv = N_kv;
+    a.W = window;
+    a.R = G * window;
+    a.keep = keep;
+    a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
+    return hip_status(launch_evict(a, static_cast<hipStream_t>(stream)));
+}
+
 int spark_read_stream(const void* src, size_t bytes, uint32_t* sink, int blocks, void* stream) {
     if (!src || !sink || blocks < 1 || blocks > 65535) return SPARK_EINVAL;
     if (!aligned(src, 16) || (bytes & 15)) return SPARK_EALIGN;

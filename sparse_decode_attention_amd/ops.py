@@ -38,6 +38,8 @@ _SIGS = {
     "spark_decode_attn": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _f, _i, _vp, _vp, _sz, _vp]),
     "spark_decode_ws_init": (_i, [_vp, _sz, _vp]),
     "spark_read_stream": (_i, [_vp, _sz, _vp, _i, _vp]),
+    "spark_window_evict_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "spark_window_evict": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
 }
 
 
@@ -195,3 +197,34 @@ def read_stream(src: torch.Tensor, sink: torch.Tensor, blocks: int = 2048) -> No
     """Diagnostic streaming read of `src` (measures the practical HBM read rate)."""
     _check("spark_read_stream", lib().spark_read_stream(_ptr(src), src.numel() * src.element_size(),
                                                         _ptr(sink), int(blocks), _stream(src.device)))
+
+
+def window_evict(q_win: torch.Tensor, k: torch.Tensor, v: torch.Tensor | None, n_kv: int, keep: int,
+                 gather: bool = True, scores: torch.Tensor | None = None) -> dict:
+    """spark_window_evict: q_win bf16 [B][N_q][W][D], k/v bf16 [B][N_kv][S][D].
+
+    Returns {"idx" int32 [B][N_kv][keep], "scores" fp32 [B][N_kv][S] (if
+    requested or allocated here), "k", "v" bf16 [B][N_kv][keep][D] (gather)}.
+    """
+    B, N_q, W, D = q_win.shape
+    S = k.shape[2]
+    _need(q_win, "q_win", torch.bfloat16)
+    _need(k, "k", torch.bfloat16, (B, n_kv, S, D))
+    if gather:
+        _need(v, "v", torch.bfloat16, (B, n_kv, S, D))
+    dev = k.device
+    idx = torch.empty((B, n_kv, keep), dtype=torch.int32, device=dev)
+    o = {"idx": idx}
+    if scores is None:
+        scores = torch.empty((B, n_kv, S), dtype=torch.float32, device=dev)
+    o["scores"] = scores
+    if gather:
+        o["k"] = torch.empty((B, n_kv, keep, D), dtype=torch.bfloat16, device=dev)
+        o["v"] = torch.empty((B, n_kv, keep, D), dtype=torch.bfloat16, device=dev)
+    nb = int(lib().spark_window_evict_workspace_bytes(B, S, N_q, n_kv, D, W))
+    ws = workspace(dev, "evict", nb)
+    st = lib().spark_window_evict(_ptr(q_win), _ptr(k), _ptr(v) if gather else None, B, S, N_q, n_kv, D, W, keep,
+                                  _ptr(idx), _ptr(o.get("k")), _ptr(o.get("v")), _ptr(scores), _ptr(ws), ws.numel(),
+                                  _stream(dev))
+    _check("spark_window_evict", st)
+    return o

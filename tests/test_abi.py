@@ -130,3 +130,28 @@ def test_read_stream_checks():
     assert l.spark_read_stream(FAKE, 16, FAKE, 0, None) == ops.EINVAL
     assert l.spark_read_stream(FAKE + 8, 16, FAKE, 4, None) == ops.EALIGN
     assert l.spark_read_stream(FAKE, 24, FAKE, 4, None) == ops.EALIGN
+
+
+def test_window_evict_checks():
+    l = ops.lib()
+    assert l.spark_window_evict_workspace_bytes(8, 32768, 32, 8, 128, 32) > 0
+    assert l.spark_window_evict_workspace_bytes(8, 32768, 30, 8, 128, 32) == 0
+
+    def call(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, B=1, S=1024, N_q=32, N_kv=8, D=128, W=32, keep=128, idx=FAKE,
+                 ko=FAKE, vo=FAKE, sc=None, ws=FAKE, nws=0)
+        a.update(kw)
+        return l.spark_window_evict(a["q"], a["k"], a["v"], a["B"], a["S"], a["N_q"], a["N_kv"], a["D"], a["W"],
+                                    a["keep"], a["idx"], a["ko"], a["vo"], a["sc"], a["ws"], a["nws"], None)
+    assert call(keep=0) == ops.EINVAL
+    assert call(keep=1025) == ops.EINVAL
+    assert call(W=0) == ops.EINVAL
+    assert call(W=1025) == ops.EINVAL
+    assert call(N_q=30) == ops.EINVAL
+    assert call(D=64) == ops.EUNSUPPORTED
+    assert call(N_q=64, W=64) == ops.EUNSUPPORTED          # G * W = 512 window rows
+    assert call(ko=None) == ops.EINVAL                      # k_out and v_out go together
+    assert call(idx=None) == ops.EINVAL
+    assert call(k=MIS) == ops.EALIGN
+    assert call(ws=FAKE + 16) == ops.EALIGN
+    assert call() == ops.ENOSPACE
