@@ -24,6 +24,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Each wave owns EVICT_WAVE_ROWS window rows (two 16-row blocks); a block has
 // one wave per 32 rows and all its waves walk the same tokens.
@@ -51,29 +52,54 @@ __device__ __forceinline__ void load_rows(const EvictArgs& a, int b, int h, int 
     }
 }
 
-// B operands of 16 tokens t0 .. t0+15: lane holds token t0 + (lane & 15),
-// dims 32 kb + 8 (lane >> 4) .. +8 (tokens past S read row S-1).
-__device__ __forceinline__ void load_keys(const EvictArgs& a, const uint16_t* kbh, int t0, int L, uint4 (&kv)[4]) {
-    const int tc = min(t0 + (L & 15), a.S - 1);
+// K tiles of EVICT_TILE tokens pass through LDS: every wave of the block
+// loads a quarter of the next tiles into registers (coalesced 16-byte chunks:
+// lanes 0-15 read one 256-byte row), writes it to one of two LDS buffers,
+// and after a barrier all waves read their MFMA B operands from it. Rows are
+// padded to 272 bytes to spread the B-operand reads over the banks.
+constexpr int TILE_ROW = 128 * 2 + 16;
+constexpr int TILE_BYTES = EVICT_TILE * TILE_ROW;
+constexpr int NWV = EVICT_MAX_ROWS / EVICT_WAVE_ROWS;
+constexpr int CPL = EVICT_TILE * 16 / (NWV * 64);   // 16-byte chunks per lane per tile
+
+__device__ __forceinline__ void fetch_tile(const EvictArgs& a, const uint16_t* kbh, int t0, int tid, u32x4 (&r)[CPL]) {
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) kv[kb] = *reinterpret_cast<const uint4*>(kbh + (size_t)tc * 128 + 32 * kb + 8 * (L >> 4));
+    for (int j = 0; j < CPL; ++j) {
+        const int c = tid + j * NWV * 64;             // chunk of the tile: token c >> 4, dims 8 (c & 15)
+        const int t = min(t0 + (c >> 4), a.S - 1);
+        r[j] = *reinterpret_cast<const u32x4*>(kbh + (size_t)t * 128 + 8 * (c & 15));
+    }
 }
 
-// Logits times log2(e)/sqrt(D): s[mb][e] is row r0 + 16 mb + 4 (lane >> 4) + e,
-// token t0 + (lane & 15); tokens past S or not visible to the row are -inf.
-__device__ __forceinline__ void logits16(const EvictArgs& a, const bf16x8 (&q)[MBW][4], const uint4 (&kv)[4], int r0,
-                                         int t0, int L, f32x4 (&s)[MBW]) {
+__device__ __forceinline__ void stash_tile(unsigned char* buf, int tid, const u32x4 (&r)[CPL]) {
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+        const int c = tid + j * NWV * 64;
+        *reinterpret_cast<u32x4*>(buf + (c >> 4) * TILE_ROW + 16 * (c & 15)) = r[j];
+    }
+}
+
+// Logits times log2(e)/sqrt(D) of the wave's rows against tokens t0 + 16 n ..
+// +15 of the LDS tile: s[mb][e] is row r0 + 16 mb + 4 (lane >> 4) + e, token
+// t0 + 16 n + (lane & 15); tokens past S or not visible to the row are -inf.
+__device__ __forceinline__ void logits16(const EvictArgs& a, const bf16x8 (&q)[MBW][4], const unsigned char* buf, int n,
+                                         int r0, int t0, int L, f32x4 (&s)[MBW]) {
+    bf16x8 kv[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+        kv[kb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(buf + (16 * n + (L & 15)) * TILE_ROW + 64 * kb +
+                                                                           16 * (L >> 4)));
 #pragma unroll
     for (int mb = 0; mb < MBW; ++mb) {
         f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q[mb][kb], __builtin_bit_cast(bf16x8, kv[kb]), c, 0, 0, 0);
+        for (int kb = 0; kb < 4; ++kb) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q[mb][kb], kv[kb], c, 0, 0, 0);
         s[mb] = c * a.scale_log2;
     }
+    const int tn = t0 + 16 * n;
     // visibility: row r (window position w = r % W) sees t <= S - W + w
-    if (t0 + 15 > a.S - a.W) {
-        const int t = t0 + (L & 15);
+    if (tn + 15 > a.S - a.W) {
+        const int t = tn + (L & 15);
 #pragma unroll
         for (int mb = 0; mb < MBW; ++mb)
 #pragma unroll
@@ -81,6 +107,31 @@ __device__ __forceinline__ void logits16(const EvictArgs& a, const bf16x8 (&q)[M
                 const int r = r0 + 16 * mb + 4 * (L >> 4) + e;
                 if (t >= a.S || r >= a.R || t > a.S - a.W + r % a.W) s[mb][e] = -INFINITY;
             }
+    }
+}
+
+// Walk the block's chunk tile by tile: the next two tiles are in flight in
+// registers while the current one is used from LDS. f.tile(buf, t0) handles
+// the EVICT_TILE tokens from t0 of the tile in buf.
+template <typename F>
+__device__ __forceinline__ void walk_tiles(const EvictArgs& a, const uint16_t* kbh, int tb, int te, unsigned char* lds,
+                                           F& f) {
+    const int tid = threadIdx.x;
+    u32x4 ra[CPL], rb[CPL];
+    fetch_tile(a, kbh, tb, tid, ra);
+    if (tb + EVICT_TILE < te) fetch_tile(a, kbh, tb + EVICT_TILE, tid, rb);
+    unsigned char* b0 = lds;
+    unsigned char* b1 = lds + TILE_BYTES;
+    for (int t0 = tb; t0 < te; t0 += 2 * EVICT_TILE) {
+        stash_tile(b0, tid, ra);
+        if (t0 + 2 * EVICT_TILE < te) fetch_tile(a, kbh, t0 + 2 * EVICT_TILE, tid, ra);
+        __syncthreads();
+        f.tile(b0, t0);
+        if (t0 + EVICT_TILE >= te) break;
+        stash_tile(b1, tid, rb);
+        if (t0 + 3 * EVICT_TILE < te) fetch_tile(a, kbh, t0 + 3 * EVICT_TILE, tid, rb);
+        __syncthreads();
+        f.tile(b1, t0 + EVICT_TILE);
     }
 }
 
@@ -94,9 +145,9 @@ __device__ __forceinline__ void ml_merge(float& m, float& l, float mo, float lo)
 }  // namespace
 
 // Pass 1: per (b*N_kv + h, chunk of EVICT_CHUNK tokens), each row's max and
-// sum of exp2 over the chunk's visible tokens. The next 16 tokens' keys are
-// requested before the current ones are used.
-__global__ void __launch_bounds__(EVICT_MAX_ROWS / EVICT_WAVE_ROWS * 64) evict_stats_kernel(const EvictArgs a) {
+// sum of exp2 over the chunk's visible tokens.
+__global__ void __launch_bounds__(NWV * 64) evict_stats_kernel(const EvictArgs a) {
+    __shared__ __align__(16) unsigned char lds[2 * TILE_BYTES];
     const int bh = blockIdx.y, chunk = blockIdx.x;
     const int b = bh / a.N_kv, h = bh % a.N_kv;
     const int L = threadIdx.x & 63;
@@ -112,23 +163,40 @@ __global__ void __launch_bounds__(EVICT_MAX_ROWS / EVICT_WAVE_ROWS * 64) evict_s
 #pragma unroll
         for (int e = 0; e < 4; ++e) { m[mb][e] = -1e30f; l[mb][e] = 0.f; }
     const int tb = chunk * EVICT_CHUNK, te = min(a.S, tb + EVICT_CHUNK);
-    uint4 kv[4], kn[4];
-    load_keys(a, kbh, tb, L, kv);
-    for (int t0 = tb; t0 < te; t0 += 16) {
-        if (t0 + 16 < te) load_keys(a, kbh, t0 + 16, L, kn);
-        f32x4 s[MBW];
-        logits16(a, q, kv, r0, t0, L, s);
+    struct Stats {
+        const EvictArgs& a;
+        const bf16x8 (&q)[MBW][4];
+        float (&m)[MBW][4];
+        float (&l)[MBW][4];
+        int r0, L, te;
+        // the tile's logits first, then one rescale per row and tile
+        __device__ __forceinline__ void tile(const unsigned char* buf, int t0) {
+            constexpr int NB = EVICT_TILE / 16;
+            f32x4 s[NB][MBW];
 #pragma unroll
-        for (int mb = 0; mb < MBW; ++mb)
+            for (int n = 0; n < NB; ++n) {
+                if (t0 + 16 * n < te) logits16(a, q, buf, n, r0, t0, L, s[n]);
+                else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float mn = fmaxf(m[mb][e], s[mb][e]);
-                l[mb][e] = l[mb][e] * exp2f(m[mb][e] - mn) + exp2f(s[mb][e] - mn);
-                m[mb][e] = mn;
+                    for (int mb = 0; mb < MBW; ++mb) s[n][mb] = (f32x4){-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+                }
             }
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) kv[kb] = kn[kb];
-    }
+            for (int mb = 0; mb < MBW; ++mb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float mn = m[mb][e];
+#pragma unroll
+                    for (int n = 0; n < NB; ++n) mn = fmaxf(mn, s[n][mb][e]);
+                    float acc = l[mb][e] * exp2f(m[mb][e] - mn);
+#pragma unroll
+                    for (int n = 0; n < NB; ++n) acc += exp2f(s[n][mb][e] - mn);
+                    l[mb][e] = acc;
+                    m[mb][e] = mn;
+                }
+        }
+    } f{a, q, m, l, r0, L, te};
+    walk_tiles(a, kbh, tb, te, lds, f);
     // combine the 16 token columns (lanes with the same lane >> 4)
 #pragma unroll
     for (int mb = 0; mb < MBW; ++mb)
@@ -174,8 +242,8 @@ __global__ void evict_combine_kernel(const EvictArgs a, int nchunk) {
 
 // Pass 2: score[t] = sum over rows of exp2(s - M) / L for the chunk's tokens;
 // each wave sums its rows, the waves' sums meet in LDS.
-__global__ void __launch_bounds__(EVICT_MAX_ROWS / EVICT_WAVE_ROWS * 64) evict_score_kernel(const EvictArgs a) {
-    constexpr int NWV = EVICT_MAX_ROWS / EVICT_WAVE_ROWS;
+__global__ void __launch_bounds__(NWV * 64) evict_score_kernel(const EvictArgs a) {
+    __shared__ __align__(16) unsigned char lds[2 * TILE_BYTES];
     __shared__ float part[NWV][EVICT_CHUNK];
     const int bh = blockIdx.y, chunk = blockIdx.x;
     const int b = bh / a.N_kv, h = bh % a.N_kv;
@@ -194,23 +262,31 @@ __global__ void __launch_bounds__(EVICT_MAX_ROWS / EVICT_WAVE_ROWS * 64) evict_s
         }
     const uint16_t* kbh = a.k + (size_t)bh * a.S * 128;
     const int tb = chunk * EVICT_CHUNK, te = min(a.S, tb + EVICT_CHUNK);
-    uint4 kv[4], kn[4];
-    load_keys(a, kbh, tb, L, kv);
-    for (int t0 = tb; t0 < te; t0 += 16) {
-        if (t0 + 16 < te) load_keys(a, kbh, t0 + 16, L, kn);
-        f32x4 s[MBW];
-        logits16(a, q, kv, r0, t0, L, s);
-        float acc = 0.f;
+    struct Score {
+        const EvictArgs& a;
+        const bf16x8 (&q)[MBW][4];
+        const float (&M)[MBW][4];
+        const float (&iL)[MBW][4];
+        float* out;                 // this wave's row of part, indexed from tb
+        int r0, L, tb, te;
+        __device__ __forceinline__ void tile(const unsigned char* buf, int t0) {
 #pragma unroll
-        for (int mb = 0; mb < MBW; ++mb)
+            for (int n = 0; n < EVICT_TILE / 16; ++n) {
+                if (t0 + 16 * n >= te) break;
+                f32x4 s[MBW];
+                logits16(a, q, buf, n, r0, t0, L, s);
+                float acc = 0.f;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc = fmaf(exp2f(s[mb][e] - M[mb][e]), iL[mb][e], acc);
-        // rows 4 (lane >> 4) + e of every block: add the four lane quarters
-        acc = xor32_sum(xor16_sum(acc));
-        if (L < 16) part[wave][t0 - tb + L] = acc;
+                for (int mb = 0; mb < MBW; ++mb)
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) kv[kb] = kn[kb];
-    }
+                    for (int e = 0; e < 4; ++e) acc = fmaf(exp2f(s[mb][e] - M[mb][e]), iL[mb][e], acc);
+                // rows 4 (lane >> 4) + e of every block: add the four lane quarters
+                acc = xor32_sum(xor16_sum(acc));
+                if (L < 16) out[t0 + 16 * n - tb + L] = acc;
+            }
+        }
+    } f{a, q, M, iL, part[wave], r0, L, tb, te};
+    walk_tiles(a, kbh, tb, te, lds, f);
     __syncthreads();
     float* sc = a.scores + (size_t)bh * a.S;
     for (int i = threadIdx.x; i < te - tb; i += blockDim.x) {
@@ -317,7 +393,7 @@ __global__ void evict_gather_kernel(const EvictArgs a) {
 
 hipError_t launch_evict(const EvictArgs& a, hipStream_t stream) {
     const int nchunk = (a.S + EVICT_CHUNK - 1) / EVICT_CHUNK;
-    const dim3 blk(EVICT_MAX_ROWS / EVICT_WAVE_ROWS * 64);
+    const dim3 blk(NWV * 64);
     hipLaunchKernelGGL(evict_stats_kernel, dim3(nchunk, a.BH), blk, 0, stream, a);
     hipLaunchKernelGGL(evict_combine_kernel, dim3(a.BH), dim3(EVICT_MAX_ROWS), 0, stream, a, nchunk);
     hipLaunchKernelGGL(evict_score_kernel, dim3(nchunk, a.BH), blk, 0, stream, a);

@@ -16,7 +16,8 @@
 // window eviction: at most 128 stacked window rows (G * W), tokens per block
 #define EVICT_MAX_ROWS 128
 #define EVICT_WAVE_ROWS 32
-#define EVICT_CHUNK 512
+#define EVICT_CHUNK 1024
+#define EVICT_TILE 64
 #define EVICT_SELECT_THREADS 1024
 #define EVICT_MAX_S (EVICT_SELECT_THREADS * 64)   // tokens per (b, KV head) the select handles
 
