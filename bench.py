@@ -13,7 +13,12 @@ value = effective decode bytes / decode time, where the effective bytes of a
 decode step are B*N_kv*S*(2T + 16 + 2D): packed K, the 16-byte mask and dense
 V. Inputs are resident in HBM before timing starts.
 
-Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME]
+Also reported (not the metric): the 128K-context layer at lambda=0.8, the
+stacked-eviction workload (window eviction of B=8, S=32K to 4096 tokens per
+KV head, then lambda=0.7 pruning and decode over the compacted cache) and the
+32-layer stack (B=4, S=64K, lambda=0.8; one decode launch per layer per step).
+
+Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME] [--no-extra]
 """
 from __future__ import annotations
 
@@ -68,13 +73,14 @@ def effective_prefill_bytes(w, T):
     return w.B * w.n_kv * w.S * (2 * w.D + 2 * T + 16)
 
 
-def run_leg(w, steps, warmup, rotate=True, seed=0, verbose=True):
+def run_leg(w, steps, warmup, rotate=True, seed=0, verbose=True, x=None):
     import torch
     from sparse_decode_attention_amd import gen, ops
 
     dev = torch.device("cuda:0")
     T = ops.num_kept(w.D, w.lam)
-    x = gen.torch_layer(w, dev, seed=seed, steps=w.steps)
+    if x is None:
+        x = gen.torch_layer(w, dev, seed=seed, steps=w.steps)
     dec_bytes = effective_decode_bytes(w, T)
     R = max(1, int(-(-MALL_DEFEAT_BYTES // dec_bytes))) if rotate else 1
     # replica 0 is written by the prefill every step; replicas 1..R-1 hold copies of it
@@ -204,9 +210,111 @@ def stream_ceiling(nbytes: int, reps: int = 7, blocks: int = 512) -> float:
     return n * 2 / ts[len(ts) // 2] / 1e9
 
 
+def evict_leg(w, steps, warmup):
+    """Stacked-eviction workload: window eviction of the S-token layer to
+    `keep` tokens per KV head (timed on its own), then the pruned-cache decode
+    over the compacted cache (run_leg on the kept K and V)."""
+    import dataclasses
+
+    import torch
+    from sparse_decode_attention_amd import gen, ops
+
+    dev = torch.device("cuda:0")
+    x = gen.torch_layer(w, dev, seed=0, steps=w.steps)
+    ev = ops.window_evict(x["q_win"], x["k"], x["v"], w.n_kv, w.keep)
+    for _ in range(warmup):
+        ops.window_evict(x["q_win"], x["k"], x["v"], w.n_kv, w.keep)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        ops.window_evict(x["q_win"], x["k"], x["v"], w.n_kv, w.keep)
+    e1.record()
+    torch.cuda.synchronize()
+    evict_us = e0.elapsed_time(e1) * 1e3 / steps
+    wk = dataclasses.replace(w, S=w.keep)
+    xk = {"q_win": x["q_win"], "k": ev["k"], "v": ev["v"], "q_dec": x["q_dec"]}
+    del x
+    leg = run_leg(wk, steps, warmup, x=xk)
+    kv_read = 2 * w.B * w.n_kv * w.S * w.D * 2          # K twice
+    return {"workload": w.name, "keep": w.keep, "lambda": w.lam, "T": leg["T"],
+            "evict_us": round(evict_us, 1), "evict_K_read_GBps": round(kv_read / (evict_us * 1e-6) / 1e9, 1),
+            "decode_GBps": round(leg["decode_GBps"], 2),
+            "decode_pct_hbm_peak": round(100 * leg["decode_GBps"] / HBM_PEAK_GBS, 2),
+            "decode_us_per_launch": round(leg["decode_us_per_launch"], 3),
+            "prefill_us": round(leg["prefill_us"], 2), "replicas": leg["replicas"]}
+
+
+def stack_leg(w, steps, warmup):
+    """The 32-layer stack: every layer pruned once (prefill timed per layer),
+    then each decode step runs one decode launch per layer over all layers'
+    pruned caches (one graph of `layers` launches per step). The stack
+    (about 21.7 GB at B=4, S=64K, lambda 0.8) is far beyond the 256 MB cache,
+    so no replica rotation is needed."""
+    import torch
+    from sparse_decode_attention_amd import gen, ops
+
+    dev = torch.device("cuda:0")
+    T = ops.num_kept(w.D, w.lam)
+    layers = []
+    pre_ms = []
+    for li in range(w.layers):
+        x = gen.torch_layer(w, dev, seed=0, layer=li, steps=1)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g = ops.prefill_prune(x["q_win"], x["k"], w.n_kv, w.lam)
+        e1.record()
+        torch.cuda.synchronize()
+        pre_ms.append(e0.elapsed_time(e1))
+        layers.append({"q": x["q_dec"][0], "k_packed": g["k_packed"], "mask": g["mask"], "v": x["v"], "r": g["r"]})
+        del x, g
+    torch.cuda.empty_cache()
+    outs = torch.empty((w.layers, w.B, w.n_q, w.D), dtype=torch.float32, device=dev)
+
+    def step():
+        for li, L in enumerate(layers):
+            ops.decode_attn(L["q"], L["k_packed"], L["mask"], L["v"], L["r"], w.lam, out=outs[li])
+    step()
+    torch.cuda.synchronize()
+    eager = outs.clone()
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(gr, stream=side):
+            step()
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        gr.replay()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        gr.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    if not torch.equal(outs, eager):
+        raise RuntimeError("stack graph replay differs from eager decode")
+    ts.sort()
+    step_ms = ts[len(ts) // 2]
+    per_layer = effective_decode_bytes(w, T)
+    pre_ms.sort()
+    return {"workload": w.name, "layers": w.layers, "B": w.B, "S": w.S, "lambda": w.lam, "T": T,
+            "decode_ms_per_step": round(step_ms, 4),
+            "decode_GBps": round(per_layer * w.layers / (step_ms * 1e-3) / 1e9, 2),
+            "decode_pct_hbm_peak": round(100 * per_layer * w.layers / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+            "stack_bytes": per_layer * w.layers,
+            "prefill_us_per_layer_median": round(pre_ms[len(pre_ms) // 2] * 1e3, 1),
+            "prefill_GBps_per_layer": round(effective_prefill_bytes(w, T) / (pre_ms[len(pre_ms) // 2] * 1e-3) / 1e9, 1)}
+
+
 def cpu_baseline(w, x, reps, T):
     """The oracle (NumPy, float64) on the host cores: one prefill prune of the
-    layer and 3 decode steps at full shape."""
+    layer and 48 decode steps at full shape (about 10-15 s of CPU work)."""
     import numpy as np
     import torch
 
@@ -217,12 +325,12 @@ def cpu_baseline(w, x, reps, T):
         return gen.bf16_bits_to_f32(t.view(torch.int16).cpu().numpy().view(np.uint16))
 
     q_win, k, v = host(x["q_win"]), host(x["k"]), host(x["v"])
-    q_dec = host(x["q_dec"][:3])
+    n_dec = 48
+    q_dec = host(x["q_dec"][:n_dec])
     t0 = time.perf_counter()
     pr = oracle.prune(q_win, k, w.n_kv, w.lam)
     r, _ = oracle.stats(k, pr["mask"], pr["A"])
     t1 = time.perf_counter()
-    n_dec = 3
     for s in range(n_dec):
         oracle.decode_attn(q_dec[s], pr["packed"], pr["mask"], v, r)
     t2 = time.perf_counter()
@@ -309,6 +417,8 @@ def main():
     ap.add_argument("--workload", default="llama8b_s32k_l05")
     ap.add_argument("--second", default="llama8b_s32k_l08", help="second reported workload ('' to skip)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the 128K-context, stacked-eviction and 32-layer workloads")
     ap.add_argument("--warm", action="store_true", help="also report a run without replica rotation")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="run a plain device copy of this size after the legs (counter calibration)")
@@ -377,6 +487,26 @@ def main():
                           "decode_us_per_launch": round(leg2["decode_us_per_launch"], 3),
                           "prefill_GBps": round(leg2["prefill_GBps"], 1), "replicas": leg2["replicas"]}
         del leg2
+    if not args.no_extra:
+        w3 = WORKLOADS["llama8b_s128k_l08"]
+        print(f"bench: {w3.name}", file=sys.stderr, flush=True)
+        leg3 = run_leg(w3, min(args.steps, 5), min(args.warmup, 2))
+        line["s128k"] = {"workload": w3.name, "lambda": w3.lam, "T": leg3["T"],
+                         "GBps": round(leg3["decode_GBps"], 2),
+                         "pct_hbm_peak": round(100 * leg3["decode_GBps"] / HBM_PEAK_GBS, 2),
+                         "decode_us_per_launch": round(leg3["decode_us_per_launch"], 3),
+                         "prefill_us": round(leg3["prefill_us"], 2), "prefill_GBps": round(leg3["prefill_GBps"], 1),
+                         "replicas": leg3["replicas"]}
+        del leg3
+        torch.cuda.empty_cache()
+        print("bench: stacked eviction", file=sys.stderr, flush=True)
+        line["evict_stack"] = evict_leg(WORKLOADS["snapkv_b8_s32k_keep4k_l07"], min(args.steps, 5),
+                                        min(args.warmup, 2))
+        torch.cuda.empty_cache()
+        print("bench: 32-layer stack", file=sys.stderr, flush=True)
+        line["layer_stack"] = stack_leg(WORKLOADS["llama8b_32L_b4_s64k_l08"], min(args.steps, 5),
+                                        min(args.warmup, 2))
+        torch.cuda.empty_cache()
     if args.warm:
         wl = run_leg(w, args.steps, args.warmup, rotate=False)
         line["warm_single_replica_GBps"] = round(wl["decode_GBps"], 2)
