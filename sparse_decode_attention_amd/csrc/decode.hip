@@ -726,25 +726,23 @@ __device__ __forceinline__ void build_list(const uint4& mw, uint8_t* lst, int L)
     }
 }
 
-// One 64-token tile of the fast kernel. The tile's V rows (already in flight
-// unless LOAD_V) and the next tile's packed rows are requested first, so they
-// arrive during the list build, the score loop and the softmax; then P.V.
-// With LIST_READY the slot list was built before the call.
+// One 64-token tile of the fast kernel. The slot list is built from the
+// tile's mask (before the call when LIST_READY); then the tile's V rows are
+// requested (unless LOAD_V is false: then the prologue did), so they arrive
+// during the score loop and the softmax; the next tile's mask and packed
+// rows are requested once the scores have consumed this tile's; then P.V.
+// A request made while the memory queue is full stalls the wave, so none is
+// placed ahead of work that needs no memory.
 template <int G, int T, bool LOAD_V, bool LIST_READY>
 __device__ __forceinline__ void fast_tile(const DecodeArgs& a, int bh, const unsigned char* tab, uint8_t* lst,
                                           float* ptab, const uint16_t* vbh, const float (&cq)[G], int t0, int nt,
                                           int nt_next, int L, uint4& mw, uint32_t (&kr)[(T + 1) / 2],
                                           uint4 (&vr)[16], float (&m_run)[G], float (&l_run)[G],
                                           f32x4 (&accm)[8]) {
-        const int tau = L >> 4, oct = L & 15;
+    const int tau = L >> 4, oct = L & 15;
     const int t1 = t0 + (DECODE_FAST_THREADS / 64) * DECODE_TILE;
+    if constexpr (!LIST_READY) build_list<T>(mw, lst, L);
     if constexpr (LOAD_V) load_v_tile(vbh, t0, nt, tau, oct, vr);
-    const uint4 mw_cur = mw;
-    uint32_t kc[(T + 1) / 2];
-#pragma unroll
-    for (int i = 0; i < (T + 1) / 2; ++i) kc[i] = kr[i];
-    if (nt_next > 0) load_row<T>(a, bh, t1, nt_next, L, mw, kr);
-    if constexpr (!LIST_READY) build_list<T>(mw_cur, lst, L);
     wave_lds_sync();
     // scores: s_g = q'_g . r + sum over kept c of q'_g(c) (k_c - r_c), with
     // q' = q * scale * log2(e) as fp32 float4 per channel (tab) and r as fp32
@@ -779,7 +777,7 @@ __device__ __forceinline__ void fast_tile(const DecodeArgs& a, int bh, const uns
         for (int k = 0; k < NB; ++k) {
             if (r0 + k < T) {
                 const int rho = r0 + k;
-                const float kv = (rho & 1) ? bf16_hi(kc[rho >> 1]) : bf16_lo(kc[rho >> 1]);
+                const float kv = (rho & 1) ? bf16_hi(kr[rho >> 1]) : bf16_lo(kr[rho >> 1]);
                 const float e = kv - rv[k];
                 s[0] = fmaf(qv[k].x, e, s[0]);
                 s[1] = fmaf(qv[k].y, e, s[1]);
@@ -796,6 +794,8 @@ __device__ __forceinline__ void fast_tile(const DecodeArgs& a, int bh, const uns
 #pragma unroll
         for (int g = 0; g < G; ++g) s[g] = -INFINITY;
     }
+    // the packed rows are consumed: request the next tile's into them
+    if (nt_next > 0) load_row<T>(a, bh, t1, nt_next, L, mw, kr);
     softmax_tile_mf<G>(s, m_run, l_run, accm, ptab, L);
     wave_lds_sync();
     // the list is dead: the same LDS region takes the V tile
@@ -806,8 +806,8 @@ __device__ __forceinline__ void fast_tile(const DecodeArgs& a, int bh, const uns
 // Decode block specialised for a compile-time T (the pruning ratios in use):
 // DECODE_FAST_THREADS threads (8 waves) per block, one block per CU. Each
 // lane loads its token's packed row straight into registers (T/2 dwords, no
-// LDS staging) and builds the list of its kept channels in LDS as bytes; the
-// score loop then knows each slot's register at compile time.
+// LDS staging) and builds the list of its kept channels in LDS as u16 table
+// offsets; the score loop then knows each slot's register at compile time.
 template <int G, int T>
 __global__ void __launch_bounds__(DECODE_FAST_THREADS)
 decode_fast_kernel(const DecodeArgs a) {

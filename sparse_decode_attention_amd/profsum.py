@@ -1,5 +1,6 @@
-"""Render rocprofv3 --kernel-trace --stats output as a short Markdown table
-(the summaries kept under profiles/)."""
+"""Render rocprofv3 output as short Markdown tables (the summaries kept under
+profiles/): kernel durations from --kernel-trace --stats, and per-dispatch
+counter averages from --pmc runs."""
 from __future__ import annotations
 
 import csv
@@ -22,6 +23,53 @@ def kernel_table(stats_dir: str, title: str, command: str, note: str = "", match
         name = r["Name"].split("(")[0].replace("void ", "")
         out.append(f"| {name} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
                    f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |")
+    return "\n".join(out) + "\n"
+
+
+def counter_means(pmc_dir: str, match: str) -> dict:
+    """Per kernel whose name contains `match`: each counter summed over its
+    dimension entries within a dispatch, then averaged over dispatches."""
+    per = {}
+    for f in glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if match not in r["Kernel_Name"]:
+                continue
+            name = r["Kernel_Name"].split("(")[0].replace("void ", "")
+            key = (r["Dispatch_Id"], r["Counter_Name"])
+            per.setdefault(name, {}).setdefault(key, 0.0)
+            per[name][key] += float(r["Counter_Value"])
+    out = {}
+    for name, d in per.items():
+        acc = {}
+        for (_, c), v in d.items():
+            acc.setdefault(c, []).append(v)
+        out[name] = {c: sum(v) / len(v) for c, v in acc.items()}
+    return out
+
+
+def counter_table(runs: list, counters: list, title: str, note: str = "") -> str:
+    """runs: (label, pmc_dir, kernel-name match, command) per column."""
+    cols = []
+    for label, d, match, _ in runs:
+        means = counter_means(d, match)
+        if len(means) != 1:
+            raise ValueError(f"{d}: {len(means)} kernels match {match!r}")
+        cols.append((label, *next(iter(means.items()))))
+    out = [f"# {title}", ""]
+    for label, _, _, cmd in runs:
+        out += [f"Command ({label}):", "", f"    {cmd}", ""]
+    if note:
+        out += [note, ""]
+    out += ["| counter (per dispatch) | " + " | ".join(f"{lab}: {k}" for lab, k, _ in cols) + " |",
+            "|---|" + "---|" * len(cols)]
+    for c in counters:
+        out.append(f"| {c} | " + " | ".join(f"{v.get(c, float('nan')):.0f}" for _, _, v in cols) + " |")
+    waves = [v.get("SQ_WAVES") for _, _, v in cols]
+    if all(waves):
+        for c in counters:
+            if c.startswith("SQ_INSTS_"):
+                out.append(f"| {c} per wave | " + " | ".join(f"{v.get(c, 0) / v['SQ_WAVES']:.1f}" for _, _, v in cols)
+                           + " |")
     return "\n".join(out) + "\n"
 
 
