@@ -321,9 +321,9 @@ __device__ __forceinline__ void load_v_tile(const uint16_t* vbh, int t0, int nt,
 //
 // Two accumulator layouts: the VALU one (MF false), where lane (tau, oct)
 // holds acc[g][e] for d = 8 oct + e summed over tokens 4i + tau; and the
-// matrix-core one (MF true), where acc[g][nb] is row g (lanes 0-15: hi part of
-// p) or row 4 + g (lanes 16-31: lo part) of the 16x16 tile nb, column
-// d = 16 nb + (lane & 15); lanes 32-63 hold zero rows.
+// matrix-core one (MF true), where acc[g][j] is row g (lanes 0-15: hi part of
+// p) or row 4 + g (lanes 16-31: lo part) of the 16x16 tile j, column
+// d = 8 (lane & 15) + j; lanes 32-63 hold zero rows.
 template <int G, int NT, bool MF>
 __device__ void finish_block(const DecodeArgs& a, float (&m_run)[G], float (&l_run)[G], float (&acc)[G][8],
                              unsigned char* wbase, int* s_last, int bh, int b, int h, int split) {
@@ -348,7 +348,7 @@ __device__ void finish_block(const DecodeArgs& a, float (&m_run)[G], float (&l_r
 #pragma unroll
         for (int g = 0; g < G; ++g)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) wacc[(wave * G + g) * 128 + (MF ? 16 * e + oct : oct * 8 + e)] = acc[g][e];
+            for (int e = 0; e < 8; ++e) wacc[(wave * G + g) * 128 + oct * 8 + e] = acc[g][e];
     }
     if (L == 0) {
 #pragma unroll
@@ -588,23 +588,20 @@ typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-// V tile of one wave in LDS for the matrix-core P.V: 64 rows of 256 bytes;
-// the eight 32-byte column blocks of row t are stored in the order
-// block ^ vt_swz(t), so that each transposing read below spreads its 16 rows
-// over all bank groups (two rows per group, the minimum for 512 bytes).
-__device__ __forceinline__ uint32_t vt_swz(uint32_t t) { return (t & 3u) | (((t >> 3) & 1u) << 2); }
-__device__ __forceinline__ uint32_t vt_off(uint32_t t, uint32_t blk, uint32_t byte) {
-    return t * 256u + ((blk ^ vt_swz(t)) << 5) + byte;
-}
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Two fp32 -> packed bf16 pair (round to nearest even).
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
 }
 
+// Slot of token t (0..63) in a ptab row: within each 16-token group the
+// token 16 grp + 4 e + tau sits at 16 grp + 4 tau + e, so the four tokens
+// that one lane of the matrix-core P.V needs are adjacent.
+__device__ __forceinline__ uint32_t ptab_slot(uint32_t t) { return (t & 48u) | ((t & 3u) << 2) | ((t >> 2) & 3u); }
+
 // Online softmax of one tile for the matrix-core P.V: p goes to ptab as
-// [g][64 tokens] fp32; accm[nb][g] (the rows of head g) are rescaled.
+// [g][64 token slots] fp32; accm[j][g] (the rows of head g) are rescaled.
 template <int G>
 __device__ __forceinline__ void softmax_tile_mf(const float (&s)[G], float (&m_run)[G], float (&l_run)[G],
                                                 f32x4 (&accm)[8], float* ptab, int L) {
@@ -618,55 +615,45 @@ __device__ __forceinline__ void softmax_tile_mf(const float (&s)[G], float (&m_r
         const float p = exp2f(s[g] - mn);
         l_run[g] = l_run[g] * alpha[g] + p;
         m_run[g] = mn;
-        ptab[g * 64 + L] = p;
+        ptab[g * 64 + ptab_slot((uint32_t)L)] = p;
     }
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) accm[nb] *= alpha;
 }
 
-// P.V of one 64-token tile on the matrix cores (v_mfma_f32_16x16x32_bf16,
-// four heads). Per 32-token block kb and 16-column block nb:
-//   A (16 x 32): row g < 4 is bf16(p_g), row 4 + g is bf16(p_g - bf16(p_g)),
+// P.V of one 64-token tile on the matrix cores (v_mfma_f32_16x16x16_bf16,
+// four heads), with V taken from the registers it was loaded into: lane
+// (tau, oct) holds vr[i] = V row 4i + tau, d in [8 oct, 8 oct + 8). Per
+// 16-token group grp and column offset j (0..7), with K index k = 4 tau + e
+// standing for token 16 grp + 4 e + tau:
+//   A (16 x 16): row g < 4 is bf16(p_g), row 4 + g is bf16(p_g - bf16(p_g)),
 //                rows 8-15 are zero, so the hi and lo rows carry p to ~2^-16;
-//   B (32 x 16): V rows of the 32 tokens, columns 16 nb .. 16 nb + 15, read
-//                from the LDS V tile with ds_read_b64_tr_b16 (two reads of
-//                four rows each per lane);
-//   D (16 x 16): accm[nb]; lane l holds rows 4 (l >> 4) + e, column l & 15.
-// vr holds the tile's V rows in the load layout (lane (tau, oct): rows
-// 4i + tau, d in [8 oct, 8 oct + 8)); they are written to the swizzled tile
-// vt first.
-__device__ __forceinline__ void pv_tile_mf(const uint4 (&vr)[16], unsigned char* vt, const float* ptab,
-                                           f32x4 (&accm)[8], int L) {
-    const uint32_t tau = (uint32_t)L >> 4, oct = (uint32_t)L & 15u;
-#pragma unroll
-    for (int i = 0; i < 16; ++i)   // component-wise: keeps vr in registers
-        *reinterpret_cast<u32x4*>(vt + vt_off(4u * i + tau, oct >> 1, (oct & 1u) << 4)) =
-            (u32x4){vr[i].x, vr[i].y, vr[i].z, vr[i].w};
-    wave_lds_sync();
+//   B (16 x 16): B[k][n] = V[token(k)][8 n + j], element j of
+//                vr[4 grp + e] in lane (tau, n), two byte permutes per MFMA;
+//   D (16 x 16): accm[j]; lane l holds rows 4 (l >> 4) + e (hi rows in lanes
+//                0-15, lo rows in lanes 16-31), column n = l & 15, i.e.
+//                d = 8 (l & 15) + j.
+// No V bytes go through LDS.
+__device__ __forceinline__ uint32_t dword_of(const uint4& x, int j) {
+    return j == 0 ? x.x : j == 1 ? x.y : j == 2 ? x.z : x.w;
+}
+__device__ __forceinline__ void pv_tile_mf(const uint4 (&vr)[16], const float* ptab, f32x4 (&accm)[8], int L) {
     const uint32_t m = (uint32_t)L & 15u, q = (uint32_t)L >> 4;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-        const float4* pp = reinterpret_cast<const float4*>(ptab + (m & 3u) * 64u + 32u * kb + 8u * q);
-        const float4 p0 = pp[0], p1 = pp[1];
-        const float x[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-        uint32_t aw[4];
+    for (int grp = 0; grp < 4; ++grp) {
+        const float4 pv = *reinterpret_cast<const float4*>(ptab + (m & 3u) * 64u + 16u * grp + 4u * q);
+        const uint32_t hi0 = pack_bf16(pv.x, pv.y), hi1 = pack_bf16(pv.z, pv.w);
+        const uint32_t lo0 = pack_bf16(pv.x - bf16_lo(hi0), pv.y - bf16_hi(hi0));
+        const uint32_t lo1 = pack_bf16(pv.z - bf16_lo(hi1), pv.w - bf16_hi(hi1));
+        const u32x2 aw = {m < 4u ? hi0 : (m < 8u ? lo0 : 0u), m < 4u ? hi1 : (m < 8u ? lo1 : 0u)};
+        const i16x4 av = __builtin_bit_cast(i16x4, aw);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t hi = pack_bf16(x[2 * j], x[2 * j + 1]);
-            const uint32_t lo = pack_bf16(x[2 * j] - bf16_lo(hi), x[2 * j + 1] - bf16_hi(hi));
-            aw[j] = m < 4u ? hi : (m < 8u ? lo : 0u);
-        }
-        const bf16x8 av = __builtin_bit_cast(bf16x8, make_uint4(aw[0], aw[1], aw[2], aw[3]));
-#pragma unroll
-        for (int nb = 0; nb < 8; ++nb) {
-            const uint32_t t0 = 32u * kb + 8u * q + (m >> 2);
-            const uint32_t byte = (m & 3u) << 3;
-            const i16x4 w0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (i16x4 __attribute__((address_space(3)))*)(vt + vt_off(t0, nb, byte)));
-            const i16x4 w1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (i16x4 __attribute__((address_space(3)))*)(vt + vt_off(t0 + 4u, nb, byte)));
-            const bf16x8 bv = __builtin_bit_cast(bf16x8, __builtin_shufflevector(w0, w1, 0, 1, 2, 3, 4, 5, 6, 7));
-            accm[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, accm[nb], 0, 0, 0);
+        for (int j = 0; j < 8; ++j) {
+            // bf16 element j of four V rows: low halves for even j, high for odd
+            const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+            const u32x2 bw = {__builtin_amdgcn_perm(dword_of(vr[4 * grp + 1], j >> 1), dword_of(vr[4 * grp], j >> 1), sel),
+                              __builtin_amdgcn_perm(dword_of(vr[4 * grp + 3], j >> 1), dword_of(vr[4 * grp + 2], j >> 1), sel)};
+            accm[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, __builtin_bit_cast(i16x4, bw), accm[j], 0, 0, 0);
         }
     }
 }
@@ -694,8 +681,13 @@ __device__ __forceinline__ void load_row(const DecodeArgs& a, int bh, int t0, in
 // Row stride (u16 elements) of the lane-major slot list: room for T slots and
 // a spare one, rounded so that the stride in dwords is odd, which puts the 64
 // lanes of a dword read on distinct bank pairs.
+__host__ __device__ constexpr uint32_t list_stride_of(int T) {
+    return ((T / 2) % 2 == 1) ? (uint32_t)T + 2u : (uint32_t)T + 4u;
+}
 template <int T>
-constexpr uint32_t list_stride() { return ((T / 2) % 2 == 1) ? (uint32_t)T + 2u : (uint32_t)T + 4u; }
+constexpr uint32_t list_stride() { return list_stride_of(T); }
+// LDS bytes of one wave's slot list, in whole 16-byte units
+__host__ __device__ constexpr uint32_t list_bytes_of(int T) { return (64u * list_stride_of(T) * 2u + 15u) & ~15u; }
 
 // Slot list of one tile, lane-major: lst[lane * stride + rho] = 4 * c for the
 // lane's rho-th kept channel c (ascending), i.e. the byte offset of c's r in
@@ -798,8 +790,7 @@ __device__ __forceinline__ void fast_tile(const DecodeArgs& a, int bh, const uns
     if (nt_next > 0) load_row<T>(a, bh, t1, nt_next, L, mw, kr);
     softmax_tile_mf<G>(s, m_run, l_run, accm, ptab, L);
     wave_lds_sync();
-    // the list is dead: the same LDS region takes the V tile
-    pv_tile_mf(vr, lst, ptab, accm, L);
+    pv_tile_mf(vr, ptab, accm, L);
     wave_lds_sync();
 }
 
@@ -818,10 +809,8 @@ decode_fast_kernel(const DecodeArgs a) {
     // r as one float per channel (512 bytes)
     constexpr uint32_t TAB = 16u;
     constexpr uint32_t TABLES = 128u * 16u + 128u * 4u;     // then a 16-byte flag slot
-    // per wave: the slot list (u16, lane-major) during the scores, then the V
-    // tile (64 x 256 bytes) during P.V, in one region; then p as [G][64] fp32
-    constexpr uint32_t LIST = 64u * 256u;
-    static_assert(64u * list_stride<T>() * 2u <= LIST, "list fits the V tile region");
+    // per wave: the slot list (u16, lane-major), then p as [G][64] fp32
+    constexpr uint32_t LIST = list_bytes_of(T);
     constexpr uint32_t WAVE = LIST + 64u * G * 4u;
     constexpr int NW = DECODE_FAST_THREADS / 64;
     static_assert(T % 2 == 0 && T > 0 && T < 128, "fast path needs an even 0 < T < 128");
@@ -932,13 +921,12 @@ decode_fast_kernel(const DecodeArgs a) {
                                                reinterpret_cast<int*>(smem + TABLES), bh, b, h, split);
 }
 
-// LDS bytes the fast kernel needs: tables and flag, then per wave the list /
-// V tile region and p, or the block / split merge scratch (reused after the
-// tile loop). Must not exceed its static DECODE_FAST_LDS_BYTES.
+// LDS bytes the fast kernel needs: tables and flag, then per wave the slot
+// list and p, or the block / split merge scratch (reused after the tile
+// loop). Must not exceed its static DECODE_FAST_LDS_BYTES.
 uint32_t decode_fast_lds_bytes(int G, int T, int nsplit) {
     const uint32_t tab = 128u * 16u + 128u * 4u + 16u;   // q' float4 and r per channel, flag
-    const uint32_t list = 64u * 256u;     // slot list, then the V tile
-    (void)T;
+    const uint32_t list = list_bytes_of(T);
     const uint32_t waves = DECODE_FAST_THREADS / 64;
     uint32_t dyn = waves * (list + 64u * (uint32_t)G * 4u);
     const uint32_t fin = finish_scratch_bytes(G, DECODE_FAST_THREADS, nsplit);

@@ -9,8 +9,8 @@
 #define DECODE_THREADS 256
 #define DECODE_FAST_THREADS 512
 // LDS of the fast decode kernel: q' and r tables with a flag slot (2576 B),
-// then per wave a 16 KiB list / V tile region and 1 KiB of p
-#define DECODE_FAST_LDS_BYTES (2576 + (DECODE_FAST_THREADS / 64) * (16384 + 1024))
+// then per wave the slot list of the largest T (64 lanes x 68 u16) and 1 KiB of p
+#define DECODE_FAST_LDS_BYTES (2576 + (DECODE_FAST_THREADS / 64) * (8704 + 1024))
 #define DECODE_TILE 64
 #define DECODE_MAX_SPLITS 256
 // window eviction: at most 128 stacked window rows (G * W), tokens per block
