@@ -3,7 +3,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#define PRUNE_TOKENS_PER_BLOCK 256
+#define PRUNE_TOKENS_PER_BLOCK 64
 #define CHAN_ENERGY_ROWS 128
 #define STATS_PARTS 8
 #define DECODE_THREADS 256
