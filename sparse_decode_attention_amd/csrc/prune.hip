@@ -108,15 +108,18 @@ select_pack_kernel(const uint16_t* __restrict__ k, const float* __restrict__ A,
             } else if (T <= 0) {
                 kept0 = kept1 = false;
             } else {
+                // v, n and the loop state are wave-uniform (scalar registers);
+                // the unrolled steps each cost two compares, two scalar
+                // popcounts and a scalar select, and leave at the first
+                // count of exactly T
                 uint32_t v = 0;
                 bool exact = false;
+#pragma unroll
                 for (int bit = 30; bit >= 0; --bit) {
-                    const uint32_t c = v | (1u << bit);
+                    const uint32_t c = __builtin_amdgcn_readfirstlane(v | (1u << bit));
                     const int n = __popcll(ballot(key0 >= c)) + __popcll(ballot(key1 >= c));
-                    if (n >= T) {
-                        v = c;
-                        if (n == T) { exact = true; break; }
-                    }
+                    v = n >= T ? c : v;
+                    if (n == T) { exact = true; break; }
                 }
                 if (exact) {
                     kept0 = key0 >= v;
