@@ -297,16 +297,47 @@ __global__ void __launch_bounds__(NWV * 64) evict_score_kernel(const EvictArgs a
     }
 }
 
+// Exclusive prefix sum of v over the block (thread order), and the block
+// total: a shuffle scan inside each wave, then the wave totals. Every thread
+// of the block must call it.
+template <int NT>
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wtot, uint32_t& total) {
+    constexpr int NWV = NT / 64;
+    const int tid = threadIdx.x, L = tid & 63, wave = tid >> 6;
+    uint32_t s = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t t = __shfl_up(s, o, 64);
+        if (L >= o) s += t;
+    }
+    if (L == 63) wtot[wave] = s;
+    __syncthreads();
+    uint32_t off = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) {
+        const uint32_t t = wtot[w];
+        off += w < wave ? t : 0u;
+        tot += t;
+    }
+    __syncthreads();          // wtot may be reused by the next call
+    total = tot;
+    return off + s - v;
+}
+
 // Per (b*N_kv + h): the `keep` largest scores (fp32 >= 0, compared as their
-// uint32 bits), ties to the lower t, written to idx in ascending t. Bitwise
-// radix select from the top bit (counts by wave sums, no atomics), then an
-// ordered compaction. Each thread owns a contiguous run of at most PER tokens,
-// held in registers.
+// uint32 bits), ties to the lower t, written to idx in ascending t. The
+// keep-th largest value theta is found bit by bit from the top by counting
+// the values >= each candidate (one compare per value, wave sums, one
+// barrier per bit); the search stops as soon as exactly `keep` values are >=
+// the candidate. Then an ordered compaction: every value > theta, and the
+// first values == theta in t order until `keep` are taken. Each thread owns a
+// contiguous run of at most PER tokens, held in registers.
 template <int PER>
 __global__ void __launch_bounds__(EVICT_SELECT_THREADS) evict_select_kernel(const EvictArgs a) {
-    constexpr int NWV = EVICT_SELECT_THREADS / 64;
+    constexpr int NT = EVICT_SELECT_THREADS;
+    constexpr int NWV = NT / 64;
     __shared__ uint32_t wsum[2][NWV];
-    __shared__ uint32_t scan[EVICT_SELECT_THREADS];
+    __shared__ uint32_t wtot[NWV];
     const int bh = blockIdx.x;
     const int tid = threadIdx.x, L = tid & 63, wave = tid >> 6;
     const uint32_t* u = reinterpret_cast<const uint32_t*>(a.scores) + (size_t)bh * a.S;
@@ -315,64 +346,61 @@ __global__ void __launch_bounds__(EVICT_SELECT_THREADS) evict_select_kernel(cons
     uint32_t x[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) x[i] = i < n ? u[t_begin + i] : 0u;
-    // prefix of the keep-th largest value, found bit by bit: among values
-    // whose higher bits equal the prefix, count those with this bit set
-    uint32_t prefix = 0, krem = (uint32_t)a.keep;
-    for (int bit = 31; bit >= 0; --bit) {
-        uint32_t c = 0;
+    const uint32_t keep = (uint32_t)a.keep;
+    // theta: the largest v with #{x >= v} >= keep (values past n are 0 and
+    // are never counted: a candidate always has a set bit)
+    uint32_t v = 0;
+    bool exact = false;
+    for (int bit = 31, par = 0; bit >= 0; --bit, par ^= 1) {
+        const uint32_t c = v | (1u << bit);
+        uint32_t cnt = 0;
 #pragma unroll
-        for (int i = 0; i < PER; ++i) c += (i < n) && (((x[i] ^ prefix) >> bit) == 1u);
-        const float cw = wave_sum_dpp((float)c);                   // exact: counts < 2^24
-        if (L == 0) wsum[bit & 1][wave] = (uint32_t)cw;
+        for (int i = 0; i < PER; ++i) cnt += x[i] >= c ? 1u : 0u;
+        const float cw = wave_sum_dpp((float)cnt);                   // exact: counts < 2^24
+        if (L == 0) wsum[par][wave] = (uint32_t)cw;
         __syncthreads();
         uint32_t total = 0;
 #pragma unroll
-        for (int w = 0; w < NWV; ++w) total += wsum[bit & 1][w];
-        if (total >= krem) prefix |= 1u << bit;
-        else krem -= total;
+        for (int w = 0; w < NWV; ++w) total += wsum[par][w];
+        if (total >= keep) {
+            v = c;
+            if (total == keep) { exact = true; break; }
+        }
     }
-    // keep every x > prefix and the first krem tokens with x == prefix
-    uint32_t n_eq = 0;
+    // with an exact count every value >= v is kept; otherwise the values > v
+    // and the first (keep - #{x > v}) values == v in t order
+    uint32_t n_gt = 0, n_eq = 0;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) n_eq += (i < n) && (x[i] == prefix);
-    scan[tid] = n_eq;
-    __syncthreads();
-    for (int o = 1; o < EVICT_SELECT_THREADS; o <<= 1) {
-        const uint32_t v = tid >= o ? scan[tid - o] : 0u;
-        __syncthreads();
-        scan[tid] += v;
-        __syncthreads();
+    for (int i = 0; i < PER; ++i) {
+        n_gt += (i < n && x[i] > v) ? 1u : 0u;
+        n_eq += (i < n && x[i] == v) ? 1u : 0u;
     }
-    const uint32_t eq_before = scan[tid] - n_eq;
-    __syncthreads();
-    uint32_t n_keep = 0;
+    uint32_t eq_before = 0, take_eq = 0;
+    if (!exact) {      // uniform
+        uint32_t gt_total, eq_total;
+        (void)block_excl_scan<NT>(n_gt, wtot, gt_total);
+        eq_before = block_excl_scan<NT>(n_eq, wtot, eq_total);
+        take_eq = keep - gt_total;
+    } else {
+        take_eq = 0xffffffffu;     // every value == v is kept
+    }
+    uint32_t n_keep = n_gt;
     {
         uint32_t e = eq_before;
 #pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            if (i < n) {
-                if (x[i] > prefix) ++n_keep;
-                else if (x[i] == prefix) { if (e < krem) ++n_keep; ++e; }
-            }
-        }
+        for (int i = 0; i < PER; ++i)
+            if (i < n && x[i] == v) { n_keep += e < take_eq ? 1u : 0u; ++e; }
     }
-    scan[tid] = n_keep;
-    __syncthreads();
-    for (int o = 1; o < EVICT_SELECT_THREADS; o <<= 1) {
-        const uint32_t v = tid >= o ? scan[tid - o] : 0u;
-        __syncthreads();
-        scan[tid] += v;
-        __syncthreads();
-    }
-    uint32_t pos = scan[tid] - n_keep;
+    uint32_t kept_total;
+    uint32_t pos = block_excl_scan<NT>(n_keep, wtot, kept_total);
     int32_t* idx = a.idx + (size_t)bh * a.keep;
     uint32_t e = eq_before;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         if (i < n) {
-            bool k = x[i] > prefix;
-            if (x[i] == prefix) { k = e < krem; ++e; }
-            if (k && pos < (uint32_t)a.keep) idx[pos++] = t_begin + i;
+            bool k = x[i] > v;
+            if (x[i] == v) { k = e < take_eq; ++e; }
+            if (k && pos < keep) idx[pos++] = t_begin + i;
         }
     }
 }
