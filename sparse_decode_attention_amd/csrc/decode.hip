@@ -308,10 +308,13 @@ __device__ __forceinline__ void pv_tile(const uint4 (&vr)[16], const float* ptab
 // d in [8 oct, 8 oct + 8). Rows past the end of a partial tile re-read the
 // last valid row; their p is 0.
 __device__ __forceinline__ void load_v_tile(const uint16_t* vbh, int t0, int nt, int tau, int oct, uint4 (&vr)[16]) {
+    // 32-bit byte offsets from the head's V slab (at most 64K rows of 256 B),
+    // so each request is a scalar base plus one vector offset
+    const unsigned char* vb = reinterpret_cast<const unsigned char*>(vbh);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-        const int tok = min(4 * i + tau, nt - 1);
-        vr[i] = *reinterpret_cast<const uint4*>(vbh + (size_t)(t0 + tok) * 128 + oct * 8);
+        const uint32_t row = (uint32_t)(t0 + min(4 * i + tau, nt - 1));
+        vr[i] = *reinterpret_cast<const uint4*>(vb + (row * 256u + (uint32_t)oct * 16u));
     }
 }
 
