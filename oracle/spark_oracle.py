@@ -33,6 +33,14 @@ Readings of points the pages leave open (each is listed in the design doc):
     walkthrough's Degenerate F (section 3.3, F table) is "score_mean_pruned".
   * Decode: one new query per head attends to all S cached tokens (no causal
     mask), scale 1/sqrt(D), recovery only in the scores, V dense.
+  * Sampled F ("gaussian", "exponential", the other rows of the section 3.3 F
+    table): mu and sigma are the mean and population standard deviation of
+    the pruned saliency a_j |k_tj| per (batch, KV head); each pruned (t, j)
+    draws its own w~ from a Philox4x32-10 stream keyed by a caller seed and
+    counted by (t, j // 4, b * N_kv + h); Exp(1/mu) has mean mu.
+    Parity unpinned against published generator test vectors (the pages hold
+    none): the generator is pinned by its inverse, avalanche and uniformity,
+    the transforms by their moments and the Box-Muller identity.
 """
 from __future__ import annotations
 
@@ -47,6 +55,9 @@ F_MEAN_RETAINED = "mean_retained"
 F_ZERO = "zero"
 F_CONST = "const"
 F_SCORE_MEAN_PRUNED = "score_mean_pruned"
+F_GAUSSIAN = "gaussian"
+F_EXPONENTIAL = "exponential"
+F_SAMPLED = (F_GAUSSIAN, F_EXPONENTIAL)
 
 
 def num_kept(D: int, lam: float) -> int:
@@ -168,6 +179,12 @@ def stats(k: np.ndarray, mask: np.ndarray, A: np.ndarray, mode: str = F_MEAN_RET
       score_mean_pruned: section 3.3 steps 1-4 with the Degenerate F:
                          mu = mean over pruned (t, j) of a_j |k_tj|, a_j = sqrt(A_j);
                          the back-solved key is mu / a_j (0 if a_j = 0).
+      gaussian, exponential: the sampled F of the section 3.3 F table; the
+                         statistics of step 1 are mu and sigma (population
+                         standard deviation) of the pruned saliency a_j |k_tj|
+                         per (batch, KV head), stored as r[..., 0] = mu,
+                         r[..., 1] = sigma, the other entries 0. The samples
+                         themselves are drawn at decode (decode_attn_sampled).
     """
     k64 = np.asarray(k, dtype=np.float64)
     cnt = mask.sum(axis=2).astype(np.int32)
@@ -185,6 +202,18 @@ def stats(k: np.ndarray, mask: np.ndarray, A: np.ndarray, mode: str = F_MEAN_RET
         npruned = (~mask).sum(axis=(2, 3))
         mu = np.where(npruned > 0, np.where(~mask, w, 0.0).sum(axis=(2, 3)) / np.maximum(npruned, 1), 0.0)
         r = np.where(a > 0, mu[:, :, None] / np.where(a > 0, a, 1.0), 0.0)
+    elif mode in F_SAMPLED:
+        a = np.sqrt(np.asarray(A, dtype=np.float64))
+        w = np.abs(k64) * a[:, :, None, :]
+        pr = ~mask
+        npruned = pr.sum(axis=(2, 3))
+        n1 = np.maximum(npruned, 1)
+        mu = np.where(npruned > 0, np.where(pr, w, 0.0).sum(axis=(2, 3)) / n1, 0.0)
+        m2 = np.where(npruned > 0, np.where(pr, w * w, 0.0).sum(axis=(2, 3)) / n1, 0.0)
+        sigma = np.sqrt(np.maximum(m2 - mu * mu, 0.0))
+        r = np.zeros((B, H, D))
+        r[:, :, 0] = mu
+        r[:, :, 1] = sigma
     else:
         raise ValueError(mode)
     return r.astype(np.float32), cnt
@@ -234,6 +263,99 @@ def dense_attn(q, k, v, scale: float | None = None) -> np.ndarray:
     D = k.shape[-1]
     scale = 1.0 / math.sqrt(D) if scale is None or scale <= 0 else float(scale)
     return _attend(q, np.asarray(k, dtype=np.float64), v, scale)
+
+
+# ---------------------------------------------------------------- sampled recovery F
+#
+# Counter-based generator: Philox4x32 with 10 rounds, from its published
+# definition (J. K. Salmon, M. A. Moraes, R. O. Dror, D. E. Shaw, "Parallel
+# random numbers: as easy as 1, 2, 3", SC 2011, section on the Philox
+# family). One round maps the counter (c0, c1, c2, c3) under the round key
+# (k0, k1) to (hi(M1 c2) ^ c1 ^ k0, lo(M1 c2), hi(M0 c0) ^ c3 ^ k1, lo(M0 c0)),
+# with 32 x 32 -> 64-bit products; the key is advanced by the Weyl constants
+# between rounds.
+PHILOX_M0 = 0xD2511F53
+PHILOX_M1 = 0xCD9E8D57
+PHILOX_W0 = 0x9E3779B9
+PHILOX_W1 = 0xBB67AE85
+_M32 = np.uint64(0xFFFFFFFF)
+
+
+def philox4x32_10(ctr, key):
+    """Philox4x32-10 of counters ctr = (c0, c1, c2, c3) (arrays, broadcast
+    together) under key = (k0, k1) (ints): four uint32 arrays."""
+    c = [np.asarray(x, dtype=np.uint64) & _M32 for x in ctr]
+    c0, c1, c2, c3 = np.broadcast_arrays(*c)
+    k0, k1 = int(key[0]) & 0xFFFFFFFF, int(key[1]) & 0xFFFFFFFF
+    for rnd in range(10):
+        if rnd:
+            k0 = (k0 + PHILOX_W0) & 0xFFFFFFFF
+            k1 = (k1 + PHILOX_W1) & 0xFFFFFFFF
+        p0 = np.uint64(PHILOX_M0) * c0
+        p1 = np.uint64(PHILOX_M1) * c2
+        c0, c1, c2, c3 = ((p1 >> np.uint64(32)) ^ c1 ^ np.uint64(k0), p1 & _M32,
+                          (p0 >> np.uint64(32)) ^ c3 ^ np.uint64(k1), p0 & _M32)
+    return tuple(x.astype(np.uint32) for x in (c0, c1, c2, c3))
+
+
+def uniform01(x) -> np.ndarray:
+    """u = (x + 1/2) / 2^32 in (0, 1) for uint32 x, float64."""
+    return (np.asarray(x, dtype=np.float64) + 0.5) * 2.0 ** -32
+
+
+def recovery_samples(b: int, h: int, n_kv: int, S: int, D: int, mode: str, mu: float, sigma: float,
+                     seed: int) -> np.ndarray:
+    """Sampled saliency w~[t][j] for one (b, KV head), float64 (walkthrough
+    section 3.3 step 2 and F table).
+
+    Counter (t, j // 4, b * n_kv + h, 0), key (seed low 32 bits, seed high 32
+    bits); the four outputs x0..x3 serve channels 4 (j // 4) + 0..3:
+      exponential (mean mu):  w = -mu ln(u_i) for each output
+      gaussian N(mu, sigma^2): Box-Muller on (u0, u1) and on (u2, u3):
+                              R = sqrt(-2 ln u_even), theta = 2 pi u_odd,
+                              z_even = R cos theta, z_odd = R sin theta,
+                              w = mu + sigma z
+    """
+    t = np.arange(S, dtype=np.uint64)[:, None]
+    jg = np.arange(D // 4, dtype=np.uint64)[None, :]
+    x = philox4x32_10((t, jg, b * n_kv + h, 0), (seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF))
+    u = [uniform01(xi) for xi in x]                                   # each [S][D/4]
+    if mode == F_EXPONENTIAL:
+        w = [-mu * np.log(ui) for ui in u]
+    elif mode == F_GAUSSIAN:
+        w = []
+        for e in (0, 2):
+            R = np.sqrt(-2.0 * np.log(u[e]))
+            th = 2.0 * math.pi * u[e + 1]
+            w += [mu + sigma * R * np.cos(th), mu + sigma * R * np.sin(th)]
+    else:
+        raise ValueError(mode)
+    return np.stack(w, axis=-1).reshape(S, D)                        # channel 4 jg + i
+
+
+def expand_keys_sampled(packed, mask, A, r, mode: str, seed: int) -> np.ndarray:
+    """K_hat with sampled recovery, float64: mask ? stored value : w~_tj / a_j
+    (0 if a_j = 0), a_j = sqrt(A_j), mu = r[..., 0], sigma = r[..., 1]
+    (walkthrough section 3.3 steps 2-3)."""
+    B, H, S, D = mask.shape
+    a = np.sqrt(np.asarray(A, dtype=np.float64))
+    r64 = np.asarray(r, dtype=np.float64)
+    khat = np.zeros(mask.shape)
+    for b in range(B):
+        for h in range(H):
+            w = recovery_samples(b, h, H, S, D, mode, float(r64[b, h, 0]), float(r64[b, h, 1]), seed)
+            khat[b, h] = np.where(a[b, h] > 0, w / np.where(a[b, h] > 0, a[b, h], 1.0), 0.0)
+    khat[mask] = np.asarray(packed, dtype=np.float64).reshape(-1)
+    return khat
+
+
+def decode_attn_sampled(q, packed, mask, v, A, r, mode: str, seed: int, scale: float | None = None) -> np.ndarray:
+    """One decode step with a sampled recovery F: sample, back-solve, then
+    standard attention (walkthrough section 3.3 steps 2-4 and F table).
+    Returns out [B][N_q][D] in float64."""
+    D = mask.shape[-1]
+    scale = 1.0 / math.sqrt(D) if scale is None or scale <= 0 else float(scale)
+    return _attend(q, expand_keys_sampled(packed, mask, A, r, mode, seed), v, scale)
 
 
 def window_scores(q_win: np.ndarray, k: np.ndarray) -> np.ndarray:

@@ -335,6 +335,143 @@ def test_score_mean_pruned_closed_form():
     assert (rz == 0).all() and (rc == np.float32(0.01)).all()
 
 
+# ------------------------------------------------------------------ sampled recovery F
+
+def _philox_inverse(y, key):
+    """Inverse of Philox4x32-10, written from the round's algebra: lo(M c) and
+    the key-free hi half recover c through the inverse of M modulo 2^32."""
+    M0, M1 = oracle.PHILOX_M0, oracle.PHILOX_M1
+    W0, W1 = oracle.PHILOX_W0, oracle.PHILOX_W1
+    i0, i1 = pow(M0, -1, 1 << 32), pow(M1, -1, 1 << 32)
+    keys = []
+    k0, k1 = key
+    for rnd in range(10):
+        if rnd:
+            k0, k1 = (k0 + W0) % (1 << 32), (k1 + W1) % (1 << 32)
+        keys.append((k0, k1))
+    out = []
+    for y0, y1, y2, y3 in zip(*[np.asarray(v, dtype=np.uint64).tolist() for v in y]):
+        for k0, k1 in reversed(keys):
+            c2 = (y1 * i1) % (1 << 32)
+            c0 = (y3 * i0) % (1 << 32)
+            c1 = y0 ^ ((M1 * c2) >> 32) ^ k0
+            c3 = y2 ^ ((M0 * c0) >> 32) ^ k1
+            y0, y1, y2, y3 = c0, c1, c2, c3
+        out.append((y0, y1, y2, y3))
+    return out
+
+
+def test_philox_is_a_keyed_bijection():
+    rng = np.random.default_rng(21)
+    ctr = [rng.integers(0, 1 << 32, size=200, dtype=np.uint64) for _ in range(4)]
+    key = (int(rng.integers(0, 1 << 32)), int(rng.integers(0, 1 << 32)))
+    y = oracle.philox4x32_10(ctr, key)
+    back = _philox_inverse(y, key)
+    assert back == list(zip(*[c.tolist() for c in ctr]))
+    y2 = oracle.philox4x32_10(ctr, (key[0] ^ 1, key[1]))
+    assert not np.array_equal(y[0], y2[0])
+
+
+def test_philox_avalanche_and_uniformity():
+    """One flipped counter bit changes about half of the 128 output bits; the
+    top bytes of a counter sweep are uniform (chi-square, 255 dof)."""
+    rng = np.random.default_rng(22)
+    n = 400
+    ctr = [rng.integers(0, 1 << 32, size=n, dtype=np.uint64) for _ in range(4)]
+    y = oracle.philox4x32_10(ctr, (5, 9))
+    flips = []
+    for word in range(4):
+        for bit in (0, 17, 31):
+            c2 = [c.copy() for c in ctr]
+            c2[word] ^= np.uint64(1 << bit)
+            z = oracle.philox4x32_10(c2, (5, 9))
+            d = sum(np.unpackbits((a ^ b).view(np.uint8)).reshape(n, 32).sum(axis=1) for a, b in zip(y, z))
+            flips.append(d.mean())
+    assert all(abs(f - 64) < 3 for f in flips), flips
+    x = oracle.philox4x32_10((np.arange(1 << 16), 3, 1, 0), (11, 0))
+    top = np.concatenate([(xi >> 24).astype(np.int64) for xi in x])
+    hist = np.bincount(top, minlength=256)
+    e = top.size / 256
+    chi2 = ((hist - e) ** 2 / e).sum()
+    assert 180 < chi2 < 340, chi2
+
+
+def test_sampler_moments_and_box_muller_pairing():
+    D, S = 128, 2000
+    w = oracle.recovery_samples(1, 2, 8, S, D, "exponential", 1.5, 0.0, 123)
+    assert (w > 0).all()
+    n = w.size
+    assert abs(w.mean() - 1.5) < 4 * 1.5 / math.sqrt(n)           # mean mu, sd mu
+    assert abs(w.var() / 1.5 ** 2 - 1.0) < 0.03
+    g = oracle.recovery_samples(1, 2, 8, S, D, "gaussian", -0.5, 2.0, 123)
+    assert abs(g.mean() + 0.5) < 4 * 2.0 / math.sqrt(n)
+    assert abs(g.std() / 2.0 - 1.0) < 0.01
+    z = (g + 0.5) / 2.0                                            # standard normal draws
+    assert abs(((z > 1.0).mean()) - 0.158655) < 0.004
+    # pairing: channels 4jg, 4jg+1 come from (x0, x1); z0^2 + z1^2 = -2 ln u0
+    x = oracle.philox4x32_10((np.arange(S, dtype=np.uint64)[:, None], np.arange(D // 4, dtype=np.uint64)[None, :],
+                              1 * 8 + 2, 0), (123, 0))
+    u0 = oracle.uniform01(x[0])
+    np.testing.assert_allclose(z[:, 0::4] ** 2 + z[:, 1::4] ** 2, -2 * np.log(u0), rtol=1e-9)
+    u2 = oracle.uniform01(x[2])
+    np.testing.assert_allclose(z[:, 2::4] ** 2 + z[:, 3::4] ** 2, -2 * np.log(u2), rtol=1e-9)
+    e = oracle.recovery_samples(1, 2, 8, S, D, "exponential", 1.0, 0.0, 123)
+    np.testing.assert_allclose(e[:, 1::4], -np.log(oracle.uniform01(x[1])), rtol=1e-12)
+
+
+def test_sampled_stats_brute_force():
+    rng = np.random.default_rng(23)
+    B, H, S, D = 1, 2, 7, 8
+    k = rng.choice([0.5, -1.0, 2.0, -0.25, 1.5], size=(B, H, S, D)).astype(np.float32)
+    mask = rng.random((B, H, S, D)) < 0.4
+    A = rng.choice([0.25, 1.0, 4.0, 9.0], size=(B, H, D)).astype(np.float32)
+    for mode in ("gaussian", "exponential"):
+        r, _ = oracle.stats(k, mask, A, mode)
+        for h in range(H):
+            vals = [math.sqrt(A[0, h, j]) * abs(float(k[0, h, t, j]))
+                    for t in range(S) for j in range(D) if not mask[0, h, t, j]]
+            mu = sum(vals) / len(vals)
+            sd = math.sqrt(sum((v - mu) ** 2 for v in vals) / len(vals))
+            assert r[0, h, 0] == np.float32(mu) and abs(r[0, h, 1] - sd) <= 1e-6 * max(sd, 1)
+            assert (r[0, h, 2:] == 0).all()
+
+
+def test_sampled_gaussian_with_zero_sigma_is_the_degenerate_f():
+    """sigma = 0 makes every Gaussian draw mu: the sampled decode then equals
+    the Degenerate F (score_mean_pruned) decode."""
+    w, f, pr, r, cnt = _tiny(lam=0.5)
+    q = f["q_dec"][0]
+    rs, _ = oracle.stats(f["k"], pr["mask"], pr["A"], "gaussian")
+    rs[..., 1] = 0.0
+    rd, _ = oracle.stats(f["k"], pr["mask"], pr["A"], "score_mean_pruned")
+    got = oracle.decode_attn_sampled(q, pr["packed"], pr["mask"], f["v"], pr["A"], rs, "gaussian", 5)
+    a = np.sqrt(pr["A"].astype(np.float64))
+    r_exact = np.where(a > 0, rs[..., :1].astype(np.float64) / np.where(a > 0, a, 1.0), 0.0)
+    ref = oracle.decode_attn(q, pr["packed"], pr["mask"], f["v"], r_exact)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+    deg = oracle.decode_attn(q, pr["packed"], pr["mask"], f["v"], rd)
+    np.testing.assert_allclose(got, deg, rtol=1e-5, atol=1e-6)       # rd is r rounded to fp32
+
+
+@pytest.mark.parametrize("mode", ["gaussian", "exponential"])
+def test_sampled_lambda0_is_dense(mode):
+    w, f, pr, r, cnt = _tiny(lam=0.0)
+    rs, _ = oracle.stats(f["k"], pr["mask"], pr["A"], mode)
+    q = f["q_dec"][0]
+    got = oracle.decode_attn_sampled(q, pr["packed"], pr["mask"], f["v"], pr["A"], rs, mode, 1)
+    np.testing.assert_array_equal(got, oracle.dense_attn(q, f["k"], f["v"]))
+
+
+def test_sampled_decode_depends_on_seed_only_through_pruned_channels():
+    w, f, pr, r, cnt = _tiny(lam=0.5)
+    q = f["q_dec"][0]
+    rs, _ = oracle.stats(f["k"], pr["mask"], pr["A"], "exponential")
+    k1 = oracle.expand_keys_sampled(pr["packed"], pr["mask"], pr["A"], rs, "exponential", 1)
+    k2 = oracle.expand_keys_sampled(pr["packed"], pr["mask"], pr["A"], rs, "exponential", 2)
+    assert (k1[pr["mask"]] == k2[pr["mask"]]).all()
+    assert (k1[~pr["mask"]] != k2[~pr["mask"]]).mean() > 0.99
+
+
 # ------------------------------------------------------------------ window-score eviction
 
 def test_window_scores_closed_form_zero_queries():
