@@ -51,8 +51,12 @@ typedef enum {
     SPARK_F_MEAN_RETAINED = 0,     /* r_j = mean of retained k_tj over tokens t keeping channel j */
     SPARK_F_ZERO = 1,              /* r_j = 0 */
     SPARK_F_CONST = 2,             /* r_j = f_const */
-    SPARK_F_SCORE_MEAN_PRUNED = 3  /* Degenerate F: mu = mean over pruned (t,j) of a_j |k_tj|,
+    SPARK_F_SCORE_MEAN_PRUNED = 3, /* Degenerate F: mu = mean over pruned (t,j) of a_j |k_tj|,
                                       a_j = sqrt(A_j); r_j = mu / a_j (0 if a_j = 0) */
+    SPARK_F_GAUSSIAN = 4,          /* sampled F, Gaussian row of the F table: r[0] = mu, r[1] = sigma
+                                      (population) of the pruned a_j |k_tj|, r[2..] = 0; decode with
+                                      spark_decode_attn_sampled */
+    SPARK_F_EXPONENTIAL = 5        /* sampled F, Exponential row (mean mu): r as for SPARK_F_GAUSSIAN */
 } spark_recovery;
 
 /* How the window queries form the channel energy A_j = ||q^j||_2^2. */
@@ -106,8 +110,9 @@ int spark_prefill_prune(const void* q_win, const void* k,
  * Recovery statistics recomputed from a stored pruned cache (walkthrough
  * section 3.3 step 1), e.g. to switch F without pruning again.
  *  k_packed, mask, chan_energy   as written by spark_prefill_prune
- *  k_dense      bf16 [B][N_kv][S][D]; required by SPARK_F_SCORE_MEAN_PRUNED
- *               (the pruned values are not in the packed store), else ignored
+ *  k_dense      bf16 [B][N_kv][S][D]; required by SPARK_F_SCORE_MEAN_PRUNED and
+ *               the sampled F (the pruned values are not in the packed store),
+ *               else ignored
  *  r, cnt       outputs as in spark_prefill_prune (cnt may be NULL)
  */
 int spark_stats(const void* k_packed, const uint32_t* mask, const float* chan_energy,
@@ -135,6 +140,33 @@ int spark_stats(const void* k_packed, const uint32_t* mask, const float* chan_en
 int spark_decode_attn(const void* q, const void* k_packed, const uint32_t* mask, const void* v,
                       const float* r, int B, int S, int N_q, int N_kv, int D, float lambda,
                       float scale, int splits, float* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * One decode step with a sampled recovery F (walkthrough section 3.3, steps
+ * 2-4 and the Gaussian and Exponential rows of the F table): every pruned
+ * channel j of every cached key t draws its own saliency sample w_tj and is
+ * back-solved to w_tj / a_j (0 if a_j = 0), a_j = sqrt(A_j); then attention
+ * runs as in spark_decode_attn.
+ *  chan_energy  fp32 [B][N_kv][D]  A_j, as written by spark_prefill_prune
+ *  r            fp32 [B][N_kv][D]  (mu, sigma, 0, ...) as written for the same recovery
+ *  recovery     SPARK_F_GAUSSIAN: w = mu + sigma z, z standard normal;
+ *               SPARK_F_EXPONENTIAL: w exponential with mean mu
+ *  seed         Philox4x32-10 key (low word, high word). Token t, channel
+ *               group jg = j / 4 of (b, KV head h) uses the counter
+ *               (t, jg, b * N_kv + h, 0); its four outputs x_i give
+ *               u_i = (x_i + 1/2) 2^-32 for channels 4 jg + i. Gaussian: z by
+ *               Box-Muller, R = sqrt(-2 ln u_0) with angle 2 pi u_1 giving
+ *               z_0 = R cos, z_1 = R sin, and likewise (u_2, u_3) for z_2, z_3.
+ *               Exponential: w = -mu ln u_i. The same seed gives the same
+ *               samples on every call and every split count.
+ * Other arguments, the workspace and the return codes as for
+ * spark_decode_attn; SPARK_EINVAL also for another recovery or a NULL
+ * chan_energy. Samples are drawn in fp32 (logf, sqrtf, sincospif).
+ */
+int spark_decode_attn_sampled(const void* q, const void* k_packed, const uint32_t* mask, const void* v,
+                              const float* chan_energy, const float* r, int recovery, uint64_t seed,
+                              int B, int S, int N_q, int N_kv, int D, float lambda, float scale, int splits,
+                              float* out, void* ws, size_t ws_bytes, void* stream);
 
 /* Zero the decode completion counters of a workspace (a fill kernel on
  * `stream`; safe to record in a HIP graph). */

@@ -38,12 +38,15 @@ namespace {
 template <int G>
 struct QRow { float v[G]; };
 
-// One channel of the decode table: q'_g for the G heads of the group, then r.
-// Entries are 16-byte aligned so q' is read with vector LDS loads.
+// One channel of the decode table: q'_g for the G heads of the group, then r,
+// then (sampled F only) the scale of the channel's zero-mean sample noise.
+// Entries are 16-byte aligned so q' is read with vector LDS loads; ns sits in
+// what would otherwise be padding for every G.
 template <int G>
 struct alignas(16) TabEntry {
     float q[G];
     float r;
+    float ns;
 };
 
 // Split partials cross blocks that may run on different XCDs (separate L2s).
@@ -318,6 +321,87 @@ __device__ __forceinline__ void load_v_tile(const uint16_t* vbh, int t0, int nt,
     }
 }
 
+// ---- sampled recovery F (walkthrough section 3.3, F table, Gaussian and
+// Exponential rows): every pruned (t, j) draws its own sample.
+//
+// Philox4x32 with 10 rounds, from its published definition (Salmon, Moraes,
+// Dror and Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC 2011): a
+// round takes the two 32 x 32 -> 64-bit products of words 0 and 2 with the
+// multipliers and xors their high halves into words 1 and 3 with the round
+// key; the key advances by the two Weyl constants between rounds. Each
+// product is one 64-bit multiply-add on the vector ALU.
+constexpr uint32_t kPhiloxM0 = 0xD2511F53u, kPhiloxM1 = 0xCD9E8D57u;
+constexpr uint32_t kPhiloxW0 = 0x9E3779B9u, kPhiloxW1 = 0xBB67AE85u;
+
+__device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+    for (int rnd = 0; rnd < 10; ++rnd) {
+        if (rnd) { k0 += kPhiloxW0; k1 += kPhiloxW1; }
+        const uint64_t p0 = (uint64_t)kPhiloxM0 * c.x;
+        const uint64_t p1 = (uint64_t)kPhiloxM1 * c.z;
+        c = make_uint4((uint32_t)(p1 >> 32) ^ c.y ^ k0, (uint32_t)p1, (uint32_t)(p0 >> 32) ^ c.w ^ k1, (uint32_t)p0);
+    }
+    return c;
+}
+
+// u = (x + 1/2) 2^-32 in (0, 1], rounded to fp32.
+__device__ __forceinline__ float unit_of(uint32_t x) { return fmaf((float)x, 0x1p-32f, 0x1p-33f); }
+
+// Zero-mean noise of one Philox block for channels 4 jg + 0..3. Gaussian:
+// Box-Muller on (u0, u1) and (u2, u3), z_even = R cos(2 pi u_odd),
+// z_odd = R sin(2 pi u_odd), R = sqrt(-2 ln u_even). Exponential: -ln u has
+// mean 1, so the noise is -ln u - 1 (the sample is mu times -ln u).
+__device__ __forceinline__ void sample_noise4(uint4 x, bool gauss, float (&n)[4]) {
+    const float u[4] = {unit_of(x.x), unit_of(x.y), unit_of(x.z), unit_of(x.w)};
+    if (gauss) {
+#pragma unroll
+        for (int e = 0; e < 4; e += 2) {
+            const float R = sqrtf(-2.0f * logf(u[e]));
+            float sn, cs;
+            sincospif(2.0f * u[e + 1], &sn, &cs);
+            n[e] = R * cs;
+            n[e + 1] = R * sn;
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) n[e] = -logf(u[e]) - 1.0f;
+    }
+}
+
+// Sample term of the scores of one tile: with the table's r_j = mu / a_j
+// (the sample mean back-solved) already in the scores, every pruned channel
+// j of the lane's token adds q'_g,j ns_j n_tj. The counter of token t and
+// channel group jg is (t, jg, b * N_kv + h, 0). Groups that every lane of the
+// wave keeps are skipped.
+template <int G>
+__device__ __forceinline__ void sampled_scores(const DecodeArgs& a, const unsigned char* tab, uint4 mw, int bh,
+                                               int t0, int nt, int L, float (&s)[G]) {
+    const bool gauss = a.sampled == 4;
+    const uint32_t tok = (uint32_t)(t0 + L);
+    const bool live = L < nt;
+    const uint32_t words[4] = {mw.x, mw.y, mw.z, mw.w};
+    const TabEntry<G>* te = reinterpret_cast<const TabEntry<G>*>(tab);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const uint32_t pr = live ? ~words[w] : 0u;
+        for (int jj = 0; jj < 8; ++jj) {
+            const uint32_t nib = (pr >> (4 * jj)) & 15u;
+            if (ballot(nib != 0) == 0) continue;
+            const int jg = 8 * w + jj;
+            const uint4 x = philox4x32_10(make_uint4(tok, (uint32_t)jg, (uint32_t)bh, 0u), a.seed_lo, a.seed_hi);
+            float n[4];
+            sample_noise4(x, gauss, n);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const TabEntry<G>& e = te[4 * jg + i];
+                const float xn = ((nib >> i) & 1u) ? n[i] * e.ns : 0.0f;
+#pragma unroll
+                for (int g = 0; g < G; ++g) s[g] = fmaf(e.q[g], xn, s[g]);
+            }
+        }
+    }
+}
+
 // End of a decode block: reduce each wave's (m, l, acc) over its token phases
 // and lanes, merge the waves in LDS, publish the block's split partial, and,
 // in the last block of the (b, KV head) to finish, merge all splits.
@@ -410,7 +494,7 @@ __device__ void finish_block(const DecodeArgs& a, float (&m_run)[G], float (&l_r
     if (tid == 0) __hip_atomic_store(a.counters + bh, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int G>
+template <int G, bool SAMPLED>
 __global__ void __launch_bounds__(DECODE_THREADS)
 decode_kernel(const DecodeArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
@@ -436,7 +520,19 @@ decode_kernel(const DecodeArgs a) {
         const uint16_t qb = a.q[((size_t)b * a.N_q + (size_t)h * G + g) * 128 + j];
         reinterpret_cast<TabEntry<G>*>(tab)[j].q[g] = bf16_to_f32(qb) * a.qscale;
     }
-    if (tid < 128) reinterpret_cast<TabEntry<G>*>(tab)[tid].r = a.r[(size_t)bh * 128 + tid];
+    if (tid < 128) {
+        TabEntry<G>& e = reinterpret_cast<TabEntry<G>*>(tab)[tid];
+        if (SAMPLED) {
+            // r holds (mu, sigma); a pruned key is (mu + noise) / a_j, a_j = sqrt(A_j)
+            const float mu = a.r[(size_t)bh * 128], sigma = a.r[(size_t)bh * 128 + 1];
+            const float Aj = a.A[(size_t)bh * 128 + tid];
+            const float inv_a = Aj > 0.0f ? 1.0f / sqrtf(Aj) : 0.0f;
+            e.r = mu * inv_a;
+            e.ns = (a.sampled == 4 ? sigma : mu) * inv_a;
+        } else {
+            e.r = a.r[(size_t)bh * 128 + tid];
+        }
+    }
 
     uint16_t* lst = reinterpret_cast<uint16_t*>(wbase + (size_t)wave * lay.wave_bytes);     // [T][64]
     unsigned char* stage = wbase + (size_t)wave * lay.wave_bytes + lay.list_bytes;
@@ -566,6 +662,7 @@ decode_kernel(const DecodeArgs a) {
                 for (int g = 0; g < G; ++g) s[g] = fmaf(te.q[g], e, s[g]);
             }
         }
+        if (SAMPLED) sampled_scores<G>(a, tab, mw, bh, t0, nt, L, s);
 #pragma unroll
         for (int g = 0; g < G; ++g) s[g] = (L < nt) ? s[g] + cq[g] : -INFINITY;
 
@@ -940,10 +1037,36 @@ uint32_t decode_fast_lds_bytes(int G, int T, int nsplit) {
 bool decode_fast_supported(int G, int T) { return G == 4 && (T == 26 || T == 38 || T == 64); }
 
 
+template <bool SAMPLED>
+hipError_t launch_generic(const DecodeArgs& a, int G, dim3 grid, dim3 block, hipStream_t stream) {
+    const size_t lds = a.lay.lds_bytes;
+    const void* fn = nullptr;
+    switch (G) {
+        case 1: fn = reinterpret_cast<const void*>(&decode_kernel<1, SAMPLED>); break;
+        case 2: fn = reinterpret_cast<const void*>(&decode_kernel<2, SAMPLED>); break;
+        case 4: fn = reinterpret_cast<const void*>(&decode_kernel<4, SAMPLED>); break;
+        case 8: fn = reinterpret_cast<const void*>(&decode_kernel<8, SAMPLED>); break;
+        default: return hipErrorInvalidValue;
+    }
+    if (lds > 65536) {
+        // LDS above 64 KiB per workgroup must be requested explicitly (160 KiB per CU on gfx950)
+        const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    switch (G) {
+        case 1: hipLaunchKernelGGL((decode_kernel<1, SAMPLED>), grid, block, lds, stream, a); break;
+        case 2: hipLaunchKernelGGL((decode_kernel<2, SAMPLED>), grid, block, lds, stream, a); break;
+        case 4: hipLaunchKernelGGL((decode_kernel<4, SAMPLED>), grid, block, lds, stream, a); break;
+        default: hipLaunchKernelGGL((decode_kernel<8, SAMPLED>), grid, block, lds, stream, a); break;
+    }
+    return hipGetLastError();
+}
+
 // One launch: the split blocks, the last of which per (b, KV head) merges.
+// The sampled F always takes the generic kernel.
 hipError_t launch_decode(const DecodeArgs& a, int G, int BH, hipStream_t stream) {
     const dim3 grid(a.nsplit, BH), block(DECODE_THREADS);
-    if (decode_fast_supported(G, a.T)) {
+    if (!a.sampled && decode_fast_supported(G, a.T)) {
         const dim3 fblock(DECODE_FAST_THREADS);
         // the fast kernel's LDS is static (DECODE_FAST_LDS_BYTES)
         if (decode_fast_lds_bytes(G, a.T, a.nsplit) > (uint32_t)DECODE_FAST_LDS_BYTES) return hipErrorInvalidValue;
@@ -954,27 +1077,7 @@ hipError_t launch_decode(const DecodeArgs& a, int G, int BH, hipStream_t stream)
         }
         return hipGetLastError();
     }
-    const size_t lds = a.lay.lds_bytes;
-    const void* fn = nullptr;
-    switch (G) {
-        case 1: fn = reinterpret_cast<const void*>(&decode_kernel<1>); break;
-        case 2: fn = reinterpret_cast<const void*>(&decode_kernel<2>); break;
-        case 4: fn = reinterpret_cast<const void*>(&decode_kernel<4>); break;
-        case 8: fn = reinterpret_cast<const void*>(&decode_kernel<8>); break;
-        default: return hipErrorInvalidValue;
-    }
-    if (lds > 65536) {
-        // LDS above 64 KiB per workgroup must be requested explicitly (160 KiB per CU on gfx950)
-        const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-    }
-    switch (G) {
-        case 1: hipLaunchKernelGGL(decode_kernel<1>, grid, block, lds, stream, a); break;
-        case 2: hipLaunchKernelGGL(decode_kernel<2>, grid, block, lds, stream, a); break;
-        case 4: hipLaunchKernelGGL(decode_kernel<4>, grid, block, lds, stream, a); break;
-        default: hipLaunchKernelGGL(decode_kernel<8>, grid, block, lds, stream, a); break;
-    }
-    return hipGetLastError();
+    return a.sampled ? launch_generic<true>(a, G, grid, block, stream) : launch_generic<false>(a, G, grid, block, stream);
 }
 
 __global__ void fill_u32_kernel(uint32_t* p, uint32_t value, size_t n) {

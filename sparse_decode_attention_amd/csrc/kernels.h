@@ -55,7 +55,8 @@ struct DecodeArgs {
     const uint16_t* packed;   // [B][N_kv][S][T]
     const uint32_t* mask;     // [B][N_kv][S][4]
     const uint16_t* v;        // [B][N_kv][S][128]
-    const float* r;           // [B][N_kv][128]
+    const float* r;           // [B][N_kv][128]; sampled F: (mu, sigma) in entries 0, 1
+    const float* A;           // [B][N_kv][128] channel energy (sampled F only)
     float* out;               // [B][N_q][128]
     float* part_ml;           // [B*N_kv][nsplit][2][G]
     float* part_acc;          // [B*N_kv][nsplit][G][128]
@@ -63,6 +64,8 @@ struct DecodeArgs {
     size_t packed_elems;      // B*N_kv*S*T
     int S, T, N_q, N_kv, nsplit, chunk;
     float qscale;             // softmax scale * log2(e)
+    int sampled;              // 0, or the sampled F (4 Gaussian, 5 Exponential)
+    uint32_t seed_lo, seed_hi;  // Philox key of the sampled F
     DecodeLayout lay;
 };
 

@@ -65,7 +65,7 @@ select_pack_kernel(const uint16_t* __restrict__ k, const float* __restrict__ A,
     __shared__ uint4 stage[4][64];            // 4 tokens x 256 B per wave
     __shared__ double red_sum[4][128];
     __shared__ int red_cnt[4][128];
-    __shared__ double red_pr[4];
+    __shared__ double red_pr[4][2];
 
     const int bh = blockIdx.y;
     const int blk = blockIdx.x;
@@ -78,7 +78,7 @@ select_pack_kernel(const uint16_t* __restrict__ k, const float* __restrict__ A,
     const float A1 = A[(size_t)bh * 128 + 64 + L];
     const double a0 = sqrt((double)A0), a1 = sqrt((double)A1);
 
-    double sum0 = 0.0, sum1 = 0.0, pruned = 0.0;
+    double sum0 = 0.0, sum1 = 0.0, pruned = 0.0, pruned2 = 0.0;
     int cnt0 = 0, cnt1 = 0;
 
     const uint16_t* kbh = k + (size_t)bh * S * 128;
@@ -147,9 +147,11 @@ select_pack_kernel(const uint16_t* __restrict__ k, const float* __restrict__ A,
             } else {
                 cnt0 += kept0;
                 cnt1 += kept1;
-                if (recovery == 3) {
-                    if (!kept0) pruned += a0 * (double)fabsf(k0);
-                    if (!kept1) pruned += a1 * (double)fabsf(k1);
+                if (recovery >= 3) {
+                    const double w0 = kept0 ? 0.0 : a0 * (double)fabsf(k0);
+                    const double w1 = kept1 ? 0.0 : a1 * (double)fabsf(k1);
+                    pruned += w0 + w1;
+                    if (recovery >= 4) pruned2 += w0 * w0 + w1 * w1;
                 }
             }
         }
@@ -161,10 +163,13 @@ select_pack_kernel(const uint16_t* __restrict__ k, const float* __restrict__ A,
     red_sum[wave][64 + L] = sum1;
     red_cnt[wave][L] = cnt0;
     red_cnt[wave][64 + L] = cnt1;
-    if (recovery == 3) {
-        double p = pruned;
-        for (int o = 32; o > 0; o >>= 1) p += __shfl_xor(p, o, 64);
-        if (L == 0) red_pr[wave] = p;
+    if (recovery >= 3) {
+        double p = pruned, p2 = pruned2;
+        for (int o = 32; o > 0; o >>= 1) {
+            p += __shfl_xor(p, o, 64);
+            p2 += __shfl_xor(p2, o, 64);
+        }
+        if (L == 0) { red_pr[wave][0] = p; red_pr[wave][1] = p2; }
     }
     __syncthreads();
     if (threadIdx.x < 128) {
@@ -173,8 +178,8 @@ select_pack_kernel(const uint16_t* __restrict__ k, const float* __restrict__ A,
         const int c = red_cnt[0][j] + red_cnt[1][j] + red_cnt[2][j] + red_cnt[3][j];
         part_sum[((size_t)bh * nblk + blk) * 128 + j] = s;
         part_cnt[((size_t)bh * nblk + blk) * 128 + j] = c;
-        if (j == 0) part_pruned[(size_t)bh * nblk + blk] =
-            (recovery == 3) ? ((red_pr[0] + red_pr[1]) + red_pr[2]) + red_pr[3] : 0.0;
+        if (j < 2) part_pruned[((size_t)bh * nblk + blk) * 2 + j] =
+            (recovery >= 3) ? ((red_pr[0][j] + red_pr[1][j]) + red_pr[2][j]) + red_pr[3][j] : 0.0;
     }
 }
 
@@ -188,14 +193,14 @@ stats_partial_kernel(const uint16_t* __restrict__ k_packed, const uint32_t* __re
                      double* __restrict__ part_pruned, int S, int T, int nblk, int recovery) {
     __shared__ double red_sum[4][128];
     __shared__ int red_cnt[4][128];
-    __shared__ double red_pr[4];
+    __shared__ double red_pr[4][2];
     const int bh = blockIdx.y, blk = blockIdx.x;
     const int wave = threadIdx.x >> 6, L = threadIdx.x & 63;
     const int t_begin = blk * PRUNE_TOKENS_PER_BLOCK;
     const int t_end = min(S, t_begin + PRUNE_TOKENS_PER_BLOCK);
     const double a0 = sqrt((double)A[(size_t)bh * 128 + L]);
     const double a1 = sqrt((double)A[(size_t)bh * 128 + 64 + L]);
-    double sum0 = 0.0, sum1 = 0.0, pruned = 0.0;
+    double sum0 = 0.0, sum1 = 0.0, pruned = 0.0, pruned2 = 0.0;
     int cnt0 = 0, cnt1 = 0;
     for (int t = t_begin + wave; t < t_end; t += 4) {
         const uint4 mw = *reinterpret_cast<const uint4*>(mask + ((size_t)bh * S + t) * 4);
@@ -210,20 +215,25 @@ stats_partial_kernel(const uint16_t* __restrict__ k_packed, const uint32_t* __re
             const int rk0 = (int)mbcnt(m0), rk1 = __popcll(m0) + (int)mbcnt(m1);
             if (kept0 && rk0 < T) sum0 += (double)bf16_to_f32(row[rk0]);
             if (kept1 && rk1 < T) sum1 += (double)bf16_to_f32(row[rk1]);
-        } else if (recovery == 3) {
+        } else if (recovery >= 3) {
             const uint16_t* row = k_dense + ((size_t)bh * S + t) * 128;
-            if (!kept0) pruned += a0 * (double)fabsf(bf16_to_f32(row[L]));
-            if (!kept1) pruned += a1 * (double)fabsf(bf16_to_f32(row[64 + L]));
+            const double w0 = kept0 ? 0.0 : a0 * (double)fabsf(bf16_to_f32(row[L]));
+            const double w1 = kept1 ? 0.0 : a1 * (double)fabsf(bf16_to_f32(row[64 + L]));
+            pruned += w0 + w1;
+            if (recovery >= 4) pruned2 += w0 * w0 + w1 * w1;
         }
     }
     red_sum[wave][L] = sum0;
     red_sum[wave][64 + L] = sum1;
     red_cnt[wave][L] = cnt0;
     red_cnt[wave][64 + L] = cnt1;
-    if (recovery == 3) {
-        double p = pruned;
-        for (int o = 32; o > 0; o >>= 1) p += __shfl_xor(p, o, 64);
-        if (L == 0) red_pr[wave] = p;
+    if (recovery >= 3) {
+        double p = pruned, p2 = pruned2;
+        for (int o = 32; o > 0; o >>= 1) {
+            p += __shfl_xor(p, o, 64);
+            p2 += __shfl_xor(p2, o, 64);
+        }
+        if (L == 0) { red_pr[wave][0] = p; red_pr[wave][1] = p2; }
     }
     __syncthreads();
     if (threadIdx.x < 128) {
@@ -231,8 +241,8 @@ stats_partial_kernel(const uint16_t* __restrict__ k_packed, const uint32_t* __re
         part_sum[((size_t)bh * nblk + blk) * 128 + j] =
             ((red_sum[0][j] + red_sum[1][j]) + red_sum[2][j]) + red_sum[3][j];
         part_cnt[((size_t)bh * nblk + blk) * 128 + j] = red_cnt[0][j] + red_cnt[1][j] + red_cnt[2][j] + red_cnt[3][j];
-        if (j == 0) part_pruned[(size_t)bh * nblk + blk] =
-            (recovery == 3) ? ((red_pr[0] + red_pr[1]) + red_pr[2]) + red_pr[3] : 0.0;
+        if (j < 2) part_pruned[((size_t)bh * nblk + blk) * 2 + j] =
+            (recovery >= 3) ? ((red_pr[0][j] + red_pr[1][j]) + red_pr[2][j]) + red_pr[3][j] : 0.0;
     }
 }
 
@@ -247,7 +257,7 @@ stats_reduce_kernel(const double* __restrict__ part_sum, const int32_t* __restri
                     int S, int T, int nblk, int recovery, float f_const) {
     __shared__ double sh_s[STATS_PARTS][128];
     __shared__ long long sh_c[STATS_PARTS][128];
-    __shared__ double sh_p[STATS_PARTS];
+    __shared__ double sh_p[STATS_PARTS][2];
     const int bh = blockIdx.x, j = threadIdx.x & 127, part = threadIdx.x >> 7;
     const int per = (nblk + STATS_PARTS - 1) / STATS_PARTS;
     const int lo = part * per, hi = min(nblk, lo + per);
@@ -258,9 +268,9 @@ stats_reduce_kernel(const double* __restrict__ part_sum, const int32_t* __restri
         s += part_sum[((size_t)bh * nblk + blk) * 128 + j];
         c += part_cnt[((size_t)bh * nblk + blk) * 128 + j];
     }
-    if (recovery == 3 && j == 0) {
-        for (int blk = lo; blk < hi; ++blk) p += part_pruned[(size_t)bh * nblk + blk];
-        sh_p[part] = p;
+    if (recovery >= 3 && j < 2) {
+        for (int blk = lo; blk < hi; ++blk) p += part_pruned[((size_t)bh * nblk + blk) * 2 + j];
+        sh_p[part][j] = p;
     }
     sh_s[part][j] = s;
     sh_c[part][j] = c;
@@ -274,13 +284,20 @@ stats_reduce_kernel(const double* __restrict__ part_sum, const int32_t* __restri
         out = c > 0 ? (float)(s / (double)c) : 0.f;
     } else if (recovery == 2) {
         out = f_const;
-    } else if (recovery == 3) {
+    } else if (recovery >= 3) {
+        double p2 = 0.0;
         p = 0.0;
-        for (int q = 0; q < STATS_PARTS; ++q) p += sh_p[q];
+        for (int q = 0; q < STATS_PARTS; ++q) { p += sh_p[q][0]; p2 += sh_p[q][1]; }
         const double npruned = (double)S * (double)(128 - T);
         const double mu = npruned > 0 ? p / npruned : 0.0;
-        const double a = sqrt((double)A[(size_t)bh * 128 + j]);
-        out = a > 0 ? (float)(mu / a) : 0.f;
+        if (recovery == 3) {
+            const double a = sqrt((double)A[(size_t)bh * 128 + j]);
+            out = a > 0 ? (float)(mu / a) : 0.f;
+        } else {
+            // sampled F: (mu, sigma) of the pruned saliency in entries 0 and 1
+            const double m2 = npruned > 0 ? p2 / npruned : 0.0;
+            out = j == 0 ? (float)mu : j == 1 ? (float)sqrt(fmax(m2 - mu * mu, 0.0)) : 0.f;
+        }
     }
     r[(size_t)bh * 128 + j] = out;
     if (cnt) cnt[(size_t)bh * 128 + j] = (int32_t)c;

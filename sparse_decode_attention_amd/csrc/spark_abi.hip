@@ -25,7 +25,8 @@ int check_group(int N_q, int N_kv) {
     return SPARK_OK;
 }
 
-// prefill workspace: part_sum double [BH][nblk][128] | part_cnt int32 [BH][nblk][128] | part_pruned double [BH][nblk]
+// prefill workspace: part_sum double [BH][nblk][128] | part_cnt int32 [BH][nblk][128] |
+// part_pruned double [BH][nblk][2] (sum of the pruned saliency, sum of its squares)
 struct PrefillWs {
     double* sum;
     int32_t* cnt;
@@ -41,7 +42,7 @@ PrefillWs prefill_layout(void* ws, int B, int S, int N_kv) {
     const size_t n = BH * (size_t)w.nblk;
     const size_t s_sum = round_up(n * 128 * sizeof(double), 256);
     const size_t s_cnt = round_up(n * 128 * sizeof(int32_t), 256);
-    const size_t s_pr = round_up(n * sizeof(double), 256);
+    const size_t s_pr = round_up(n * 2 * sizeof(double), 256);
     char* base = static_cast<char*>(ws);
     w.sum = reinterpret_cast<double*>(base);
     w.cnt = reinterpret_cast<int32_t*>(base + s_sum);
@@ -116,7 +117,7 @@ int spark_prefill_prune(const void* q_win, const void* k, int B, int S, int N_q,
     const int T = kept_or_neg(D, lambda);
     if (T < 0) return SPARK_EINVAL;
     if (qagg != SPARK_QAGG_L2 && qagg != SPARK_QAGG_MEAN) return SPARK_EINVAL;
-    if (recovery < SPARK_F_MEAN_RETAINED || recovery > SPARK_F_SCORE_MEAN_PRUNED) return SPARK_EINVAL;
+    if (recovery < SPARK_F_MEAN_RETAINED || recovery > SPARK_F_EXPONENTIAL) return SPARK_EINVAL;
     if (int e = check_group(N_q, N_kv)) return e;
     if (D != 128) return SPARK_EUNSUPPORTED;
     if (!q_win || !k || !mask || !chan_energy || !r || !ws || (T > 0 && !k_packed)) return SPARK_EINVAL;
@@ -144,11 +145,11 @@ int spark_stats(const void* k_packed, const uint32_t* mask, const float* chan_en
     if (B < 1 || S < 1 || N_kv < 1 || D < 1) return SPARK_EINVAL;
     const int T = kept_or_neg(D, lambda);
     if (T < 0) return SPARK_EINVAL;
-    if (recovery < SPARK_F_MEAN_RETAINED || recovery > SPARK_F_SCORE_MEAN_PRUNED) return SPARK_EINVAL;
+    if (recovery < SPARK_F_MEAN_RETAINED || recovery > SPARK_F_EXPONENTIAL) return SPARK_EINVAL;
     if (D != 128) return SPARK_EUNSUPPORTED;
     if (!mask || !chan_energy || !r || !ws) return SPARK_EINVAL;
     if (recovery == SPARK_F_MEAN_RETAINED && T > 0 && !k_packed) return SPARK_EINVAL;
-    if (recovery == SPARK_F_SCORE_MEAN_PRUNED && !k_dense) return SPARK_EINVAL;
+    if (recovery >= SPARK_F_SCORE_MEAN_PRUNED && !k_dense) return SPARK_EINVAL;
     if (!aligned(mask, 16) || !aligned(chan_energy, 16) || !aligned(r, 16) || (cnt && !aligned(cnt, 16)) ||
         (k_packed && !aligned(k_packed, 16)) || (k_dense && !aligned(k_dense, 16)) || !aligned(ws, 256))
         return SPARK_EALIGN;
@@ -164,9 +165,16 @@ int spark_stats(const void* k_packed, const uint32_t* mask, const float* chan_en
     return hip_status(hipGetLastError());
 }
 
-int spark_decode_attn(const void* q, const void* k_packed, const uint32_t* mask, const void* v, const float* r,
-                      int B, int S, int N_q, int N_kv, int D, float lambda, float scale, int splits,
-                      float* out, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks, workspace carving and launch shared by both decode entry points.
+// sampled = 0: the fixed recovery vector r; else the sampled F of that mode,
+// with r = (mu, sigma, ...) and the channel energy A.
+int decode_call(const void* q, const void* k_packed, const uint32_t* mask, const void* v, const float* r,
+                const float* A, int sampled, uint64_t seed, int B, int S, int N_q, int N_kv, int D, float lambda,
+                float scale, int splits, float* out, void* ws, size_t ws_bytes, void* stream) {
     if (B < 1 || S < 1 || D < 1 || splits < 0) return SPARK_EINVAL;
     const int T = kept_or_neg(D, lambda);
     if (T < 0) return SPARK_EINVAL;
@@ -175,9 +183,9 @@ int spark_decode_attn(const void* q, const void* k_packed, const uint32_t* mask,
     if (D != 128) return SPARK_EUNSUPPORTED;
     const int BH = B * N_kv;
     if ((size_t)BH > (SPARK_DECODE_COUNTER_BYTES / 4)) return SPARK_EUNSUPPORTED;
-    if (!q || !mask || !v || !r || !out || !ws || (T > 0 && !k_packed)) return SPARK_EINVAL;
+    if (!q || !mask || !v || !r || !out || !ws || (T > 0 && !k_packed) || (sampled && !A)) return SPARK_EINVAL;
     if (!aligned(q, 16) || !aligned(mask, 16) || !aligned(v, 16) || !aligned(r, 16) || !aligned(out, 16) ||
-        (k_packed && !aligned(k_packed, 16)) || !aligned(ws, 256))
+        (k_packed && !aligned(k_packed, 16)) || (A && !aligned(A, 16)) || !aligned(ws, 256))
         return SPARK_EALIGN;
     const int G = N_q / N_kv;
     int nsplit, chunk;
@@ -191,6 +199,7 @@ int spark_decode_attn(const void* q, const void* k_packed, const uint32_t* mask,
     a.mask = mask;
     a.v = static_cast<const uint16_t*>(v);
     a.r = r;
+    a.A = A;
     a.out = out;
     a.counters = reinterpret_cast<uint32_t*>(base);
     a.part_ml = reinterpret_cast<float*>(base + SPARK_DECODE_COUNTER_BYTES);
@@ -205,8 +214,32 @@ int spark_decode_attn(const void* q, const void* k_packed, const uint32_t* mask,
     a.chunk = chunk;
     const float sc = scale > 0.f ? scale : (float)(1.0 / sqrt((double)D));
     a.qscale = sc * 1.4426950408889634f;
+    a.sampled = sampled;
+    a.seed_lo = (uint32_t)seed;
+    a.seed_hi = (uint32_t)(seed >> 32);
     a.lay = decode_layout(G, T, nsplit);
     return hip_status(launch_decode(a, G, BH, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int spark_decode_attn(const void* q, const void* k_packed, const uint32_t* mask, const void* v, const float* r,
+                      int B, int S, int N_q, int N_kv, int D, float lambda, float scale, int splits,
+                      float* out, void* ws, size_t ws_bytes, void* stream) {
+    return decode_call(q, k_packed, mask, v, r, nullptr, 0, 0, B, S, N_q, N_kv, D, lambda, scale, splits, out, ws,
+                       ws_bytes, stream);
+}
+
+int spark_decode_attn_sampled(const void* q, const void* k_packed, const uint32_t* mask, const void* v,
+                              const float* chan_energy, const float* r, int recovery, uint64_t seed,
+                              int B, int S, int N_q, int N_kv, int D, float lambda, float scale, int splits,
+                              float* out, void* ws, size_t ws_bytes, void* stream) {
+    if (recovery != SPARK_F_GAUSSIAN && recovery != SPARK_F_EXPONENTIAL) return SPARK_EINVAL;
+    if (!chan_energy) return SPARK_EINVAL;
+    return decode_call(q, k_packed, mask, v, r, chan_energy, recovery, seed, B, S, N_q, N_kv, D, lambda, scale,
+                       splits, out, ws, ws_bytes, stream);
 }
 
 int spark_decode_ws_init(void* ws, size_t ws_bytes, void* stream) {

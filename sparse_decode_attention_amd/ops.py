@@ -19,14 +19,14 @@ LIB_PATH = os.path.join(_PKG, "libspark.so")
 HEADER = os.path.join(os.path.dirname(_PKG), "include", "spark.h")
 
 OK, EINVAL, EUNSUPPORTED, EALIGN, ENOSPACE, EHIP = 0, -1, -2, -3, -4, -5
-RECOVERY = {"mean_retained": 0, "zero": 1, "const": 2, "score_mean_pruned": 3}
+RECOVERY = {"mean_retained": 0, "zero": 1, "const": 2, "score_mean_pruned": 3, "gaussian": 4, "exponential": 5}
 QAGG = {"l2": 0, "mean": 1}
 DECODE_COUNTER_BYTES = 4096
 
 _lib = None
 _lock = threading.Lock()
 
-_vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_vp, _i, _f, _sz, _u64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t, ctypes.c_uint64
 _SIGS = {
     "spark_num_kept": (_i, [_i, _f]),
     "spark_strerror": (ctypes.c_char_p, [_i]),
@@ -36,6 +36,8 @@ _SIGS = {
                                  _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "spark_stats": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _f, _vp, _vp, _vp, _sz, _vp]),
     "spark_decode_attn": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _f, _i, _vp, _vp, _sz, _vp]),
+    "spark_decode_attn_sampled": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _u64, _i, _i, _i, _i, _i, _f, _f, _i,
+                                       _vp, _vp, _sz, _vp]),
     "spark_decode_ws_init": (_i, [_vp, _sz, _vp]),
     "spark_read_stream": (_i, [_vp, _sz, _vp, _i, _vp]),
     "spark_window_evict_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
@@ -186,6 +188,31 @@ def decode_attn(q, k_packed, mask, v, r, lam: float, scale: float = 0.0, splits:
                                  B, S, N_q, n_kv, D, float(lam), float(scale), int(splits), _ptr(out),
                                  _ptr(ws), ws.numel(), _stream(dev))
     _check("spark_decode_attn", st)
+    return out
+
+
+def decode_attn_sampled(q, k_packed, mask, v, chan_energy, r, recovery: str, seed: int, lam: float,
+                        scale: float = 0.0, splits: int = 0, out=None, ws=None):
+    """spark_decode_attn_sampled: decode with a sampled recovery F ("gaussian"
+    or "exponential"); r holds (mu, sigma) from prefill_prune / stats of the
+    same recovery, chan_energy the A_j."""
+    B, N_q, D = q.shape
+    n_kv, S = v.shape[1], v.shape[2]
+    _need(q, "q", torch.bfloat16)
+    _need(v, "v", torch.bfloat16, (B, n_kv, S, D))
+    _need(chan_energy, "chan_energy", torch.float32, (B, n_kv, D))
+    _need(r, "r", torch.float32, (B, n_kv, D))
+    dev = q.device
+    out = torch.empty((B, N_q, D), dtype=torch.float32, device=dev) if out is None else out
+    nb = decode_ws_bytes(B, S, N_q, n_kv, D, splits)
+    if ws is None:
+        ws = workspace(dev, "decode", nb)
+    T = num_kept(D, lam)
+    st = lib().spark_decode_attn_sampled(_ptr(q), _ptr(k_packed) if T > 0 else None, _ptr(mask), _ptr(v),
+                                         _ptr(chan_energy), _ptr(r), RECOVERY[recovery], int(seed) & (2**64 - 1),
+                                         B, S, N_q, n_kv, D, float(lam), float(scale), int(splits), _ptr(out),
+                                         _ptr(ws), ws.numel(), _stream(dev))
+    _check("spark_decode_attn_sampled", st)
     return out
 
 

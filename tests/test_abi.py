@@ -100,6 +100,30 @@ def test_decode_rejects_bad_arguments():
     assert _decode(nws=ops.DECODE_COUNTER_BYTES) == ops.ENOSPACE
 
 
+def _decode_sampled(**kw):
+    a = dict(q=FAKE, kp=FAKE, mask=FAKE, v=FAKE, A=FAKE, r=FAKE, rec=4, seed=2**64 - 1, B=1, S=64, N_q=32,
+             N_kv=8, D=128, lam=0.5, scale=0.0, splits=0, out=FAKE, ws=FAKE, nws=0, st=None)
+    a.update(kw)
+    return ops.lib().spark_decode_attn_sampled(a["q"], a["kp"], a["mask"], a["v"], a["A"], a["r"], a["rec"],
+                                               a["seed"], a["B"], a["S"], a["N_q"], a["N_kv"], a["D"], a["lam"],
+                                               a["scale"], a["splits"], a["out"], a["ws"], a["nws"], a["st"])
+
+
+def test_decode_sampled_rejects_bad_arguments():
+    for rec in (0, 1, 2, 3, 6, -1):
+        assert _decode_sampled(rec=rec) == ops.EINVAL
+    assert _decode_sampled(A=None) == ops.EINVAL
+    assert _decode_sampled(A=MIS) == ops.EALIGN
+    assert _decode_sampled(r=None) == ops.EINVAL
+    assert _decode_sampled(S=0) == ops.EINVAL
+    assert _decode_sampled(N_q=24) == ops.EUNSUPPORTED
+    assert _decode_sampled(D=64) == ops.EUNSUPPORTED
+    assert _decode_sampled(kp=None) == ops.EINVAL
+    assert _decode_sampled(kp=None, lam=1.0, nws=0) == ops.ENOSPACE     # T = 0 needs no packed store
+    assert _decode_sampled(rec=5) == ops.ENOSPACE
+    assert _decode_sampled(nws=ops.DECODE_COUNTER_BYTES) == ops.ENOSPACE
+
+
 def test_stats_rejects_bad_arguments():
     l = ops.lib()
 
@@ -110,8 +134,10 @@ def test_stats_rejects_bad_arguments():
         return l.spark_stats(a["kp"], a["mask"], a["A"], a["kd"], a["B"], a["S"], a["N_kv"], a["D"], a["lam"],
                              a["rec"], a["fc"], a["r"], a["cnt"], a["ws"], a["nws"], None)
     assert call(rec=3) == ops.EINVAL                     # pruned-score mean needs the dense keys
+    assert call(rec=4) == ops.EINVAL                     # so do the sampled F
+    assert call(rec=5) == ops.EINVAL
     assert call(kp=None) == ops.EINVAL
-    assert call(rec=4) == ops.EINVAL
+    assert call(rec=6, kd=FAKE) == ops.EINVAL
     assert call(D=96) == ops.EUNSUPPORTED
     assert call(mask=MIS) == ops.EALIGN
     assert call() == ops.ENOSPACE
