@@ -35,6 +35,7 @@ sys.path.insert(0, ROOT)
 METRIC = "SparK decode attn effective KV GB/s & %HBM peak, S=32K, λ=0.5/0.8"
 HBM_PEAK_GBS = 8000.0
 MALL_DEFEAT_BYTES = 768e6
+SAMPLE_SEED = 0x5EED5A3B1E0F2C47   # Philox key of the sampled-F legs
 DECODE_SOURCES = ["sparse_decode_attention_amd/csrc/decode.hip", "sparse_decode_attention_amd/csrc/kernels.h",
                   "sparse_decode_attention_amd/csrc/common.h", "sparse_decode_attention_amd/csrc/spark_abi.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_kernel_llama8b_s32k_traffic.md")
@@ -73,7 +74,8 @@ def effective_prefill_bytes(w, T):
     return w.B * w.n_kv * w.S * (2 * w.D + 2 * T + 16)
 
 
-def run_leg(w, steps, warmup, rotate=True, seed=0, verbose=True, x=None):
+def run_leg(w, steps, warmup, rotate=True, seed=0, verbose=True, x=None, recovery="mean_retained",
+            rng_seed=SAMPLE_SEED):
     import torch
     from sparse_decode_attention_amd import gen, ops
 
@@ -96,13 +98,19 @@ def run_leg(w, steps, warmup, rotate=True, seed=0, verbose=True, x=None):
         })
     outs = torch.empty((w.steps, w.B, w.n_q, w.D), dtype=torch.float32, device=dev)
 
+    sampled = recovery in ("gaussian", "exponential")
+
     def prefill():
-        ops.prefill_prune(x["q_win"], x["k"], w.n_kv, w.lam, out=reps[0])
+        ops.prefill_prune(x["q_win"], x["k"], w.n_kv, w.lam, recovery=recovery, out=reps[0])
 
     def decode_all():
         for s in range(w.steps):
             rp = reps[s % R]
-            ops.decode_attn(x["q_dec"][s], rp["k_packed"], rp["mask"], rp["v"], rp["r"], w.lam, out=outs[s])
+            if sampled:
+                ops.decode_attn_sampled(x["q_dec"][s], rp["k_packed"], rp["mask"], rp["v"], rp["chan_energy"],
+                                        rp["r"], recovery, rng_seed, w.lam, out=outs[s])
+            else:
+                ops.decode_attn(x["q_dec"][s], rp["k_packed"], rp["mask"], rp["v"], rp["r"], w.lam, out=outs[s])
 
     # eager pass: fills every replica and allocates the cached workspaces
     prefill()
@@ -425,6 +433,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the 128K-context, stacked-eviction and 32-layer workloads")
+    ap.add_argument("--no-sampled", action="store_true", help="skip the sampled recovery F legs")
     ap.add_argument("--warm", action="store_true", help="also report a run without replica rotation")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="run a plain device copy of this size after the legs (counter calibration)")
@@ -494,6 +503,19 @@ def main():
                           "decode_us_per_launch": round(leg2["decode_us_per_launch"], 3),
                           "prefill_GBps": round(leg2["prefill_GBps"], 1), "replicas": leg2["replicas"]}
         del leg2
+    if not args.no_sampled:
+        line["sampled_f"] = {}
+        for rec in ("gaussian", "exponential"):
+            print(f"bench: sampled F ({rec}) on {w.name}", file=sys.stderr, flush=True)
+            lg = run_leg(w, min(args.steps, 5), min(args.warmup, 2), x=main_leg["x"], recovery=rec)
+            line["sampled_f"][rec] = {
+                "workload": w.name, "kernel": f"decode_kernel<{w.G}, {ops.RECOVERY[rec]}>",
+                "decode_us_per_launch": round(lg["decode_us_per_launch"], 3),
+                "GBps": round(lg["decode_GBps"], 2),
+                "x_fixed_r_time": round(lg["decode_us_per_launch"] / main_leg["decode_us_per_launch"], 3),
+                "prefill_us": round(lg["prefill_us"], 2), "seed": hex(SAMPLE_SEED)}
+            del lg
+        torch.cuda.empty_cache()
     if not args.no_extra:
         w3 = WORKLOADS["llama8b_s128k_l08"]
         print(f"bench: {w3.name}", file=sys.stderr, flush=True)

@@ -75,7 +75,8 @@ int spark_num_kept(int D, float lambda);
 /* Human-readable name of a spark_status. Never NULL. */
 const char* spark_strerror(int status);
 
-/* Workspace sizes in bytes (0 on invalid sizes). */
+/* Workspace sizes in bytes (0 on invalid sizes). The decode size serves both
+ * spark_decode_attn and spark_decode_attn_sampled. */
 size_t spark_prefill_workspace_bytes(int B, int S, int N_kv, int D);
 size_t spark_decode_workspace_bytes(int B, int S, int N_q, int N_kv, int D, int splits);
 
@@ -128,7 +129,8 @@ int spark_stats(const void* k_packed, const uint32_t* mask, const float* chan_en
  *  k_packed, mask, r         the pruned cache (layouts as above)
  *  v        bf16 [B][N_kv][S][D]
  *  scale    softmax scale; <= 0 selects 1/sqrt(D)
- *  splits   sequence splits per (b, KV head); 0 lets the library choose;
+ *  splits   sequence splits per (b, KV head); 0 lets the library choose
+ *           (about 256 blocks in all; 512 for spark_decode_attn_sampled);
  *           larger values are clamped to min(256, ceil(S / 64))
  *  out      fp32 [B][N_q][D]
  * No causal mask: the query attends to every cached token. fp32 arithmetic

@@ -38,15 +38,12 @@ namespace {
 template <int G>
 struct QRow { float v[G]; };
 
-// One channel of the decode table: q'_g for the G heads of the group, then r,
-// then (sampled F only) the scale of the channel's zero-mean sample noise.
-// Entries are 16-byte aligned so q' is read with vector LDS loads; ns sits in
-// what would otherwise be padding for every G.
+// One channel of the decode table: q'_g for the G heads of the group, then r.
+// Entries are 16-byte aligned so q' is read with vector LDS loads.
 template <int G>
 struct alignas(16) TabEntry {
     float q[G];
     float r;
-    float ns;
 };
 
 // Split partials cross blocks that may run on different XCDs (separate L2s).
@@ -94,10 +91,11 @@ __host__ __device__ inline uint32_t finish_scratch_bytes(int G, int NT, int nspl
     return finish_own_offset(G, NT, nsplit) + (2u * G + (uint32_t)G * 128u) * 4u;
 }
 
-DecodeLayout decode_layout(int G, int T, int nsplit) {
+DecodeLayout decode_layout(int G, int T, int nsplit, bool sampled) {
     DecodeLayout L{};
     L.tab_stride = (uint32_t)tab_stride_for(G);
-    L.tab_bytes = 128u * L.tab_stride;
+    // sampled F: the q'_g ns_j table [128][G] follows the q'/r table
+    L.tab_bytes = 128u * L.tab_stride + (sampled ? 128u * (uint32_t)G * 4u : 0u);
     L.padded = (T > 0 && T % 2 == 0 && (T / 2) % 2 == 0) ? 1u : 0u;
     L.half_T = (uint32_t)(T / 2);
     L.magic = L.padded ? (uint32_t)((0x100000000ull + L.half_T - 1) / L.half_T) : 0u;
@@ -333,70 +331,86 @@ __device__ __forceinline__ void load_v_tile(const uint16_t* vbh, int t0, int nt,
 constexpr uint32_t kPhiloxM0 = 0xD2511F53u, kPhiloxM1 = 0xCD9E8D57u;
 constexpr uint32_t kPhiloxW0 = 0x9E3779B9u, kPhiloxW1 = 0xBB67AE85u;
 
+// a ^ b ^ c in one v_bitop3_b32 (truth table 0x96: the parity of the three
+// input bits, the same for any operand order).
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+    return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
+}
+
+// The first round is written with plain xors so that the compiler can fold
+// its wave-uniform counter words (channel group, head) into scalar code.
 __device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
 #pragma unroll
     for (int rnd = 0; rnd < 10; ++rnd) {
         if (rnd) { k0 += kPhiloxW0; k1 += kPhiloxW1; }
         const uint64_t p0 = (uint64_t)kPhiloxM0 * c.x;
         const uint64_t p1 = (uint64_t)kPhiloxM1 * c.z;
-        c = make_uint4((uint32_t)(p1 >> 32) ^ c.y ^ k0, (uint32_t)p1, (uint32_t)(p0 >> 32) ^ c.w ^ k1, (uint32_t)p0);
+        const uint32_t h1 = (uint32_t)(p1 >> 32), h0 = (uint32_t)(p0 >> 32);
+        c = rnd == 0 ? make_uint4(h1 ^ c.y ^ k0, (uint32_t)p1, h0 ^ c.w ^ k1, (uint32_t)p0)
+                     : make_uint4(xor3(h1, c.y, k0), (uint32_t)p1, xor3(h0, c.w, k1), (uint32_t)p0);
     }
     return c;
 }
 
-// u = (x + 1/2) 2^-32 in (0, 1], rounded to fp32.
+// u = (x + 1/2) 2^-32 in [2^-33, 1], rounded to fp32 (never denormal).
 __device__ __forceinline__ float unit_of(uint32_t x) { return fmaf((float)x, 0x1p-32f, 0x1p-33f); }
 
-// Zero-mean noise of one Philox block for channels 4 jg + 0..3. Gaussian:
-// Box-Muller on (u0, u1) and (u2, u3), z_even = R cos(2 pi u_odd),
-// z_odd = R sin(2 pi u_odd), R = sqrt(-2 ln u_even). Exponential: -ln u has
-// mean 1, so the noise is -ln u - 1 (the sample is mu times -ln u).
-__device__ __forceinline__ void sample_noise4(uint4 x, bool gauss, float (&n)[4]) {
+// Zero-mean noise of one Philox block for channels 4 jg + 0..3, from the
+// hardware log2, square root, sine and cosine (the last two take their
+// argument in turns, so 2 pi u needs no multiply); u is a normal number, so
+// no denormal rescaling is needed. Gaussian: Box-Muller on (u0, u1) and
+// (u2, u3), z_even = R cos(2 pi u_odd), z_odd = R sin(2 pi u_odd),
+// R = sqrt(-2 ln u_even). Exponential: -ln u has mean 1, so the noise is
+// -ln u - 1 (the sample is mu times -ln u).
+template <bool GAUSS>
+__device__ __forceinline__ void sample_noise4(uint4 x, float (&n)[4]) {
+    constexpr float kLn2 = 0.693147180559945309f;
     const float u[4] = {unit_of(x.x), unit_of(x.y), unit_of(x.z), unit_of(x.w)};
-    if (gauss) {
+    if (GAUSS) {
 #pragma unroll
         for (int e = 0; e < 4; e += 2) {
-            const float R = sqrtf(-2.0f * logf(u[e]));
-            float sn, cs;
-            sincospif(2.0f * u[e + 1], &sn, &cs);
-            n[e] = R * cs;
-            n[e + 1] = R * sn;
+            const float R = __builtin_amdgcn_sqrtf(-2.0f * kLn2 * __builtin_amdgcn_logf(u[e]));
+            n[e] = R * __builtin_amdgcn_cosf(u[e + 1]);
+            n[e + 1] = R * __builtin_amdgcn_sinf(u[e + 1]);
         }
     } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) n[e] = -logf(u[e]) - 1.0f;
+        for (int e = 0; e < 4; ++e) n[e] = fmaf(-__builtin_amdgcn_logf(u[e]), kLn2, -1.0f);
     }
 }
 
 // Sample term of the scores of one tile: with the table's r_j = mu / a_j
 // (the sample mean back-solved) already in the scores, every pruned channel
-// j of the lane's token adds q'_g,j ns_j n_tj. The counter of token t and
-// channel group jg is (t, jg, b * N_kv + h, 0). Groups that every lane of the
-// wave keeps are skipped.
-template <int G>
-__device__ __forceinline__ void sampled_scores(const DecodeArgs& a, const unsigned char* tab, uint4 mw, int bh,
+// j of the lane's token adds (q'_g,j ns_j) n_tj, ns_j the noise scale of the
+// back-solved sample. The counter of token t and channel group jg is
+// (t, jg, b * N_kv + h, 0). The four q' ns rows of a group are read (LDS
+// broadcast) before its Philox block, so they arrive during it; a kept
+// channel's noise is cleared with the sign-extended mask bit; groups that
+// every lane of the wave keeps are skipped.
+template <int G, bool GAUSS>
+__device__ __forceinline__ void sampled_scores(const DecodeArgs& a, const float* qn, uint4 mw, int bh,
                                                int t0, int nt, int L, float (&s)[G]) {
-    const bool gauss = a.sampled == 4;
     const uint32_t tok = (uint32_t)(t0 + L);
     const bool live = L < nt;
     const uint32_t words[4] = {mw.x, mw.y, mw.z, mw.w};
-    const TabEntry<G>* te = reinterpret_cast<const TabEntry<G>*>(tab);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
         const uint32_t pr = live ? ~words[w] : 0u;
         for (int jj = 0; jj < 8; ++jj) {
-            const uint32_t nib = (pr >> (4 * jj)) & 15u;
-            if (ballot(nib != 0) == 0) continue;
+            if (ballot(((pr >> (4 * jj)) & 15u) != 0) == 0) continue;
             const int jg = 8 * w + jj;
+            QRow<G> row[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) row[i] = reinterpret_cast<const QRow<G>*>(qn)[4 * jg + i];
             const uint4 x = philox4x32_10(make_uint4(tok, (uint32_t)jg, (uint32_t)bh, 0u), a.seed_lo, a.seed_hi);
             float n[4];
-            sample_noise4(x, gauss, n);
+            sample_noise4<GAUSS>(x, n);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const TabEntry<G>& e = te[4 * jg + i];
-                const float xn = ((nib >> i) & 1u) ? n[i] * e.ns : 0.0f;
+                const uint32_t keep_bits = (uint32_t)__builtin_amdgcn_sbfe((int)pr, 4 * jj + i, 1);
+                const float xn = __uint_as_float(__float_as_uint(n[i]) & keep_bits);
 #pragma unroll
-                for (int g = 0; g < G; ++g) s[g] = fmaf(e.q[g], xn, s[g]);
+                for (int g = 0; g < G; ++g) s[g] = fmaf(row[i].v[g], xn, s[g]);
             }
         }
     }
@@ -494,9 +508,14 @@ __device__ void finish_block(const DecodeArgs& a, float (&m_run)[G], float (&l_r
     if (tid == 0) __hip_atomic_store(a.counters + bh, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int G, bool SAMPLED>
-__global__ void __launch_bounds__(DECODE_THREADS)
+// SMODE: 0 for the recovery vector r, else the sampled F (4 Gaussian,
+// 5 Exponential). Sampled F, G <= 4: two waves per SIMD (it fits without
+// spills), so the Philox and sample arithmetic of one wave covers the
+// latency of the other.
+template <int G, int SMODE>
+__global__ void __launch_bounds__(DECODE_THREADS) __attribute__((amdgpu_waves_per_eu(SMODE && G <= 4 ? 2 : 1)))
 decode_kernel(const DecodeArgs a) {
+    constexpr bool SAMPLED = SMODE != 0;
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr int NW = DECODE_THREADS / 64;
     const DecodeLayout& lay = a.lay;
@@ -514,25 +533,25 @@ decode_kernel(const DecodeArgs a) {
     constexpr uint32_t TAB = (uint32_t)sizeof(TabEntry<G>);
     const bool even_T = (T % 2) == 0;
 
-    // ---- table of q' (q * scale * log2 e) and r per channel
+    // ---- table of q' (q * scale * log2 e) and r per channel. Sampled F: r
+    // holds (mu, sigma); a pruned key is w / a_j, a_j = sqrt(A_j), with the
+    // sample w = mu + ns n: the table takes r_j = mu / a_j and, in a second
+    // table, q'_g ns / a_j (ns = sigma for the Gaussian, mu for the Exponential)
+    float* qn = reinterpret_cast<float*>(tab + 128 * TAB);                 // [128][G], sampled F only
     for (int i = tid; i < 128 * G; i += DECODE_THREADS) {
         const int g = i >> 7, j = i & 127;
         const uint16_t qb = a.q[((size_t)b * a.N_q + (size_t)h * G + g) * 128 + j];
-        reinterpret_cast<TabEntry<G>*>(tab)[j].q[g] = bf16_to_f32(qb) * a.qscale;
-    }
-    if (tid < 128) {
-        TabEntry<G>& e = reinterpret_cast<TabEntry<G>*>(tab)[tid];
+        const float qv = bf16_to_f32(qb) * a.qscale;
+        reinterpret_cast<TabEntry<G>*>(tab)[j].q[g] = qv;
         if (SAMPLED) {
-            // r holds (mu, sigma); a pruned key is (mu + noise) / a_j, a_j = sqrt(A_j)
-            const float mu = a.r[(size_t)bh * 128], sigma = a.r[(size_t)bh * 128 + 1];
-            const float Aj = a.A[(size_t)bh * 128 + tid];
+            const float Aj = a.A[(size_t)bh * 128 + j];
             const float inv_a = Aj > 0.0f ? 1.0f / sqrtf(Aj) : 0.0f;
-            e.r = mu * inv_a;
-            e.ns = (a.sampled == 4 ? sigma : mu) * inv_a;
-        } else {
-            e.r = a.r[(size_t)bh * 128 + tid];
+            const float ns = a.r[(size_t)bh * 128 + (SMODE == 4 ? 1 : 0)];
+            qn[j * G + g] = qv * (ns * inv_a);
+            if (g == 0) reinterpret_cast<TabEntry<G>*>(tab)[j].r = a.r[(size_t)bh * 128] * inv_a;
         }
     }
+    if (!SAMPLED && tid < 128) reinterpret_cast<TabEntry<G>*>(tab)[tid].r = a.r[(size_t)bh * 128 + tid];
 
     uint16_t* lst = reinterpret_cast<uint16_t*>(wbase + (size_t)wave * lay.wave_bytes);     // [T][64]
     unsigned char* stage = wbase + (size_t)wave * lay.wave_bytes + lay.list_bytes;
@@ -662,7 +681,7 @@ decode_kernel(const DecodeArgs a) {
                 for (int g = 0; g < G; ++g) s[g] = fmaf(te.q[g], e, s[g]);
             }
         }
-        if (SAMPLED) sampled_scores<G>(a, tab, mw, bh, t0, nt, L, s);
+        if (SAMPLED) sampled_scores<G, SMODE == 4>(a, qn, mw, bh, t0, nt, L, s);
 #pragma unroll
         for (int g = 0; g < G; ++g) s[g] = (L < nt) ? s[g] + cq[g] : -INFINITY;
 
@@ -1037,15 +1056,15 @@ uint32_t decode_fast_lds_bytes(int G, int T, int nsplit) {
 bool decode_fast_supported(int G, int T) { return G == 4 && (T == 26 || T == 38 || T == 64); }
 
 
-template <bool SAMPLED>
+template <int SMODE>
 hipError_t launch_generic(const DecodeArgs& a, int G, dim3 grid, dim3 block, hipStream_t stream) {
     const size_t lds = a.lay.lds_bytes;
     const void* fn = nullptr;
     switch (G) {
-        case 1: fn = reinterpret_cast<const void*>(&decode_kernel<1, SAMPLED>); break;
-        case 2: fn = reinterpret_cast<const void*>(&decode_kernel<2, SAMPLED>); break;
-        case 4: fn = reinterpret_cast<const void*>(&decode_kernel<4, SAMPLED>); break;
-        case 8: fn = reinterpret_cast<const void*>(&decode_kernel<8, SAMPLED>); break;
+        case 1: fn = reinterpret_cast<const void*>(&decode_kernel<1, SMODE>); break;
+        case 2: fn = reinterpret_cast<const void*>(&decode_kernel<2, SMODE>); break;
+        case 4: fn = reinterpret_cast<const void*>(&decode_kernel<4, SMODE>); break;
+        case 8: fn = reinterpret_cast<const void*>(&decode_kernel<8, SMODE>); break;
         default: return hipErrorInvalidValue;
     }
     if (lds > 65536) {
@@ -1054,10 +1073,10 @@ hipError_t launch_generic(const DecodeArgs& a, int G, dim3 grid, dim3 block, hip
         if (e != hipSuccess) return e;
     }
     switch (G) {
-        case 1: hipLaunchKernelGGL((decode_kernel<1, SAMPLED>), grid, block, lds, stream, a); break;
-        case 2: hipLaunchKernelGGL((decode_kernel<2, SAMPLED>), grid, block, lds, stream, a); break;
-        case 4: hipLaunchKernelGGL((decode_kernel<4, SAMPLED>), grid, block, lds, stream, a); break;
-        default: hipLaunchKernelGGL((decode_kernel<8, SAMPLED>), grid, block, lds, stream, a); break;
+        case 1: hipLaunchKernelGGL((decode_kernel<1, SMODE>), grid, block, lds, stream, a); break;
+        case 2: hipLaunchKernelGGL((decode_kernel<2, SMODE>), grid, block, lds, stream, a); break;
+        case 4: hipLaunchKernelGGL((decode_kernel<4, SMODE>), grid, block, lds, stream, a); break;
+        default: hipLaunchKernelGGL((decode_kernel<8, SMODE>), grid, block, lds, stream, a); break;
     }
     return hipGetLastError();
 }
@@ -1077,7 +1096,12 @@ hipError_t launch_decode(const DecodeArgs& a, int G, int BH, hipStream_t stream)
         }
         return hipGetLastError();
     }
-    return a.sampled ? launch_generic<true>(a, G, grid, block, stream) : launch_generic<false>(a, G, grid, block, stream);
+    switch (a.sampled) {
+        case 0: return launch_generic<0>(a, G, grid, block, stream);
+        case 4: return launch_generic<4>(a, G, grid, block, stream);
+        case 5: return launch_generic<5>(a, G, grid, block, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 __global__ void fill_u32_kernel(uint32_t* p, uint32_t value, size_t n) {

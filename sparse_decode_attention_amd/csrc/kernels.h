@@ -13,6 +13,7 @@
 #define DECODE_FAST_LDS_BYTES (2576 + (DECODE_FAST_THREADS / 64) * (8704 + 1024))
 #define DECODE_TILE 64
 #define DECODE_MAX_SPLITS 256
+#define DECODE_SAMPLED_BLOCKS 512    // blocks the sampled F's decode aims for when splits = 0
 // window eviction: at most 128 stacked window rows (G * W), tokens per block
 #define EVICT_MAX_ROWS 128
 #define EVICT_WAVE_ROWS 32
@@ -46,7 +47,7 @@ struct DecodeLayout {
     uint32_t stage_bytes;  // per wave: staged packed rows of one 64-token tile
     uint32_t ptab_bytes;   // per wave: p of the tile, [64][G] fp32
     uint32_t wave_bytes;   // list + stage + ptab
-    uint32_t tab_bytes;    // 128 * tab_stride
+    uint32_t tab_bytes;    // 128 * tab_stride, plus the [128][G] fp32 q' ns table of the sampled F
     uint32_t lds_bytes;    // whole block (dynamic LDS)
 };
 
@@ -90,6 +91,6 @@ hipError_t launch_read_stream(const void* src, size_t bytes, uint32_t* sink, int
 
 // Launch the decode kernel for group size G; returns a hipError_t.
 hipError_t launch_decode(const DecodeArgs& a, int G, int BH, hipStream_t stream);
-DecodeLayout decode_layout(int G, int T, int nsplit);
+DecodeLayout decode_layout(int G, int T, int nsplit, bool sampled);
 
 }  // namespace spark

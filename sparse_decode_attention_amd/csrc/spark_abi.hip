@@ -51,18 +51,20 @@ PrefillWs prefill_layout(void* ws, int B, int S, int N_kv) {
     return w;
 }
 
-// About 256 blocks in all (one 8-wave block per CU for the fast kernel).
-int auto_splits(int BH, int S) {
+// About `blocks` blocks in all: 256 (one 8-wave block per CU) for the fast
+// kernel; the sampled F, which is bound by its arithmetic, asks for more so
+// that each SIMD holds two waves.
+int auto_splits(int BH, int S, int blocks) {
     const int max_splits = (S + DECODE_TILE - 1) / DECODE_TILE;
-    int want = (256 + BH - 1) / BH;
+    int want = (blocks + BH - 1) / BH;
     if (want < 1) want = 1;
     if (want > max_splits) want = max_splits;
     return want;
 }
 
 // decode: the number of splits actually launched and the tokens per split
-void decode_plan(int BH, int S, int splits, int* nsplit, int* chunk) {
-    int n = splits > 0 ? splits : auto_splits(BH, S);
+void decode_plan(int BH, int S, int splits, int* nsplit, int* chunk, int blocks = 256) {
+    int n = splits > 0 ? splits : auto_splits(BH, S, blocks);
     const int max_splits = (S + DECODE_TILE - 1) / DECODE_TILE;
     if (n > max_splits) n = max_splits;
     if (n > DECODE_MAX_SPLITS) n = DECODE_MAX_SPLITS;
@@ -105,7 +107,8 @@ size_t spark_prefill_workspace_bytes(int B, int S, int N_kv, int D) {
 size_t spark_decode_workspace_bytes(int B, int S, int N_q, int N_kv, int D, int splits) {
     if (B < 1 || S < 1 || N_kv < 1 || N_q < 1 || D < 1 || splits < 0 || N_q % N_kv) return 0;
     int nsplit, chunk;
-    decode_plan(B * N_kv, S, splits, &nsplit, &chunk);
+    // sized for the larger of the two entry points' split plans
+    decode_plan(B * N_kv, S, splits, &nsplit, &chunk, DECODE_SAMPLED_BLOCKS);
     return decode_ws_bytes(B * N_kv, N_q / N_kv, nsplit);
 }
 
@@ -189,7 +192,7 @@ int decode_call(const void* q, const void* k_packed, const uint32_t* mask, const
         return SPARK_EALIGN;
     const int G = N_q / N_kv;
     int nsplit, chunk;
-    decode_plan(BH, S, splits, &nsplit, &chunk);
+    decode_plan(BH, S, splits, &nsplit, &chunk, sampled ? DECODE_SAMPLED_BLOCKS : 256);
     if (ws_bytes < decode_ws_bytes(BH, G, nsplit)) return SPARK_ENOSPACE;
 
     char* base = static_cast<char*>(ws);
@@ -217,7 +220,7 @@ int decode_call(const void* q, const void* k_packed, const uint32_t* mask, const
     a.sampled = sampled;
     a.seed_lo = (uint32_t)seed;
     a.seed_hi = (uint32_t)(seed >> 32);
-    a.lay = decode_layout(G, T, nsplit);
+    a.lay = decode_layout(G, T, nsplit, sampled != 0);
     return hip_status(launch_decode(a, G, BH, static_cast<hipStream_t>(stream)));
 }
 
