@@ -66,6 +66,23 @@ def read_traffic(workload: str):
         return None
 
 
+# 32-bit VALU lane operations per second: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
+VALU_PEAK_GOPS = 256 * 64 * 2.4
+
+
+def sampled_alu_ops_per_token(G, T, rec):
+    """Algorithmic 32-bit VALU operations per (token, KV head) of the sampled
+    decode: per 4-channel group a Philox4x32-10 block (10 rounds of two wide
+    multiplies and two three-way xors), four uniforms (convert, scale), the
+    transform (Exponential: log, fma each; Gaussian: two of log, scale, sqrt,
+    sin, cos, two products), the kept-channel masks and 4 G FMAs; then the
+    fixed-r part: G T FMAs and T subtractions of the kept channels and G 128
+    FMAs of P.V on the VALU."""
+    transform = 8 if rec == "exponential" else 14
+    per_group = 40 + 8 + transform + 4 + 4 * G
+    return 32 * per_group + G * T + T + G * 128
+
+
 def effective_decode_bytes(w, T):
     return w.B * w.n_kv * w.S * (2 * T + 16 + 2 * w.D)
 
@@ -508,10 +525,15 @@ def main():
         for rec in ("gaussian", "exponential"):
             print(f"bench: sampled F ({rec}) on {w.name}", file=sys.stderr, flush=True)
             lg = run_leg(w, min(args.steps, 5), min(args.warmup, 2), x=main_leg["x"], recovery=rec)
+            alu_ops = w.B * w.n_kv * w.S * sampled_alu_ops_per_token(w.G, T, rec)
+            alu_gops = alu_ops / (lg["decode_us_per_launch"] * 1e-6) / 1e9
             line["sampled_f"][rec] = {
                 "workload": w.name, "kernel": f"decode_kernel<{w.G}, {ops.RECOVERY[rec]}>",
                 "decode_us_per_launch": round(lg["decode_us_per_launch"], 3),
                 "GBps": round(lg["decode_GBps"], 2),
+                "roofline": {"bound": "alu", "achieved": round(alu_gops, 1), "peak": VALU_PEAK_GOPS, "unit": "Gop/s",
+                             "frac": round(alu_gops / VALU_PEAK_GOPS, 4), "traffic": None,
+                             "ops_per_token_head": sampled_alu_ops_per_token(w.G, T, rec)},
                 "x_fixed_r_time": round(lg["decode_us_per_launch"] / main_leg["decode_us_per_launch"], 3),
                 "prefill_us": round(lg["prefill_us"], 2), "seed": hex(SAMPLE_SEED)}
             del lg
