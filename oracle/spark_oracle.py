@@ -33,6 +33,8 @@ Readings of points the pages leave open (each is listed in the design doc):
     walkthrough's Degenerate F (section 3.3, F table) is "score_mean_pruned".
   * Decode: one new query per head attends to all S cached tokens (no causal
     mask), scale 1/sqrt(D), recovery only in the scores, V dense.
+  * V-channel pruning (section 4.4, "norm-based"): per-token top-T_v of
+    |v_tj|, ties to the lower channel, retained-mean recovery of V.
   * Sampled F ("gaussian", "exponential", the other rows of the section 3.3 F
     table): mu and sigma are the mean and population standard deviation of
     the pruned saliency a_j |k_tj| per (batch, KV head); each pruned (t, j)
@@ -356,6 +358,40 @@ def decode_attn_sampled(q, packed, mask, v, A, r, mode: str, seed: int, scale: f
     D = mask.shape[-1]
     scale = 1.0 / math.sqrt(D) if scale is None or scale <= 0 else float(scale)
     return _attend(q, expand_keys_sampled(packed, mask, A, r, mode, seed), v, scale)
+
+
+# ---------------------------------------------------------------- V-channel pruning
+#
+# Walkthrough section 4.4 prunes the V cache too, with a norm-based heuristic
+# that the page does not spell out. Reading taken here: per token, keep the
+# T_v channels of largest |v_tj| (the norm of the single entry), ties to the
+# lower channel, T_v = num_kept(D, lambda_v); a pruned entry is recovered by
+# the channel's mean over the tokens that retain it (the retained-mean F of
+# the keys), 0 if no token does.
+
+def value_keys(v: np.ndarray) -> np.ndarray:
+    """key = v^2 in fp32 (exact for bf16 v): ranks channels by |v_tj|."""
+    v = _f32(v)
+    return v * v
+
+
+def prune_v(v: np.ndarray, lam_v: float) -> dict:
+    """V-channel pruning of one cache: {"T", "mask", "words", "packed", "r",
+    "cnt"} with r the retained-mean recovery of the pruned entries."""
+    D = v.shape[-1]
+    T = num_kept(D, lam_v)
+    mask = select_top_t(value_keys(v), T)
+    r, cnt = stats(v, mask, None, F_MEAN_RETAINED)
+    return {"T": T, "mask": mask, "words": mask_words(mask), "packed": pack_kept(v, mask), "r": r, "cnt": cnt}
+
+
+def decode_attn_kv(q, k_packed, k_mask, r, v_packed, v_mask, rv, scale: float | None = None) -> np.ndarray:
+    """Decode over a cache with both K and V channels pruned: K_hat as in
+    decode_attn, V_hat = v_mask ? stored value : rv_j, then softmax attention
+    (walkthrough sections 3.3 and 4.4). Returns out [B][N_q][D] in float64."""
+    D = k_mask.shape[-1]
+    scale = 1.0 / math.sqrt(D) if scale is None or scale <= 0 else float(scale)
+    return _attend(q, expand_keys(k_packed, k_mask, r), expand_keys(v_packed, v_mask, rv), scale)
 
 
 def window_scores(q_win: np.ndarray, k: np.ndarray) -> np.ndarray:

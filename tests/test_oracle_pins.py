@@ -503,3 +503,94 @@ def test_window_scores_keep_the_aligned_token():
     assert 17 in idx[0, 0].tolist()
     assert idx[0, 0].tolist() == sorted(idx[0, 0].tolist())
     np.testing.assert_array_equal(kk[0, 0], k[0, 0, idx[0, 0]])
+
+
+# ------------------------------------------------------------------ V-channel pruning
+
+def test_v_pruned_hand_case():
+    c = json.load(open(os.path.join(GOLDEN, "decode_v_pruned_hand_case.json")))
+    D = c["D"]
+    v = np.asarray(c["v"])[None, None]
+    pv = oracle.prune_v(v, c["lambda_v"])
+    assert pv["T"] == 2
+    np.testing.assert_array_equal(pv["words"][0, 0, :, 0], c["v_mask_words"])
+    np.testing.assert_array_equal(pv["packed"][0, 0], c["v_packed"])
+    np.testing.assert_array_equal(pv["r"][0, 0], c["r_v"])
+    k = np.asarray(c["k"])[None, None]
+    k_mask = np.ones(k.shape, bool)
+    out = oracle.decode_attn_kv(np.asarray(c["q"])[None, None], k.reshape(1, 1, 3, D), k_mask, np.zeros((1, 1, D)),
+                                pv["packed"], pv["mask"], pv["r"])
+    np.testing.assert_allclose(out[0, 0], c["out"], rtol=1e-12, atol=1e-12)
+
+
+def test_v_selection_matches_brute_force_with_ties():
+    """Few-valued entries (exact ties): the kept set is the first subset, in
+    lexicographic order, of largest sum |v|."""
+    rng = np.random.default_rng(31)
+    D, S = 8, 150
+    n_tied = 0
+    v = rng.choice([0.0, 1.0, -1.0, 2.0, -2.0, 3.0, 0.5, -0.5], size=(1, 1, S, D))
+    for T in range(D + 1):
+        got = oracle.prune_v(v, _lam_for(T, D))
+        assert got["T"] == T
+        for t in range(S):
+            w = [Fraction(abs(float(v[0, 0, t, j]))) for j in range(D)]
+            assert tuple(np.flatnonzero(got["mask"][0, 0, t]).tolist()) == _brute_reduced(w, T), (T, t)
+            n_tied += len(set(w)) < D
+        np.testing.assert_array_equal(got["packed"][0, 0], v[0, 0][got["mask"][0, 0]].reshape(S, T))
+    assert n_tied > 500
+
+
+def test_v_retained_mean_brute_force():
+    rng = np.random.default_rng(32)
+    v = rng.standard_normal((2, 3, 40, 16)).astype(np.float32)
+    pv = oracle.prune_v(v, 0.7)
+    for b in range(2):
+        for h in range(3):
+            for j in range(16):
+                vals = [float(v[b, h, t, j]) for t in range(40) if pv["mask"][b, h, t, j]]
+                want = sum(vals) / len(vals) if vals else 0.0
+                assert abs(float(pv["r"][b, h, j]) - want) <= 1e-6 * max(1.0, abs(want))
+                assert pv["cnt"][b, h, j] == len(vals)
+
+
+def test_v_lambda0_is_the_dense_v_decode():
+    w = WORKLOADS["tiny_s1k"].with_(S=300, n_q=8, n_kv=2)
+    x = gen.numpy_layer(w, seed=33, steps=1)
+    f = {n: gen.bf16_bits_to_f32(a) for n, a in x.items()}
+    pk = oracle.prune(f["q_win"], f["k"], w.n_kv, 0.5)
+    r, _ = oracle.stats(f["k"], pk["mask"], pk["A"])
+    pv = oracle.prune_v(f["v"], 0.0)
+    assert pv["mask"].all()
+    got = oracle.decode_attn_kv(f["q_dec"][0], pk["packed"], pk["mask"], r, pv["packed"], pv["mask"], pv["r"])
+    np.testing.assert_array_equal(got, oracle.decode_attn(f["q_dec"][0], pk["packed"], pk["mask"], f["v"], r))
+
+
+def test_v_lambda1_gives_zero_output():
+    """T_v = 0: no entry is retained, every recovery value is 0, so is the output."""
+    rng = np.random.default_rng(34)
+    v = rng.standard_normal((1, 2, 50, 8))
+    pv = oracle.prune_v(v, 1.0)
+    assert pv["T"] == 0 and not pv["mask"].any() and (pv["r"] == 0).all()
+    q = rng.standard_normal((1, 4, 8))
+    k = rng.standard_normal((1, 2, 50, 8))
+    out = oracle.decode_attn_kv(q, k, np.ones(k.shape, bool), np.zeros((1, 2, 8)), pv["packed"], pv["mask"], pv["r"])
+    assert (out == 0).all()
+
+
+def test_v_constant_channels_closed_form():
+    """v_tj = c_j with distinct |c_j|: every token keeps the same T_v channels
+    (largest |c|), which recover exactly; the others are never retained and
+    recover to 0. So out_j = c_j on the kept channels and 0 elsewhere, for any
+    attention weights."""
+    rng = np.random.default_rng(35)
+    D, S, T = 16, 64, 6
+    c = rng.permutation(np.arange(1, D + 1)) * rng.choice([-1.0, 1.0], size=D) * 0.25
+    v = np.broadcast_to(c, (1, 1, S, D)).copy()
+    pv = oracle.prune_v(v, _lam_for(T, D))
+    top = set(np.argsort(-np.abs(c))[:T].tolist())
+    want = np.array([c[j] if j in top else 0.0 for j in range(D)])
+    q = rng.standard_normal((1, 3, D))
+    k = rng.standard_normal((1, 1, S, D))
+    out = oracle.decode_attn_kv(q, k, np.ones(k.shape, bool), np.zeros((1, 1, D)), pv["packed"], pv["mask"], pv["r"])
+    np.testing.assert_allclose(out[0], np.broadcast_to(want, (3, D)), rtol=1e-12, atol=1e-12)
