@@ -75,8 +75,9 @@ int spark_num_kept(int D, float lambda);
 /* Human-readable name of a spark_status. Never NULL. */
 const char* spark_strerror(int status);
 
-/* Workspace sizes in bytes (0 on invalid sizes). The decode size serves both
- * spark_decode_attn and spark_decode_attn_sampled. */
+/* Workspace sizes in bytes (0 on invalid sizes). The prefill size serves
+ * spark_prefill_prune, spark_prefill_prune_v and spark_stats; the decode size
+ * serves every decode entry point. */
 size_t spark_prefill_workspace_bytes(int B, int S, int N_kv, int D);
 size_t spark_decode_workspace_bytes(int B, int S, int N_q, int N_kv, int D, int splits);
 
@@ -169,6 +170,43 @@ int spark_decode_attn_sampled(const void* q, const void* k_packed, const uint32_
                               const float* chan_energy, const float* r, int recovery, uint64_t seed,
                               int B, int S, int N_q, int N_kv, int D, float lambda, float scale, int splits,
                               float* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * V-channel pruning (walkthrough section 4.4: V channels are pruned together
+ * with K by a norm-based heuristic, which the page does not spell out; read
+ * here as per-token top-T_v of |v_tj|). Same selection, packing and retained-
+ * mean statistics as the keys' with every channel energy equal to 1.
+ *  v            bf16 [B][N_kv][S][D]
+ *  lambda_v     pruned fraction of V channels; T_v = spark_num_kept(D, lambda_v)
+ * Outputs (caller-allocated, fully overwritten):
+ *  v_packed     bf16 [B][N_kv][S][T_v]  retained values, ascending channel order (NULL only if T_v = 0)
+ *  v_mask       uint32 [B][N_kv][S][D/32]  exactly T_v bits per token; order |v| descending
+ *               (key fl32(v^2)), ties to the lower channel
+ *  r_v          fp32 [B][N_kv][D]  mean of the retained v_tj over the tokens keeping
+ *               channel j (0 if none): the value a pruned V entry takes
+ *  cnt          int32 [B][N_kv][D]  tokens keeping channel j (may be NULL)
+ * Workspace: spark_prefill_workspace_bytes(B, S, N_kv, D).
+ */
+int spark_prefill_prune_v(const void* v, int B, int S, int N_kv, int D, float lambda_v, void* v_packed,
+                          uint32_t* v_mask, float* r_v, int32_t* cnt, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * One decode step over a cache whose K and V channels are both pruned
+ * (walkthrough sections 3.3 and 4.4): K_hat as in spark_decode_attn and
+ * V_hat = v_mask ? stored value : r_v[j], then softmax attention. V is read
+ * from the packed store only (2 T_v + 16 bytes per token and KV head instead
+ * of 2 D).
+ *  k_packed, k_mask, r        the K cache, as for spark_decode_attn
+ *  v_packed, v_mask, r_v      the V cache, as written by spark_prefill_prune_v
+ *  lambda, lambda_v           pruned fractions of K and V
+ * Other arguments, the workspace and the return codes as for
+ * spark_decode_attn (SPARK_EINVAL also for a NULL v_mask or r_v, or a NULL
+ * v_packed with T_v > 0).
+ */
+int spark_decode_attn_kv(const void* q, const void* k_packed, const uint32_t* k_mask, const float* r,
+                         const void* v_packed, const uint32_t* v_mask, const float* r_v, int B, int S, int N_q,
+                         int N_kv, int D, float lambda, float lambda_v, float scale, int splits, float* out, void* ws,
+                         size_t ws_bytes, void* stream);
 
 /* Zero the decode completion counters of a workspace (a fill kernel on
  * `stream`; safe to record in a HIP graph). */

@@ -91,7 +91,7 @@ __host__ __device__ inline uint32_t finish_scratch_bytes(int G, int NT, int nspl
     return finish_own_offset(G, NT, nsplit) + (2u * G + (uint32_t)G * 128u) * 4u;
 }
 
-DecodeLayout decode_layout(int G, int T, int nsplit, bool sampled) {
+DecodeLayout decode_layout(int G, int T, int nsplit, bool sampled, int Tv) {
     DecodeLayout L{};
     L.tab_stride = (uint32_t)tab_stride_for(G);
     // sampled F: the q'_g ns_j table [128][G] follows the q'/r table
@@ -110,7 +110,15 @@ DecodeLayout decode_layout(int G, int T, int nsplit, bool sampled) {
     L.list_bytes = (uint32_t)T * DECODE_TILE * 2u;
     L.list_bytes = (L.list_bytes + 15u) & ~15u;
     L.ptab_bytes = (uint32_t)DECODE_TILE * G * 4u;
-    L.wave_bytes = L.list_bytes + L.stage_bytes + L.ptab_bytes;
+    // packed V (Tv >= 0): the tile's rows unpadded (up to 7 elements of 16-byte
+    // misalignment) plus 256 bytes of slack for the expansion's reads, then
+    // the 64 token masks. They are staged after the scores, over the key
+    // list and staged keys, so the wave's region is the larger of the two.
+    L.vstage_bytes = Tv >= 0 ? ((((uint32_t)DECODE_TILE * (uint32_t)Tv + 8u) * 2u + 15u) & ~15u) + 256u : 0u;
+    L.vmask_bytes = Tv >= 0 ? (uint32_t)DECODE_TILE * 16u : 0u;
+    L.kv_bytes = L.list_bytes + L.stage_bytes;
+    if (L.vstage_bytes + L.vmask_bytes > L.kv_bytes) L.kv_bytes = L.vstage_bytes + L.vmask_bytes;
+    L.wave_bytes = L.kv_bytes + L.ptab_bytes;
     const uint32_t waves = DECODE_THREADS / 64;
     uint32_t dyn = waves * L.wave_bytes;
     const uint32_t fin = finish_scratch_bytes(G, DECODE_THREADS, nsplit);
@@ -215,18 +223,29 @@ struct TileMeta {
     int nchunks;     // 16-byte chunks covering the tile
 };
 
-__device__ __forceinline__ uint4 load_chunk(const DecodeArgs& a, size_t ce) {
-    if (ce + 8 <= a.packed_elems) return *reinterpret_cast<const uint4*>(a.packed + ce);
+// One packed store: the K cache (packed keys and their masks) or, with V
+// channels pruned, the V cache.
+struct PackedSrc {
+    const uint16_t* packed;   // [B*N_kv][S][T]
+    const uint32_t* mask;     // [B*N_kv][S][4]
+    size_t elems;             // B*N_kv*S*T
+    int T;
+};
+__device__ __forceinline__ PackedSrc k_src(const DecodeArgs& a) { return {a.packed, a.mask, a.packed_elems, a.T}; }
+__device__ __forceinline__ PackedSrc v_src(const DecodeArgs& a) { return {a.v_packed, a.v_mask, a.v_packed_elems, a.Tv}; }
+
+__device__ __forceinline__ uint4 load_chunk(const PackedSrc& p, size_t ce) {
+    if (ce + 8 <= p.elems) return *reinterpret_cast<const uint4*>(p.packed + ce);
     uint16_t t[8];
 #pragma unroll
-    for (int x = 0; x < 8; ++x) t[x] = (ce + x < a.packed_elems) ? a.packed[ce + x] : 0;
+    for (int x = 0; x < 8; ++x) t[x] = (ce + x < p.elems) ? p.packed[ce + x] : 0;
     return make_uint4(t[0] | ((uint32_t)t[1] << 16), t[2] | ((uint32_t)t[3] << 16),
                       t[4] | ((uint32_t)t[5] << 16), t[6] | ((uint32_t)t[7] << 16));
 }
 
-__device__ __forceinline__ void issue_meta(const DecodeArgs& a, int bh, int t0, int nt, int L, TileMeta& m) {
-    const int T = a.T;
-    const size_t e0 = ((size_t)bh * a.S + t0) * (size_t)T;
+__device__ __forceinline__ void issue_meta(const PackedSrc& p, int S, int bh, int t0, int nt, int L, TileMeta& m) {
+    const int T = p.T;
+    const size_t e0 = ((size_t)bh * S + t0) * (size_t)T;
     m.ea = e0 & ~(size_t)7;
     m.shift = (int)(e0 - m.ea);
     m.nchunks = T > 0 ? (int)((e0 + (size_t)nt * T - m.ea + 7) >> 3) : 0;
@@ -234,10 +253,10 @@ __device__ __forceinline__ void issue_meta(const DecodeArgs& a, int bh, int t0, 
     for (int u = 0; u < 8; ++u) {
         const int c = L + 64 * u;
         m.pk[u] = make_uint4(0, 0, 0, 0);
-        if (c < m.nchunks) m.pk[u] = load_chunk(a, m.ea + (size_t)c * 8);
+        if (c < m.nchunks) m.pk[u] = load_chunk(p, m.ea + (size_t)c * 8);
     }
     m.mw = make_uint4(0, 0, 0, 0);
-    if (L < nt) m.mw = *reinterpret_cast<const uint4*>(a.mask + ((size_t)bh * a.S + t0 + L) * 4);
+    if (L < nt) m.mw = *reinterpret_cast<const uint4*>(p.mask + ((size_t)bh * S + t0 + L) * 4);
 }
 
 // Write one 16-byte chunk c of the tile into the staged rows.
@@ -297,6 +316,43 @@ __device__ __forceinline__ void pv_tile(const uint4 (&vr)[16], const float* ptab
         for (int e = 0; e < 4; ++e) {
             vf[2 * e] = bf16_lo(w4[e]);
             vf[2 * e + 1] = bf16_hi(w4[e]);
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(p.v[g], vf[e], acc[g][e]);
+    }
+}
+
+// P.V of one tile over a packed V cache (V channels pruned): lane (tau, oct)
+// expands, for each of its rows 4i + tau, the 8 channels d in [8 oct, 8 oct + 8)
+// from the staged packed row. Those channels' retained values are contiguous
+// in the row (ascending channel order), starting at the number of kept
+// channels below 8 oct; a pruned channel takes its recovery value rv (fp32).
+// Every read stays inside the staged tile plus its slack: the rank is below
+// the number of set mask bits, at most 128.
+template <int G>
+__device__ __forceinline__ void pv_tile_vpacked(const uint16_t* vst, const uint4* vmask, int Tv, const float* ptab,
+                                                const float (&rvl)[8], float (&acc)[G][8], int tau, int oct) {
+    const int wsel = oct >> 2;
+    const uint32_t sh = 8u * (uint32_t)(oct & 3);
+#pragma unroll 4
+    for (int i = 0; i < 16; ++i) {
+        const int tok = 4 * i + tau;
+        const uint4 mw = vmask[tok];
+        const uint32_t word = wsel == 0 ? mw.x : wsel == 1 ? mw.y : wsel == 2 ? mw.z : mw.w;
+        uint32_t idx = (wsel > 0 ? __popc(mw.x) : 0u) + (wsel > 1 ? __popc(mw.y) : 0u) +
+                       (wsel > 2 ? __popc(mw.z) : 0u) + __popc(word & ((1u << sh) - 1u));
+        const uint32_t bits = (word >> sh) & 0xFFu;
+        const uint16_t* row = vst + tok * Tv;
+        const QRow<G> p = *reinterpret_cast<const QRow<G>*>(ptab + tok * G);
+        float vf[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const bool kept = (bits >> e) & 1u;
+            const float x = bf16_to_f32(row[idx]);
+            vf[e] = kept ? x : rvl[e];
+            idx += kept ? 1u : 0u;
         }
 #pragma unroll
         for (int g = 0; g < G; ++g)
@@ -512,7 +568,10 @@ __device__ void finish_block(const DecodeArgs& a, float (&m_run)[G], float (&l_r
 // 5 Exponential). Sampled F, G <= 4: two waves per SIMD (it fits without
 // spills), so the Philox and sample arithmetic of one wave covers the
 // latency of the other.
-template <int G, int SMODE>
+//
+// VP: the V cache is packed too (V channels pruned): its rows and masks are
+// loaded one tile ahead like the keys', staged in LDS, and expanded in P.V.
+template <int G, int SMODE, bool VP>
 __global__ void __launch_bounds__(DECODE_THREADS) __attribute__((amdgpu_waves_per_eu(SMODE && G <= 4 ? 2 : 1)))
 decode_kernel(const DecodeArgs a) {
     constexpr bool SAMPLED = SMODE != 0;
@@ -555,7 +614,10 @@ decode_kernel(const DecodeArgs a) {
 
     uint16_t* lst = reinterpret_cast<uint16_t*>(wbase + (size_t)wave * lay.wave_bytes);     // [T][64]
     unsigned char* stage = wbase + (size_t)wave * lay.wave_bytes + lay.list_bytes;
-    float* ptab = reinterpret_cast<float*>(stage + lay.stage_bytes);                      // [64][G]
+    float* ptab = reinterpret_cast<float*>(wbase + (size_t)wave * lay.wave_bytes + lay.kv_bytes);   // [64][G]
+    // VP: packed V rows and masks, over the list and staged keys (dead after the scores)
+    unsigned char* vstage = wbase + (size_t)wave * lay.wave_bytes;
+    uint4* vmask = reinterpret_cast<uint4*>(vstage + lay.vstage_bytes);                  // [64] V masks
     // every list entry holds a valid table offset from the start
     for (int rho = 0; rho < T; ++rho) lst[rho * 64 + L] = 0;
     __syncthreads();
@@ -584,12 +646,18 @@ decode_kernel(const DecodeArgs a) {
         for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
     }
 
-    const uint16_t* vbh = a.v + (size_t)bh * S * 128;
+    const uint16_t* vbh = VP ? nullptr : a.v + (size_t)bh * S * 128;
+    float rvl[8];          // VP: recovery values of this lane's 8 V channels
+    if (VP) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) rvl[e] = a.rv[(size_t)bh * 128 + oct * 8 + e];
+    }
 
-    TileMeta meta;
+    TileMeta meta, vmeta;
     if (wave < ntiles) {
         const int t0 = blk_begin + wave * DECODE_TILE;
-        issue_meta(a, bh, t0, min(DECODE_TILE, blk_end - t0), L, meta);
+        issue_meta(k_src(a), S, bh, t0, min(DECODE_TILE, blk_end - t0), L, meta);
+        if (VP) issue_meta(v_src(a), S, bh, t0, min(DECODE_TILE, blk_end - t0), L, vmeta);
     }
 
     for (int tile = wave; tile < ntiles; tile += NW) {
@@ -605,17 +673,17 @@ decode_kernel(const DecodeArgs a) {
                 if (c < meta.nchunks) stage_chunk(lay, meta, c, meta.pk[u], stage, tile_dwords);
             }
             for (int c = L + 512; c < meta.nchunks; c += 64)      // rows longer than 64 elements
-                stage_chunk(lay, meta, c, load_chunk(a, meta.ea + (size_t)c * 8), stage, tile_dwords);
+                stage_chunk(lay, meta, c, load_chunk(k_src(a), meta.ea + (size_t)c * 8), stage, tile_dwords);
         }
         const uint4 mw = meta.mw;
         const int row_base = (lay.padded ? 0 : 2 * meta.shift) + L * (int)lay.row_bytes;
 
-        // -- V of this tile, then the next tile's packed rows and mask
+        // -- V of this tile (dense V), then the next tile's packed keys and mask
         uint4 vr[16];
-        load_v_tile(vbh, t0, nt, tau, oct, vr);
+        if (!VP) load_v_tile(vbh, t0, nt, tau, oct, vr);
         if (tile + NW < ntiles) {
             const int t1 = t0 + NW * DECODE_TILE;
-            issue_meta(a, bh, t1, min(DECODE_TILE, blk_end - t1), L, meta);
+            issue_meta(k_src(a), S, bh, t1, min(DECODE_TILE, blk_end - t1), L, meta);
         }
 
         // -- 2. list of kept channels (table byte offsets), slot-major [rho][lane]
@@ -689,8 +757,32 @@ decode_kernel(const DecodeArgs a) {
         softmax_tile<G>(s, m_run, l_run, acc, ptab, L);
         wave_lds_sync();
 
+        int vshift = 0;
+        if (VP) {
+            // packed V rows (16-byte chunks as loaded) and the tile's V masks,
+            // over the list and staged keys; then the next tile's V rows
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int c = L + 64 * u;
+                if (c < vmeta.nchunks) reinterpret_cast<uint4*>(vstage)[c] = vmeta.pk[u];
+            }
+            for (int c = L + 512; c < vmeta.nchunks; c += 64)
+                reinterpret_cast<uint4*>(vstage)[c] = load_chunk(v_src(a), vmeta.ea + (size_t)c * 8);
+            vmask[L] = vmeta.mw;
+            vshift = vmeta.shift;
+            if (tile + NW < ntiles) {
+                const int t1 = t0 + NW * DECODE_TILE;
+                issue_meta(v_src(a), S, bh, t1, min(DECODE_TILE, blk_end - t1), L, vmeta);
+            }
+            wave_lds_sync();
+        }
+
         // -- 5. P.V
-        pv_tile<G>(vr, ptab, acc, tau);
+        if (VP)
+            pv_tile_vpacked<G>(reinterpret_cast<const uint16_t*>(vstage) + vshift, vmask, a.Tv, ptab, rvl, acc, tau,
+                               oct);
+        else
+            pv_tile<G>(vr, ptab, acc, tau);
         wave_lds_sync();
     }
 
@@ -1056,15 +1148,15 @@ uint32_t decode_fast_lds_bytes(int G, int T, int nsplit) {
 bool decode_fast_supported(int G, int T) { return G == 4 && (T == 26 || T == 38 || T == 64); }
 
 
-template <int SMODE>
+template <int SMODE, bool VP>
 hipError_t launch_generic(const DecodeArgs& a, int G, dim3 grid, dim3 block, hipStream_t stream) {
     const size_t lds = a.lay.lds_bytes;
     const void* fn = nullptr;
     switch (G) {
-        case 1: fn = reinterpret_cast<const void*>(&decode_kernel<1, SMODE>); break;
-        case 2: fn = reinterpret_cast<const void*>(&decode_kernel<2, SMODE>); break;
-        case 4: fn = reinterpret_cast<const void*>(&decode_kernel<4, SMODE>); break;
-        case 8: fn = reinterpret_cast<const void*>(&decode_kernel<8, SMODE>); break;
+        case 1: fn = reinterpret_cast<const void*>(&decode_kernel<1, SMODE, VP>); break;
+        case 2: fn = reinterpret_cast<const void*>(&decode_kernel<2, SMODE, VP>); break;
+        case 4: fn = reinterpret_cast<const void*>(&decode_kernel<4, SMODE, VP>); break;
+        case 8: fn = reinterpret_cast<const void*>(&decode_kernel<8, SMODE, VP>); break;
         default: return hipErrorInvalidValue;
     }
     if (lds > 65536) {
@@ -1073,10 +1165,10 @@ hipError_t launch_generic(const DecodeArgs& a, int G, dim3 grid, dim3 block, hip
         if (e != hipSuccess) return e;
     }
     switch (G) {
-        case 1: hipLaunchKernelGGL((decode_kernel<1, SMODE>), grid, block, lds, stream, a); break;
-        case 2: hipLaunchKernelGGL((decode_kernel<2, SMODE>), grid, block, lds, stream, a); break;
-        case 4: hipLaunchKernelGGL((decode_kernel<4, SMODE>), grid, block, lds, stream, a); break;
-        default: hipLaunchKernelGGL((decode_kernel<8, SMODE>), grid, block, lds, stream, a); break;
+        case 1: hipLaunchKernelGGL((decode_kernel<1, SMODE, VP>), grid, block, lds, stream, a); break;
+        case 2: hipLaunchKernelGGL((decode_kernel<2, SMODE, VP>), grid, block, lds, stream, a); break;
+        case 4: hipLaunchKernelGGL((decode_kernel<4, SMODE, VP>), grid, block, lds, stream, a); break;
+        default: hipLaunchKernelGGL((decode_kernel<8, SMODE, VP>), grid, block, lds, stream, a); break;
     }
     return hipGetLastError();
 }
@@ -1085,6 +1177,7 @@ hipError_t launch_generic(const DecodeArgs& a, int G, dim3 grid, dim3 block, hip
 // The sampled F always takes the generic kernel.
 hipError_t launch_decode(const DecodeArgs& a, int G, int BH, hipStream_t stream) {
     const dim3 grid(a.nsplit, BH), block(DECODE_THREADS);
+    if (a.v_packed_mode) return launch_generic<0, true>(a, G, grid, block, stream);
     if (!a.sampled && decode_fast_supported(G, a.T)) {
         const dim3 fblock(DECODE_FAST_THREADS);
         // the fast kernel's LDS is static (DECODE_FAST_LDS_BYTES)
@@ -1097,9 +1190,9 @@ hipError_t launch_decode(const DecodeArgs& a, int G, int BH, hipStream_t stream)
         return hipGetLastError();
     }
     switch (a.sampled) {
-        case 0: return launch_generic<0>(a, G, grid, block, stream);
-        case 4: return launch_generic<4>(a, G, grid, block, stream);
-        case 5: return launch_generic<5>(a, G, grid, block, stream);
+        case 0: return launch_generic<0, false>(a, G, grid, block, stream);
+        case 4: return launch_generic<4, false>(a, G, grid, block, stream);
+        case 5: return launch_generic<5, false>(a, G, grid, block, stream);
         default: return hipErrorInvalidValue;
     }
 }

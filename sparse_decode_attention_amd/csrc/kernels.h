@@ -46,7 +46,10 @@ struct DecodeLayout {
     uint32_t list_bytes;   // per wave: kept-channel table offsets, u16 [T][64]
     uint32_t stage_bytes;  // per wave: staged packed rows of one 64-token tile
     uint32_t ptab_bytes;   // per wave: p of the tile, [64][G] fp32
-    uint32_t wave_bytes;   // list + stage + ptab
+    uint32_t vstage_bytes; // per wave, packed V only: staged packed V rows of one tile (+ slack)
+    uint32_t vmask_bytes;  // per wave, packed V only: the tile's V masks, [64] x 16 B
+    uint32_t kv_bytes;     // per wave: max(list + stage, vstage + vmask) (packed V reuses the key region)
+    uint32_t wave_bytes;   // kv + ptab
     uint32_t tab_bytes;    // 128 * tab_stride, plus the [128][G] fp32 q' ns table of the sampled F
     uint32_t lds_bytes;    // whole block (dynamic LDS)
 };
@@ -58,14 +61,20 @@ struct DecodeArgs {
     const uint16_t* v;        // [B][N_kv][S][128]
     const float* r;           // [B][N_kv][128]; sampled F: (mu, sigma) in entries 0, 1
     const float* A;           // [B][N_kv][128] channel energy (sampled F only)
+    const uint16_t* v_packed; // [B][N_kv][S][Tv] (V channels pruned only)
+    const uint32_t* v_mask;   // [B][N_kv][S][4]
+    const float* rv;          // [B][N_kv][128] recovery of pruned V entries
     float* out;               // [B][N_q][128]
     float* part_ml;           // [B*N_kv][nsplit][2][G]
     float* part_acc;          // [B*N_kv][nsplit][G][128]
     uint32_t* counters;       // [B*N_kv]
     size_t packed_elems;      // B*N_kv*S*T
+    size_t v_packed_elems;    // B*N_kv*S*Tv
     int S, T, N_q, N_kv, nsplit, chunk;
     float qscale;             // softmax scale * log2(e)
     int sampled;              // 0, or the sampled F (4 Gaussian, 5 Exponential)
+    int v_packed_mode;        // 1: V channels pruned (v_packed, v_mask, rv; v unused)
+    int Tv;                   // V channels kept per token (v_packed_mode)
     uint32_t seed_lo, seed_hi;  // Philox key of the sampled F
     DecodeLayout lay;
 };
@@ -91,6 +100,6 @@ hipError_t launch_read_stream(const void* src, size_t bytes, uint32_t* sink, int
 
 // Launch the decode kernel for group size G; returns a hipError_t.
 hipError_t launch_decode(const DecodeArgs& a, int G, int BH, hipStream_t stream);
-DecodeLayout decode_layout(int G, int T, int nsplit, bool sampled);
+DecodeLayout decode_layout(int G, int T, int nsplit, bool sampled, int Tv);
 
 }  // namespace spark

@@ -45,6 +45,10 @@ chan_energy_kernel(const uint16_t* __restrict__ q_win, float* __restrict__ A,
 }
 
 // ---------------------------------------------------------------- select + pack
+// Also serves V-channel pruning (walkthrough section 4.4): with A == nullptr
+// every channel energy is 1 and the key is v^2, exact for bf16 v, which ranks
+// the channels of a token by |v|.
+//
 // Block: 4 waves over PRUNE_TOKENS_PER_BLOCK consecutive tokens of one
 // (b, kv head). Each wave takes one token at a time with lane L holding
 // channels L and L + 64, so the two 64-lane ballots of "kept" are the mask
@@ -74,8 +78,9 @@ select_pack_kernel(const uint16_t* __restrict__ k, const float* __restrict__ A,
     const int t_begin = blk * PRUNE_TOKENS_PER_BLOCK;
     const int t_end = min(S, t_begin + PRUNE_TOKENS_PER_BLOCK);
 
-    const float A0 = A[(size_t)bh * 128 + L];
-    const float A1 = A[(size_t)bh * 128 + 64 + L];
+    // A == nullptr: unit channel energy, so the key is v^2 (V-channel pruning)
+    const float A0 = A ? A[(size_t)bh * 128 + L] : 1.0f;
+    const float A1 = A ? A[(size_t)bh * 128 + 64 + L] : 1.0f;
     const double a0 = sqrt((double)A0), a1 = sqrt((double)A1);
 
     double sum0 = 0.0, sum1 = 0.0, pruned = 0.0, pruned2 = 0.0;

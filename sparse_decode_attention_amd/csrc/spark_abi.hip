@@ -142,6 +142,28 @@ int spark_prefill_prune(const void* q_win, const void* k, int B, int S, int N_q,
     return hip_status(hipGetLastError());
 }
 
+int spark_prefill_prune_v(const void* v, int B, int S, int N_kv, int D, float lambda_v, void* v_packed,
+                          uint32_t* v_mask, float* r_v, int32_t* cnt, void* ws, size_t ws_bytes, void* stream) {
+    if (B < 1 || S < 1 || N_kv < 1 || D < 1) return SPARK_EINVAL;
+    const int T = kept_or_neg(D, lambda_v);
+    if (T < 0) return SPARK_EINVAL;
+    if (D != 128) return SPARK_EUNSUPPORTED;
+    if (!v || !v_mask || !r_v || !ws || (T > 0 && !v_packed)) return SPARK_EINVAL;
+    if (!aligned(v, 16) || !aligned(v_mask, 16) || !aligned(r_v, 16) || (v_packed && !aligned(v_packed, 16)) ||
+        (cnt && !aligned(cnt, 16)) || !aligned(ws, 256))
+        return SPARK_EALIGN;
+    const PrefillWs w = prefill_layout(ws, B, S, N_kv);
+    if (ws_bytes < w.bytes) return SPARK_ENOSPACE;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int BH = B * N_kv;
+    hipLaunchKernelGGL(select_pack_kernel, dim3(w.nblk, BH), dim3(256), 0, st, static_cast<const uint16_t*>(v),
+                       static_cast<const float*>(nullptr), static_cast<uint16_t*>(v_packed), v_mask, w.sum, w.cnt,
+                       w.pruned, S, T, w.nblk, (int)SPARK_F_MEAN_RETAINED);
+    hipLaunchKernelGGL(stats_reduce_kernel, dim3(BH), dim3(128 * STATS_PARTS), 0, st, w.sum, w.cnt, w.pruned,
+                       static_cast<const float*>(nullptr), r_v, cnt, S, T, w.nblk, (int)SPARK_F_MEAN_RETAINED, 0.0f);
+    return hip_status(hipGetLastError());
+}
+
 int spark_stats(const void* k_packed, const uint32_t* mask, const float* chan_energy, const void* k_dense,
                 int B, int S, int N_kv, int D, float lambda, int recovery, float f_const,
                 float* r, int32_t* cnt, void* ws, size_t ws_bytes, void* stream) {
@@ -175,20 +197,34 @@ namespace {
 // Checks, workspace carving and launch shared by both decode entry points.
 // sampled = 0: the fixed recovery vector r; else the sampled F of that mode,
 // with r = (mu, sigma, ...) and the channel energy A.
+// Packed V (V channels pruned): vp.mask != nullptr.
+struct PackedV {
+    const void* packed;
+    const uint32_t* mask;
+    const float* r;
+    float lambda;
+};
+
 int decode_call(const void* q, const void* k_packed, const uint32_t* mask, const void* v, const float* r,
                 const float* A, int sampled, uint64_t seed, int B, int S, int N_q, int N_kv, int D, float lambda,
-                float scale, int splits, float* out, void* ws, size_t ws_bytes, void* stream) {
+                float scale, int splits, float* out, void* ws, size_t ws_bytes, void* stream,
+                const PackedV* vp = nullptr) {
     if (B < 1 || S < 1 || D < 1 || splits < 0) return SPARK_EINVAL;
     const int T = kept_or_neg(D, lambda);
     if (T < 0) return SPARK_EINVAL;
+    const int Tv = vp ? kept_or_neg(D, vp->lambda) : -1;
+    if (vp && Tv < 0) return SPARK_EINVAL;
     if (!(scale == scale)) return SPARK_EINVAL;
     if (int e = check_group(N_q, N_kv)) return e;
     if (D != 128) return SPARK_EUNSUPPORTED;
     const int BH = B * N_kv;
     if ((size_t)BH > (SPARK_DECODE_COUNTER_BYTES / 4)) return SPARK_EUNSUPPORTED;
-    if (!q || !mask || !v || !r || !out || !ws || (T > 0 && !k_packed) || (sampled && !A)) return SPARK_EINVAL;
-    if (!aligned(q, 16) || !aligned(mask, 16) || !aligned(v, 16) || !aligned(r, 16) || !aligned(out, 16) ||
+    if (!q || !mask || !r || !out || !ws || (T > 0 && !k_packed) || (sampled && !A)) return SPARK_EINVAL;
+    if (vp ? (!vp->mask || !vp->r || (Tv > 0 && !vp->packed)) : !v) return SPARK_EINVAL;
+    if (!aligned(q, 16) || !aligned(mask, 16) || (v && !aligned(v, 16)) || !aligned(r, 16) || !aligned(out, 16) ||
         (k_packed && !aligned(k_packed, 16)) || (A && !aligned(A, 16)) || !aligned(ws, 256))
+        return SPARK_EALIGN;
+    if (vp && (!aligned(vp->mask, 16) || !aligned(vp->r, 16) || (vp->packed && !aligned(vp->packed, 16))))
         return SPARK_EALIGN;
     const int G = N_q / N_kv;
     int nsplit, chunk;
@@ -203,6 +239,14 @@ int decode_call(const void* q, const void* k_packed, const uint32_t* mask, const
     a.v = static_cast<const uint16_t*>(v);
     a.r = r;
     a.A = A;
+    if (vp) {
+        a.v_packed = static_cast<const uint16_t*>(vp->packed);
+        a.v_mask = vp->mask;
+        a.rv = vp->r;
+        a.v_packed_elems = (size_t)BH * S * Tv;
+        a.v_packed_mode = 1;
+        a.Tv = Tv;
+    }
     a.out = out;
     a.counters = reinterpret_cast<uint32_t*>(base);
     a.part_ml = reinterpret_cast<float*>(base + SPARK_DECODE_COUNTER_BYTES);
@@ -220,7 +264,7 @@ int decode_call(const void* q, const void* k_packed, const uint32_t* mask, const
     a.sampled = sampled;
     a.seed_lo = (uint32_t)seed;
     a.seed_hi = (uint32_t)(seed >> 32);
-    a.lay = decode_layout(G, T, nsplit, sampled != 0);
+    a.lay = decode_layout(G, T, nsplit, sampled != 0, Tv);
     return hip_status(launch_decode(a, G, BH, static_cast<hipStream_t>(stream)));
 }
 
@@ -233,6 +277,15 @@ int spark_decode_attn(const void* q, const void* k_packed, const uint32_t* mask,
                       float* out, void* ws, size_t ws_bytes, void* stream) {
     return decode_call(q, k_packed, mask, v, r, nullptr, 0, 0, B, S, N_q, N_kv, D, lambda, scale, splits, out, ws,
                        ws_bytes, stream);
+}
+
+int spark_decode_attn_kv(const void* q, const void* k_packed, const uint32_t* k_mask, const float* r,
+                         const void* v_packed, const uint32_t* v_mask, const float* r_v, int B, int S, int N_q,
+                         int N_kv, int D, float lambda, float lambda_v, float scale, int splits, float* out, void* ws,
+                         size_t ws_bytes, void* stream) {
+    const PackedV vp{v_packed, v_mask, r_v, lambda_v};
+    return decode_call(q, k_packed, k_mask, nullptr, r, nullptr, 0, 0, B, S, N_q, N_kv, D, lambda, scale, splits, out,
+                       ws, ws_bytes, stream, &vp);
 }
 
 int spark_decode_attn_sampled(const void* q, const void* k_packed, const uint32_t* mask, const void* v,

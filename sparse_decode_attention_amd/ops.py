@@ -38,6 +38,9 @@ _SIGS = {
     "spark_decode_attn": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _f, _i, _vp, _vp, _sz, _vp]),
     "spark_decode_attn_sampled": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _u64, _i, _i, _i, _i, _i, _f, _f, _i,
                                        _vp, _vp, _sz, _vp]),
+    "spark_prefill_prune_v": (_i, [_vp, _i, _i, _i, _i, _f, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "spark_decode_attn_kv": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _f, _f, _i,
+                                  _vp, _vp, _sz, _vp]),
     "spark_decode_ws_init": (_i, [_vp, _sz, _vp]),
     "spark_read_stream": (_i, [_vp, _sz, _vp, _i, _vp]),
     "spark_window_evict_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
@@ -213,6 +216,50 @@ def decode_attn_sampled(q, k_packed, mask, v, chan_energy, r, recovery: str, see
                                          B, S, N_q, n_kv, D, float(lam), float(scale), int(splits), _ptr(out),
                                          _ptr(ws), ws.numel(), _stream(dev))
     _check("spark_decode_attn_sampled", st)
+    return out
+
+
+def prefill_prune_v(v: torch.Tensor, lam_v: float, out: dict | None = None) -> dict:
+    """spark_prefill_prune_v: v bf16 [B][N_kv][S][D] -> {"T", "v_packed",
+    "v_mask", "r_v", "cnt"} (new tensors unless `out` supplies them)."""
+    B, n_kv, S, D = v.shape
+    _need(v, "v", torch.bfloat16)
+    T = num_kept(D, lam_v)
+    if T < 0:
+        raise SparkError("spark_num_kept", EINVAL)
+    dev = v.device
+    o = dict(out or {})
+    o.setdefault("v_packed", torch.empty((B, n_kv, S, T), dtype=torch.bfloat16, device=dev))
+    o.setdefault("v_mask", torch.empty((B, n_kv, S, (D + 31) // 32), dtype=torch.int32, device=dev))
+    o.setdefault("r_v", torch.empty((B, n_kv, D), dtype=torch.float32, device=dev))
+    o.setdefault("cnt", torch.empty((B, n_kv, D), dtype=torch.int32, device=dev))
+    ws = workspace(dev, "prefill", lib().spark_prefill_workspace_bytes(B, S, n_kv, D))
+    st = lib().spark_prefill_prune_v(_ptr(v), B, S, n_kv, D, float(lam_v), _ptr(o["v_packed"]) if T > 0 else None,
+                                     _ptr(o["v_mask"]), _ptr(o["r_v"]), _ptr(o["cnt"]), _ptr(ws), ws.numel(),
+                                     _stream(dev))
+    _check("spark_prefill_prune_v", st)
+    o["T"] = T
+    return o
+
+
+def decode_attn_kv(q, k_packed, k_mask, r, v_packed, v_mask, r_v, lam: float, lam_v: float, scale: float = 0.0,
+                   splits: int = 0, out=None, ws=None):
+    """spark_decode_attn_kv: decode over a cache with K and V channels pruned."""
+    B, N_q, D = q.shape
+    n_kv, S = v_mask.shape[1], v_mask.shape[2]
+    _need(q, "q", torch.bfloat16)
+    _need(v_mask, "v_mask", torch.int32, (B, n_kv, S, (D + 31) // 32))
+    _need(r_v, "r_v", torch.float32, (B, n_kv, D))
+    dev = q.device
+    out = torch.empty((B, N_q, D), dtype=torch.float32, device=dev) if out is None else out
+    if ws is None:
+        ws = workspace(dev, "decode", decode_ws_bytes(B, S, N_q, n_kv, D, splits))
+    T, Tv = num_kept(D, lam), num_kept(D, lam_v)
+    st = lib().spark_decode_attn_kv(_ptr(q), _ptr(k_packed) if T > 0 else None, _ptr(k_mask), _ptr(r),
+                                    _ptr(v_packed) if Tv > 0 else None, _ptr(v_mask), _ptr(r_v), B, S, N_q, n_kv, D,
+                                    float(lam), float(lam_v), float(scale), int(splits), _ptr(out), _ptr(ws),
+                                    ws.numel(), _stream(dev))
+    _check("spark_decode_attn_kv", st)
     return out
 
 

@@ -124,6 +124,40 @@ def test_decode_sampled_rejects_bad_arguments():
     assert _decode_sampled(nws=ops.DECODE_COUNTER_BYTES) == ops.ENOSPACE
 
 
+def test_prefill_prune_v_rejects_bad_arguments():
+    def call(**kw):
+        a = dict(v=FAKE, B=1, S=64, N_kv=8, D=128, lam=0.5, vp=FAKE, vm=FAKE, rv=FAKE, cnt=None, ws=FAKE, nws=0)
+        a.update(kw)
+        return ops.lib().spark_prefill_prune_v(a["v"], a["B"], a["S"], a["N_kv"], a["D"], a["lam"], a["vp"], a["vm"],
+                                               a["rv"], a["cnt"], a["ws"], a["nws"], None)
+    assert call(S=0) == ops.EINVAL
+    assert call(lam=1.5) == ops.EINVAL
+    assert call(D=64) == ops.EUNSUPPORTED
+    assert call(v=None) == ops.EINVAL
+    assert call(vp=None) == ops.EINVAL                   # T_v > 0 needs the packed store
+    assert call(vp=None, lam=1.0) == ops.ENOSPACE        # T_v = 0 does not
+    assert call(rv=MIS) == ops.EALIGN
+    assert call() == ops.ENOSPACE
+
+
+def test_decode_kv_rejects_bad_arguments():
+    def call(**kw):
+        a = dict(q=FAKE, kp=FAKE, km=FAKE, r=FAKE, vp=FAKE, vm=FAKE, rv=FAKE, B=1, S=64, N_q=32, N_kv=8, D=128,
+                 lam=0.5, lam_v=0.5, scale=0.0, splits=0, out=FAKE, ws=FAKE, nws=0)
+        a.update(kw)
+        return ops.lib().spark_decode_attn_kv(a["q"], a["kp"], a["km"], a["r"], a["vp"], a["vm"], a["rv"], a["B"],
+                                              a["S"], a["N_q"], a["N_kv"], a["D"], a["lam"], a["lam_v"], a["scale"],
+                                              a["splits"], a["out"], a["ws"], a["nws"], None)
+    assert call(lam_v=-0.1) == ops.EINVAL
+    assert call(vm=None) == ops.EINVAL
+    assert call(rv=None) == ops.EINVAL
+    assert call(vp=None) == ops.EINVAL
+    assert call(vp=None, lam_v=1.0) == ops.ENOSPACE
+    assert call(vp=MIS) == ops.EALIGN
+    assert call(N_q=24) == ops.EUNSUPPORTED
+    assert call() == ops.ENOSPACE
+
+
 def test_stats_rejects_bad_arguments():
     l = ops.lib()
 
