@@ -83,8 +83,10 @@ def sampled_alu_ops_per_token(G, T, rec):
     return 32 * per_group + G * T + T + G * 128
 
 
-def effective_decode_bytes(w, T):
-    return w.B * w.n_kv * w.S * (2 * T + 16 + 2 * w.D)
+def effective_decode_bytes(w, T, Tv=None):
+    """Packed K and its mask, then dense V (Tv None) or packed V and its mask."""
+    v_bytes = 2 * w.D if Tv is None else 2 * Tv + 16
+    return w.B * w.n_kv * w.S * (2 * T + 16 + v_bytes)
 
 
 def effective_prefill_bytes(w, T):
@@ -92,7 +94,7 @@ def effective_prefill_bytes(w, T):
 
 
 def run_leg(w, steps, warmup, rotate=True, seed=0, verbose=True, x=None, recovery="mean_retained",
-            rng_seed=SAMPLE_SEED):
+            rng_seed=SAMPLE_SEED, lam_v=None):
     import torch
     from sparse_decode_attention_amd import gen, ops
 
@@ -100,7 +102,8 @@ def run_leg(w, steps, warmup, rotate=True, seed=0, verbose=True, x=None, recover
     T = ops.num_kept(w.D, w.lam)
     if x is None:
         x = gen.torch_layer(w, dev, seed=seed, steps=w.steps)
-    dec_bytes = effective_decode_bytes(w, T)
+    Tv = None if lam_v is None else ops.num_kept(w.D, lam_v)
+    dec_bytes = effective_decode_bytes(w, T, Tv)
     R = max(1, int(-(-MALL_DEFEAT_BYTES // dec_bytes))) if rotate else 1
     # replica 0 is written by the prefill every step; replicas 1..R-1 hold copies of it
     reps = []
@@ -111,19 +114,33 @@ def run_leg(w, steps, warmup, rotate=True, seed=0, verbose=True, x=None, recover
             "chan_energy": torch.empty((w.B, w.n_kv, w.D), dtype=torch.float32, device=dev),
             "r": torch.empty((w.B, w.n_kv, w.D), dtype=torch.float32, device=dev),
             "cnt": torch.empty((w.B, w.n_kv, w.D), dtype=torch.int32, device=dev),
-            "v": x["v"] if i == 0 else x["v"].clone(),
+            "v": x["v"] if (i == 0 or Tv is not None) else x["v"].clone(),
         })
+        if Tv is not None:
+            reps[-1].update({
+                "v_packed": torch.empty((w.B, w.n_kv, w.S, Tv), dtype=torch.bfloat16, device=dev),
+                "v_mask": torch.empty((w.B, w.n_kv, w.S, 4), dtype=torch.int32, device=dev),
+                "r_v": torch.empty((w.B, w.n_kv, w.D), dtype=torch.float32, device=dev),
+                "cnt_v": torch.empty((w.B, w.n_kv, w.D), dtype=torch.int32, device=dev),
+            })
     outs = torch.empty((w.steps, w.B, w.n_q, w.D), dtype=torch.float32, device=dev)
 
     sampled = recovery in ("gaussian", "exponential")
 
     def prefill():
         ops.prefill_prune(x["q_win"], x["k"], w.n_kv, w.lam, recovery=recovery, out=reps[0])
+        if Tv is not None:
+            r0 = reps[0]
+            ops.prefill_prune_v(x["v"], lam_v, out={"v_packed": r0["v_packed"], "v_mask": r0["v_mask"],
+                                                    "r_v": r0["r_v"], "cnt": r0["cnt_v"]})
 
     def decode_all():
         for s in range(w.steps):
             rp = reps[s % R]
-            if sampled:
+            if Tv is not None:
+                ops.decode_attn_kv(x["q_dec"][s], rp["k_packed"], rp["mask"], rp["r"], rp["v_packed"], rp["v_mask"],
+                                   rp["r_v"], w.lam, lam_v, out=outs[s])
+            elif sampled:
                 ops.decode_attn_sampled(x["q_dec"][s], rp["k_packed"], rp["mask"], rp["v"], rp["chan_energy"],
                                         rp["r"], recovery, rng_seed, w.lam, out=outs[s])
             else:
@@ -132,7 +149,7 @@ def run_leg(w, steps, warmup, rotate=True, seed=0, verbose=True, x=None, recover
     # eager pass: fills every replica and allocates the cached workspaces
     prefill()
     for rp in reps[1:]:
-        for n in ("k_packed", "mask", "chan_energy", "r", "cnt"):
+        for n in ("k_packed", "mask", "chan_energy", "r", "cnt") + (("v_packed", "v_mask", "r_v") if Tv else ()):
             rp[n].copy_(reps[0][n])
     decode_all()
     torch.cuda.synchronize()
@@ -189,6 +206,7 @@ def run_leg(w, steps, warmup, rotate=True, seed=0, verbose=True, x=None, recover
         "decode_GBps": dec_bytes / (dec_launch_us * 1e-6) / 1e9,
         "prefill_us": med(pre_ms) * 1e3,
         "prefill_GBps": effective_prefill_bytes(w, T) / (med(pre_ms) * 1e-3) / 1e9,
+        "Tv": Tv,
         "step_ms_median": med(step_ms),
         "step_ms_mean": sum(step_ms) / len(step_ms),
         "wall_s": wall,
@@ -451,6 +469,7 @@ def main():
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the 128K-context, stacked-eviction and 32-layer workloads")
     ap.add_argument("--no-sampled", action="store_true", help="skip the sampled recovery F legs")
+    ap.add_argument("--no-vprune", action="store_true", help="skip the K-and-V-pruned leg")
     ap.add_argument("--warm", action="store_true", help="also report a run without replica rotation")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="run a plain device copy of this size after the legs (counter calibration)")
@@ -536,6 +555,20 @@ def main():
                              "ops_per_token_head": sampled_alu_ops_per_token(w.G, T, rec)},
                 "x_fixed_r_time": round(lg["decode_us_per_launch"] / main_leg["decode_us_per_launch"], 3),
                 "prefill_us": round(lg["prefill_us"], 2), "seed": hex(SAMPLE_SEED)}
+            del lg
+        torch.cuda.empty_cache()
+    if not args.no_vprune:
+        line["v_pruned"] = {}
+        for lam_v in (0.5,):
+            print(f"bench: K and V pruned, lambda_v={lam_v}, on {w.name}", file=sys.stderr, flush=True)
+            lg = run_leg(w, min(args.steps, 5), min(args.warmup, 2), x=main_leg["x"], lam_v=lam_v)
+            line["v_pruned"][f"lambda_v={lam_v}"] = {
+                "workload": w.name, "kernel": f"decode_kernel<{w.G}, 0, true>", "T_v": lg["Tv"],
+                "decode_us_per_launch": round(lg["decode_us_per_launch"], 3),
+                "bytes_per_launch": lg["decode_bytes_per_step"],
+                "GBps": round(lg["decode_GBps"], 2), "pct_hbm_peak": round(100 * lg["decode_GBps"] / HBM_PEAK_GBS, 2),
+                "x_dense_v_time": round(lg["decode_us_per_launch"] / main_leg["decode_us_per_launch"], 3),
+                "prefill_us_k_and_v": round(lg["prefill_us"], 2), "replicas": lg["replicas"]}
             del lg
         torch.cuda.empty_cache()
     if not args.no_extra:

@@ -13,7 +13,8 @@
 #define DECODE_FAST_LDS_BYTES (2576 + (DECODE_FAST_THREADS / 64) * (8704 + 1024))
 #define DECODE_TILE 64
 #define DECODE_MAX_SPLITS 256
-#define DECODE_SAMPLED_BLOCKS 512    // blocks the sampled F's decode aims for when splits = 0
+#define DECODE_GENERIC_BLOCKS 512    // blocks the generic decode kernel aims for when splits = 0
+#define DECODE_LDS_PER_CU (160 * 1024)
 // window eviction: at most 128 stacked window rows (G * W), tokens per block
 #define EVICT_MAX_ROWS 128
 #define EVICT_WAVE_ROWS 32
@@ -100,6 +101,7 @@ hipError_t launch_read_stream(const void* src, size_t bytes, uint32_t* sink, int
 
 // Launch the decode kernel for group size G; returns a hipError_t.
 hipError_t launch_decode(const DecodeArgs& a, int G, int BH, hipStream_t stream);
+bool decode_fast_supported(int G, int T);
 DecodeLayout decode_layout(int G, int T, int nsplit, bool sampled, int Tv);
 
 }  // namespace spark

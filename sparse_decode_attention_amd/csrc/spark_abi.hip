@@ -108,7 +108,7 @@ size_t spark_decode_workspace_bytes(int B, int S, int N_q, int N_kv, int D, int 
     if (B < 1 || S < 1 || N_kv < 1 || N_q < 1 || D < 1 || splits < 0 || N_q % N_kv) return 0;
     int nsplit, chunk;
     // sized for the larger of the two entry points' split plans
-    decode_plan(B * N_kv, S, splits, &nsplit, &chunk, DECODE_SAMPLED_BLOCKS);
+    decode_plan(B * N_kv, S, splits, &nsplit, &chunk, DECODE_GENERIC_BLOCKS);
     return decode_ws_bytes(B * N_kv, N_q / N_kv, nsplit);
 }
 
@@ -228,7 +228,12 @@ int decode_call(const void* q, const void* k_packed, const uint32_t* mask, const
         return SPARK_EALIGN;
     const int G = N_q / N_kv;
     int nsplit, chunk;
-    decode_plan(BH, S, splits, &nsplit, &chunk, sampled ? DECODE_SAMPLED_BLOCKS : 256);
+    // the fast kernel (8 waves, one block per CU) aims for 256 blocks; the
+    // generic kernel (4 waves) for 512, two per CU, when two fit in LDS
+    const bool generic = vp || sampled || !decode_fast_supported(G, T);
+    decode_plan(BH, S, splits, &nsplit, &chunk, generic ? DECODE_GENERIC_BLOCKS : 256);
+    if (generic && splits == 0 && decode_layout(G, T, nsplit, sampled != 0, Tv).lds_bytes > DECODE_LDS_PER_CU / 2)
+        decode_plan(BH, S, splits, &nsplit, &chunk, 256);
     if (ws_bytes < decode_ws_bytes(BH, G, nsplit)) return SPARK_ENOSPACE;
 
     char* base = static_cast<char*>(ws);
