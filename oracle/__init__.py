@@ -4,4 +4,5 @@ from .spark_oracle import (num_kept, chan_energy, saliency_keys, select_top_t, m
                            mask_from_words, pack_kept, prune, stats, expand_keys, decode_attn,
                            dense_attn, window_scores, snapkv_evict, window_rows, philox4x32_10,
                            uniform01, recovery_samples, expand_keys_sampled, decode_attn_sampled,
-                           value_keys, prune_v, decode_attn_kv)
+                           value_keys, prune_v, decode_attn_kv, channel_groups,
+                           grouped_num_kept, select_grouped, prune_grouped)

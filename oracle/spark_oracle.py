@@ -33,6 +33,8 @@ Readings of points the pages leave open (each is listed in the design doc):
     walkthrough's Degenerate F (section 3.3, F table) is "score_mean_pruned".
   * Decode: one new query per head attends to all S cached tokens (no causal
     mask), scale 1/sqrt(D), recovery only in the scores, V dense.
+  * SparK-g (section 5.2): channel groups by channel energy rank (equal
+    groups, most important first), per-group top-T_i by saliency key.
   * V-channel pruning (section 4.4, "norm-based"): per-token top-T_v of
     |v_tj|, ties to the lower channel, retained-mean recovery of V.
   * Sampled F ("gaussian", "exponential", the other rows of the section 3.3 F
@@ -358,6 +360,60 @@ def decode_attn_sampled(q, packed, mask, v, A, r, mode: str, seed: int, scale: f
     D = mask.shape[-1]
     scale = 1.0 / math.sqrt(D) if scale is None or scale <= 0 else float(scale)
     return _attend(q, expand_keys_sampled(packed, mask, A, r, mode, seed), v, scale)
+
+
+# ---------------------------------------------------------------- SparK-g (grouped ratios)
+#
+# Walkthrough section 5.2: channels are grouped by importance and each group
+# is pruned at its own ratio, low-importance groups harder; with g = 4 the
+# ratios are (0.25, 0.5, 0.75, 1.0). Reading taken here: per (batch, KV
+# head), rank the channels by the channel energy A_j (descending, ties to the
+# lower channel) and cut the ranking into g equal groups; group i (i = 0 the
+# most important) gets the i-th ratio; every token keeps, in each group, the
+# T_i = num_kept(D / g, ratio_i) members of largest saliency key (ties to the
+# lower channel). Every token then keeps the same T = sum T_i channels.
+
+def channel_groups(A: np.ndarray, g: int) -> np.ndarray:
+    """Group index [B][N_kv][D] of each channel: rank by A descending (ties
+    to the lower channel), cut into g equal groups."""
+    A = _f32(A)
+    D = A.shape[-1]
+    if D % g:
+        raise ValueError("g must divide D")
+    order = np.argsort(-A, axis=-1, kind="stable")
+    rank = np.empty_like(order)
+    np.put_along_axis(rank, order, np.arange(D)[None, None, :].repeat(A.shape[0], 0).repeat(A.shape[1], 1), axis=-1)
+    return rank // (D // g)
+
+
+def grouped_num_kept(D: int, ratios) -> list:
+    """T_i per group for group ratios (each group has D / g channels)."""
+    g = len(ratios)
+    return [num_kept(D // g, r) for r in ratios]
+
+
+def select_grouped(keys: np.ndarray, groups: np.ndarray, Ts) -> np.ndarray:
+    """Per token and group i, the T_i members of largest key (ties to the
+    lower channel)."""
+    mask = np.zeros(keys.shape, dtype=bool)
+    gb = groups[:, :, None, :]
+    for i, Ti in enumerate(Ts):
+        member = np.broadcast_to(gb == i, keys.shape)
+        # non-members rank below every member (keys are >= 0)
+        k_i = np.where(member, keys.astype(np.float64), -1.0)
+        mask |= select_top_t(k_i, Ti) & member
+    return mask
+
+
+def prune_grouped(q_win: np.ndarray, k: np.ndarray, n_kv: int, ratios, qagg: str = QAGG_L2) -> dict:
+    """SparK-g prefill pruning: like prune() with the group-wise selection."""
+    D = k.shape[-1]
+    A = chan_energy(q_win, n_kv, qagg)
+    groups = channel_groups(A, len(ratios))
+    Ts = grouped_num_kept(D, ratios)
+    mask = select_grouped(saliency_keys(A, k), groups, Ts)
+    return {"T": int(sum(Ts)), "Ts": Ts, "A": A, "groups": groups, "mask": mask, "words": mask_words(mask),
+            "packed": pack_kept(k, mask)}
 
 
 # ---------------------------------------------------------------- V-channel pruning

@@ -594,3 +594,53 @@ def test_v_constant_channels_closed_form():
     k = rng.standard_normal((1, 1, S, D))
     out = oracle.decode_attn_kv(q, k, np.ones(k.shape, bool), np.zeros((1, 1, D)), pv["packed"], pv["mask"], pv["r"])
     np.testing.assert_allclose(out[0], np.broadcast_to(want, (3, D)), rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------------------------ SparK-g
+
+def test_grouped_one_group_is_plain_top_t():
+    w = WORKLOADS["tiny_s1k"].with_(S=200, n_q=8, n_kv=2)
+    x = gen.numpy_layer(w, seed=50, steps=0)
+    f = {n: gen.bf16_bits_to_f32(a) for n, a in x.items()}
+    for lam in (0.3, 0.5, 0.8):
+        a = oracle.prune_grouped(f["q_win"], f["k"], w.n_kv, [lam])
+        b = oracle.prune(f["q_win"], f["k"], w.n_kv, lam)
+        np.testing.assert_array_equal(a["mask"], b["mask"])
+
+
+def test_grouped_page_ratios_keep_48():
+    assert oracle.grouped_num_kept(128, [0.25, 0.5, 0.75, 1.0]) == [24, 16, 8, 0]
+
+
+def test_channel_groups_brute_force_with_ties():
+    rng = np.random.default_rng(51)
+    A = rng.choice([0.0, 1.0, 2.0, 4.0], size=(2, 3, 16)).astype(np.float32)
+    gr = oracle.channel_groups(A, 4)
+    for b in range(2):
+        for h in range(3):
+            for j in range(16):
+                rank = sum(1 for i in range(16) if A[b, h, i] > A[b, h, j] or (A[b, h, i] == A[b, h, j] and i < j))
+                assert gr[b, h, j] == rank // 4
+
+
+def test_grouped_selection_brute_force_with_ties():
+    """Small-integer energies and keys (exact ties): in every group the kept
+    members are the first subset, in lexicographic order, of largest key sum;
+    groups follow the energy ranking."""
+    rng = np.random.default_rng(52)
+    D, S, ratios = 8, 120, [0.0, 0.5, 0.75, 1.0]          # groups of 2: keep 2, 1, 1, 0
+    qrow = rng.choice([0.0, 1.0, 2.0, 3.0], size=D)
+    k = rng.choice([0.0, 1.0, -1.0, 2.0, -2.0, 0.5], size=(S, D))
+    q_win, kk = _single(qrow, k)
+    out = oracle.prune_grouped(q_win, kk, 1, ratios)
+    assert out["Ts"] == [2, 1, 1, 0] and out["T"] == 4
+    A = out["A"][0, 0]
+    rank = [sum(1 for i in range(D) if A[i] > A[j] or (A[i] == A[j] and i < j)) for j in range(D)]
+    for t in range(S):
+        w = [Fraction(abs(float(qrow[j]))) * Fraction(abs(float(k[t, j]))) for j in range(D)]
+        got = set(np.flatnonzero(out["mask"][0, 0, t]).tolist())
+        for gi, Ti in enumerate(out["Ts"]):
+            members = [j for j in range(D) if rank[j] // 2 == gi]
+            best = _brute_reduced([w[j] for j in members], Ti)
+            assert got & set(members) == {members[i] for i in best}, (t, gi)
+        assert int(out["mask"][0, 0, t].sum()) == 4
