@@ -72,6 +72,11 @@ typedef enum {
  * Table 1 caption). Returns -1 if lambda is outside [0, 1] or D < 1. */
 int spark_num_kept(int D, float lambda);
 
+/* SparK-g (walkthrough section 5.2): T = sum over the ngroups equal channel
+ * groups of floor((1 - ratios[i]) * D / ngroups + 0.5). Returns -1 if
+ * ngroups is outside 1..8, does not divide D, or a ratio is outside [0, 1]. */
+int spark_num_kept_grouped(int D, int ngroups, const float* ratios);
+
 /* Human-readable name of a spark_status. Never NULL. */
 const char* spark_strerror(int status);
 
@@ -107,6 +112,27 @@ int spark_prefill_prune(const void* q_win, const void* k,
                         int qagg, int recovery, float f_const,
                         void* k_packed, uint32_t* mask, float* chan_energy, float* r, int32_t* cnt,
                         void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * SparK-g prefill pruning (walkthrough section 5.2: channels grouped by
+ * importance, each group pruned at its own ratio, the least important
+ * hardest). Per (b, KV head) the channels are ranked by the channel energy
+ * A_j (descending, ties to the lower channel) and cut into ngroups equal
+ * groups; group i (0 = most important) keeps, for every token, its
+ * floor((1 - ratios[i]) * D / ngroups + 0.5) members of largest saliency key
+ * (ties to the lower channel). Every token keeps the same
+ * T = spark_num_kept_grouped(D, ngroups, ratios) channels, so the outputs
+ * have the layouts of spark_prefill_prune with that T, and decode runs
+ * through spark_decode_attn with lambda = 1 - T / D.
+ *  ngroups, ratios   1..8 groups dividing D; ratios: host array of ngroups
+ *                    pruned fractions in [0, 1] (the page's g = 4 uses
+ *                    0.25, 0.5, 0.75, 1.0)
+ * Other arguments, outputs and return codes as for spark_prefill_prune.
+ */
+int spark_prefill_prune_grouped(const void* q_win, const void* k, int B, int S, int N_q, int N_kv, int D,
+                                int ngroups, const float* ratios, int window, int qagg, int recovery, float f_const,
+                                void* k_packed, uint32_t* mask, float* chan_energy, float* r, int32_t* cnt,
+                                void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Recovery statistics recomputed from a stored pruned cache (walkthrough

@@ -1145,7 +1145,7 @@ uint32_t decode_fast_lds_bytes(int G, int T, int nsplit) {
     return tab + dyn;
 }
 
-bool decode_fast_supported(int G, int T) { return G == 4 && (T == 26 || T == 38 || T == 64); }
+bool decode_fast_supported(int G, int T) { return G == 4 && (T == 26 || T == 38 || T == 48 || T == 64); }
 
 
 template <int SMODE, bool VP>
@@ -1185,6 +1185,7 @@ hipError_t launch_decode(const DecodeArgs& a, int G, int BH, hipStream_t stream)
         switch (a.T) {
             case 26: hipLaunchKernelGGL((decode_fast_kernel<4, 26>), grid, fblock, 0, stream, a); break;
             case 38: hipLaunchKernelGGL((decode_fast_kernel<4, 38>), grid, fblock, 0, stream, a); break;
+            case 48: hipLaunchKernelGGL((decode_fast_kernel<4, 48>), grid, fblock, 0, stream, a); break;
             default: hipLaunchKernelGGL((decode_fast_kernel<4, 64>), grid, fblock, 0, stream, a); break;
         }
         return hipGetLastError();

@@ -26,9 +26,18 @@
 namespace spark {
 
 __global__ void chan_energy_kernel(const uint16_t* q_win, float* A, int N_q, int N_kv, int W, int qagg);
+#define SPARK_MAX_GROUPS 8
+// SparK-g: ngroups equal channel groups, each keeping T[i] of its `size` members per token
+struct GroupSpec {
+    int n;
+    int size;
+    int T[SPARK_MAX_GROUPS];
+};
+template <bool GROUPED>
 __global__ void select_pack_kernel(const uint16_t* k, const float* A, uint16_t* k_packed, uint32_t* mask,
                                    double* part_sum, int32_t* part_cnt, double* part_pruned,
-                                   int S, int T, int nblk, int recovery);
+                                   int S, int T, int nblk, int recovery, const uint8_t* gid, GroupSpec grp);
+__global__ void channel_groups_kernel(const float* A, uint8_t* gid, int ngroups);
 __global__ void stats_partial_kernel(const uint16_t* k_packed, const uint32_t* mask, const uint16_t* k_dense,
                                      const float* A, double* part_sum, int32_t* part_cnt, double* part_pruned,
                                      int S, int T, int nblk, int recovery);

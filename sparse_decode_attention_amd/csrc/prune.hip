@@ -60,12 +60,47 @@ chan_energy_kernel(const uint16_t* __restrict__ q_win, float* __restrict__ A,
 // >= the candidate: those T are the answer and no tie straddles it.
 // Otherwise theta is exact and the channels equal to theta are taken in
 // ascending channel order until T are kept.
+// The T keys at or above the T-th largest among the lanes' candidates (two
+// per lane; with MASKED, only members in0 / in1 take part and Tg counts
+// members), ties to the lower channel. v, n and the loop state are
+// wave-uniform (scalar registers); each unrolled step costs two compares, two
+// scalar popcounts and a scalar select, and the search leaves at the first
+// count of exactly Tg.
+template <bool MASKED>
+__device__ __forceinline__ void select_top(uint32_t key0, uint32_t key1, bool in0, bool in1, int Tg, bool& kept0,
+                                           bool& kept1) {
+    uint32_t v = 0;
+    bool exact = false;
+#pragma unroll
+    for (int bit = 30; bit >= 0; --bit) {
+        const uint32_t c = __builtin_amdgcn_readfirstlane(v | (1u << bit));
+        const int n = __popcll(ballot((!MASKED || in0) && key0 >= c)) + __popcll(ballot((!MASKED || in1) && key1 >= c));
+        v = n >= Tg ? c : v;
+        if (n == Tg) { exact = true; break; }
+    }
+    if (exact) {
+        kept0 = (!MASKED || in0) && key0 >= v;
+        kept1 = (!MASKED || in1) && key1 >= v;
+    } else {
+        const bool gt0 = (!MASKED || in0) && key0 > v, gt1 = (!MASKED || in1) && key1 > v;
+        const int need = Tg - (__popcll(ballot(gt0)) + __popcll(ballot(gt1)));
+        const uint64_t eq0 = ballot((!MASKED || in0) && key0 == v), eq1 = ballot((!MASKED || in1) && key1 == v);
+        const int r0 = (int)mbcnt(eq0);
+        const int r1 = __popcll(eq0) + (int)mbcnt(eq1);
+        kept0 = gt0 || ((!MASKED || in0) && key0 == v && r0 < need);
+        kept1 = gt1 || ((!MASKED || in1) && key1 == v && r1 < need);
+    }
+}
+
+// GROUPED (SparK-g): channel c belongs to group gid[bh][c] (0..ngroups-1)
+// and each group keeps its own grp.T[i] members; T is their sum.
+template <bool GROUPED>
 __global__ void __launch_bounds__(256)
 select_pack_kernel(const uint16_t* __restrict__ k, const float* __restrict__ A,
                    uint16_t* __restrict__ k_packed, uint32_t* __restrict__ mask,
                    double* __restrict__ part_sum, int32_t* __restrict__ part_cnt,
                    double* __restrict__ part_pruned,
-                   int S, int T, int nblk, int recovery) {
+                   int S, int T, int nblk, int recovery, const uint8_t* __restrict__ gid, GroupSpec grp) {
     __shared__ uint4 stage[4][64];            // 4 tokens x 256 B per wave
     __shared__ double red_sum[4][128];
     __shared__ int red_cnt[4][128];
@@ -82,6 +117,8 @@ select_pack_kernel(const uint16_t* __restrict__ k, const float* __restrict__ A,
     const float A0 = A ? A[(size_t)bh * 128 + L] : 1.0f;
     const float A1 = A ? A[(size_t)bh * 128 + 64 + L] : 1.0f;
     const double a0 = sqrt((double)A0), a1 = sqrt((double)A1);
+    const int g0 = GROUPED ? gid[(size_t)bh * 128 + L] : 0;
+    const int g1 = GROUPED ? gid[(size_t)bh * 128 + 64 + L] : 0;
 
     double sum0 = 0.0, sum1 = 0.0, pruned = 0.0, pruned2 = 0.0;
     int cnt0 = 0, cnt1 = 0;
@@ -107,36 +144,26 @@ select_pack_kernel(const uint16_t* __restrict__ k, const float* __restrict__ A,
             const float k0 = bf16_to_f32(kb0), k1 = bf16_to_f32(kb1);
             const uint32_t key0 = __float_as_uint(__fmul_rn(A0, __fmul_rn(k0, k0)));
             const uint32_t key1 = __float_as_uint(__fmul_rn(A1, __fmul_rn(k1, k1)));
-            bool kept0, kept1;
-            if (T >= 128) {
-                kept0 = kept1 = true;
-            } else if (T <= 0) {
-                kept0 = kept1 = false;
-            } else {
-                // v, n and the loop state are wave-uniform (scalar registers);
-                // the unrolled steps each cost two compares, two scalar
-                // popcounts and a scalar select, and leave at the first
-                // count of exactly T
-                uint32_t v = 0;
-                bool exact = false;
-#pragma unroll
-                for (int bit = 30; bit >= 0; --bit) {
-                    const uint32_t c = __builtin_amdgcn_readfirstlane(v | (1u << bit));
-                    const int n = __popcll(ballot(key0 >= c)) + __popcll(ballot(key1 >= c));
-                    v = n >= T ? c : v;
-                    if (n == T) { exact = true; break; }
+            bool kept0 = false, kept1 = false;
+            if (!GROUPED) {
+                if (T >= 128) {
+                    kept0 = kept1 = true;
+                } else if (T > 0) {
+                    select_top<false>(key0, key1, true, true, T, kept0, kept1);
                 }
-                if (exact) {
-                    kept0 = key0 >= v;
-                    kept1 = key1 >= v;
-                } else {
-                    const bool gt0 = key0 > v, gt1 = key1 > v;
-                    const int need = T - (__popcll(ballot(gt0)) + __popcll(ballot(gt1)));
-                    const uint64_t eq0 = ballot(key0 == v), eq1 = ballot(key1 == v);
-                    const int r0 = (int)mbcnt(eq0);
-                    const int r1 = __popcll(eq0) + (int)mbcnt(eq1);
-                    kept0 = gt0 || (key0 == v && r0 < need);
-                    kept1 = gt1 || (key1 == v && r1 < need);
+            } else {
+                for (int i = 0; i < grp.n; ++i) {
+                    const bool in0 = g0 == i, in1 = g1 == i;
+                    const int Ti = grp.T[i];
+                    if (Ti >= grp.size) {
+                        kept0 |= in0;
+                        kept1 |= in1;
+                    } else if (Ti > 0) {
+                        bool k0, k1;
+                        select_top<true>(key0, key1, in0, in1, Ti, k0, k1);
+                        kept0 |= k0;
+                        kept1 |= k1;
+                    }
                 }
             }
             const uint64_t m0 = ballot(kept0), m1 = ballot(kept1);
@@ -186,6 +213,26 @@ select_pack_kernel(const uint16_t* __restrict__ k, const float* __restrict__ A,
         if (j < 2) part_pruned[((size_t)bh * nblk + blk) * 2 + j] =
             (recovery >= 3) ? ((red_pr[0][j] + red_pr[1][j]) + red_pr[2][j]) + red_pr[3][j] : 0.0;
     }
+}
+
+template __global__ void select_pack_kernel<false>(const uint16_t*, const float*, uint16_t*, uint32_t*, double*,
+                                                   int32_t*, double*, int, int, int, int, const uint8_t*, GroupSpec);
+template __global__ void select_pack_kernel<true>(const uint16_t*, const float*, uint16_t*, uint32_t*, double*,
+                                                  int32_t*, double*, int, int, int, int, const uint8_t*, GroupSpec);
+
+// ---------------------------------------------------------------- SparK-g channel groups
+// One block per (b, KV head), one thread per channel: rank by A descending
+// (ties to the lower channel), group = rank / (128 / ngroups).
+__global__ void __launch_bounds__(128)
+channel_groups_kernel(const float* __restrict__ A, uint8_t* __restrict__ gid, int ngroups) {
+    __shared__ float a[128];
+    const int bh = blockIdx.x, j = threadIdx.x;
+    a[j] = A[(size_t)bh * 128 + j];
+    __syncthreads();
+    const float x = a[j];
+    int rank = 0;
+    for (int i = 0; i < 128; ++i) rank += (a[i] > x || (a[i] == x && i < j)) ? 1 : 0;
+    gid[(size_t)bh * 128 + j] = (uint8_t)(rank / (128 / ngroups));
 }
 
 // ---------------------------------------------------------------- stats from a stored cache

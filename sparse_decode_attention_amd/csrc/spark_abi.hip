@@ -26,11 +26,13 @@ int check_group(int N_q, int N_kv) {
 }
 
 // prefill workspace: part_sum double [BH][nblk][128] | part_cnt int32 [BH][nblk][128] |
-// part_pruned double [BH][nblk][2] (sum of the pruned saliency, sum of its squares)
+// part_pruned double [BH][nblk][2] (sum of the pruned saliency, sum of its squares) |
+// gid uint8 [BH][128] (SparK-g channel groups)
 struct PrefillWs {
     double* sum;
     int32_t* cnt;
     double* pruned;
+    uint8_t* gid;
     size_t bytes;
     int nblk;
 };
@@ -47,7 +49,8 @@ PrefillWs prefill_layout(void* ws, int B, int S, int N_kv) {
     w.sum = reinterpret_cast<double*>(base);
     w.cnt = reinterpret_cast<int32_t*>(base + s_sum);
     w.pruned = reinterpret_cast<double*>(base + s_sum + s_cnt);
-    w.bytes = s_sum + s_cnt + s_pr;
+    w.gid = reinterpret_cast<uint8_t*>(base + s_sum + s_cnt + s_pr);
+    w.bytes = s_sum + s_cnt + s_pr + round_up(BH * 128, 256);
     return w;
 }
 
@@ -86,6 +89,17 @@ int hip_status(hipError_t e) { return e == hipSuccess ? SPARK_OK : SPARK_EHIP; }
 extern "C" {
 
 int spark_num_kept(int D, float lambda) { return kept_or_neg(D, lambda); }
+
+int spark_num_kept_grouped(int D, int ngroups, const float* ratios) {
+    if (D < 1 || ngroups < 1 || ngroups > SPARK_MAX_GROUPS || D % ngroups || !ratios) return -1;
+    int T = 0;
+    for (int i = 0; i < ngroups; ++i) {
+        const int t = kept_or_neg(D / ngroups, ratios[i]);
+        if (t < 0) return -1;
+        T += t;
+    }
+    return T;
+}
 
 const char* spark_strerror(int status) {
     switch (status) {
@@ -134,9 +148,10 @@ int spark_prefill_prune(const void* q_win, const void* k, int B, int S, int N_q,
     const int BH = B * N_kv;
     hipLaunchKernelGGL(chan_energy_kernel, dim3(BH), dim3(256), 0, st,
                        static_cast<const uint16_t*>(q_win), chan_energy, N_q, N_kv, window, qagg);
-    hipLaunchKernelGGL(select_pack_kernel, dim3(w.nblk, BH), dim3(256), 0, st,
+    hipLaunchKernelGGL(select_pack_kernel<false>, dim3(w.nblk, BH), dim3(256), 0, st,
                        static_cast<const uint16_t*>(k), chan_energy, static_cast<uint16_t*>(k_packed), mask,
-                       w.sum, w.cnt, w.pruned, S, T, w.nblk, recovery);
+                       w.sum, w.cnt, w.pruned, S, T, w.nblk, recovery, static_cast<const uint8_t*>(nullptr),
+                       GroupSpec{});
     hipLaunchKernelGGL(stats_reduce_kernel, dim3(BH), dim3(128 * STATS_PARTS), 0, st,
                        w.sum, w.cnt, w.pruned, chan_energy, r, cnt, S, T, w.nblk, recovery, f_const);
     return hip_status(hipGetLastError());
@@ -156,11 +171,49 @@ int spark_prefill_prune_v(const void* v, int B, int S, int N_kv, int D, float la
     if (ws_bytes < w.bytes) return SPARK_ENOSPACE;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int BH = B * N_kv;
-    hipLaunchKernelGGL(select_pack_kernel, dim3(w.nblk, BH), dim3(256), 0, st, static_cast<const uint16_t*>(v),
-                       static_cast<const float*>(nullptr), static_cast<uint16_t*>(v_packed), v_mask, w.sum, w.cnt,
-                       w.pruned, S, T, w.nblk, (int)SPARK_F_MEAN_RETAINED);
+    hipLaunchKernelGGL(select_pack_kernel<false>, dim3(w.nblk, BH), dim3(256), 0, st,
+                       static_cast<const uint16_t*>(v), static_cast<const float*>(nullptr),
+                       static_cast<uint16_t*>(v_packed), v_mask, w.sum, w.cnt, w.pruned, S, T, w.nblk,
+                       (int)SPARK_F_MEAN_RETAINED, static_cast<const uint8_t*>(nullptr), GroupSpec{});
     hipLaunchKernelGGL(stats_reduce_kernel, dim3(BH), dim3(128 * STATS_PARTS), 0, st, w.sum, w.cnt, w.pruned,
                        static_cast<const float*>(nullptr), r_v, cnt, S, T, w.nblk, (int)SPARK_F_MEAN_RETAINED, 0.0f);
+    return hip_status(hipGetLastError());
+}
+
+int spark_prefill_prune_grouped(const void* q_win, const void* k, int B, int S, int N_q, int N_kv, int D,
+                                int ngroups, const float* ratios, int window, int qagg, int recovery, float f_const,
+                                void* k_packed, uint32_t* mask, float* chan_energy, float* r, int32_t* cnt,
+                                void* ws, size_t ws_bytes, void* stream) {
+    if (B < 1 || S < 1 || D < 1 || window < 1) return SPARK_EINVAL;
+    const int T = spark_num_kept_grouped(D, ngroups, ratios);
+    if (T < 0) return SPARK_EINVAL;
+    if (qagg != SPARK_QAGG_L2 && qagg != SPARK_QAGG_MEAN) return SPARK_EINVAL;
+    if (recovery < SPARK_F_MEAN_RETAINED || recovery > SPARK_F_EXPONENTIAL) return SPARK_EINVAL;
+    if (int e = check_group(N_q, N_kv)) return e;
+    if (D != 128) return SPARK_EUNSUPPORTED;
+    if (!q_win || !k || !mask || !chan_energy || !r || !ws || (T > 0 && !k_packed)) return SPARK_EINVAL;
+    if (!aligned(q_win, 16) || !aligned(k, 16) || !aligned(mask, 16) || !aligned(chan_energy, 16) ||
+        !aligned(r, 16) || (k_packed && !aligned(k_packed, 16)) || (cnt && !aligned(cnt, 16)) || !aligned(ws, 256))
+        return SPARK_EALIGN;
+    const PrefillWs w = prefill_layout(ws, B, S, N_kv);
+    if (ws_bytes < w.bytes) return SPARK_ENOSPACE;
+    GroupSpec grp{};
+    grp.n = ngroups;
+    grp.size = D / ngroups;
+    for (int i = 0; i < ngroups; ++i) grp.T[i] = kept_or_neg(D / ngroups, ratios[i]);
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int BH = B * N_kv;
+    hipLaunchKernelGGL(chan_energy_kernel, dim3(BH), dim3(256), 0, st,
+                       static_cast<const uint16_t*>(q_win), chan_energy, N_q, N_kv, window, qagg);
+    hipLaunchKernelGGL(channel_groups_kernel, dim3(BH), dim3(128), 0, st, static_cast<const float*>(chan_energy),
+                       w.gid, ngroups);
+    hipLaunchKernelGGL(select_pack_kernel<true>, dim3(w.nblk, BH), dim3(256), 0, st,
+                       static_cast<const uint16_t*>(k), static_cast<const float*>(chan_energy),
+                       static_cast<uint16_t*>(k_packed), mask, w.sum, w.cnt, w.pruned, S, T, w.nblk, recovery,
+                       static_cast<const uint8_t*>(w.gid), grp);
+    hipLaunchKernelGGL(stats_reduce_kernel, dim3(BH), dim3(128 * STATS_PARTS), 0, st,
+                       w.sum, w.cnt, w.pruned, chan_energy, r, cnt, S, T, w.nblk, recovery, f_const);
     return hip_status(hipGetLastError());
 }
 

@@ -39,6 +39,9 @@ _SIGS = {
     "spark_decode_attn_sampled": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _u64, _i, _i, _i, _i, _i, _f, _f, _i,
                                        _vp, _vp, _sz, _vp]),
     "spark_prefill_prune_v": (_i, [_vp, _i, _i, _i, _i, _f, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "spark_num_kept_grouped": (_i, [_i, _i, ctypes.POINTER(ctypes.c_float)]),
+    "spark_prefill_prune_grouped": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, ctypes.POINTER(ctypes.c_float), _i, _i,
+                                         _i, _f, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "spark_decode_attn_kv": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _f, _f, _i,
                                   _vp, _vp, _sz, _vp]),
     "spark_decode_ws_init": (_i, [_vp, _sz, _vp]),
@@ -82,6 +85,15 @@ def strerror(status: int) -> str:
 
 def num_kept(D: int, lam: float) -> int:
     return int(lib().spark_num_kept(int(D), float(lam)))
+
+
+def _floats(xs):
+    return (ctypes.c_float * len(xs))(*[float(x) for x in xs])
+
+
+def num_kept_grouped(D: int, ratios) -> int:
+    """SparK-g: channels kept per token for equal groups pruned at `ratios`."""
+    return int(lib().spark_num_kept_grouped(int(D), len(ratios), _floats(ratios)))
 
 
 def _check(fn: str, status: int) -> None:
@@ -150,6 +162,36 @@ def prefill_prune(q_win: torch.Tensor, k: torch.Tensor, n_kv: int, lam: float, q
                                    _ptr(ws), ws.numel(), _stream(dev))
     _check("spark_prefill_prune", st)
     o["T"] = T
+    return o
+
+
+def prefill_prune_grouped(q_win: torch.Tensor, k: torch.Tensor, n_kv: int, ratios, qagg: str = "l2",
+                          recovery: str = "mean_retained", f_const: float = 0.01, out: dict | None = None) -> dict:
+    """spark_prefill_prune_grouped (SparK-g). Same outputs as prefill_prune
+    with T = num_kept_grouped(D, ratios); "lam" is the lambda to decode with."""
+    B, N_q, W, D = q_win.shape
+    S = k.shape[2]
+    _need(q_win, "q_win", torch.bfloat16)
+    _need(k, "k", torch.bfloat16, (B, n_kv, S, D))
+    T = num_kept_grouped(D, ratios)
+    if T < 0:
+        raise SparkError("spark_num_kept_grouped", EINVAL)
+    dev = k.device
+    o = dict(out or {})
+    o.setdefault("k_packed", torch.empty((B, n_kv, S, T), dtype=torch.bfloat16, device=dev))
+    o.setdefault("mask", torch.empty((B, n_kv, S, (D + 31) // 32), dtype=torch.int32, device=dev))
+    o.setdefault("chan_energy", torch.empty((B, n_kv, D), dtype=torch.float32, device=dev))
+    o.setdefault("r", torch.empty((B, n_kv, D), dtype=torch.float32, device=dev))
+    o.setdefault("cnt", torch.empty((B, n_kv, D), dtype=torch.int32, device=dev))
+    ws = workspace(dev, "prefill", lib().spark_prefill_workspace_bytes(B, S, n_kv, D))
+    st = lib().spark_prefill_prune_grouped(_ptr(q_win), _ptr(k), B, S, N_q, n_kv, D, len(ratios), _floats(ratios), W,
+                                           QAGG[qagg], RECOVERY[recovery], float(f_const),
+                                           _ptr(o["k_packed"]) if T > 0 else None, _ptr(o["mask"]),
+                                           _ptr(o["chan_energy"]), _ptr(o["r"]), _ptr(o["cnt"]), _ptr(ws), ws.numel(),
+                                           _stream(dev))
+    _check("spark_prefill_prune_grouped", st)
+    o["T"] = T
+    o["lam"] = 1.0 - T / D
     return o
 
 

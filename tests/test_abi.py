@@ -158,6 +158,36 @@ def test_decode_kv_rejects_bad_arguments():
     assert call() == ops.ENOSPACE
 
 
+def test_num_kept_grouped():
+    assert ops.num_kept_grouped(128, [0.25, 0.5, 0.75, 1.0]) == 48
+    assert ops.num_kept_grouped(128, [0.5]) == ops.num_kept(128, 0.5)
+    assert ops.num_kept_grouped(128, [0.0, 1.0]) == 64
+    assert ops.num_kept_grouped(128, [0.5] * 8) == 64
+    assert ops.num_kept_grouped(128, [0.5] * 3) == -1              # 3 does not divide 128
+    assert ops.num_kept_grouped(128, [0.5] * 16) == -1             # more than 8 groups
+    assert ops.num_kept_grouped(128, [0.5, 1.5]) == -1
+    assert ops.lib().spark_num_kept_grouped(128, 4, None) == -1
+
+
+def test_prefill_grouped_rejects_bad_arguments():
+    def call(ratios=(0.25, 0.5, 0.75, 1.0), **kw):
+        a = dict(q_win=FAKE, k=FAKE, B=1, S=64, N_q=32, N_kv=8, D=128, W=4, qagg=0, rec=0, fc=0.01,
+                 kp=FAKE, mask=FAKE, A=FAKE, r=FAKE, cnt=FAKE, ws=FAKE, nws=0)
+        a.update(kw)
+        arr = ops._floats(ratios)
+        return ops.lib().spark_prefill_prune_grouped(a["q_win"], a["k"], a["B"], a["S"], a["N_q"], a["N_kv"], a["D"],
+                                                     len(ratios), arr, a["W"], a["qagg"], a["rec"], a["fc"], a["kp"],
+                                                     a["mask"], a["A"], a["r"], a["cnt"], a["ws"], a["nws"], None)
+    assert call(ratios=(0.5, 0.5, 0.5)) == ops.EINVAL
+    assert call(ratios=(0.5, -1.0)) == ops.EINVAL
+    assert call(rec=6) == ops.EINVAL
+    assert call(N_q=24) == ops.EUNSUPPORTED
+    assert call(kp=None) == ops.EINVAL
+    assert call(kp=None, ratios=(1.0, 1.0)) == ops.ENOSPACE       # T = 0 needs no packed store
+    assert call(mask=MIS) == ops.EALIGN
+    assert call() == ops.ENOSPACE
+
+
 def test_stats_rejects_bad_arguments():
     l = ops.lib()
 
