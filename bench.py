@@ -94,12 +94,13 @@ def effective_prefill_bytes(w, T):
 
 
 def run_leg(w, steps, warmup, rotate=True, seed=0, verbose=True, x=None, recovery="mean_retained",
-            rng_seed=SAMPLE_SEED, lam_v=None):
+            rng_seed=SAMPLE_SEED, lam_v=None, ratios=None):
     import torch
     from sparse_decode_attention_amd import gen, ops
 
     dev = torch.device("cuda:0")
-    T = ops.num_kept(w.D, w.lam)
+    T = ops.num_kept(w.D, w.lam) if ratios is None else ops.num_kept_grouped(w.D, ratios)
+    lam = w.lam if ratios is None else 1.0 - T / w.D
     if x is None:
         x = gen.torch_layer(w, dev, seed=seed, steps=w.steps)
     Tv = None if lam_v is None else ops.num_kept(w.D, lam_v)
@@ -128,7 +129,10 @@ def run_leg(w, steps, warmup, rotate=True, seed=0, verbose=True, x=None, recover
     sampled = recovery in ("gaussian", "exponential")
 
     def prefill():
-        ops.prefill_prune(x["q_win"], x["k"], w.n_kv, w.lam, recovery=recovery, out=reps[0])
+        if ratios is not None:
+            ops.prefill_prune_grouped(x["q_win"], x["k"], w.n_kv, ratios, recovery=recovery, out=reps[0])
+        else:
+            ops.prefill_prune(x["q_win"], x["k"], w.n_kv, w.lam, recovery=recovery, out=reps[0])
         if Tv is not None:
             r0 = reps[0]
             ops.prefill_prune_v(x["v"], lam_v, out={"v_packed": r0["v_packed"], "v_mask": r0["v_mask"],
@@ -139,12 +143,12 @@ def run_leg(w, steps, warmup, rotate=True, seed=0, verbose=True, x=None, recover
             rp = reps[s % R]
             if Tv is not None:
                 ops.decode_attn_kv(x["q_dec"][s], rp["k_packed"], rp["mask"], rp["r"], rp["v_packed"], rp["v_mask"],
-                                   rp["r_v"], w.lam, lam_v, out=outs[s])
+                                   rp["r_v"], lam, lam_v, out=outs[s])
             elif sampled:
                 ops.decode_attn_sampled(x["q_dec"][s], rp["k_packed"], rp["mask"], rp["v"], rp["chan_energy"],
-                                        rp["r"], recovery, rng_seed, w.lam, out=outs[s])
+                                        rp["r"], recovery, rng_seed, lam, out=outs[s])
             else:
-                ops.decode_attn(x["q_dec"][s], rp["k_packed"], rp["mask"], rp["v"], rp["r"], w.lam, out=outs[s])
+                ops.decode_attn(x["q_dec"][s], rp["k_packed"], rp["mask"], rp["v"], rp["r"], lam, out=outs[s])
 
     # eager pass: fills every replica and allocates the cached workspaces
     prefill()
@@ -470,6 +474,7 @@ def main():
                     help="skip the 128K-context, stacked-eviction and 32-layer workloads")
     ap.add_argument("--no-sampled", action="store_true", help="skip the sampled recovery F legs")
     ap.add_argument("--no-vprune", action="store_true", help="skip the K-and-V-pruned leg")
+    ap.add_argument("--no-grouped", action="store_true", help="skip the SparK-g leg")
     ap.add_argument("--warm", action="store_true", help="also report a run without replica rotation")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="run a plain device copy of this size after the legs (counter calibration)")
@@ -570,6 +575,17 @@ def main():
                 "x_dense_v_time": round(lg["decode_us_per_launch"] / main_leg["decode_us_per_launch"], 3),
                 "prefill_us_k_and_v": round(lg["prefill_us"], 2), "replicas": lg["replicas"]}
             del lg
+        torch.cuda.empty_cache()
+    if not args.no_grouped:
+        ratios = [0.25, 0.5, 0.75, 1.0]
+        print(f"bench: SparK-g {ratios} on {w.name}", file=sys.stderr, flush=True)
+        lg = run_leg(w, min(args.steps, 5), min(args.warmup, 2), x=main_leg["x"], ratios=ratios)
+        line["grouped"] = {
+            "workload": w.name, "ratios": ratios, "T": lg["T"], "kernel": f"decode_fast_kernel<4, {lg['T']}>",
+            "decode_us_per_launch": round(lg["decode_us_per_launch"], 3), "GBps": round(lg["decode_GBps"], 2),
+            "pct_hbm_peak": round(100 * lg["decode_GBps"] / HBM_PEAK_GBS, 2), "prefill_us": round(lg["prefill_us"], 2),
+            "prefill_GBps": round(lg["prefill_GBps"], 1), "replicas": lg["replicas"]}
+        del lg
         torch.cuda.empty_cache()
     if not args.no_extra:
         w3 = WORKLOADS["llama8b_s128k_l08"]
