@@ -5,4 +5,5 @@ from .spark_oracle import (num_kept, chan_energy, saliency_keys, select_top_t, m
                            dense_attn, window_scores, snapkv_evict, window_rows, philox4x32_10,
                            uniform01, recovery_samples, expand_keys_sampled, decode_attn_sampled,
                            value_keys, prune_v, decode_attn_kv, channel_groups,
-                           grouped_num_kept, select_grouped, prune_grouped)
+                           grouped_num_kept, select_grouped, prune_grouped, tree_sum32,
+                           select_top_p, prune_topp)

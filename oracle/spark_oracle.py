@@ -33,6 +33,9 @@ Readings of points the pages leave open (each is listed in the design doc):
     walkthrough's Degenerate F (section 3.3, F table) is "score_mean_pruned".
   * Decode: one new query per head attends to all S cached tokens (no causal
     mask), scale 1/sqrt(D), recovery only in the scores, V dense.
+  * SparK-p (section 5.2): per token the fewest channels reaching p of the
+    total saliency, decided in fp32 with a fixed pairwise summation tree;
+    ties at the threshold kept together; ragged packed rows.
   * SparK-g (section 5.2): channel groups by channel energy rank (equal
     groups, most important first), per-group top-T_i by saliency key.
   * V-channel pruning (section 4.4, "norm-based"): per-token top-T_v of
@@ -360,6 +363,64 @@ def decode_attn_sampled(q, packed, mask, v, A, r, mode: str, seed: int, scale: f
     D = mask.shape[-1]
     scale = 1.0 / math.sqrt(D) if scale is None or scale <= 0 else float(scale)
     return _attend(q, expand_keys_sampled(packed, mask, A, r, mode, seed), v, scale)
+
+
+# ---------------------------------------------------------------- SparK-p (top-p)
+#
+# Walkthrough section 5.2: per token, the fewest channels whose cumulative
+# saliency reaches p = 99% of the token's total. Reading taken here, chosen
+# so that the integer decision is made in one defined fp32 arithmetic:
+#   w_tj = fl32(sqrt(key_tj)) (correctly rounded), the saliency a_j |k_tj|;
+#   every sum over a token's channels is the pairwise tree that folds the
+#   upper half onto the lower half (channel j with j + 64, then + 32, ...,
+#   + 1), in fp32;
+#   target = fl32(p * total), total the tree sum of all w;
+#   theta* = the largest key value theta with tree_sum(w [key >= theta]) >=
+#   target (the sum cannot fall as theta falls); the token keeps the channels
+#   with key >= theta*. Channels tied at theta* are kept together; a token
+#   whose saliency is all zero keeps none.
+# The kept count T_t varies per token, so the packed store is ragged: token
+# t's values sit at [row_off[t], row_off[t + 1]) of its head's region.
+
+def tree_sum32(v: np.ndarray) -> np.ndarray:
+    """fp32 pairwise sum over the last axis (length a power of two), folding
+    the upper half onto the lower half at each level."""
+    x = np.asarray(v, dtype=np.float32)
+    n = x.shape[-1]
+    if n & (n - 1):
+        raise ValueError("length must be a power of two")
+    while n > 1:
+        h = n // 2
+        x = (x[..., :h] + x[..., h:n]).astype(np.float32)
+        n = h
+    return x[..., 0]
+
+
+def select_top_p(keys: np.ndarray, p: float) -> np.ndarray:
+    """SparK-p kept set per token (see the section comment)."""
+    k32 = _f32(keys)
+    w = np.sqrt(k32).astype(np.float32)
+    target = (np.float32(p) * tree_sum32(w)).astype(np.float32)
+    bits = k32.view(np.uint32)
+    v = np.zeros(keys.shape[:-1], dtype=np.uint32)
+    for bit in range(30, -1, -1):
+        c = v | np.uint32(1 << bit)
+        s = tree_sum32(np.where(bits >= c[..., None], w, np.float32(0)))
+        v = np.where(s >= target, c, v)
+    return bits >= v[..., None]
+
+
+def prune_topp(q_win: np.ndarray, k: np.ndarray, n_kv: int, p: float, qagg: str = QAGG_L2) -> dict:
+    """SparK-p prefill pruning. Returns A, mask, words, counts [B][N_kv][S],
+    row_off [B][N_kv][S + 1] (offsets within the head) and packed: all kept
+    values in (b, head, token, channel) order, ragged."""
+    A = chan_energy(q_win, n_kv, qagg)
+    mask = select_top_p(saliency_keys(A, k), p)
+    counts = mask.sum(axis=-1).astype(np.int32)
+    row_off = np.zeros(counts.shape[:-1] + (counts.shape[-1] + 1,), dtype=np.int64)
+    row_off[..., 1:] = np.cumsum(counts, axis=-1)
+    return {"A": A, "mask": mask, "words": mask_words(mask), "counts": counts, "row_off": row_off,
+            "packed": np.asarray(k)[mask]}
 
 
 # ---------------------------------------------------------------- SparK-g (grouped ratios)

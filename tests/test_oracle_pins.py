@@ -644,3 +644,94 @@ def test_grouped_selection_brute_force_with_ties():
             best = _brute_reduced([w[j] for j in members], Ti)
             assert got & set(members) == {members[i] for i in best}, (t, gi)
         assert int(out["mask"][0, 0, t].sum()) == 4
+
+
+# ------------------------------------------------------------------ SparK-p
+
+def _topp_brute(w, p):
+    """Exact: the largest tau among the w values with sum(w >= tau) >= p total;
+    kept = {w >= tau}; empty when the total is 0."""
+    total = sum(w, Fraction(0))
+    if total == 0:
+        return set()
+    best = None
+    for tau in sorted(set(w), reverse=True):
+        if sum((x for x in w if x >= tau), Fraction(0)) >= Fraction(p) * total:
+            best = tau
+            break
+    return {j for j, x in enumerate(w) if x >= best}
+
+
+@pytest.mark.parametrize("D", [8, 128])
+def test_top_p_matches_exact_brute_force(D):
+    """Unit energy and few-valued keys: w = |k| and every fp32 tree sum are
+    exact, so the fp32 decision equals exact arithmetic."""
+    rng = np.random.default_rng(70)
+    S = 300 if D == 8 else 60
+    k = rng.choice([0.0, 0.5, -0.5, 1.0, -1.0, 2.0, -3.0, 4.0], size=(1, 1, S, D))
+    k[0, 0, 0] = 0.0                                   # an all-zero token keeps nothing
+    keys = oracle.saliency_keys(np.ones((1, 1, D), np.float32), k)
+    for p in (0.5, 0.75, 0.875, 1.0):
+        mask = oracle.select_top_p(keys, p)
+        for t in range(S):
+            w = [Fraction(abs(float(k[0, 0, t, j]))) for j in range(D)]
+            assert set(np.flatnonzero(mask[0, 0, t]).tolist()) == _topp_brute(w, p), (p, t)
+
+
+def test_tree_sum_order():
+    """Pairwise fold: ((x0 + x4) + (x2 + x6)) + ((x1 + x5) + (x3 + x7)) for 8 values."""
+    x = np.array([1e8, 1.0, -1e8, 1.0, 1.0, 3.0, 1.0, 1.0], np.float32)
+    f = np.float32
+    want = f(f(f(x[0] + x[4]) + f(x[2] + x[6])) + f(f(x[1] + x[5]) + f(x[3] + x[7])))
+    assert oracle.tree_sum32(x) == want
+    assert oracle.tree_sum32(x) != np.float32(np.sum(x.astype(np.float64)))     # order matters here
+
+
+def test_top_p_monotone_in_p_and_scale_invariant():
+    w = WORKLOADS["tiny_s1k"].with_(S=300, n_q=8, n_kv=2)
+    x = gen.numpy_layer(w, seed=71, steps=0)
+    f = {n: gen.bf16_bits_to_f32(a) for n, a in x.items()}
+    prev = None
+    for p in (0.5, 0.8, 0.9, 0.99, 0.999):
+        m = oracle.prune_topp(f["q_win"], f["k"], w.n_kv, p)["mask"]
+        if prev is not None:
+            assert (m | prev == m).all()          # a larger p keeps a superset
+        prev = m
+    a = oracle.prune_topp(f["q_win"], f["k"], w.n_kv, 0.99)
+    b = oracle.prune_topp(2 * f["q_win"], f["k"], w.n_kv, 0.99)
+    np.testing.assert_array_equal(a["mask"], b["mask"])
+
+
+def test_top_p_agrees_with_sorted_float64_cumsum():
+    """Against the textbook form (sort by saliency, float64 cumulative sum,
+    first count reaching p of the total): the fp32 tree decision may differ
+    only in rare near-ties."""
+    w = WORKLOADS["tiny_s1k"].with_(S=1024)
+    x = gen.numpy_layer(w, seed=72, steps=0)
+    f = {n: gen.bf16_bits_to_f32(a) for n, a in x.items()}
+    out = oracle.prune_topp(f["q_win"], f["k"], w.n_kv, 0.99)
+    keys = oracle.saliency_keys(out["A"], f["k"]).astype(np.float64)
+    sal = np.sqrt(keys)
+    srt = -np.sort(-sal, axis=-1)
+    cs = np.cumsum(srt, axis=-1)
+    n_ref = 1 + np.argmax(cs >= 0.99 * cs[..., -1:], axis=-1)
+    agree = (n_ref == out["counts"]).mean()
+    assert agree >= 0.995, agree
+    assert 0.2 < 1 - out["counts"].mean() / 128 < 0.9          # a real pruning ratio
+
+
+def test_top_p_ragged_layout():
+    rng = np.random.default_rng(73)
+    q = rng.standard_normal((2, 4, 3, 16)).astype(np.float32)
+    k = rng.standard_normal((2, 2, 50, 16)).astype(np.float32)
+    out = oracle.prune_topp(q, k, 2, 0.9)
+    assert (out["row_off"][..., 0] == 0).all()
+    np.testing.assert_array_equal(np.diff(out["row_off"], axis=-1), out["counts"])
+    np.testing.assert_array_equal(out["counts"], out["mask"].sum(-1))
+    flat = out["packed"]
+    for b in range(2):
+        for h in range(2):
+            base = int(out["counts"][:b].sum() + out["counts"][b, :h].sum())
+            for t in (0, 17, 49):
+                lo, hi = out["row_off"][b, h, t], out["row_off"][b, h, t + 1]
+                np.testing.assert_array_equal(flat[base + lo: base + hi], k[b, h, t][out["mask"][b, h, t]])
