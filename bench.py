@@ -94,12 +94,14 @@ def effective_prefill_bytes(w, T):
 
 
 def run_leg(w, steps, warmup, rotate=True, seed=0, verbose=True, x=None, recovery="mean_retained",
-            rng_seed=SAMPLE_SEED, lam_v=None, ratios=None):
+            rng_seed=SAMPLE_SEED, lam_v=None, ratios=None, top_p=None):
     import torch
     from sparse_decode_attention_amd import gen, ops
 
     dev = torch.device("cuda:0")
     T = ops.num_kept(w.D, w.lam) if ratios is None else ops.num_kept_grouped(w.D, ratios)
+    if top_p is not None:
+        T = w.D            # ragged rows: sized (and replicas counted) for the longest row
     lam = w.lam if ratios is None else 1.0 - T / w.D
     if x is None:
         x = gen.torch_layer(w, dev, seed=seed, steps=w.steps)
@@ -111,6 +113,7 @@ def run_leg(w, steps, warmup, rotate=True, seed=0, verbose=True, x=None, recover
     for i in range(R):
         reps.append({
             "k_packed": torch.empty((w.B, w.n_kv, w.S, T), dtype=torch.bfloat16, device=dev),
+            "row_off": torch.empty((w.B, w.n_kv, w.S + 1), dtype=torch.int32, device=dev),
             "mask": torch.empty((w.B, w.n_kv, w.S, 4), dtype=torch.int32, device=dev),
             "chan_energy": torch.empty((w.B, w.n_kv, w.D), dtype=torch.float32, device=dev),
             "r": torch.empty((w.B, w.n_kv, w.D), dtype=torch.float32, device=dev),
@@ -129,7 +132,11 @@ def run_leg(w, steps, warmup, rotate=True, seed=0, verbose=True, x=None, recover
     sampled = recovery in ("gaussian", "exponential")
 
     def prefill():
-        if ratios is not None:
+        if top_p is not None:
+            r0 = dict(reps[0])
+            r0["k_packed"] = r0["k_packed"].view(w.B, w.n_kv, w.S * w.D)
+            ops.prefill_prune_topp(x["q_win"], x["k"], w.n_kv, top_p, recovery=recovery, out=r0)
+        elif ratios is not None:
             ops.prefill_prune_grouped(x["q_win"], x["k"], w.n_kv, ratios, recovery=recovery, out=reps[0])
         else:
             ops.prefill_prune(x["q_win"], x["k"], w.n_kv, w.lam, recovery=recovery, out=reps[0])
@@ -141,7 +148,10 @@ def run_leg(w, steps, warmup, rotate=True, seed=0, verbose=True, x=None, recover
     def decode_all():
         for s in range(w.steps):
             rp = reps[s % R]
-            if Tv is not None:
+            if top_p is not None:
+                ops.decode_attn_ragged(x["q_dec"][s], rp["k_packed"].view(w.B, w.n_kv, w.S * w.D), rp["row_off"],
+                                       rp["mask"], rp["v"], rp["r"], out=outs[s])
+            elif Tv is not None:
                 ops.decode_attn_kv(x["q_dec"][s], rp["k_packed"], rp["mask"], rp["r"], rp["v_packed"], rp["v_mask"],
                                    rp["r_v"], lam, lam_v, out=outs[s])
             elif sampled:
@@ -153,8 +163,14 @@ def run_leg(w, steps, warmup, rotate=True, seed=0, verbose=True, x=None, recover
     # eager pass: fills every replica and allocates the cached workspaces
     prefill()
     for rp in reps[1:]:
-        for n in ("k_packed", "mask", "chan_energy", "r", "cnt") + (("v_packed", "v_mask", "r_v") if Tv else ()):
+        for n in ("k_packed", "mask", "chan_energy", "r", "cnt") + (("v_packed", "v_mask", "r_v") if Tv else ()) + \
+                (("row_off",) if top_p is not None else ()):
             rp[n].copy_(reps[0][n])
+    if top_p is not None:
+        # the bytes a ragged decode reads: kept values, masks and row offsets, dense V
+        kept = int(reps[0]["row_off"][..., -1].sum().item())
+        dec_bytes = 2 * kept + w.B * w.n_kv * (w.S * (16 + 2 * w.D) + 4 * (w.S + 1))
+        T = kept / (w.B * w.n_kv * w.S)
     decode_all()
     torch.cuda.synchronize()
     eager = outs.clone()
@@ -475,6 +491,7 @@ def main():
     ap.add_argument("--no-sampled", action="store_true", help="skip the sampled recovery F legs")
     ap.add_argument("--no-vprune", action="store_true", help="skip the K-and-V-pruned leg")
     ap.add_argument("--no-grouped", action="store_true", help="skip the SparK-g leg")
+    ap.add_argument("--no-topp", action="store_true", help="skip the SparK-p leg")
     ap.add_argument("--warm", action="store_true", help="also report a run without replica rotation")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="run a plain device copy of this size after the legs (counter calibration)")
@@ -575,6 +592,17 @@ def main():
                 "x_dense_v_time": round(lg["decode_us_per_launch"] / main_leg["decode_us_per_launch"], 3),
                 "prefill_us_k_and_v": round(lg["prefill_us"], 2), "replicas": lg["replicas"]}
             del lg
+        torch.cuda.empty_cache()
+    if not args.no_topp:
+        print(f"bench: SparK-p 0.99 on {w.name}", file=sys.stderr, flush=True)
+        lg = run_leg(w, min(args.steps, 5), min(args.warmup, 2), x=main_leg["x"], top_p=0.99)
+        line["top_p"] = {
+            "workload": w.name, "p": 0.99, "mean_kept": round(lg["T"], 2),
+            "pruning_ratio": round(1 - lg["T"] / w.D, 4), "kernel": f"decode_kernel<{w.G}, 0, false, true>",
+            "decode_us_per_launch": round(lg["decode_us_per_launch"], 3), "bytes_per_launch": lg["decode_bytes_per_step"],
+            "GBps": round(lg["decode_GBps"], 2), "pct_hbm_peak": round(100 * lg["decode_GBps"] / HBM_PEAK_GBS, 2),
+            "prefill_us": round(lg["prefill_us"], 2), "replicas": lg["replicas"]}
+        del lg
         torch.cuda.empty_cache()
     if not args.no_grouped:
         ratios = [0.25, 0.5, 0.75, 1.0]

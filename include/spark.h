@@ -114,6 +114,32 @@ int spark_prefill_prune(const void* q_win, const void* k,
                         void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * SparK-p prefill pruning (walkthrough section 5.2: per token, the fewest
+ * channels whose cumulative saliency reaches p of the token's total). With
+ * key_tj as in spark_prefill_prune, w_tj = fl32(sqrt(key_tj)) (correctly
+ * rounded) and every sum over a token's D = 128 channels taken as the fp32
+ * pairwise tree that adds channel j + 64 to j, then j + 32, ..., j + 1:
+ * target = fl32(p * sum of all w); theta = the largest key value whose sum
+ * of w over {key >= theta} reaches the target; the token keeps the channels
+ * with key >= theta (ties at theta kept together; none if all w are 0).
+ *  p          in (0, 1] (the page uses 0.99), fp32
+ * Outputs (caller-allocated):
+ *  k_packed   bf16 [B][N_kv][S * D]: each head's region holds its tokens'
+ *             kept values back to back, token t at [row_off[t], row_off[t+1])
+ *             (ascending channel); the rest of the region is not written
+ *  row_off    int32 [B][N_kv][S + 1]: row offsets within the head's region,
+ *             row_off[0] = 0, row_off[S] = the head's kept total
+ *  mask, chan_energy, r, cnt   as for spark_prefill_prune (r for every
+ *             recovery mode; the pruned count of the score means is
+ *             S * D minus the kept total)
+ * Workspace: spark_prefill_workspace_bytes. Requires S * D < 2^31.
+ */
+int spark_prefill_prune_topp(const void* q_win, const void* k, int B, int S, int N_q, int N_kv, int D, float p,
+                             int window, int qagg, int recovery, float f_const, void* k_packed, int32_t* row_off,
+                             uint32_t* mask, float* chan_energy, float* r, int32_t* cnt, void* ws, size_t ws_bytes,
+                             void* stream);
+
+/*
  * SparK-g prefill pruning (walkthrough section 5.2: channels grouped by
  * importance, each group pruned at its own ratio, the least important
  * hardest). Per (b, KV head) the channels are ranked by the channel energy
@@ -197,6 +223,18 @@ int spark_decode_attn_sampled(const void* q, const void* k_packed, const uint32_
                               const float* chan_energy, const float* r, int recovery, uint64_t seed,
                               int B, int S, int N_q, int N_kv, int D, float lambda, float scale, int splits,
                               float* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * One decode step over a ragged pruned cache (spark_prefill_prune_topp):
+ * as spark_decode_attn with the kept values of token t at
+ * [row_off[t], row_off[t + 1]) of its head's region of S * D elements.
+ * mask and row_off must agree (the popcount of token t's mask equals
+ * row_off[t + 1] - row_off[t]); otherwise results are undefined but every
+ * read stays inside the head's region.
+ */
+int spark_decode_attn_ragged(const void* q, const void* k_packed, const int32_t* row_off, const uint32_t* mask,
+                             const void* v, const float* r, int B, int S, int N_q, int N_kv, int D, float scale,
+                             int splits, float* out, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * V-channel pruning (walkthrough section 4.4: V channels are pruned together

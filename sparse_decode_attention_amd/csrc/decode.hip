@@ -91,12 +91,14 @@ __host__ __device__ inline uint32_t finish_scratch_bytes(int G, int NT, int nspl
     return finish_own_offset(G, NT, nsplit) + (2u * G + (uint32_t)G * 128u) * 4u;
 }
 
-DecodeLayout decode_layout(int G, int T, int nsplit, bool sampled, int Tv) {
+DecodeLayout decode_layout(int G, int T, int nsplit, bool sampled, int Tv, bool ragged) {
     DecodeLayout L{};
     L.tab_stride = (uint32_t)tab_stride_for(G);
-    // sampled F: the q'_g ns_j table [128][G] follows the q'/r table
-    L.tab_bytes = 128u * L.tab_stride + (sampled ? 128u * (uint32_t)G * 4u : 0u);
-    L.padded = (T > 0 && T % 2 == 0 && (T / 2) % 2 == 0) ? 1u : 0u;
+    // 129 entries (the last one zero: the ragged score loop's filler), then,
+    // for the sampled F, the q'_g ns_j table [128][G]
+    L.tab_bytes = ((129u * L.tab_stride + 15u) & ~15u) + (sampled ? 128u * (uint32_t)G * 4u : 0u);
+    if (ragged) T = 128;      // sized for the longest row
+    L.padded = (!ragged && T > 0 && T % 2 == 0 && (T / 2) % 2 == 0) ? 1u : 0u;
     L.half_T = (uint32_t)(T / 2);
     L.magic = L.padded ? (uint32_t)((0x100000000ull + L.half_T - 1) / L.half_T) : 0u;
     if (L.padded) {
@@ -104,8 +106,9 @@ DecodeLayout decode_layout(int G, int T, int nsplit, bool sampled, int Tv) {
         L.stage_bytes = (uint32_t)DECODE_TILE * L.row_bytes;
     } else {
         L.row_bytes = (uint32_t)(2 * T);
-        // 64 rows plus up to 7 elements of 16-byte misalignment, in whole 16-byte chunks
-        L.stage_bytes = ((((uint32_t)DECODE_TILE * (uint32_t)T + 8u) * 2u) + 15u) & ~15u;
+        // 64 rows plus up to 7 elements of 16-byte misalignment, in whole 16-byte chunks;
+        // ragged rows: plus 256 bytes, as a short row's lane reads up to the longest row's length
+        L.stage_bytes = (((((uint32_t)DECODE_TILE * (uint32_t)T + 8u) * 2u) + 15u) & ~15u) + (ragged ? 256u : 0u);
     }
     L.list_bytes = (uint32_t)T * DECODE_TILE * 2u;
     L.list_bytes = (L.list_bytes + 15u) & ~15u;
@@ -221,6 +224,7 @@ struct TileMeta {
     size_t ea;       // first loaded element (multiple of 8)
     int shift;       // elements between ea and the tile's first element
     int nchunks;     // 16-byte chunks covering the tile
+    int loff;        // ragged rows: the lane's row start within the tile's elements
 };
 
 // One packed store: the K cache (packed keys and their masks) or, with V
@@ -257,6 +261,28 @@ __device__ __forceinline__ void issue_meta(const PackedSrc& p, int S, int bh, in
     }
     m.mw = make_uint4(0, 0, 0, 0);
     if (L < nt) m.mw = *reinterpret_cast<const uint4*>(p.mask + ((size_t)bh * S + t0 + L) * 4);
+}
+
+// Ragged rows (SparK-p): token t of head bh holds its kept values at
+// [row_off[t], row_off[t + 1]) of the head's region of S * 128 elements. The
+// tile's rows are contiguous; the chunk count is capped at the staging area.
+__device__ __forceinline__ void issue_meta_ragged(const DecodeArgs& a, int bh, int t0, int nt, int L, TileMeta& m) {
+    const int32_t* ro = a.row_off + (size_t)bh * (a.S + 1);
+    const int o0 = ro[t0], o1 = ro[t0 + nt];
+    const size_t e0 = (size_t)bh * a.S * 128 + (size_t)o0;
+    m.ea = e0 & ~(size_t)7;
+    m.shift = (int)(e0 - m.ea);
+    const long long n = o1 > o0 ? ((long long)(e0 - m.ea) + (o1 - o0) + 7) >> 3 : 0;
+    m.nchunks = (int)min(n, (long long)DECODE_RAGGED_CHUNKS);
+    m.loff = L < nt ? ro[t0 + L] - o0 : 0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        const int c = L + 64 * u;
+        m.pk[u] = make_uint4(0, 0, 0, 0);
+        if (c < m.nchunks) m.pk[u] = load_chunk(k_src(a), m.ea + (size_t)c * 8);
+    }
+    m.mw = make_uint4(0, 0, 0, 0);
+    if (L < nt) m.mw = *reinterpret_cast<const uint4*>(a.mask + ((size_t)bh * a.S + t0 + L) * 4);
 }
 
 // Write one 16-byte chunk c of the tile into the staged rows.
@@ -571,8 +597,12 @@ __device__ void finish_block(const DecodeArgs& a, float (&m_run)[G], float (&l_r
 //
 // VP: the V cache is packed too (V channels pruned): its rows and masks are
 // loaded one tile ahead like the keys', staged in LDS, and expanded in P.V.
-template <int G, int SMODE, bool VP>
-__global__ void __launch_bounds__(DECODE_THREADS) __attribute__((amdgpu_waves_per_eu(SMODE && G <= 4 ? 2 : 1)))
+//
+// RG: ragged packed rows (SparK-p): per-lane row starts and counts; the score
+// loop runs to the wave's longest row, shorter rows pointing their surplus
+// slots at a zero table entry and reading 0 for their values.
+template <int G, int SMODE, bool VP, bool RG>
+__global__ void __launch_bounds__(DECODE_THREADS) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 2 : 1)))
 decode_kernel(const DecodeArgs a) {
     constexpr bool SAMPLED = SMODE != 0;
     extern __shared__ __align__(16) unsigned char smem[];
@@ -588,15 +618,15 @@ decode_kernel(const DecodeArgs a) {
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int L = tid & 63;
-    const int S = a.S, T = a.T;
+    const int S = a.S, T = RG ? 128 : a.T;
     constexpr uint32_t TAB = (uint32_t)sizeof(TabEntry<G>);
-    const bool even_T = (T % 2) == 0;
+    const bool even_T = !RG && (T % 2) == 0;
 
     // ---- table of q' (q * scale * log2 e) and r per channel. Sampled F: r
     // holds (mu, sigma); a pruned key is w / a_j, a_j = sqrt(A_j), with the
     // sample w = mu + ns n: the table takes r_j = mu / a_j and, in a second
     // table, q'_g ns / a_j (ns = sigma for the Gaussian, mu for the Exponential)
-    float* qn = reinterpret_cast<float*>(tab + 128 * TAB);                 // [128][G], sampled F only
+    float* qn = reinterpret_cast<float*>(tab + ((129 * TAB + 15) & ~15u));   // [128][G], sampled F only
     for (int i = tid; i < 128 * G; i += DECODE_THREADS) {
         const int g = i >> 7, j = i & 127;
         const uint16_t qb = a.q[((size_t)b * a.N_q + (size_t)h * G + g) * 128 + j];
@@ -611,6 +641,7 @@ decode_kernel(const DecodeArgs a) {
         }
     }
     if (!SAMPLED && tid < 128) reinterpret_cast<TabEntry<G>*>(tab)[tid].r = a.r[(size_t)bh * 128 + tid];
+    if (tid < (int)(TAB / 4)) reinterpret_cast<float*>(tab + 128 * TAB)[tid] = 0.0f;     // the zero entry
 
     uint16_t* lst = reinterpret_cast<uint16_t*>(wbase + (size_t)wave * lay.wave_bytes);     // [T][64]
     unsigned char* stage = wbase + (size_t)wave * lay.wave_bytes + lay.list_bytes;
@@ -656,7 +687,8 @@ decode_kernel(const DecodeArgs a) {
     TileMeta meta, vmeta;
     if (wave < ntiles) {
         const int t0 = blk_begin + wave * DECODE_TILE;
-        issue_meta(k_src(a), S, bh, t0, min(DECODE_TILE, blk_end - t0), L, meta);
+        if (RG) issue_meta_ragged(a, bh, t0, min(DECODE_TILE, blk_end - t0), L, meta);
+        else issue_meta(k_src(a), S, bh, t0, min(DECODE_TILE, blk_end - t0), L, meta);
         if (VP) issue_meta(v_src(a), S, bh, t0, min(DECODE_TILE, blk_end - t0), L, vmeta);
     }
 
@@ -665,7 +697,7 @@ decode_kernel(const DecodeArgs a) {
         const int nt = min(DECODE_TILE, blk_end - t0);
 
         // -- 1. stage this tile's packed rows (loaded one tile ahead)
-        if (T > 0) {
+        if (RG || T > 0) {
             const int tile_dwords = (nt * T) >> 1;
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
@@ -676,19 +708,22 @@ decode_kernel(const DecodeArgs a) {
                 stage_chunk(lay, meta, c, load_chunk(k_src(a), meta.ea + (size_t)c * 8), stage, tile_dwords);
         }
         const uint4 mw = meta.mw;
-        const int row_base = (lay.padded ? 0 : 2 * meta.shift) + L * (int)lay.row_bytes;
+        const int row_base = RG ? 2 * (meta.shift + meta.loff)
+                                : (lay.padded ? 0 : 2 * meta.shift) + L * (int)lay.row_bytes;
 
         // -- V of this tile (dense V), then the next tile's packed keys and mask
         uint4 vr[16];
         if (!VP) load_v_tile(vbh, t0, nt, tau, oct, vr);
         if (tile + NW < ntiles) {
             const int t1 = t0 + NW * DECODE_TILE;
-            issue_meta(k_src(a), S, bh, t1, min(DECODE_TILE, blk_end - t1), L, meta);
+            if (RG) issue_meta_ragged(a, bh, t1, min(DECODE_TILE, blk_end - t1), L, meta);
+            else issue_meta(k_src(a), S, bh, t1, min(DECODE_TILE, blk_end - t1), L, meta);
         }
 
         // -- 2. list of kept channels (table byte offsets), slot-major [rho][lane]
+        int nslots = T;     // ragged rows: the wave's longest row
+        int cnt = 0;        // this lane's kept channels
         {
-            int cnt = 0;
             const uint32_t words[4] = {mw.x, mw.y, mw.z, mw.w};
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
@@ -699,6 +734,10 @@ decode_kernel(const DecodeArgs a) {
                     lst[cnt * 64 + L] = (uint16_t)(j * TAB);
                     ++cnt;
                 }
+            }
+            if (RG) {
+                nslots = (int)__builtin_amdgcn_readfirstlane((uint32_t)wave_max_dpp((float)cnt));
+                for (int rho = cnt; rho < nslots; ++rho) lst[rho * 64 + L] = (uint16_t)(128u * TAB);
             }
         }
         wave_lds_sync();
@@ -712,13 +751,19 @@ decode_kernel(const DecodeArgs a) {
         {
             const uint16_t* lrow = lst + L;
             const unsigned char* krow = stage + row_base;
-            const int T8 = T & ~7;
+            const int T8 = nslots & ~7;
             for (int rho = 0; rho < T8; rho += 8) {
                 uint32_t off[8];
 #pragma unroll
                 for (int k = 0; k < 8; ++k) off[k] = lrow[(rho + k) * 64];
                 float kv[8];
-                if (even_T) {
+                if (RG) {
+                    // slots past this lane's row read other rows or unwritten
+                    // memory: their values are replaced by 0 (q' is 0 there too)
+                    const uint16_t* k16 = reinterpret_cast<const uint16_t*>(krow + 2 * rho);
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) kv[k] = rho + k < cnt ? bf16_to_f32(k16[k]) : 0.0f;
+                } else if (even_T) {
                     // rows start 4-byte aligned when T is even: two bf16 per dword read
                     const uint32_t* k32 = reinterpret_cast<const uint32_t*>(krow + 2 * rho);
 #pragma unroll
@@ -741,10 +786,11 @@ decode_kernel(const DecodeArgs a) {
                     for (int g = 0; g < G; ++g) s[g] = fmaf(te.q[g], e, s[g]);
                 }
             }
-            for (int rho = T8; rho < T; ++rho) {
+            for (int rho = T8; rho < nslots; ++rho) {
                 const TabEntry<G>& te = *reinterpret_cast<const TabEntry<G>*>(
                     __builtin_assume_aligned(tab + lrow[rho * 64], 16));
-                const float e = bf16_to_f32(*reinterpret_cast<const uint16_t*>(krow + 2 * rho)) - te.r;
+                const float kx = bf16_to_f32(*reinterpret_cast<const uint16_t*>(krow + 2 * rho));
+                const float e = (RG && rho >= cnt ? 0.0f : kx) - te.r;
 #pragma unroll
                 for (int g = 0; g < G; ++g) s[g] = fmaf(te.q[g], e, s[g]);
             }
@@ -1148,15 +1194,15 @@ uint32_t decode_fast_lds_bytes(int G, int T, int nsplit) {
 bool decode_fast_supported(int G, int T) { return G == 4 && (T == 26 || T == 38 || T == 48 || T == 64); }
 
 
-template <int SMODE, bool VP>
+template <int SMODE, bool VP, bool RG>
 hipError_t launch_generic(const DecodeArgs& a, int G, dim3 grid, dim3 block, hipStream_t stream) {
     const size_t lds = a.lay.lds_bytes;
     const void* fn = nullptr;
     switch (G) {
-        case 1: fn = reinterpret_cast<const void*>(&decode_kernel<1, SMODE, VP>); break;
-        case 2: fn = reinterpret_cast<const void*>(&decode_kernel<2, SMODE, VP>); break;
-        case 4: fn = reinterpret_cast<const void*>(&decode_kernel<4, SMODE, VP>); break;
-        case 8: fn = reinterpret_cast<const void*>(&decode_kernel<8, SMODE, VP>); break;
+        case 1: fn = reinterpret_cast<const void*>(&decode_kernel<1, SMODE, VP, RG>); break;
+        case 2: fn = reinterpret_cast<const void*>(&decode_kernel<2, SMODE, VP, RG>); break;
+        case 4: fn = reinterpret_cast<const void*>(&decode_kernel<4, SMODE, VP, RG>); break;
+        case 8: fn = reinterpret_cast<const void*>(&decode_kernel<8, SMODE, VP, RG>); break;
         default: return hipErrorInvalidValue;
     }
     if (lds > 65536) {
@@ -1165,10 +1211,10 @@ hipError_t launch_generic(const DecodeArgs& a, int G, dim3 grid, dim3 block, hip
         if (e != hipSuccess) return e;
     }
     switch (G) {
-        case 1: hipLaunchKernelGGL((decode_kernel<1, SMODE, VP>), grid, block, lds, stream, a); break;
-        case 2: hipLaunchKernelGGL((decode_kernel<2, SMODE, VP>), grid, block, lds, stream, a); break;
-        case 4: hipLaunchKernelGGL((decode_kernel<4, SMODE, VP>), grid, block, lds, stream, a); break;
-        default: hipLaunchKernelGGL((decode_kernel<8, SMODE, VP>), grid, block, lds, stream, a); break;
+        case 1: hipLaunchKernelGGL((decode_kernel<1, SMODE, VP, RG>), grid, block, lds, stream, a); break;
+        case 2: hipLaunchKernelGGL((decode_kernel<2, SMODE, VP, RG>), grid, block, lds, stream, a); break;
+        case 4: hipLaunchKernelGGL((decode_kernel<4, SMODE, VP, RG>), grid, block, lds, stream, a); break;
+        default: hipLaunchKernelGGL((decode_kernel<8, SMODE, VP, RG>), grid, block, lds, stream, a); break;
     }
     return hipGetLastError();
 }
@@ -1177,7 +1223,8 @@ hipError_t launch_generic(const DecodeArgs& a, int G, dim3 grid, dim3 block, hip
 // The sampled F always takes the generic kernel.
 hipError_t launch_decode(const DecodeArgs& a, int G, int BH, hipStream_t stream) {
     const dim3 grid(a.nsplit, BH), block(DECODE_THREADS);
-    if (a.v_packed_mode) return launch_generic<0, true>(a, G, grid, block, stream);
+    if (a.row_off) return launch_generic<0, false, true>(a, G, grid, block, stream);
+    if (a.v_packed_mode) return launch_generic<0, true, false>(a, G, grid, block, stream);
     if (!a.sampled && decode_fast_supported(G, a.T)) {
         const dim3 fblock(DECODE_FAST_THREADS);
         // the fast kernel's LDS is static (DECODE_FAST_LDS_BYTES)
@@ -1191,9 +1238,9 @@ hipError_t launch_decode(const DecodeArgs& a, int G, int BH, hipStream_t stream)
         return hipGetLastError();
     }
     switch (a.sampled) {
-        case 0: return launch_generic<0, false>(a, G, grid, block, stream);
-        case 4: return launch_generic<4, false>(a, G, grid, block, stream);
-        case 5: return launch_generic<5, false>(a, G, grid, block, stream);
+        case 0: return launch_generic<0, false, false>(a, G, grid, block, stream);
+        case 4: return launch_generic<4, false, false>(a, G, grid, block, stream);
+        case 5: return launch_generic<5, false, false>(a, G, grid, block, stream);
         default: return hipErrorInvalidValue;
     }
 }

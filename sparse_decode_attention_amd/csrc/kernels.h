@@ -13,6 +13,7 @@
 #define DECODE_FAST_LDS_BYTES (2576 + (DECODE_FAST_THREADS / 64) * (8704 + 1024))
 #define DECODE_TILE 64
 #define DECODE_MAX_SPLITS 256
+#define DECODE_RAGGED_CHUNKS (DECODE_TILE * 128 * 2 / 16 + 1)   // 16-byte chunks of a tile of full rows, + misalignment
 #define DECODE_GENERIC_BLOCKS 512    // blocks the generic decode kernel aims for when splits = 0
 #define DECODE_LDS_PER_CU (160 * 1024)
 // window eviction: at most 128 stacked window rows (G * W), tokens per block
@@ -33,10 +34,14 @@ struct GroupSpec {
     int size;
     int T[SPARK_MAX_GROUPS];
 };
-template <bool GROUPED>
+template <int SEL>
 __global__ void select_pack_kernel(const uint16_t* k, const float* A, uint16_t* k_packed, uint32_t* mask,
                                    double* part_sum, int32_t* part_cnt, double* part_pruned,
-                                   int S, int T, int nblk, int recovery, const uint8_t* gid, GroupSpec grp);
+                                   int S, int T, int nblk, int recovery, const uint8_t* gid, GroupSpec grp,
+                                   float top_p, int32_t* tok_cnt, int32_t* blk_cnt);
+__global__ void topp_scan_kernel(int32_t* blk_cnt, int nblk);
+__global__ void topp_pack_kernel(const uint16_t* k, const uint32_t* mask, uint16_t* k_packed, int32_t* row_off,
+                                 const int32_t* blk_base, int S, int nblk);
 __global__ void channel_groups_kernel(const float* A, uint8_t* gid, int ngroups);
 __global__ void stats_partial_kernel(const uint16_t* k_packed, const uint32_t* mask, const uint16_t* k_dense,
                                      const float* A, double* part_sum, int32_t* part_cnt, double* part_pruned,
@@ -74,6 +79,8 @@ struct DecodeArgs {
     const uint16_t* v_packed; // [B][N_kv][S][Tv] (V channels pruned only)
     const uint32_t* v_mask;   // [B][N_kv][S][4]
     const float* rv;          // [B][N_kv][128] recovery of pruned V entries
+    const int32_t* row_off;   // ragged packed rows (SparK-p): [B][N_kv][S + 1] offsets within a head's
+                              // region of S * 128 elements of `packed`; null otherwise
     float* out;               // [B][N_q][128]
     float* part_ml;           // [B*N_kv][nsplit][2][G]
     float* part_acc;          // [B*N_kv][nsplit][G][128]
@@ -111,6 +118,6 @@ hipError_t launch_read_stream(const void* src, size_t bytes, uint32_t* sink, int
 // Launch the decode kernel for group size G; returns a hipError_t.
 hipError_t launch_decode(const DecodeArgs& a, int G, int BH, hipStream_t stream);
 bool decode_fast_supported(int G, int T);
-DecodeLayout decode_layout(int G, int T, int nsplit, bool sampled, int Tv);
+DecodeLayout decode_layout(int G, int T, int nsplit, bool sampled, int Tv, bool ragged = false);
 
 }  // namespace spark

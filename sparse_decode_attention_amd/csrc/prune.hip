@@ -92,19 +92,51 @@ __device__ __forceinline__ void select_top(uint32_t key0, uint32_t key1, bool in
     }
 }
 
-// GROUPED (SparK-g): channel c belongs to group gid[bh][c] (0..ngroups-1)
-// and each group keeps its own grp.T[i] members; T is their sum.
-template <bool GROUPED>
+// fp32 sum over the wave of each lane's x (= w_L + w_{L+64}): the pairwise
+// tree that folds lanes L + 32 onto L, then L + 16, ..., L + 1. Lane L and its
+// partner add the same two values, so every lane ends with the same sum.
+__device__ __forceinline__ float tree_sum_wave(float x) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) x = __fadd_rn(x, __shfl_xor(x, m, 64));
+    return x;
+}
+
+// SparK-p: with w = fl32(sqrt(key)) and target = fl32(p * total), the largest
+// theta whose tree sum of w over {key >= theta} reaches the target, decided
+// bit by bit from the top (the sum cannot rise as theta rises); keep
+// key >= theta. An all-zero row ends with theta = 2^31 - 1 and keeps nothing.
+__device__ __forceinline__ void select_top_p(uint32_t key0, uint32_t key1, float p, bool& kept0, bool& kept1) {
+    const float w0 = sqrtf(__uint_as_float(key0)), w1 = sqrtf(__uint_as_float(key1));
+    const float target = __fmul_rn(p, tree_sum_wave(__fadd_rn(w0, w1)));
+    uint32_t v = 0;
+    for (int bit = 30; bit >= 0; --bit) {
+        const uint32_t c = __builtin_amdgcn_readfirstlane(v | (1u << bit));
+        const float s = tree_sum_wave(__fadd_rn(key0 >= c ? w0 : 0.0f, key1 >= c ? w1 : 0.0f));
+        v = __builtin_amdgcn_readfirstlane(s >= target ? c : v);
+    }
+    kept0 = key0 >= v;
+    kept1 = key1 >= v;
+}
+
+// SEL: 0 top-T; 1 SparK-g, channel c in group gid[bh][c] (0..ngroups-1), each
+// group keeping its own grp.T[i] members (T is their sum); 2 SparK-p with
+// threshold fraction top_p: nothing is packed here (the rows are ragged); the
+// token counts go to tok_cnt[bh * (S + 1) + t] (row_off + 1: its count slots)
+// and the block totals to blk_cnt[bh][blk].
+template <int SEL>
 __global__ void __launch_bounds__(256)
 select_pack_kernel(const uint16_t* __restrict__ k, const float* __restrict__ A,
                    uint16_t* __restrict__ k_packed, uint32_t* __restrict__ mask,
                    double* __restrict__ part_sum, int32_t* __restrict__ part_cnt,
                    double* __restrict__ part_pruned,
-                   int S, int T, int nblk, int recovery, const uint8_t* __restrict__ gid, GroupSpec grp) {
+                   int S, int T, int nblk, int recovery, const uint8_t* __restrict__ gid, GroupSpec grp,
+                   float top_p, int32_t* __restrict__ tok_cnt, int32_t* __restrict__ blk_cnt) {
+    constexpr bool GROUPED = SEL == 1;
     __shared__ uint4 stage[4][64];            // 4 tokens x 256 B per wave
     __shared__ double red_sum[4][128];
     __shared__ int red_cnt[4][128];
     __shared__ double red_pr[4][2];
+    __shared__ int red_tok[4];
 
     const int bh = blockIdx.y;
     const int blk = blockIdx.x;
@@ -124,7 +156,8 @@ select_pack_kernel(const uint16_t* __restrict__ k, const float* __restrict__ A,
     int cnt0 = 0, cnt1 = 0;
 
     const uint16_t* kbh = k + (size_t)bh * S * 128;
-    uint16_t* pbh = k_packed ? k_packed + (size_t)bh * S * T : nullptr;
+    uint16_t* pbh = (SEL != 2 && k_packed) ? k_packed + (size_t)bh * S * T : nullptr;
+    int kept_tokens = 0;     // SEL 2: channels kept by this wave's tokens
     uint32_t* mbh = mask + (size_t)bh * S * 4;
     uint16_t* st = reinterpret_cast<uint16_t*>(&stage[wave][0]);
 
@@ -145,7 +178,9 @@ select_pack_kernel(const uint16_t* __restrict__ k, const float* __restrict__ A,
             const uint32_t key0 = __float_as_uint(__fmul_rn(A0, __fmul_rn(k0, k0)));
             const uint32_t key1 = __float_as_uint(__fmul_rn(A1, __fmul_rn(k1, k1)));
             bool kept0 = false, kept1 = false;
-            if (!GROUPED) {
+            if (SEL == 2) {
+                select_top_p(key0, key1, top_p, kept0, kept1);
+            } else if (!GROUPED) {
                 if (T >= 128) {
                     kept0 = kept1 = true;
                 } else if (T > 0) {
@@ -171,8 +206,14 @@ select_pack_kernel(const uint16_t* __restrict__ k, const float* __restrict__ A,
                 *reinterpret_cast<uint4*>(mbh + (size_t)t * 4) =
                     make_uint4((uint32_t)m0, (uint32_t)(m0 >> 32), (uint32_t)m1, (uint32_t)(m1 >> 32));
             }
-            if (kept0) pbh[(size_t)t * T + mbcnt(m0)] = kb0;
-            if (kept1) pbh[(size_t)t * T + __popcll(m0) + mbcnt(m1)] = kb1;
+            if (SEL == 2) {
+                const int n = __popcll(m0) + __popcll(m1);
+                if (L == 0) tok_cnt[(size_t)bh * (S + 1) + t] = n;    // row_off[bh][t + 1]
+                kept_tokens += n;
+            } else {
+                if (kept0) pbh[(size_t)t * T + mbcnt(m0)] = kb0;
+                if (kept1) pbh[(size_t)t * T + __popcll(m0) + mbcnt(m1)] = kb1;
+            }
             if (recovery == 0) {
                 if (kept0) { sum0 += (double)k0; ++cnt0; }
                 if (kept1) { sum1 += (double)k1; ++cnt1; }
@@ -191,6 +232,7 @@ select_pack_kernel(const uint16_t* __restrict__ k, const float* __restrict__ A,
     }
 
     // fixed-order combination of the 4 waves, then one partial per block
+    if (SEL == 2 && L == 0) red_tok[wave] = kept_tokens;
     red_sum[wave][L] = sum0;
     red_sum[wave][64 + L] = sum1;
     red_cnt[wave][L] = cnt0;
@@ -212,13 +254,85 @@ select_pack_kernel(const uint16_t* __restrict__ k, const float* __restrict__ A,
         part_cnt[((size_t)bh * nblk + blk) * 128 + j] = c;
         if (j < 2) part_pruned[((size_t)bh * nblk + blk) * 2 + j] =
             (recovery >= 3) ? ((red_pr[0][j] + red_pr[1][j]) + red_pr[2][j]) + red_pr[3][j] : 0.0;
+        if (SEL == 2 && j == 0) blk_cnt[(size_t)bh * nblk + blk] = red_tok[0] + red_tok[1] + red_tok[2] + red_tok[3];
     }
 }
 
-template __global__ void select_pack_kernel<false>(const uint16_t*, const float*, uint16_t*, uint32_t*, double*,
-                                                   int32_t*, double*, int, int, int, int, const uint8_t*, GroupSpec);
-template __global__ void select_pack_kernel<true>(const uint16_t*, const float*, uint16_t*, uint32_t*, double*,
-                                                  int32_t*, double*, int, int, int, int, const uint8_t*, GroupSpec);
+template __global__ void select_pack_kernel<0>(const uint16_t*, const float*, uint16_t*, uint32_t*, double*, int32_t*,
+                                               double*, int, int, int, int, const uint8_t*, GroupSpec, float, int32_t*,
+                                               int32_t*);
+template __global__ void select_pack_kernel<1>(const uint16_t*, const float*, uint16_t*, uint32_t*, double*, int32_t*,
+                                               double*, int, int, int, int, const uint8_t*, GroupSpec, float, int32_t*,
+                                               int32_t*);
+template __global__ void select_pack_kernel<2>(const uint16_t*, const float*, uint16_t*, uint32_t*, double*, int32_t*,
+                                               double*, int, int, int, int, const uint8_t*, GroupSpec, float, int32_t*,
+                                               int32_t*);
+
+// ---------------------------------------------------------------- SparK-p ragged packing
+// One wave per (b, KV head): exclusive scan of the block totals in place
+// (blk_cnt becomes each block's first element offset within the head).
+__global__ void __launch_bounds__(64)
+topp_scan_kernel(int32_t* __restrict__ blk_cnt, int nblk) {
+    const int bh = blockIdx.x, L = threadIdx.x;
+    int32_t* c = blk_cnt + (size_t)bh * nblk;
+    const int per = (nblk + 63) / 64, lo = min(nblk, L * per), hi = min(nblk, lo + per);
+    int local = 0;
+    for (int i = lo; i < hi; ++i) local += c[i];
+    int incl = local;
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o, 64);
+        if (L >= o) incl += y;
+    }
+    int run = incl - local;
+    for (int i = lo; i < hi; ++i) {
+        const int x = c[i];
+        c[i] = run;
+        run += x;
+    }
+}
+
+// Grid (nblk, B*N_kv), 256 threads: turns the block's token counts (written
+// by the select kernel into row_off[t + 1]) into offsets within the head,
+// row_off[t + 1] = blk_base + inclusive prefix, and packs each token's kept
+// values (ascending channel) at row_off[t] of the head's region (S * 128
+// elements per head).
+__global__ void __launch_bounds__(256)
+topp_pack_kernel(const uint16_t* __restrict__ k, const uint32_t* __restrict__ mask, uint16_t* __restrict__ k_packed,
+                 int32_t* __restrict__ row_off, const int32_t* __restrict__ blk_base, int S, int nblk) {
+    __shared__ int off[PRUNE_TOKENS_PER_BLOCK + 1];
+    const int bh = blockIdx.y, blk = blockIdx.x;
+    const int t_begin = blk * PRUNE_TOKENS_PER_BLOCK;
+    const int nt = min(PRUNE_TOKENS_PER_BLOCK, S - t_begin);
+    int32_t* ro = row_off + (size_t)bh * (S + 1);
+    if (threadIdx.x < 64) {
+        const int L = threadIdx.x;
+        const int n = L < nt ? ro[t_begin + L + 1] : 0;
+        int incl = n;
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(incl, o, 64);
+            if (L >= o) incl += y;
+        }
+        const int base = blk_base[(size_t)bh * nblk + blk];
+        off[L + 1] = base + incl;
+        if (L == 0) off[0] = base;
+    }
+    __syncthreads();
+    if (threadIdx.x < nt) ro[t_begin + threadIdx.x + 1] = off[threadIdx.x + 1];
+    if (blk == 0 && threadIdx.x == 0) ro[0] = 0;
+    const int wave = threadIdx.x >> 6, L = threadIdx.x & 63;
+    const uint16_t* kbh = k + (size_t)bh * S * 128;
+    uint16_t* pbh = k_packed + (size_t)bh * S * 128;
+    for (int i = wave; i < nt; i += 4) {
+        const int t = t_begin + i;
+        const uint4 mw = *reinterpret_cast<const uint4*>(mask + ((size_t)bh * S + t) * 4);
+        const uint64_t m0 = ((uint64_t)mw.y << 32) | mw.x, m1 = ((uint64_t)mw.w << 32) | mw.z;
+        const bool kept0 = (m0 >> L) & 1, kept1 = (m1 >> L) & 1;
+        // ranks are bounded by the row's count (the mask's popcount), so the
+        // writes stay in [row_off[t], row_off[t + 1])
+        if (kept0) pbh[off[i] + (int)mbcnt(m0)] = kbh[(size_t)t * 128 + L];
+        if (kept1) pbh[off[i] + __popcll(m0) + (int)mbcnt(m1)] = kbh[(size_t)t * 128 + 64 + L];
+    }
+}
 
 // ---------------------------------------------------------------- SparK-g channel groups
 // One block per (b, KV head), one thread per channel: rank by A descending
@@ -310,6 +424,7 @@ stats_reduce_kernel(const double* __restrict__ part_sum, const int32_t* __restri
     __shared__ double sh_s[STATS_PARTS][128];
     __shared__ long long sh_c[STATS_PARTS][128];
     __shared__ double sh_p[STATS_PARTS][2];
+    __shared__ long long sh_tot[128];
     const int bh = blockIdx.x, j = threadIdx.x & 127, part = threadIdx.x >> 7;
     const int per = (nblk + STATS_PARTS - 1) / STATS_PARTS;
     const int lo = part * per, hi = min(nblk, lo + per);
@@ -327,10 +442,18 @@ stats_reduce_kernel(const double* __restrict__ part_sum, const int32_t* __restri
     sh_s[part][j] = s;
     sh_c[part][j] = c;
     __syncthreads();
-    if (part != 0) return;
     s = 0.0;
     c = 0;
     for (int q = 0; q < STATS_PARTS; ++q) { s += sh_s[q][j]; c += sh_c[q][j]; }
+    // ragged rows (T < 0): the pruned count is S * 128 minus all kept entries
+    if (part == 0) sh_tot[j] = c;
+    __syncthreads();
+    if (part != 0) return;
+    long long kept_all = (long long)S * (T < 0 ? 0 : T);
+    if (T < 0) {
+        kept_all = 0;
+        for (int q = 0; q < 128; ++q) kept_all += sh_tot[q];
+    }
     float out = 0.f;
     if (recovery == 0) {
         out = c > 0 ? (float)(s / (double)c) : 0.f;
@@ -340,7 +463,7 @@ stats_reduce_kernel(const double* __restrict__ part_sum, const int32_t* __restri
         double p2 = 0.0;
         p = 0.0;
         for (int q = 0; q < STATS_PARTS; ++q) { p += sh_p[q][0]; p2 += sh_p[q][1]; }
-        const double npruned = (double)S * (double)(128 - T);
+        const double npruned = (double)S * 128.0 - (double)kept_all;
         const double mu = npruned > 0 ? p / npruned : 0.0;
         if (recovery == 3) {
             const double a = sqrt((double)A[(size_t)bh * 128 + j]);

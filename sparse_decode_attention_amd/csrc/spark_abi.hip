@@ -27,12 +27,13 @@ int check_group(int N_q, int N_kv) {
 
 // prefill workspace: part_sum double [BH][nblk][128] | part_cnt int32 [BH][nblk][128] |
 // part_pruned double [BH][nblk][2] (sum of the pruned saliency, sum of its squares) |
-// gid uint8 [BH][128] (SparK-g channel groups)
+// gid uint8 [BH][128] (SparK-g channel groups) | blk int32 [BH][nblk] (SparK-p block totals, then bases)
 struct PrefillWs {
     double* sum;
     int32_t* cnt;
     double* pruned;
     uint8_t* gid;
+    int32_t* blk;
     size_t bytes;
     int nblk;
 };
@@ -50,7 +51,9 @@ PrefillWs prefill_layout(void* ws, int B, int S, int N_kv) {
     w.cnt = reinterpret_cast<int32_t*>(base + s_sum);
     w.pruned = reinterpret_cast<double*>(base + s_sum + s_cnt);
     w.gid = reinterpret_cast<uint8_t*>(base + s_sum + s_cnt + s_pr);
-    w.bytes = s_sum + s_cnt + s_pr + round_up(BH * 128, 256);
+    const size_t s_gid = round_up(BH * 128, 256);
+    w.blk = reinterpret_cast<int32_t*>(base + s_sum + s_cnt + s_pr + s_gid);
+    w.bytes = s_sum + s_cnt + s_pr + s_gid + round_up(n * sizeof(int32_t), 256);
     return w;
 }
 
@@ -148,10 +151,10 @@ int spark_prefill_prune(const void* q_win, const void* k, int B, int S, int N_q,
     const int BH = B * N_kv;
     hipLaunchKernelGGL(chan_energy_kernel, dim3(BH), dim3(256), 0, st,
                        static_cast<const uint16_t*>(q_win), chan_energy, N_q, N_kv, window, qagg);
-    hipLaunchKernelGGL(select_pack_kernel<false>, dim3(w.nblk, BH), dim3(256), 0, st,
+    hipLaunchKernelGGL(select_pack_kernel<0>, dim3(w.nblk, BH), dim3(256), 0, st,
                        static_cast<const uint16_t*>(k), chan_energy, static_cast<uint16_t*>(k_packed), mask,
                        w.sum, w.cnt, w.pruned, S, T, w.nblk, recovery, static_cast<const uint8_t*>(nullptr),
-                       GroupSpec{});
+                       GroupSpec{}, 0.0f, static_cast<int32_t*>(nullptr), static_cast<int32_t*>(nullptr));
     hipLaunchKernelGGL(stats_reduce_kernel, dim3(BH), dim3(128 * STATS_PARTS), 0, st,
                        w.sum, w.cnt, w.pruned, chan_energy, r, cnt, S, T, w.nblk, recovery, f_const);
     return hip_status(hipGetLastError());
@@ -171,10 +174,11 @@ int spark_prefill_prune_v(const void* v, int B, int S, int N_kv, int D, float la
     if (ws_bytes < w.bytes) return SPARK_ENOSPACE;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int BH = B * N_kv;
-    hipLaunchKernelGGL(select_pack_kernel<false>, dim3(w.nblk, BH), dim3(256), 0, st,
+    hipLaunchKernelGGL(select_pack_kernel<0>, dim3(w.nblk, BH), dim3(256), 0, st,
                        static_cast<const uint16_t*>(v), static_cast<const float*>(nullptr),
                        static_cast<uint16_t*>(v_packed), v_mask, w.sum, w.cnt, w.pruned, S, T, w.nblk,
-                       (int)SPARK_F_MEAN_RETAINED, static_cast<const uint8_t*>(nullptr), GroupSpec{});
+                       (int)SPARK_F_MEAN_RETAINED, static_cast<const uint8_t*>(nullptr), GroupSpec{}, 0.0f,
+                       static_cast<int32_t*>(nullptr), static_cast<int32_t*>(nullptr));
     hipLaunchKernelGGL(stats_reduce_kernel, dim3(BH), dim3(128 * STATS_PARTS), 0, st, w.sum, w.cnt, w.pruned,
                        static_cast<const float*>(nullptr), r_v, cnt, S, T, w.nblk, (int)SPARK_F_MEAN_RETAINED, 0.0f);
     return hip_status(hipGetLastError());
@@ -208,12 +212,49 @@ int spark_prefill_prune_grouped(const void* q_win, const void* k, int B, int S, 
                        static_cast<const uint16_t*>(q_win), chan_energy, N_q, N_kv, window, qagg);
     hipLaunchKernelGGL(channel_groups_kernel, dim3(BH), dim3(128), 0, st, static_cast<const float*>(chan_energy),
                        w.gid, ngroups);
-    hipLaunchKernelGGL(select_pack_kernel<true>, dim3(w.nblk, BH), dim3(256), 0, st,
+    hipLaunchKernelGGL(select_pack_kernel<1>, dim3(w.nblk, BH), dim3(256), 0, st,
                        static_cast<const uint16_t*>(k), static_cast<const float*>(chan_energy),
                        static_cast<uint16_t*>(k_packed), mask, w.sum, w.cnt, w.pruned, S, T, w.nblk, recovery,
-                       static_cast<const uint8_t*>(w.gid), grp);
+                       static_cast<const uint8_t*>(w.gid), grp, 0.0f, static_cast<int32_t*>(nullptr),
+                       static_cast<int32_t*>(nullptr));
     hipLaunchKernelGGL(stats_reduce_kernel, dim3(BH), dim3(128 * STATS_PARTS), 0, st,
                        w.sum, w.cnt, w.pruned, chan_energy, r, cnt, S, T, w.nblk, recovery, f_const);
+    return hip_status(hipGetLastError());
+}
+
+int spark_prefill_prune_topp(const void* q_win, const void* k, int B, int S, int N_q, int N_kv, int D, float p,
+                             int window, int qagg, int recovery, float f_const, void* k_packed, int32_t* row_off,
+                             uint32_t* mask, float* chan_energy, float* r, int32_t* cnt, void* ws, size_t ws_bytes,
+                             void* stream) {
+    if (B < 1 || S < 1 || D < 1 || window < 1) return SPARK_EINVAL;
+    if (!(p > 0.0f && p <= 1.0f)) return SPARK_EINVAL;
+    if (qagg != SPARK_QAGG_L2 && qagg != SPARK_QAGG_MEAN) return SPARK_EINVAL;
+    if (recovery < SPARK_F_MEAN_RETAINED || recovery > SPARK_F_EXPONENTIAL) return SPARK_EINVAL;
+    if (int e = check_group(N_q, N_kv)) return e;
+    if (D != 128) return SPARK_EUNSUPPORTED;
+    if ((size_t)S * 128 > (size_t)INT32_MAX) return SPARK_EUNSUPPORTED;
+    if (!q_win || !k || !k_packed || !row_off || !mask || !chan_energy || !r || !ws) return SPARK_EINVAL;
+    if (!aligned(q_win, 16) || !aligned(k, 16) || !aligned(mask, 16) || !aligned(chan_energy, 16) ||
+        !aligned(r, 16) || !aligned(k_packed, 16) || !aligned(row_off, 4) || (cnt && !aligned(cnt, 16)) ||
+        !aligned(ws, 256))
+        return SPARK_EALIGN;
+    const PrefillWs w = prefill_layout(ws, B, S, N_kv);
+    if (ws_bytes < w.bytes) return SPARK_ENOSPACE;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int BH = B * N_kv;
+    // per-token counts go to row_off[t + 1] (as offsets of a (S + 1)-long row per head)
+    hipLaunchKernelGGL(chan_energy_kernel, dim3(BH), dim3(256), 0, st,
+                       static_cast<const uint16_t*>(q_win), chan_energy, N_q, N_kv, window, qagg);
+    hipLaunchKernelGGL(select_pack_kernel<2>, dim3(w.nblk, BH), dim3(256), 0, st, static_cast<const uint16_t*>(k),
+                       static_cast<const float*>(chan_energy), static_cast<uint16_t*>(nullptr), mask, w.sum, w.cnt,
+                       w.pruned, S, -1, w.nblk, recovery, static_cast<const uint8_t*>(nullptr), GroupSpec{}, p,
+                       row_off + 1, w.blk);
+    hipLaunchKernelGGL(topp_scan_kernel, dim3(BH), dim3(64), 0, st, w.blk, w.nblk);
+    hipLaunchKernelGGL(topp_pack_kernel, dim3(w.nblk, BH), dim3(256), 0, st, static_cast<const uint16_t*>(k),
+                       static_cast<const uint32_t*>(mask), static_cast<uint16_t*>(k_packed), row_off,
+                       static_cast<const int32_t*>(w.blk), S, w.nblk);
+    hipLaunchKernelGGL(stats_reduce_kernel, dim3(BH), dim3(128 * STATS_PARTS), 0, st,
+                       w.sum, w.cnt, w.pruned, chan_energy, r, cnt, S, -1, w.nblk, recovery, f_const);
     return hip_status(hipGetLastError());
 }
 
@@ -261,7 +302,7 @@ struct PackedV {
 int decode_call(const void* q, const void* k_packed, const uint32_t* mask, const void* v, const float* r,
                 const float* A, int sampled, uint64_t seed, int B, int S, int N_q, int N_kv, int D, float lambda,
                 float scale, int splits, float* out, void* ws, size_t ws_bytes, void* stream,
-                const PackedV* vp = nullptr) {
+                const PackedV* vp = nullptr, const int32_t* row_off = nullptr) {
     if (B < 1 || S < 1 || D < 1 || splits < 0) return SPARK_EINVAL;
     const int T = kept_or_neg(D, lambda);
     if (T < 0) return SPARK_EINVAL;
@@ -283,9 +324,11 @@ int decode_call(const void* q, const void* k_packed, const uint32_t* mask, const
     int nsplit, chunk;
     // the fast kernel (8 waves, one block per CU) aims for 256 blocks; the
     // generic kernel (4 waves) for 512, two per CU, when two fit in LDS
-    const bool generic = vp || sampled || !decode_fast_supported(G, T);
+    const bool ragged = row_off != nullptr;
+    const bool generic = vp || sampled || ragged || !decode_fast_supported(G, T);
     decode_plan(BH, S, splits, &nsplit, &chunk, generic ? DECODE_GENERIC_BLOCKS : 256);
-    if (generic && splits == 0 && decode_layout(G, T, nsplit, sampled != 0, Tv).lds_bytes > DECODE_LDS_PER_CU / 2)
+    if (generic && splits == 0 &&
+        decode_layout(G, T, nsplit, sampled != 0, Tv, ragged).lds_bytes > DECODE_LDS_PER_CU / 2)
         decode_plan(BH, S, splits, &nsplit, &chunk, 256);
     if (ws_bytes < decode_ws_bytes(BH, G, nsplit)) return SPARK_ENOSPACE;
 
@@ -310,7 +353,8 @@ int decode_call(const void* q, const void* k_packed, const uint32_t* mask, const
     a.part_ml = reinterpret_cast<float*>(base + SPARK_DECODE_COUNTER_BYTES);
     a.part_acc = reinterpret_cast<float*>(base + SPARK_DECODE_COUNTER_BYTES +
                                           round_up((size_t)BH * nsplit * 2 * G * sizeof(float), 256));
-    a.packed_elems = (size_t)BH * S * T;
+    a.packed_elems = (size_t)BH * S * (ragged ? 128 : T);
+    a.row_off = row_off;
     a.S = S;
     a.T = T;
     a.N_q = N_q;
@@ -322,7 +366,7 @@ int decode_call(const void* q, const void* k_packed, const uint32_t* mask, const
     a.sampled = sampled;
     a.seed_lo = (uint32_t)seed;
     a.seed_hi = (uint32_t)(seed >> 32);
-    a.lay = decode_layout(G, T, nsplit, sampled != 0, Tv);
+    a.lay = decode_layout(G, T, nsplit, sampled != 0, Tv, ragged);
     return hip_status(launch_decode(a, G, BH, static_cast<hipStream_t>(stream)));
 }
 
@@ -335,6 +379,16 @@ int spark_decode_attn(const void* q, const void* k_packed, const uint32_t* mask,
                       float* out, void* ws, size_t ws_bytes, void* stream) {
     return decode_call(q, k_packed, mask, v, r, nullptr, 0, 0, B, S, N_q, N_kv, D, lambda, scale, splits, out, ws,
                        ws_bytes, stream);
+}
+
+int spark_decode_attn_ragged(const void* q, const void* k_packed, const int32_t* row_off, const uint32_t* mask,
+                             const void* v, const float* r, int B, int S, int N_q, int N_kv, int D, float scale,
+                             int splits, float* out, void* ws, size_t ws_bytes, void* stream) {
+    if (!k_packed || !row_off) return SPARK_EINVAL;
+    if (!aligned(row_off, 4)) return SPARK_EALIGN;
+    if ((size_t)S * 128 > (size_t)INT32_MAX) return SPARK_EUNSUPPORTED;
+    return decode_call(q, k_packed, mask, v, r, nullptr, 0, 0, B, S, N_q, N_kv, D, 0.0f, scale, splits, out, ws,
+                       ws_bytes, stream, nullptr, row_off);
 }
 
 int spark_decode_attn_kv(const void* q, const void* k_packed, const uint32_t* k_mask, const float* r,

@@ -40,6 +40,9 @@ _SIGS = {
                                        _vp, _vp, _sz, _vp]),
     "spark_prefill_prune_v": (_i, [_vp, _i, _i, _i, _i, _f, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "spark_num_kept_grouped": (_i, [_i, _i, ctypes.POINTER(ctypes.c_float)]),
+    "spark_prefill_prune_topp": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _f, _i, _i, _i, _f, _vp, _vp, _vp, _vp, _vp, _vp,
+                                      _vp, _sz, _vp]),
+    "spark_decode_attn_ragged": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _vp, _sz, _vp]),
     "spark_prefill_prune_grouped": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, ctypes.POINTER(ctypes.c_float), _i, _i,
                                          _i, _f, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "spark_decode_attn_kv": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _f, _f, _i,
@@ -193,6 +196,53 @@ def prefill_prune_grouped(q_win: torch.Tensor, k: torch.Tensor, n_kv: int, ratio
     o["T"] = T
     o["lam"] = 1.0 - T / D
     return o
+
+
+def prefill_prune_topp(q_win: torch.Tensor, k: torch.Tensor, n_kv: int, p: float = 0.99, qagg: str = "l2",
+                       recovery: str = "mean_retained", f_const: float = 0.01, out: dict | None = None) -> dict:
+    """spark_prefill_prune_topp (SparK-p): ragged packed rows.
+
+    Returns {"k_packed" bf16 [B][N_kv][S*D] (each head's region), "row_off"
+    int32 [B][N_kv][S+1], "mask", "chan_energy", "r", "cnt"}.
+    """
+    B, N_q, W, D = q_win.shape
+    S = k.shape[2]
+    _need(q_win, "q_win", torch.bfloat16)
+    _need(k, "k", torch.bfloat16, (B, n_kv, S, D))
+    dev = k.device
+    o = dict(out or {})
+    o.setdefault("k_packed", torch.empty((B, n_kv, S * D), dtype=torch.bfloat16, device=dev))
+    o.setdefault("row_off", torch.empty((B, n_kv, S + 1), dtype=torch.int32, device=dev))
+    o.setdefault("mask", torch.empty((B, n_kv, S, (D + 31) // 32), dtype=torch.int32, device=dev))
+    o.setdefault("chan_energy", torch.empty((B, n_kv, D), dtype=torch.float32, device=dev))
+    o.setdefault("r", torch.empty((B, n_kv, D), dtype=torch.float32, device=dev))
+    o.setdefault("cnt", torch.empty((B, n_kv, D), dtype=torch.int32, device=dev))
+    ws = workspace(dev, "prefill", lib().spark_prefill_workspace_bytes(B, S, n_kv, D))
+    st = lib().spark_prefill_prune_topp(_ptr(q_win), _ptr(k), B, S, N_q, n_kv, D, float(p), W, QAGG[qagg],
+                                        RECOVERY[recovery], float(f_const), _ptr(o["k_packed"]), _ptr(o["row_off"]),
+                                        _ptr(o["mask"]), _ptr(o["chan_energy"]), _ptr(o["r"]), _ptr(o["cnt"]),
+                                        _ptr(ws), ws.numel(), _stream(dev))
+    _check("spark_prefill_prune_topp", st)
+    return o
+
+
+def decode_attn_ragged(q, k_packed, row_off, mask, v, r, scale: float = 0.0, splits: int = 0, out=None, ws=None):
+    """spark_decode_attn_ragged: decode over a SparK-p cache."""
+    B, N_q, D = q.shape
+    n_kv, S = v.shape[1], v.shape[2]
+    _need(q, "q", torch.bfloat16)
+    _need(v, "v", torch.bfloat16, (B, n_kv, S, D))
+    _need(row_off, "row_off", torch.int32, (B, n_kv, S + 1))
+    _need(k_packed, "k_packed", torch.bfloat16, (B, n_kv, S * D))
+    dev = q.device
+    out = torch.empty((B, N_q, D), dtype=torch.float32, device=dev) if out is None else out
+    if ws is None:
+        ws = workspace(dev, "decode", decode_ws_bytes(B, S, N_q, n_kv, D, splits))
+    st = lib().spark_decode_attn_ragged(_ptr(q), _ptr(k_packed), _ptr(row_off), _ptr(mask), _ptr(v), _ptr(r), B, S,
+                                        N_q, n_kv, D, float(scale), int(splits), _ptr(out), _ptr(ws), ws.numel(),
+                                        _stream(dev))
+    _check("spark_decode_attn_ragged", st)
+    return out
 
 
 def stats(k_packed, mask, chan_energy, lam: float, recovery: str = "mean_retained", f_const: float = 0.01,

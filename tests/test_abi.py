@@ -188,6 +188,40 @@ def test_prefill_grouped_rejects_bad_arguments():
     assert call() == ops.ENOSPACE
 
 
+def test_topp_entry_points_reject_bad_arguments():
+    l = ops.lib()
+
+    def pre(**kw):
+        a = dict(q_win=FAKE, k=FAKE, B=1, S=64, N_q=32, N_kv=8, D=128, p=0.99, W=4, qagg=0, rec=0, fc=0.01,
+                 kp=FAKE, ro=FAKE, mask=FAKE, A=FAKE, r=FAKE, cnt=None, ws=FAKE, nws=0)
+        a.update(kw)
+        return l.spark_prefill_prune_topp(a["q_win"], a["k"], a["B"], a["S"], a["N_q"], a["N_kv"], a["D"], a["p"],
+                                          a["W"], a["qagg"], a["rec"], a["fc"], a["kp"], a["ro"], a["mask"], a["A"],
+                                          a["r"], a["cnt"], a["ws"], a["nws"], None)
+    assert pre(p=0.0) == ops.EINVAL
+    assert pre(p=1.5) == ops.EINVAL
+    assert pre(p=float("nan")) == ops.EINVAL
+    assert pre(ro=None) == ops.EINVAL
+    assert pre(kp=None) == ops.EINVAL
+    assert pre(ro=FAKE + 2) == ops.EALIGN
+    assert pre(D=64) == ops.EUNSUPPORTED
+    assert pre() == ops.ENOSPACE
+
+    def dec(**kw):
+        a = dict(q=FAKE, kp=FAKE, ro=FAKE, mask=FAKE, v=FAKE, r=FAKE, B=1, S=64, N_q=32, N_kv=8, D=128, scale=0.0,
+                 splits=0, out=FAKE, ws=FAKE, nws=0)
+        a.update(kw)
+        return l.spark_decode_attn_ragged(a["q"], a["kp"], a["ro"], a["mask"], a["v"], a["r"], a["B"], a["S"],
+                                          a["N_q"], a["N_kv"], a["D"], a["scale"], a["splits"], a["out"], a["ws"],
+                                          a["nws"], None)
+    assert dec(ro=None) == ops.EINVAL
+    assert dec(kp=None) == ops.EINVAL
+    assert dec(ro=FAKE + 1) == ops.EALIGN
+    assert dec(v=None) == ops.EINVAL
+    assert dec(N_q=24) == ops.EUNSUPPORTED
+    assert dec() == ops.ENOSPACE
+
+
 def test_stats_rejects_bad_arguments():
     l = ops.lib()
 
