@@ -6,4 +6,4 @@ from .spark_oracle import (num_kept, chan_energy, saliency_keys, select_top_t, m
                            uniform01, recovery_samples, expand_keys_sampled, decode_attn_sampled,
                            value_keys, prune_v, decode_attn_kv, channel_groups,
                            grouped_num_kept, select_grouped, prune_grouped, tree_sum32,
-                           select_top_p, prune_topp)
+                           select_top_p, prune_topp, append_tokens, grow_cache)

@@ -33,6 +33,8 @@ Readings of points the pages leave open (each is listed in the design doc):
     walkthrough's Degenerate F (section 3.3, F table) is "score_mean_pruned".
   * Decode: one new query per head attends to all S cached tokens (no causal
     mask), scale 1/sqrt(D), recovery only in the scores, V dense.
+  * Cache growth (silent on the pages): generated keys are pruned with the
+    prefill's A by the prefill's rule and appended; V dense; r fixed.
   * SparK-p (section 5.2): per token the fewest channels reaching p of the
     total saliency, decided in fp32 with a fixed pairwise summation tree;
     ties at the threshold kept together; ragged packed rows.
@@ -363,6 +365,27 @@ def decode_attn_sampled(q, packed, mask, v, A, r, mode: str, seed: int, scale: f
     D = mask.shape[-1]
     scale = 1.0 / math.sqrt(D) if scale is None or scale <= 0 else float(scale)
     return _attend(q, expand_keys_sampled(packed, mask, A, r, mode, seed), v, scale)
+
+
+# ---------------------------------------------------------------- decode-time cache growth
+#
+# The pages prune only at prefill. Reading taken here: every generated
+# token's key is pruned with the prefill's channel energy A by the prefill's
+# own rule (top-T of fl32(A_j k^2), ties to the lower channel) and appended;
+# its V row is appended dense; r stays as the prefill computed it.
+
+def append_tokens(k_new: np.ndarray, A: np.ndarray, T: int) -> dict:
+    """k_new [B][N_kv][n][D] -> mask [B][N_kv][n][D], words, packed [..., T]."""
+    mask = select_top_t(saliency_keys(A, k_new), T)
+    return {"mask": mask, "words": mask_words(mask), "packed": pack_kept(k_new, mask)}
+
+
+def grow_cache(packed, mask, v, k_new, v_new, A, T: int):
+    """The cache (packed, mask, v over S tokens) after appending the n tokens
+    of k_new / v_new ([B][N_kv][n][D]) in order."""
+    a = append_tokens(k_new, A, T)
+    return (np.concatenate([packed, a["packed"]], axis=2), np.concatenate([mask, a["mask"]], axis=2),
+            np.concatenate([np.asarray(v), np.asarray(v_new)], axis=2))
 
 
 # ---------------------------------------------------------------- SparK-p (top-p)

@@ -735,3 +735,32 @@ def test_top_p_ragged_layout():
             for t in (0, 17, 49):
                 lo, hi = out["row_off"][b, h, t], out["row_off"][b, h, t + 1]
                 np.testing.assert_array_equal(flat[base + lo: base + hi], k[b, h, t][out["mask"][b, h, t]])
+
+
+# ------------------------------------------------------------------ decode-time cache growth
+
+def test_appended_tokens_are_pruned_like_prompt_tokens():
+    """The per-token rule does not depend on which tokens were prompt and
+    which were generated: pruning a sequence with the prefill's A equals
+    pruning its prefix at prefill and appending the rest one at a time."""
+    w = WORKLOADS["tiny_s1k"].with_(S=200, n_q=8, n_kv=2)
+    x = gen.numpy_layer(w, seed=90, steps=0)
+    f = {n: gen.bf16_bits_to_f32(a) for n, a in x.items()}
+    pre = oracle.prune(f["q_win"], f["k"][:, :, :150], w.n_kv, 0.7)
+    packed, mask, v = pre["packed"], pre["mask"], f["v"][:, :, :150]
+    for t in range(150, 200):
+        packed, mask, v = oracle.grow_cache(packed, mask, v, f["k"][:, :, t:t + 1], f["v"][:, :, t:t + 1], pre["A"],
+                                            pre["T"])
+    whole = oracle.select_top_t(oracle.saliency_keys(pre["A"], f["k"]), pre["T"])
+    np.testing.assert_array_equal(mask, whole)
+    np.testing.assert_array_equal(packed, oracle.pack_kept(f["k"], whole))
+    np.testing.assert_array_equal(v, f["v"])
+
+
+def test_appending_a_cached_key_repeats_its_mask_row():
+    rng = np.random.default_rng(91)
+    A = rng.random((1, 2, 16)).astype(np.float32)
+    k = rng.standard_normal((1, 2, 10, 16)).astype(np.float32)
+    base = oracle.select_top_t(oracle.saliency_keys(A, k), 5)
+    again = oracle.append_tokens(k[:, :, 3:4], A, 5)
+    np.testing.assert_array_equal(again["mask"][:, :, 0], base[:, :, 3])
