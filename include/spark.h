@@ -161,6 +161,33 @@ int spark_prefill_prune_grouped(const void* q_win, const void* k, int B, int S, 
                                 void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Decode-time cache growth. The pages prune only at prefill; the reading
+ * here: a cache is allocated with a capacity of S_cap tokens per (b, KV
+ * head), each generated token's key is pruned with the prefill's channel
+ * energy by the same rule as the prompt's keys and appended, its V row is
+ * appended dense, and r stays as the prefill computed it.
+ *
+ * spark_prefill_prune_cap: spark_prefill_prune writing k_packed
+ * [B][N_kv][S_cap][T] and mask [B][N_kv][S_cap][D/32] (rows S..S_cap-1 left
+ * untouched); S <= S_cap.
+ */
+int spark_prefill_prune_cap(const void* q_win, const void* k, int B, int S, int S_cap, int N_q, int N_kv, int D,
+                            float lambda, int window, int qagg, int recovery, float f_const,
+                            void* k_packed, uint32_t* mask, float* chan_energy, float* r, int32_t* cnt,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Append one token per (b, KV head) at row pos (0 <= pos < S_cap):
+ *  k_new, v_new  bf16 [B][N_kv][D]  the new token's key and value
+ *  chan_energy   fp32 [B][N_kv][D]  A_j from the prefill
+ * Writes mask[b][h][pos], k_packed[b][h][pos][0..T) (T = spark_num_kept(D,
+ * lambda); key fl32(A_j k_j^2), top-T, ties to the lower channel) and
+ * v[b][h][pos] (bf16 [B][N_kv][S_cap][D]). Other rows are untouched.
+ */
+int spark_append_token(const void* k_new, const void* v_new, const float* chan_energy, int B, int N_kv, int D,
+                       float lambda, int pos, int S_cap, void* k_packed, uint32_t* mask, void* v, void* stream);
+
+/*
  * Recovery statistics recomputed from a stored pruned cache (walkthrough
  * section 3.3 step 1), e.g. to switch F without pruning again.
  *  k_packed, mask, chan_energy   as written by spark_prefill_prune
@@ -223,6 +250,16 @@ int spark_decode_attn_sampled(const void* q, const void* k_packed, const uint32_
                               const float* chan_energy, const float* r, int recovery, uint64_t seed,
                               int B, int S, int N_q, int N_kv, int D, float lambda, float scale, int splits,
                               float* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * spark_decode_attn over the first S tokens of a cache of capacity S_cap
+ * (k_packed [B][N_kv][S_cap][T], mask [B][N_kv][S_cap][D/32], v
+ * [B][N_kv][S_cap][D]); S <= S_cap. The workspace size is that of
+ * spark_decode_workspace_bytes(B, S, ...).
+ */
+int spark_decode_attn_cap(const void* q, const void* k_packed, const uint32_t* mask, const void* v, const float* r,
+                          int B, int S, int S_cap, int N_q, int N_kv, int D, float lambda, float scale, int splits,
+                          float* out, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * One decode step over a ragged pruned cache (spark_prefill_prune_topp):

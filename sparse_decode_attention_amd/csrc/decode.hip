@@ -247,6 +247,7 @@ __device__ __forceinline__ uint4 load_chunk(const PackedSrc& p, size_t ce) {
                       t[4] | ((uint32_t)t[5] << 16), t[6] | ((uint32_t)t[7] << 16));
 }
 
+// S: the head stride in tokens (the cache capacity)
 __device__ __forceinline__ void issue_meta(const PackedSrc& p, int S, int bh, int t0, int nt, int L, TileMeta& m) {
     const int T = p.T;
     const size_t e0 = ((size_t)bh * S + t0) * (size_t)T;
@@ -677,7 +678,7 @@ decode_kernel(const DecodeArgs a) {
         for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
     }
 
-    const uint16_t* vbh = VP ? nullptr : a.v + (size_t)bh * S * 128;
+    const uint16_t* vbh = VP ? nullptr : a.v + (size_t)bh * a.S_cap * 128;
     float rvl[8];          // VP: recovery values of this lane's 8 V channels
     if (VP) {
 #pragma unroll
@@ -688,8 +689,8 @@ decode_kernel(const DecodeArgs a) {
     if (wave < ntiles) {
         const int t0 = blk_begin + wave * DECODE_TILE;
         if (RG) issue_meta_ragged(a, bh, t0, min(DECODE_TILE, blk_end - t0), L, meta);
-        else issue_meta(k_src(a), S, bh, t0, min(DECODE_TILE, blk_end - t0), L, meta);
-        if (VP) issue_meta(v_src(a), S, bh, t0, min(DECODE_TILE, blk_end - t0), L, vmeta);
+        else issue_meta(k_src(a), a.S_cap, bh, t0, min(DECODE_TILE, blk_end - t0), L, meta);
+        if (VP) issue_meta(v_src(a), a.S_cap, bh, t0, min(DECODE_TILE, blk_end - t0), L, vmeta);
     }
 
     for (int tile = wave; tile < ntiles; tile += NW) {
@@ -717,7 +718,7 @@ decode_kernel(const DecodeArgs a) {
         if (tile + NW < ntiles) {
             const int t1 = t0 + NW * DECODE_TILE;
             if (RG) issue_meta_ragged(a, bh, t1, min(DECODE_TILE, blk_end - t1), L, meta);
-            else issue_meta(k_src(a), S, bh, t1, min(DECODE_TILE, blk_end - t1), L, meta);
+            else issue_meta(k_src(a), a.S_cap, bh, t1, min(DECODE_TILE, blk_end - t1), L, meta);
         }
 
         // -- 2. list of kept channels (table byte offsets), slot-major [rho][lane]
@@ -818,7 +819,7 @@ decode_kernel(const DecodeArgs a) {
             vshift = vmeta.shift;
             if (tile + NW < ntiles) {
                 const int t1 = t0 + NW * DECODE_TILE;
-                issue_meta(v_src(a), S, bh, t1, min(DECODE_TILE, blk_end - t1), L, vmeta);
+                issue_meta(v_src(a), a.S_cap, bh, t1, min(DECODE_TILE, blk_end - t1), L, vmeta);
             }
             wave_lds_sync();
         }
@@ -919,7 +920,7 @@ template <int T>
 __device__ __forceinline__ void load_row(const DecodeArgs& a, int bh, int t0, int nt, int L,
                                          uint4& mw, uint32_t (&kr)[(T + 1) / 2]) {
     constexpr int NDW = (T + 1) / 2;
-    const size_t row = (size_t)bh * a.S + t0 + min(L, nt - 1);
+    const size_t row = (size_t)bh * a.S_cap + t0 + min(L, nt - 1);
     mw = *reinterpret_cast<const uint4*>(a.mask + row * 4);
     if constexpr (T % 8 == 0) {
         const uint4* src = reinterpret_cast<const uint4*>(a.packed + row * T);   // 16-byte aligned rows
@@ -1107,7 +1108,7 @@ decode_fast_kernel(const DecodeArgs a) {
     uint4 mw;
     uint32_t kr[(T + 1) / 2];
     uint4 vr[16];
-    const uint16_t* vbh = a.v + (size_t)bh * S * 128;
+    const uint16_t* vbh = a.v + (size_t)bh * a.S_cap * 128;
     // a wave without a tile (or an empty block) reads row min(t0, S-1)
     const int tf0 = min(blk_begin + wave * DECODE_TILE, S - 1);
     const int ntf0 = max(1, min(DECODE_TILE, blk_end - tf0));

@@ -38,7 +38,9 @@ template <int SEL>
 __global__ void select_pack_kernel(const uint16_t* k, const float* A, uint16_t* k_packed, uint32_t* mask,
                                    double* part_sum, int32_t* part_cnt, double* part_pruned,
                                    int S, int T, int nblk, int recovery, const uint8_t* gid, GroupSpec grp,
-                                   float top_p, int32_t* tok_cnt, int32_t* blk_cnt);
+                                   float top_p, int32_t* tok_cnt, int32_t* blk_cnt, int S_out);
+__global__ void append_token_kernel(const uint16_t* k_new, const uint16_t* v_new, const float* A, uint16_t* k_packed,
+                                    uint32_t* mask, uint16_t* v, int T, int pos, int S_cap);
 __global__ void topp_scan_kernel(int32_t* blk_cnt, int nblk);
 __global__ void topp_pack_kernel(const uint16_t* k, const uint32_t* mask, uint16_t* k_packed, int32_t* row_off,
                                  const int32_t* blk_base, int S, int nblk);
@@ -88,6 +90,7 @@ struct DecodeArgs {
     size_t packed_elems;      // B*N_kv*S*T
     size_t v_packed_elems;    // B*N_kv*S*Tv
     int S, T, N_q, N_kv, nsplit, chunk;
+    int S_cap;                // head stride of packed, mask and v in tokens (>= S; S unless a cache grows)
     float qscale;             // softmax scale * log2(e)
     int sampled;              // 0, or the sampled F (4 Gaussian, 5 Exponential)
     int v_packed_mode;        // 1: V channels pruned (v_packed, v_mask, rv; v unused)

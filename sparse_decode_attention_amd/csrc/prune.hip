@@ -130,7 +130,7 @@ select_pack_kernel(const uint16_t* __restrict__ k, const float* __restrict__ A,
                    double* __restrict__ part_sum, int32_t* __restrict__ part_cnt,
                    double* __restrict__ part_pruned,
                    int S, int T, int nblk, int recovery, const uint8_t* __restrict__ gid, GroupSpec grp,
-                   float top_p, int32_t* __restrict__ tok_cnt, int32_t* __restrict__ blk_cnt) {
+                   float top_p, int32_t* __restrict__ tok_cnt, int32_t* __restrict__ blk_cnt, int S_out) {
     constexpr bool GROUPED = SEL == 1;
     __shared__ uint4 stage[4][64];            // 4 tokens x 256 B per wave
     __shared__ double red_sum[4][128];
@@ -156,9 +156,10 @@ select_pack_kernel(const uint16_t* __restrict__ k, const float* __restrict__ A,
     int cnt0 = 0, cnt1 = 0;
 
     const uint16_t* kbh = k + (size_t)bh * S * 128;
-    uint16_t* pbh = (SEL != 2 && k_packed) ? k_packed + (size_t)bh * S * T : nullptr;
+    // outputs use the head stride S_out (a cache's capacity, >= S)
+    uint16_t* pbh = (SEL != 2 && k_packed) ? k_packed + (size_t)bh * S_out * T : nullptr;
     int kept_tokens = 0;     // SEL 2: channels kept by this wave's tokens
-    uint32_t* mbh = mask + (size_t)bh * S * 4;
+    uint32_t* mbh = mask + (size_t)bh * S_out * 4;
     uint16_t* st = reinterpret_cast<uint16_t*>(&stage[wave][0]);
 
     // wave w takes tokens t_begin + 4*(w + 4*i) .. +3
@@ -260,13 +261,43 @@ select_pack_kernel(const uint16_t* __restrict__ k, const float* __restrict__ A,
 
 template __global__ void select_pack_kernel<0>(const uint16_t*, const float*, uint16_t*, uint32_t*, double*, int32_t*,
                                                double*, int, int, int, int, const uint8_t*, GroupSpec, float, int32_t*,
-                                               int32_t*);
+                                               int32_t*, int);
 template __global__ void select_pack_kernel<1>(const uint16_t*, const float*, uint16_t*, uint32_t*, double*, int32_t*,
                                                double*, int, int, int, int, const uint8_t*, GroupSpec, float, int32_t*,
-                                               int32_t*);
+                                               int32_t*, int);
 template __global__ void select_pack_kernel<2>(const uint16_t*, const float*, uint16_t*, uint32_t*, double*, int32_t*,
                                                double*, int, int, int, int, const uint8_t*, GroupSpec, float, int32_t*,
-                                               int32_t*);
+                                               int32_t*, int);
+
+// ---------------------------------------------------------------- decode-time cache growth
+// One wave per (b, KV head): the new token's key is pruned with the cached
+// channel energy by the prefill's rule (key fl32(A k^2), top-T, ties to the
+// lower channel) and written at row `pos` of the capacity-S_cap packed
+// cache and mask; its V row is copied into v at `pos`.
+__global__ void __launch_bounds__(64)
+append_token_kernel(const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
+                    const float* __restrict__ A, uint16_t* __restrict__ k_packed, uint32_t* __restrict__ mask,
+                    uint16_t* __restrict__ v, int T, int pos, int S_cap) {
+    const int bh = blockIdx.x, L = threadIdx.x;
+    const uint16_t kb0 = k_new[(size_t)bh * 128 + L], kb1 = k_new[(size_t)bh * 128 + 64 + L];
+    const float k0 = bf16_to_f32(kb0), k1 = bf16_to_f32(kb1);
+    const uint32_t key0 = __float_as_uint(__fmul_rn(A[(size_t)bh * 128 + L], __fmul_rn(k0, k0)));
+    const uint32_t key1 = __float_as_uint(__fmul_rn(A[(size_t)bh * 128 + 64 + L], __fmul_rn(k1, k1)));
+    bool kept0 = false, kept1 = false;
+    if (T >= 128) {
+        kept0 = kept1 = true;
+    } else if (T > 0) {
+        select_top<false>(key0, key1, true, true, T, kept0, kept1);
+    }
+    const uint64_t m0 = ballot(kept0), m1 = ballot(kept1);
+    const size_t row = (size_t)bh * S_cap + pos;
+    if (L == 0)
+        *reinterpret_cast<uint4*>(mask + row * 4) =
+            make_uint4((uint32_t)m0, (uint32_t)(m0 >> 32), (uint32_t)m1, (uint32_t)(m1 >> 32));
+    if (kept0) k_packed[row * T + mbcnt(m0)] = kb0;
+    if (kept1) k_packed[row * T + __popcll(m0) + mbcnt(m1)] = kb1;
+    reinterpret_cast<uint32_t*>(v + row * 128)[L] = reinterpret_cast<const uint32_t*>(v_new + (size_t)bh * 128)[L];
+}
 
 // ---------------------------------------------------------------- SparK-p ragged packing
 // One wave per (b, KV head): exclusive scan of the block totals in place

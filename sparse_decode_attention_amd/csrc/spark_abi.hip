@@ -129,11 +129,11 @@ size_t spark_decode_workspace_bytes(int B, int S, int N_q, int N_kv, int D, int 
     return decode_ws_bytes(B * N_kv, N_q / N_kv, nsplit);
 }
 
-int spark_prefill_prune(const void* q_win, const void* k, int B, int S, int N_q, int N_kv, int D,
-                        float lambda, int window, int qagg, int recovery, float f_const,
-                        void* k_packed, uint32_t* mask, float* chan_energy, float* r, int32_t* cnt,
-                        void* ws, size_t ws_bytes, void* stream) {
-    if (B < 1 || S < 1 || D < 1 || window < 1) return SPARK_EINVAL;
+int spark_prefill_prune_cap(const void* q_win, const void* k, int B, int S, int S_cap, int N_q, int N_kv, int D,
+                            float lambda, int window, int qagg, int recovery, float f_const,
+                            void* k_packed, uint32_t* mask, float* chan_energy, float* r, int32_t* cnt,
+                            void* ws, size_t ws_bytes, void* stream) {
+    if (B < 1 || S < 1 || D < 1 || window < 1 || S_cap < S) return SPARK_EINVAL;
     const int T = kept_or_neg(D, lambda);
     if (T < 0) return SPARK_EINVAL;
     if (qagg != SPARK_QAGG_L2 && qagg != SPARK_QAGG_MEAN) return SPARK_EINVAL;
@@ -154,9 +154,33 @@ int spark_prefill_prune(const void* q_win, const void* k, int B, int S, int N_q,
     hipLaunchKernelGGL(select_pack_kernel<0>, dim3(w.nblk, BH), dim3(256), 0, st,
                        static_cast<const uint16_t*>(k), chan_energy, static_cast<uint16_t*>(k_packed), mask,
                        w.sum, w.cnt, w.pruned, S, T, w.nblk, recovery, static_cast<const uint8_t*>(nullptr),
-                       GroupSpec{}, 0.0f, static_cast<int32_t*>(nullptr), static_cast<int32_t*>(nullptr));
+                       GroupSpec{}, 0.0f, static_cast<int32_t*>(nullptr), static_cast<int32_t*>(nullptr), S_cap);
     hipLaunchKernelGGL(stats_reduce_kernel, dim3(BH), dim3(128 * STATS_PARTS), 0, st,
                        w.sum, w.cnt, w.pruned, chan_energy, r, cnt, S, T, w.nblk, recovery, f_const);
+    return hip_status(hipGetLastError());
+}
+
+int spark_prefill_prune(const void* q_win, const void* k, int B, int S, int N_q, int N_kv, int D,
+                        float lambda, int window, int qagg, int recovery, float f_const,
+                        void* k_packed, uint32_t* mask, float* chan_energy, float* r, int32_t* cnt,
+                        void* ws, size_t ws_bytes, void* stream) {
+    return spark_prefill_prune_cap(q_win, k, B, S, S, N_q, N_kv, D, lambda, window, qagg, recovery, f_const,
+                                   k_packed, mask, chan_energy, r, cnt, ws, ws_bytes, stream);
+}
+
+int spark_append_token(const void* k_new, const void* v_new, const float* chan_energy, int B, int N_kv, int D,
+                       float lambda, int pos, int S_cap, void* k_packed, uint32_t* mask, void* v, void* stream) {
+    if (B < 1 || N_kv < 1 || D < 1 || pos < 0 || pos >= S_cap) return SPARK_EINVAL;
+    const int T = kept_or_neg(D, lambda);
+    if (T < 0) return SPARK_EINVAL;
+    if (D != 128) return SPARK_EUNSUPPORTED;
+    if (!k_new || !v_new || !chan_energy || !mask || !v || (T > 0 && !k_packed)) return SPARK_EINVAL;
+    if (!aligned(k_new, 4) || !aligned(v_new, 4) || !aligned(chan_energy, 4) || !aligned(mask, 16) ||
+        !aligned(v, 16) || (k_packed && !aligned(k_packed, 16)))
+        return SPARK_EALIGN;
+    hipLaunchKernelGGL(append_token_kernel, dim3(B * N_kv), dim3(64), 0, static_cast<hipStream_t>(stream),
+                       static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), chan_energy,
+                       static_cast<uint16_t*>(k_packed), mask, static_cast<uint16_t*>(v), T, pos, S_cap);
     return hip_status(hipGetLastError());
 }
 
@@ -178,7 +202,7 @@ int spark_prefill_prune_v(const void* v, int B, int S, int N_kv, int D, float la
                        static_cast<const uint16_t*>(v), static_cast<const float*>(nullptr),
                        static_cast<uint16_t*>(v_packed), v_mask, w.sum, w.cnt, w.pruned, S, T, w.nblk,
                        (int)SPARK_F_MEAN_RETAINED, static_cast<const uint8_t*>(nullptr), GroupSpec{}, 0.0f,
-                       static_cast<int32_t*>(nullptr), static_cast<int32_t*>(nullptr));
+                       static_cast<int32_t*>(nullptr), static_cast<int32_t*>(nullptr), S);
     hipLaunchKernelGGL(stats_reduce_kernel, dim3(BH), dim3(128 * STATS_PARTS), 0, st, w.sum, w.cnt, w.pruned,
                        static_cast<const float*>(nullptr), r_v, cnt, S, T, w.nblk, (int)SPARK_F_MEAN_RETAINED, 0.0f);
     return hip_status(hipGetLastError());
@@ -216,7 +240,7 @@ int spark_prefill_prune_grouped(const void* q_win, const void* k, int B, int S, 
                        static_cast<const uint16_t*>(k), static_cast<const float*>(chan_energy),
                        static_cast<uint16_t*>(k_packed), mask, w.sum, w.cnt, w.pruned, S, T, w.nblk, recovery,
                        static_cast<const uint8_t*>(w.gid), grp, 0.0f, static_cast<int32_t*>(nullptr),
-                       static_cast<int32_t*>(nullptr));
+                       static_cast<int32_t*>(nullptr), S);
     hipLaunchKernelGGL(stats_reduce_kernel, dim3(BH), dim3(128 * STATS_PARTS), 0, st,
                        w.sum, w.cnt, w.pruned, chan_energy, r, cnt, S, T, w.nblk, recovery, f_const);
     return hip_status(hipGetLastError());
@@ -248,7 +272,7 @@ int spark_prefill_prune_topp(const void* q_win, const void* k, int B, int S, int
     hipLaunchKernelGGL(select_pack_kernel<2>, dim3(w.nblk, BH), dim3(256), 0, st, static_cast<const uint16_t*>(k),
                        static_cast<const float*>(chan_energy), static_cast<uint16_t*>(nullptr), mask, w.sum, w.cnt,
                        w.pruned, S, -1, w.nblk, recovery, static_cast<const uint8_t*>(nullptr), GroupSpec{}, p,
-                       row_off + 1, w.blk);
+                       row_off + 1, w.blk, S);
     hipLaunchKernelGGL(topp_scan_kernel, dim3(BH), dim3(64), 0, st, w.blk, w.nblk);
     hipLaunchKernelGGL(topp_pack_kernel, dim3(w.nblk, BH), dim3(256), 0, st, static_cast<const uint16_t*>(k),
                        static_cast<const uint32_t*>(mask), static_cast<uint16_t*>(k_packed), row_off,
@@ -302,8 +326,9 @@ struct PackedV {
 int decode_call(const void* q, const void* k_packed, const uint32_t* mask, const void* v, const float* r,
                 const float* A, int sampled, uint64_t seed, int B, int S, int N_q, int N_kv, int D, float lambda,
                 float scale, int splits, float* out, void* ws, size_t ws_bytes, void* stream,
-                const PackedV* vp = nullptr, const int32_t* row_off = nullptr) {
-    if (B < 1 || S < 1 || D < 1 || splits < 0) return SPARK_EINVAL;
+                const PackedV* vp = nullptr, const int32_t* row_off = nullptr, int S_cap = 0) {
+    if (S_cap == 0) S_cap = S;
+    if (B < 1 || S < 1 || D < 1 || splits < 0 || S_cap < S) return SPARK_EINVAL;
     const int T = kept_or_neg(D, lambda);
     if (T < 0) return SPARK_EINVAL;
     const int Tv = vp ? kept_or_neg(D, vp->lambda) : -1;
@@ -344,7 +369,7 @@ int decode_call(const void* q, const void* k_packed, const uint32_t* mask, const
         a.v_packed = static_cast<const uint16_t*>(vp->packed);
         a.v_mask = vp->mask;
         a.rv = vp->r;
-        a.v_packed_elems = (size_t)BH * S * Tv;
+        a.v_packed_elems = (size_t)BH * S_cap * Tv;
         a.v_packed_mode = 1;
         a.Tv = Tv;
     }
@@ -353,7 +378,8 @@ int decode_call(const void* q, const void* k_packed, const uint32_t* mask, const
     a.part_ml = reinterpret_cast<float*>(base + SPARK_DECODE_COUNTER_BYTES);
     a.part_acc = reinterpret_cast<float*>(base + SPARK_DECODE_COUNTER_BYTES +
                                           round_up((size_t)BH * nsplit * 2 * G * sizeof(float), 256));
-    a.packed_elems = (size_t)BH * S * (ragged ? 128 : T);
+    a.packed_elems = (size_t)BH * S_cap * (ragged ? 128 : T);
+    a.S_cap = S_cap;
     a.row_off = row_off;
     a.S = S;
     a.T = T;
@@ -379,6 +405,13 @@ int spark_decode_attn(const void* q, const void* k_packed, const uint32_t* mask,
                       float* out, void* ws, size_t ws_bytes, void* stream) {
     return decode_call(q, k_packed, mask, v, r, nullptr, 0, 0, B, S, N_q, N_kv, D, lambda, scale, splits, out, ws,
                        ws_bytes, stream);
+}
+
+int spark_decode_attn_cap(const void* q, const void* k_packed, const uint32_t* mask, const void* v, const float* r,
+                          int B, int S, int S_cap, int N_q, int N_kv, int D, float lambda, float scale, int splits,
+                          float* out, void* ws, size_t ws_bytes, void* stream) {
+    return decode_call(q, k_packed, mask, v, r, nullptr, 0, 0, B, S, N_q, N_kv, D, lambda, scale, splits, out, ws,
+                       ws_bytes, stream, nullptr, nullptr, S_cap);
 }
 
 int spark_decode_attn_ragged(const void* q, const void* k_packed, const int32_t* row_off, const uint32_t* mask,

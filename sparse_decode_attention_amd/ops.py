@@ -43,6 +43,10 @@ _SIGS = {
     "spark_prefill_prune_topp": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _f, _i, _i, _i, _f, _vp, _vp, _vp, _vp, _vp, _vp,
                                       _vp, _sz, _vp]),
     "spark_decode_attn_ragged": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _vp, _sz, _vp]),
+    "spark_prefill_prune_cap": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _i, _i, _f,
+                                     _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "spark_append_token": (_i, [_vp, _vp, _vp, _i, _i, _i, _f, _i, _i, _vp, _vp, _vp, _vp]),
+    "spark_decode_attn_cap": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _f, _i, _vp, _vp, _sz, _vp]),
     "spark_prefill_prune_grouped": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, ctypes.POINTER(ctypes.c_float), _i, _i,
                                          _i, _f, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "spark_decode_attn_kv": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _f, _f, _i,
@@ -353,6 +357,67 @@ def decode_attn_kv(q, k_packed, k_mask, r, v_packed, v_mask, r_v, lam: float, la
                                     ws.numel(), _stream(dev))
     _check("spark_decode_attn_kv", st)
     return out
+
+
+class GrowingCache:
+    """A pruned KV cache with room for S_cap tokens per (b, KV head), filled by
+    a prefill and grown one generated token at a time (spark_prefill_prune_cap,
+    spark_append_token, spark_decode_attn_cap). Buffers are torch device
+    tensors; every step runs in libspark."""
+
+    def __init__(self, q_win, k, v, n_kv: int, lam: float, S_cap: int, qagg: str = "l2",
+                 recovery: str = "mean_retained", f_const: float = 0.01):
+        B, N_q, W, D = q_win.shape
+        S = k.shape[2]
+        _need(q_win, "q_win", torch.bfloat16)
+        _need(k, "k", torch.bfloat16, (B, n_kv, S, D))
+        _need(v, "v", torch.bfloat16, (B, n_kv, S, D))
+        if S_cap < S:
+            raise ValueError("S_cap < S")
+        dev = k.device
+        self.B, self.N_q, self.n_kv, self.D, self.lam, self.S_cap = B, N_q, n_kv, D, float(lam), int(S_cap)
+        self.T = num_kept(D, lam)
+        self.k_packed = torch.empty((B, n_kv, S_cap, self.T), dtype=torch.bfloat16, device=dev)
+        self.mask = torch.zeros((B, n_kv, S_cap, (D + 31) // 32), dtype=torch.int32, device=dev)
+        self.v = torch.zeros((B, n_kv, S_cap, D), dtype=torch.bfloat16, device=dev)
+        self.v[:, :, :S].copy_(v)
+        self.chan_energy = torch.empty((B, n_kv, D), dtype=torch.float32, device=dev)
+        self.r = torch.empty((B, n_kv, D), dtype=torch.float32, device=dev)
+        self.cnt = torch.empty((B, n_kv, D), dtype=torch.int32, device=dev)
+        ws = workspace(dev, "prefill", lib().spark_prefill_workspace_bytes(B, S, n_kv, D))
+        st = lib().spark_prefill_prune_cap(_ptr(q_win), _ptr(k), B, S, S_cap, N_q, n_kv, D, self.lam, W, QAGG[qagg],
+                                           RECOVERY[recovery], float(f_const),
+                                           _ptr(self.k_packed) if self.T > 0 else None, _ptr(self.mask),
+                                           _ptr(self.chan_energy), _ptr(self.r), _ptr(self.cnt), _ptr(ws), ws.numel(),
+                                           _stream(dev))
+        _check("spark_prefill_prune_cap", st)
+        self.S = S
+
+    def append(self, k_new: torch.Tensor, v_new: torch.Tensor) -> None:
+        """k_new, v_new bf16 [B][N_kv][D]: prune and append at row S."""
+        _need(k_new, "k_new", torch.bfloat16, (self.B, self.n_kv, self.D))
+        _need(v_new, "v_new", torch.bfloat16, (self.B, self.n_kv, self.D))
+        if self.S >= self.S_cap:
+            raise SparkError("spark_append_token", ENOSPACE)
+        st = lib().spark_append_token(_ptr(k_new), _ptr(v_new), _ptr(self.chan_energy), self.B, self.n_kv, self.D,
+                                      self.lam, self.S, self.S_cap, _ptr(self.k_packed) if self.T > 0 else None,
+                                      _ptr(self.mask), _ptr(self.v), _stream(k_new.device))
+        _check("spark_append_token", st)
+        self.S += 1
+
+    def decode(self, q: torch.Tensor, scale: float = 0.0, splits: int = 0, out=None, ws=None) -> torch.Tensor:
+        """spark_decode_attn_cap over the S tokens held now."""
+        _need(q, "q", torch.bfloat16, (self.B, self.N_q, self.D))
+        dev = q.device
+        out = torch.empty((self.B, self.N_q, self.D), dtype=torch.float32, device=dev) if out is None else out
+        if ws is None:
+            ws = workspace(dev, "decode", decode_ws_bytes(self.B, self.S_cap, self.N_q, self.n_kv, self.D, splits))
+        st = lib().spark_decode_attn_cap(_ptr(q), _ptr(self.k_packed) if self.T > 0 else None, _ptr(self.mask),
+                                         _ptr(self.v), _ptr(self.r), self.B, self.S, self.S_cap, self.N_q, self.n_kv,
+                                         self.D, self.lam, float(scale), int(splits), _ptr(out), _ptr(ws), ws.numel(),
+                                         _stream(dev))
+        _check("spark_decode_attn_cap", st)
+        return out
 
 
 def decode_ws_init(ws: torch.Tensor) -> None:

@@ -222,6 +222,35 @@ def test_topp_entry_points_reject_bad_arguments():
     assert dec() == ops.ENOSPACE
 
 
+def test_growth_entry_points_reject_bad_arguments():
+    l = ops.lib()
+
+    def app(**kw):
+        a = dict(kn=FAKE, vn=FAKE, A=FAKE, B=1, N_kv=8, D=128, lam=0.5, pos=10, cap=64, kp=FAKE, mask=FAKE, v=FAKE)
+        a.update(kw)
+        return l.spark_append_token(a["kn"], a["vn"], a["A"], a["B"], a["N_kv"], a["D"], a["lam"], a["pos"],
+                                    a["cap"], a["kp"], a["mask"], a["v"], None)
+    assert app(pos=64) == ops.EINVAL
+    assert app(pos=-1) == ops.EINVAL
+    assert app(lam=2.0) == ops.EINVAL
+    assert app(D=64) == ops.EUNSUPPORTED
+    assert app(kp=None) == ops.EINVAL
+    assert app(v=None) == ops.EINVAL
+    assert app(mask=MIS) == ops.EALIGN
+
+    def dec(**kw):
+        a = dict(q=FAKE, kp=FAKE, mask=FAKE, v=FAKE, r=FAKE, B=1, S=64, cap=128, N_q=32, N_kv=8, D=128, lam=0.5,
+                 scale=0.0, splits=0, out=FAKE, ws=FAKE, nws=0)
+        a.update(kw)
+        return l.spark_decode_attn_cap(a["q"], a["kp"], a["mask"], a["v"], a["r"], a["B"], a["S"], a["cap"], a["N_q"],
+                                       a["N_kv"], a["D"], a["lam"], a["scale"], a["splits"], a["out"], a["ws"],
+                                       a["nws"], None)
+    assert dec(cap=32) == ops.EINVAL                     # S > S_cap
+    assert dec(S=0) == ops.EINVAL
+    assert dec(N_q=24) == ops.EUNSUPPORTED
+    assert dec() == ops.ENOSPACE
+
+
 def test_stats_rejects_bad_arguments():
     l = ops.lib()
 
