@@ -236,6 +236,67 @@ def run_leg(w, steps, warmup, rotate=True, seed=0, verbose=True, x=None, recover
     return res
 
 
+def growth_leg(w, steps, warmup, x):
+    """The serving loop with a growing cache: prefill w.S - w.steps prompt
+    tokens into a cache of capacity w.S, then w.steps decode steps, each
+    appending one generated token per (b, KV head) (pruned with the prefill's
+    channel energy) and decoding the step's query over the grown cache. One
+    graph holds the prefill, another the w.steps append + decode pairs."""
+    import torch
+    from sparse_decode_attention_amd import ops
+
+    dev = torch.device("cuda:0")
+    S0 = w.S - w.steps
+    k0, v0 = x["k"][:, :, :S0].contiguous(), x["v"][:, :, :S0].contiguous()
+    k_new = [x["k"][:, :, S0 + i].contiguous() for i in range(w.steps)]
+    v_new = [x["v"][:, :, S0 + i].contiguous() for i in range(w.steps)]
+    cache = ops.GrowingCache(x["q_win"], k0, v0, w.n_kv, w.lam, w.S)
+    outs = torch.empty((w.steps, w.B, w.n_q, w.D), dtype=torch.float32, device=dev)
+    ws = ops.workspace(dev, "decode", ops.decode_ws_bytes(w.B, w.S, w.n_q, w.n_kv, w.D))
+
+    def steps_all():
+        cache.S = S0
+        for i in range(w.steps):
+            cache.append(k_new[i], v_new[i])
+            cache.decode(x["q_dec"][i], out=outs[i], ws=ws)
+
+    steps_all()
+    torch.cuda.synchronize()
+    eager = outs.clone()
+    s_cap = torch.cuda.Stream(dev)
+    s_cap.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(s_cap):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s_cap):
+            steps_all()
+    torch.cuda.current_stream(dev).wait_stream(s_cap)
+    torch.cuda.synchronize()
+    for _ in range(max(1, warmup)):
+        g.replay()
+    torch.cuda.synchronize()
+    if not torch.equal(outs, eager):
+        raise RuntimeError("growth graph replay differs from eager")
+    st = torch.cuda.current_stream(dev)
+    ms = []
+    for _ in range(steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        g.replay()
+        e1.record(st)
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    ms.sort()
+    us_step = ms[len(ms) // 2] * 1e3 / w.steps
+    T = cache.T
+    mean_S = S0 + (w.steps + 1) / 2
+    step_bytes = w.B * w.n_kv * (mean_S * (2 * T + 16 + 2 * w.D) + 2 * T + 16 + 2 * w.D + 4 * w.D)
+    return {"workload": w.name, "prompt_tokens": S0, "generated": w.steps, "T": T,
+            "us_per_step_append_and_decode": round(us_step, 3), "GBps": round(step_bytes / (us_step * 1e-6) / 1e9, 2),
+            "what": "graph of 64 (append + decode) pairs over one cache (no replica rotation, so the 256 MB "
+                    "Infinity Cache may serve part of the 105 MB it reads); bytes per step: the mean cache read plus "
+                    "the appended row"}
+
+
 def stream_ceiling(nbytes: int, reps: int = 7, block_counts=(512, 1024, 2048, 4096)):
     """GB/s of a plain streaming read (spark_read_stream) of `nbytes`, rotated
     over >= 768 MB of buffers like the decode replicas: the practical HBM read
@@ -492,6 +553,7 @@ def main():
     ap.add_argument("--no-vprune", action="store_true", help="skip the K-and-V-pruned leg")
     ap.add_argument("--no-grouped", action="store_true", help="skip the SparK-g leg")
     ap.add_argument("--no-topp", action="store_true", help="skip the SparK-p leg")
+    ap.add_argument("--no-growth", action="store_true", help="skip the growing-cache serving loop")
     ap.add_argument("--warm", action="store_true", help="also report a run without replica rotation")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="run a plain device copy of this size after the legs (counter calibration)")
@@ -592,6 +654,12 @@ def main():
                 "x_dense_v_time": round(lg["decode_us_per_launch"] / main_leg["decode_us_per_launch"], 3),
                 "prefill_us_k_and_v": round(lg["prefill_us"], 2), "replicas": lg["replicas"]}
             del lg
+        torch.cuda.empty_cache()
+    if not args.no_growth:
+        print(f"bench: growing cache on {w.name}", file=sys.stderr, flush=True)
+        line["growth"] = growth_leg(w, min(args.steps, 5), min(args.warmup, 2), main_leg["x"])
+        line["growth"]["x_static_decode_time"] = round(line["growth"]["us_per_step_append_and_decode"] /
+                                                       main_leg["decode_us_per_launch"], 3)
         torch.cuda.empty_cache()
     if not args.no_topp:
         print(f"bench: SparK-p 0.99 on {w.name}", file=sys.stderr, flush=True)
