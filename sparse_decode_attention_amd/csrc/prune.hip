@@ -105,14 +105,36 @@ __device__ __forceinline__ float tree_sum_wave(float x) {
 // theta whose tree sum of w over {key >= theta} reaches the target, decided
 // bit by bit from the top (the sum cannot rise as theta rises); keep
 // key >= theta. An all-zero row ends with theta = 2^31 - 1 and keeps nothing.
+//
+// The sum depends only on the set {key >= c}. The search keeps the count of
+// that set at the last accepted threshold v (whose sum reaches the target)
+// and at the last rejected one (whose sum does not); a candidate whose set
+// equals either of them takes its decision without a tree sum, so sums run
+// only where a candidate splits the keys between the two.
 __device__ __forceinline__ void select_top_p(uint32_t key0, uint32_t key1, float p, bool& kept0, bool& kept1) {
     const float w0 = sqrtf(__uint_as_float(key0)), w1 = sqrtf(__uint_as_float(key1));
     const float target = __fmul_rn(p, tree_sum_wave(__fadd_rn(w0, w1)));
     uint32_t v = 0;
+    int n_acc = 128;    // |{key >= v}|: v = 0 takes every key, and its sum (the total) reaches the target
+    int n_rej = -1;     // |{key >= last rejected}|; none yet
     for (int bit = 30; bit >= 0; --bit) {
         const uint32_t c = __builtin_amdgcn_readfirstlane(v | (1u << bit));
-        const float s = tree_sum_wave(__fadd_rn(key0 >= c ? w0 : 0.0f, key1 >= c ? w1 : 0.0f));
-        v = __builtin_amdgcn_readfirstlane(s >= target ? c : v);
+        const int n = __popcll(ballot(key0 >= c)) + __popcll(ballot(key1 >= c));
+        bool take;
+        if (n == n_acc) {
+            take = true;
+        } else if (n == n_rej) {
+            take = false;
+        } else {
+            const float s = tree_sum_wave(__fadd_rn(key0 >= c ? w0 : 0.0f, key1 >= c ? w1 : 0.0f));
+            take = __builtin_amdgcn_readfirstlane(s >= target ? 1u : 0u) != 0;
+        }
+        if (take) {
+            v = c;
+            n_acc = n;
+        } else {
+            n_rej = n;
+        }
     }
     kept0 = key0 >= v;
     kept1 = key1 >= v;
