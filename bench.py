@@ -70,17 +70,20 @@ def read_traffic(workload: str):
 VALU_PEAK_GOPS = 256 * 64 * 2.4
 
 
-def sampled_alu_ops_per_token(G, T, rec):
+def sampled_alu_ops_per_token(G, T, rec, valu_pv=None):
     """Algorithmic 32-bit VALU operations per (token, KV head) of the sampled
     decode: per 4-channel group a Philox4x32-10 block (10 rounds of two wide
     multiplies and two three-way xors), four uniforms (convert, scale), the
     transform (Exponential: log, fma each; Gaussian: two of log, scale, sqrt,
     sin, cos, two products), the kept-channel masks and 4 G FMAs; then the
-    fixed-r part: G T FMAs and T subtractions of the kept channels and G 128
-    FMAs of P.V on the VALU."""
+    fixed-r part: G T FMAs and T subtractions of the kept channels, and, in
+    the generic kernel (valu_pv), G 128 FMAs of P.V on the VALU (the
+    matrix-core kernel for G = 4 and T in {26, 38, 48, 64} runs P.V on MFMA)."""
+    if valu_pv is None:
+        valu_pv = not (G == 4 and T in (26, 38, 48, 64))
     transform = 8 if rec == "exponential" else 14
     per_group = 40 + 8 + transform + 4 + 4 * G
-    return 32 * per_group + G * T + T + G * 128
+    return 32 * per_group + G * T + T + (G * 128 if valu_pv else 0)
 
 
 def effective_decode_bytes(w, T, Tv=None):
@@ -631,7 +634,7 @@ def main():
             alu_ops = w.B * w.n_kv * w.S * sampled_alu_ops_per_token(w.G, T, rec)
             alu_gops = alu_ops / (lg["decode_us_per_launch"] * 1e-6) / 1e9
             line["sampled_f"][rec] = {
-                "workload": w.name, "kernel": f"decode_kernel<{w.G}, {ops.RECOVERY[rec]}>",
+                "workload": w.name, "kernel": (f"decode_fast_kernel<4, {T}, {ops.RECOVERY[rec]}>" if w.G == 4 and T in (26, 38, 48, 64) else f"decode_kernel<{w.G}, {ops.RECOVERY[rec]}, false, false>"),
                 "decode_us_per_launch": round(lg["decode_us_per_launch"], 3),
                 "GBps": round(lg["decode_GBps"], 2),
                 "roofline": {"bound": "alu", "achieved": round(alu_gops, 1), "peak": VALU_PEAK_GOPS, "unit": "Gop/s",

@@ -983,12 +983,12 @@ __device__ __forceinline__ void build_list(const uint4& mw, uint8_t* lst, int L)
 // rows are requested once the scores have consumed this tile's; then P.V.
 // A request made while the memory queue is full stalls the wave, so none is
 // placed ahead of work that needs no memory.
-template <int G, int T, bool LOAD_V, bool LIST_READY>
+template <int G, int T, int SMODE, bool LOAD_V, bool LIST_READY>
 __device__ __forceinline__ void fast_tile(const DecodeArgs& a, int bh, const unsigned char* tab, uint8_t* lst,
                                           float* ptab, const uint16_t* vbh, const float (&cq)[G], int t0, int nt,
                                           int nt_next, int L, uint4& mw, uint32_t (&kr)[(T + 1) / 2],
                                           uint4 (&vr)[16], float (&m_run)[G], float (&l_run)[G],
-                                          f32x4 (&accm)[8]) {
+                                          f32x4 (&accm)[8], const float* qn) {
     const int tau = L >> 4, oct = L & 15;
     const int t1 = t0 + (DECODE_FAST_THREADS / 64) * DECODE_TILE;
     if constexpr (!LIST_READY) build_list<T>(mw, lst, L);
@@ -1040,6 +1040,9 @@ __device__ __forceinline__ void fast_tile(const DecodeArgs& a, int bh, const uns
 #pragma unroll
         for (int g = 0; g < G; ++g) asm volatile("" : "+v"(s[g]));
     }
+    // sampled F: the sample term needs this tile's mask, so it runs before
+    // the next tile's masks are requested into mw
+    if (SMODE) sampled_scores<G, SMODE == 4>(a, qn, mw, bh, t0, nt, L, s);
     if (L >= nt) {
 #pragma unroll
         for (int g = 0; g < G; ++g) s[g] = -INFINITY;
@@ -1057,12 +1060,16 @@ __device__ __forceinline__ void fast_tile(const DecodeArgs& a, int bh, const uns
 // lane loads its token's packed row straight into registers (T/2 dwords, no
 // LDS staging) and builds the list of its kept channels in LDS as u16 table
 // offsets; the score loop then knows each slot's register at compile time.
-template <int G, int T>
+//
+// SMODE 4 / 5: the sampled F (Gaussian / Exponential); the r table then holds
+// mu / a_j, and a q' ns table of 2 KiB follows the other LDS.
+template <int G, int T, int SMODE>
 __global__ void __launch_bounds__(DECODE_FAST_THREADS)
 decode_fast_kernel(const DecodeArgs a) {
     // statically sized LDS: its base address is a compile-time constant, so
     // table offsets fold into the LDS instructions' offset fields
-    __shared__ __align__(16) unsigned char smem[DECODE_FAST_LDS_BYTES];
+    __shared__ __align__(16) unsigned char smem[DECODE_FAST_LDS_BYTES + (SMODE ? 128 * G * 4 : 0)];
+    float* qn = reinterpret_cast<float*>(smem + DECODE_FAST_LDS_BYTES);   // [128][G], sampled F only
     // tables: q'_0..q'_3 of the group as a float4 per channel (2 KiB), then
     // r as one float per channel (512 bytes)
     constexpr uint32_t TAB = 16u;
@@ -1102,7 +1109,16 @@ decode_fast_kernel(const DecodeArgs a) {
         const int j = tid + i * DECODE_FAST_THREADS;
         qb[i] = a.q[((size_t)b * a.N_q + (size_t)h * G + (j >> 7)) * 128 + (j & 127)];
     }
-    const float rv = a.r[(size_t)bh * 128 + (tid & 127)];
+    float rv = a.r[(size_t)bh * 128 + (tid & 127)];
+    float ns = 0.0f;     // sampled F: the noise scale of channel tid & 127 back-solved
+    if (SMODE) {
+        // r holds (mu, sigma); a pruned key is (mu + ns n) / a_j, a_j = sqrt(A_j)
+        const float Aj = a.A[(size_t)bh * 128 + (tid & 127)];
+        const float inv_a = Aj > 0.0f ? 1.0f / sqrtf(Aj) : 0.0f;
+        const float mu = a.r[(size_t)bh * 128], sigma = a.r[(size_t)bh * 128 + 1];
+        rv = mu * inv_a;
+        ns = (SMODE == 4 ? sigma : mu) * inv_a;
+    }
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
     uint4 mw;
@@ -1126,7 +1142,9 @@ decode_fast_kernel(const DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < QPT; ++i) {
         const int j = tid + i * DECODE_FAST_THREADS;
-        reinterpret_cast<float*>(tab + (j & 127) * TAB)[j >> 7] = bf16_to_f32(qb[i]) * a.qscale;
+        const float qv = bf16_to_f32(qb[i]) * a.qscale;
+        reinterpret_cast<float*>(tab + (j & 127) * TAB)[j >> 7] = qv;
+        if (SMODE) qn[(j & 127) * G + (j >> 7)] = qv * ns;     // ns belongs to channel tid & 127 == j & 127
     }
     if (tid < 128) reinterpret_cast<float*>(tab + 128 * TAB)[tid] = rv;
     __syncthreads();
@@ -1159,15 +1177,17 @@ decode_fast_kernel(const DecodeArgs a) {
     if (wave < ntiles) {
         const int t0 = blk_begin + wave * DECODE_TILE;
         const int t1 = t0 + NW * DECODE_TILE;
-        fast_tile<G, T, false, true>(a, bh, tab, lst, ptab, vbh, cq, t0, min(DECODE_TILE, blk_end - t0),
-                               t1 < blk_end ? min(DECODE_TILE, blk_end - t1) : 0, L, mw, kr, vr, m_run, l_run, accm);
+        fast_tile<G, T, SMODE, false, true>(a, bh, tab, lst, ptab, vbh, cq, t0, min(DECODE_TILE, blk_end - t0),
+                                            t1 < blk_end ? min(DECODE_TILE, blk_end - t1) : 0, L, mw, kr, vr, m_run,
+                                            l_run, accm, qn);
     }
     for (int tile = wave + NW; tile < ntiles; tile += NW) {
         const int t0 = blk_begin + tile * DECODE_TILE;
         const int t1 = t0 + NW * DECODE_TILE;     // this wave's next tile, if any
         uint4 vt[16];
-        fast_tile<G, T, true, false>(a, bh, tab, lst, ptab, vbh, cq, t0, min(DECODE_TILE, blk_end - t0),
-                              t1 < blk_end ? min(DECODE_TILE, blk_end - t1) : 0, L, mw, kr, vt, m_run, l_run, accm);
+        fast_tile<G, T, SMODE, true, false>(a, bh, tab, lst, ptab, vbh, cq, t0, min(DECODE_TILE, blk_end - t0),
+                                            t1 < blk_end ? min(DECODE_TILE, blk_end - t1) : 0, L, mw, kr, vt, m_run,
+                                            l_run, accm, qn);
     }
 
     float acc[G][8];
@@ -1220,23 +1240,33 @@ hipError_t launch_generic(const DecodeArgs& a, int G, dim3 grid, dim3 block, hip
     return hipGetLastError();
 }
 
+template <int SMODE>
+hipError_t launch_fast(const DecodeArgs& a, dim3 grid, dim3 block, hipStream_t stream) {
+    switch (a.T) {
+        case 26: hipLaunchKernelGGL((decode_fast_kernel<4, 26, SMODE>), grid, block, 0, stream, a); break;
+        case 38: hipLaunchKernelGGL((decode_fast_kernel<4, 38, SMODE>), grid, block, 0, stream, a); break;
+        case 48: hipLaunchKernelGGL((decode_fast_kernel<4, 48, SMODE>), grid, block, 0, stream, a); break;
+        default: hipLaunchKernelGGL((decode_fast_kernel<4, 64, SMODE>), grid, block, 0, stream, a); break;
+    }
+    return hipGetLastError();
+}
+
 // One launch: the split blocks, the last of which per (b, KV head) merges.
 // The sampled F always takes the generic kernel.
 hipError_t launch_decode(const DecodeArgs& a, int G, int BH, hipStream_t stream) {
     const dim3 grid(a.nsplit, BH), block(DECODE_THREADS);
     if (a.row_off) return launch_generic<0, false, true>(a, G, grid, block, stream);
     if (a.v_packed_mode) return launch_generic<0, true, false>(a, G, grid, block, stream);
-    if (!a.sampled && decode_fast_supported(G, a.T)) {
+    if (decode_fast_supported(G, a.T)) {
         const dim3 fblock(DECODE_FAST_THREADS);
         // the fast kernel's LDS is static (DECODE_FAST_LDS_BYTES)
         if (decode_fast_lds_bytes(G, a.T, a.nsplit) > (uint32_t)DECODE_FAST_LDS_BYTES) return hipErrorInvalidValue;
-        switch (a.T) {
-            case 26: hipLaunchKernelGGL((decode_fast_kernel<4, 26>), grid, fblock, 0, stream, a); break;
-            case 38: hipLaunchKernelGGL((decode_fast_kernel<4, 38>), grid, fblock, 0, stream, a); break;
-            case 48: hipLaunchKernelGGL((decode_fast_kernel<4, 48>), grid, fblock, 0, stream, a); break;
-            default: hipLaunchKernelGGL((decode_fast_kernel<4, 64>), grid, fblock, 0, stream, a); break;
+        switch (a.sampled) {
+            case 0: return launch_fast<0>(a, grid, fblock, stream);
+            case 4: return launch_fast<4>(a, grid, fblock, stream);
+            case 5: return launch_fast<5>(a, grid, fblock, stream);
+            default: return hipErrorInvalidValue;
         }
-        return hipGetLastError();
     }
     switch (a.sampled) {
         case 0: return launch_generic<0, false, false>(a, G, grid, block, stream);

@@ -350,7 +350,7 @@ int decode_call(const void* q, const void* k_packed, const uint32_t* mask, const
     // the fast kernel (8 waves, one block per CU) aims for 256 blocks; the
     // generic kernel (4 waves) for 512, two per CU, when two fit in LDS
     const bool ragged = row_off != nullptr;
-    const bool generic = vp || sampled || ragged || !decode_fast_supported(G, T);
+    const bool generic = vp || ragged || !decode_fast_supported(G, T);
     decode_plan(BH, S, splits, &nsplit, &chunk, generic ? DECODE_GENERIC_BLOCKS : 256);
     if (generic && splits == 0 &&
         decode_layout(G, T, nsplit, sampled != 0, Tv, ragged).lds_bytes > DECODE_LDS_PER_CU / 2)
