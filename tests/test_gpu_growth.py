@@ -95,3 +95,57 @@ def test_growth_full_size_s32k():
     """LLaMA-3.1-8B layer: prefill of 32704 tokens, then 64 generated tokens
     appended one by one up to S = 32768, decode checked every 16 steps."""
     growth_case(WORKLOADS["llama8b_s32k_l05"], 0, 0.5, 64, check_every=16)
+
+
+def test_graph_replays_of_every_decode_variant_match_eager():
+    """One graph holding a sampled-F decode, a K-and-V-pruned decode, a
+    ragged (SparK-p) decode and four append + decode steps of a growing
+    cache: every replay (with eager work and synchronisations between them)
+    reproduces the eager results bit for bit."""
+    w = WORKLOADS["tiny_s1k"].with_(S=1500)
+    x = gen.numpy_layer(w, seed=104, steps=4)
+    q_win, k, v = dev_bf16(x["q_win"]), dev_bf16(x["k"]), dev_bf16(x["v"])
+    qs = [dev_bf16(x["q_dec"][s]) for s in range(4)]
+    gs = ops.prefill_prune(q_win, k, w.n_kv, 0.5, recovery="gaussian")
+    gk = ops.prefill_prune(q_win, k, w.n_kv, 0.5)
+    gv = ops.prefill_prune_v(v, 0.5)
+    gp = ops.prefill_prune_topp(q_win, k, w.n_kv, 0.95)
+    S0 = 1496
+    cache = ops.GrowingCache(q_win, k[:, :, :S0].contiguous(), v[:, :, :S0].contiguous(), w.n_kv, 0.5, 1500)
+    k_new = [k[:, :, S0 + i].contiguous() for i in range(4)]
+    v_new = [v[:, :, S0 + i].contiguous() for i in range(4)]
+    outs = [torch.empty((w.B, w.n_q, 128), dtype=torch.float32, device="cuda:0") for _ in range(7)]
+
+    def work():
+        ops.decode_attn_sampled(qs[0], gs["k_packed"], gs["mask"], v, gs["chan_energy"], gs["r"], "gaussian", 99, 0.5,
+                                out=outs[0])
+        ops.decode_attn_kv(qs[1], gk["k_packed"], gk["mask"], gk["r"], gv["v_packed"], gv["v_mask"], gv["r_v"], 0.5,
+                           0.5, out=outs[1])
+        ops.decode_attn_ragged(qs[2], gp["k_packed"], gp["row_off"], gp["mask"], v, gp["r"], out=outs[2])
+        cache.S = S0
+        for i in range(4):
+            cache.append(k_new[i], v_new[i])
+            cache.decode(qs[i], out=outs[3 + i])
+
+    work()
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            work()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for o in outs:
+            o.fill_(float("nan"))
+        cache.mask[:, :, S0:].zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, (a_, b_) in enumerate(zip(outs, eager)):
+            assert torch.equal(a_, b_), (rep, i)
+        work()
+        torch.cuda.synchronize()
