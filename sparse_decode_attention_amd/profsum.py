@@ -73,6 +73,27 @@ def counter_table(runs: list, counters: list, title: str, note: str = "") -> str
     return "\n".join(out) + "\n"
 
 
+def kernel_counter_table(pmc_dir: str, counters: list, title: str, command: str, note: str = "",
+                         match: str = "spark::") -> str:
+    """One row per kernel of a --pmc run: each counter per dispatch (summed
+    over its dimension entries, averaged over dispatches), then the
+    instruction counts per wave."""
+    means = counter_means(pmc_dir, match)
+    out = [f"# {title}", "", "Command:", "", f"    {command}", ""]
+    if note:
+        out += [note, ""]
+    inst = [c for c in counters if c.startswith("SQ_INSTS_")]
+    head = ["kernel"] + counters + [f"{c[9:]} / wave" for c in inst]
+    out += ["| " + " | ".join(head) + " |", "|" + "---|" * len(head)]
+    for name in sorted(means, key=lambda n: -means[n].get("SQ_WAVES", 0)):
+        m = means[name]
+        waves = m.get("SQ_WAVES", 0)
+        row = [name.replace("spark::", "")] + [f"{m.get(c, float('nan')):.0f}" for c in counters]
+        row += [f"{m.get(c, 0) / waves:.0f}" if waves else "" for c in inst]
+        out.append("| " + " | ".join(row) + " |")
+    return "\n".join(out) + "\n"
+
+
 if __name__ == "__main__":
     stats_dir, title, command, out = sys.argv[1:5]
     note = sys.argv[5] if len(sys.argv) > 5 else ""
