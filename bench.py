@@ -482,8 +482,18 @@ def cpu_baseline(w, x, reps, T):
         "sample": f"{w.name}: 1 prefill prune+stats ({t1 - t0:.1f} s) and {n_dec} full-shape decode steps "
                   f"({dec_s:.2f} s each) in NumPy float64; decode effective bytes / decode time; "
                   f"BLAS threads {blas}, elementwise NumPy single-threaded, host has {os.cpu_count()} CPUs",
-        "prefill_s": t1 - t0, "decode_s_per_step": dec_s,
+        "prefill_s": t1 - t0, "decode_s_per_step": dec_s, "cpu_model": cpu_model(),
     }
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def summarize(kt_dir: str, fetch_dir: str, write_dir: str, workload: str, command: str) -> str:
@@ -545,7 +555,7 @@ Command (rocprofv3, three runs; the GPU-side numbers below come from it):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama8b_s32k_l05")
     ap.add_argument("--second", default="llama8b_s32k_l08", help="second reported workload ('' to skip)")
@@ -557,6 +567,7 @@ def main():
     ap.add_argument("--no-grouped", action="store_true", help="skip the SparK-g leg")
     ap.add_argument("--no-topp", action="store_true", help="skip the SparK-p leg")
     ap.add_argument("--no-growth", action="store_true", help="skip the growing-cache serving loop")
+    ap.add_argument("--no-shard", action="store_true", help="skip the TP-8 shard-shape leg")
     ap.add_argument("--warm", action="store_true", help="also report a run without replica rotation")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="run a plain device copy of this size after the legs (counter calibration)")
@@ -602,8 +613,10 @@ def main():
         "pct_hbm_peak": round(100 * main_leg["decode_GBps"] / HBM_PEAK_GBS, 2),
         "decode_us_per_launch": round(main_leg["decode_us_per_launch"], 3),
         "tokens_heads_per_s": main_leg["tokens_heads_per_s"],
+        "tokens_kv_heads_per_s": w.B * w.S * w.n_kv / (main_leg["decode_us_per_launch"] * 1e-6),
         "prefill": {"us": round(main_leg["prefill_us"], 2), "GBps": round(main_leg["prefill_GBps"], 1),
-                    "bytes": effective_prefill_bytes(w, T)},
+                    "bytes": effective_prefill_bytes(w, T),
+                    "tokens_kv_heads_per_s": w.B * w.S * w.n_kv / (main_leg["prefill_us"] * 1e-6)},
     }
     traffic = read_traffic(w.name)
     dec_bytes = main_leg["decode_bytes_per_step"]
@@ -657,6 +670,18 @@ def main():
                 "x_dense_v_time": round(lg["decode_us_per_launch"] / main_leg["decode_us_per_launch"], 3),
                 "prefill_us_k_and_v": round(lg["prefill_us"], 2), "replicas": lg["replicas"]}
             del lg
+        torch.cuda.empty_cache()
+    if not args.no_shard:
+        # one GPU's share of a tensor-parallel split over the 8 KV heads: one KV
+        # head and its 4 query heads at S = 32K (the kernel a TP-8 deployment runs)
+        ws = w.with_(name=w.name + "_tp8_shard", n_q=w.G, n_kv=1)
+        print(f"bench: TP-8 shard shape {ws.name}", file=sys.stderr, flush=True)
+        lg = run_leg(ws, min(args.steps, 5), min(args.warmup, 2))
+        line["tp8_shard"] = {"workload": ws.name, "B": ws.B, "N_q": ws.n_q, "N_kv": ws.n_kv, "S": ws.S,
+                             "lambda": ws.lam, "decode_us_per_launch": round(lg["decode_us_per_launch"], 3),
+                             "GBps": round(lg["decode_GBps"], 2), "bytes_per_launch": lg["decode_bytes_per_step"],
+                             "replicas": lg["replicas"]}
+        del lg
         torch.cuda.empty_cache()
     if not args.no_growth:
         print(f"bench: growing cache on {w.name}", file=sys.stderr, flush=True)

@@ -210,8 +210,9 @@ int spark_stats(const void* k_packed, const uint32_t* mask, const float* chan_en
  *  v        bf16 [B][N_kv][S][D]
  *  scale    softmax scale; <= 0 selects 1/sqrt(D)
  *  splits   sequence splits per (b, KV head); 0 lets the library choose
- *           (about 256 blocks in all for the G = 4, T in {26, 38, 64} kernel,
- *           512 otherwise when two blocks fit in one CU's LDS);
+ *           (about 256 blocks in all for the G = 4, T in {26, 38, 48, 64}
+ *           kernel, 512 otherwise when two blocks fit in one CU's LDS, and
+ *           never fewer 64-token tiles per block than its 8 or 4 waves);
  *           larger values are clamped to min(256, ceil(S / 64))
  *  out      fp32 [B][N_q][D]
  * No causal mask: the query attends to every cached token. fp32 arithmetic

@@ -57,11 +57,13 @@ PrefillWs prefill_layout(void* ws, int B, int S, int N_kv) {
     return w;
 }
 
-// About `blocks` blocks in all: 256 (one 8-wave block per CU) for the fast
-// kernel; the sampled F, which is bound by its arithmetic, asks for more so
-// that each SIMD holds two waves.
-int auto_splits(int BH, int S, int blocks) {
-    const int max_splits = (S + DECODE_TILE - 1) / DECODE_TILE;
+// About `blocks` blocks in all (256: one 8-wave block per CU for the fast
+// kernel; 512: two 4-wave blocks per CU for the generic one), but never fewer
+// tiles per block than the block has waves: with few (b, KV head) pairs (a
+// tensor-parallel shard of one KV head, say) more splits would leave waves
+// without work.
+int auto_splits(int BH, int S, int blocks, int waves) {
+    const int max_splits = (S + DECODE_TILE * waves - 1) / (DECODE_TILE * waves);
     int want = (blocks + BH - 1) / BH;
     if (want < 1) want = 1;
     if (want > max_splits) want = max_splits;
@@ -69,8 +71,9 @@ int auto_splits(int BH, int S, int blocks) {
 }
 
 // decode: the number of splits actually launched and the tokens per split
-void decode_plan(int BH, int S, int splits, int* nsplit, int* chunk, int blocks = 256) {
-    int n = splits > 0 ? splits : auto_splits(BH, S, blocks);
+void decode_plan(int BH, int S, int splits, int* nsplit, int* chunk, int blocks = 256,
+                 int waves = DECODE_FAST_THREADS / 64) {
+    int n = splits > 0 ? splits : auto_splits(BH, S, blocks, waves);
     const int max_splits = (S + DECODE_TILE - 1) / DECODE_TILE;
     if (n > max_splits) n = max_splits;
     if (n > DECODE_MAX_SPLITS) n = DECODE_MAX_SPLITS;
@@ -125,7 +128,7 @@ size_t spark_decode_workspace_bytes(int B, int S, int N_q, int N_kv, int D, int 
     if (B < 1 || S < 1 || N_kv < 1 || N_q < 1 || D < 1 || splits < 0 || N_q % N_kv) return 0;
     int nsplit, chunk;
     // sized for the larger of the two entry points' split plans
-    decode_plan(B * N_kv, S, splits, &nsplit, &chunk, DECODE_GENERIC_BLOCKS);
+    decode_plan(B * N_kv, S, splits, &nsplit, &chunk, DECODE_GENERIC_BLOCKS, DECODE_THREADS / 64);
     return decode_ws_bytes(B * N_kv, N_q / N_kv, nsplit);
 }
 
@@ -351,10 +354,11 @@ int decode_call(const void* q, const void* k_packed, const uint32_t* mask, const
     // generic kernel (4 waves) for 512, two per CU, when two fit in LDS
     const bool ragged = row_off != nullptr;
     const bool generic = vp || ragged || !decode_fast_supported(G, T);
-    decode_plan(BH, S, splits, &nsplit, &chunk, generic ? DECODE_GENERIC_BLOCKS : 256);
+    const int waves = generic ? DECODE_THREADS / 64 : DECODE_FAST_THREADS / 64;
+    decode_plan(BH, S, splits, &nsplit, &chunk, generic ? DECODE_GENERIC_BLOCKS : 256, waves);
     if (generic && splits == 0 &&
         decode_layout(G, T, nsplit, sampled != 0, Tv, ragged).lds_bytes > DECODE_LDS_PER_CU / 2)
-        decode_plan(BH, S, splits, &nsplit, &chunk, 256);
+        decode_plan(BH, S, splits, &nsplit, &chunk, 256, waves);
     if (ws_bytes < decode_ws_bytes(BH, G, nsplit)) return SPARK_ENOSPACE;
 
     char* base = static_cast<char*>(ws);
