@@ -1004,16 +1004,24 @@ __device__ __forceinline__ void fast_tile(const DecodeArgs& a, int bh, const uns
     float s[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) s[g] = cq[g];
+    constexpr int NB = 8;
+    // the list entries of each batch are requested one batch ahead, so their
+    // LDS round trip overlaps the previous batch's gathers
+    uint32_t off_next[NB];
 #pragma unroll
-    for (int r0 = 0; r0 < T; r0 += 4) {
-        constexpr int NB = 4;
+    for (int k = 0; k < NB; ++k)
+        if (k < T) off_next[k] = lrow16[k];
+#pragma unroll
+    for (int r0 = 0; r0 < T; r0 += NB) {
         // keep each batch's loads inside the batch: unbounded hoisting across
         // the fully unrolled slot loop would need registers for every slot
         __builtin_amdgcn_sched_barrier(0);
         uint32_t off[NB];
 #pragma unroll
+        for (int k = 0; k < NB; ++k) off[k] = off_next[k];
+#pragma unroll
         for (int k = 0; k < NB; ++k)
-            if (r0 + k < T) off[k] = lrow16[r0 + k];
+            if (r0 + NB + k < T) off_next[k] = lrow16[r0 + NB + k];
         float4 qv[NB];
         float rv[NB];
 #pragma unroll
