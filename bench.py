@@ -694,7 +694,7 @@ def main():
         lg = run_leg(w, min(args.steps, 5), min(args.warmup, 2), x=main_leg["x"], top_p=0.99)
         line["top_p"] = {
             "workload": w.name, "p": 0.99, "mean_kept": round(lg["T"], 2),
-            "pruning_ratio": round(1 - lg["T"] / w.D, 4), "kernel": f"decode_kernel<{w.G}, 0, false, true>",
+            "pruning_ratio": round(1 - lg["T"] / w.D, 4), "kernel": ("decode_fast_kernel<4, 128, 0, true>" if w.G == 4 else f"decode_kernel<{w.G}, 0, false, true>"),
             "decode_us_per_launch": round(lg["decode_us_per_launch"], 3), "bytes_per_launch": lg["decode_bytes_per_step"],
             "GBps": round(lg["decode_GBps"], 2), "pct_hbm_peak": round(100 * lg["decode_GBps"] / HBM_PEAK_GBS, 2),
             "prefill_us": round(lg["prefill_us"], 2), "replicas": lg["replicas"]}

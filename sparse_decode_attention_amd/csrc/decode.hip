@@ -936,6 +936,47 @@ __device__ __forceinline__ void load_row(const DecodeArgs& a, int bh, int t0, in
     }
 }
 
+// Ragged rows (SparK-p): the row of lane L's token starts at element o of the
+// head's packed region (S * 128 elements) and holds c = oe - o values. The
+// lane requests the dwords that cover the row, from the one holding element o:
+// whole 16-byte requests where all four dwords belong to the row, single
+// dwords at its end, so no request leaves the row's dwords (the region may end
+// right after the head's last row). Then kr[i] holds slots 2 i - sh and
+// 2 i - sh + 1 (sh = o & 1); registers past the row keep older values, which
+// the score loop never uses.
+constexpr int RAGGED_KR = 65;
+struct RaggedRows {
+    int sh, c;        // this tile's row: element shift and count
+    int o_nx, oe_nx;  // offsets of the next tile's row (requested a tile ahead)
+};
+__device__ __forceinline__ void ragged_offsets(const DecodeArgs& a, int bh, int t, int& o, int& oe) {
+    const int32_t* ro = a.row_off + (size_t)bh * (a.S + 1);
+    o = ro[t];
+    oe = ro[t + 1];
+}
+__device__ __forceinline__ void load_row_ragged(const DecodeArgs& a, int bh, int t, int o, int oe, uint4& mw,
+                                                uint32_t (&kr)[RAGGED_KR], RaggedRows& rr) {
+    typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+    mw = *reinterpret_cast<const uint4*>(a.mask + ((size_t)bh * a.S + t) * 4);
+    const int c = min(max(oe - o, 0), 128);
+    rr.sh = o & 1;
+    rr.c = c;
+    const int ndw = (rr.sh + c + 1) >> 1;
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(a.packed + (size_t)bh * a.S * 128) + (o >> 1);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        if (4 * i + 3 < ndw) {
+            const u32x4_a4 x = *reinterpret_cast<const u32x4_a4*>(src + 4 * i);
+            kr[4 * i] = x.x; kr[4 * i + 1] = x.y; kr[4 * i + 2] = x.z; kr[4 * i + 3] = x.w;
+        } else {
+            if (4 * i < ndw) kr[4 * i] = src[4 * i];
+            if (4 * i + 1 < ndw) kr[4 * i + 1] = src[4 * i + 1];
+            if (4 * i + 2 < ndw) kr[4 * i + 2] = src[4 * i + 2];
+        }
+    }
+    if (64 < ndw) kr[64] = src[64];
+}
+
 // Row stride (u16 elements) of the lane-major slot list: room for T slots and
 // a spare one, rounded so that the stride in dwords is odd, which puts the 64
 // lanes of a dword read on distinct bank pairs.
@@ -983,12 +1024,18 @@ __device__ __forceinline__ void build_list(const uint4& mw, uint8_t* lst, int L)
 // rows are requested once the scores have consumed this tile's; then P.V.
 // A request made while the memory queue is full stalls the wave, so none is
 // placed ahead of work that needs no memory.
-template <int G, int T, int SMODE, bool LOAD_V, bool LIST_READY>
+//
+// RG (ragged rows, T = 128): the score loop runs to the wave's longest row,
+// and a slot past its lane's row adds nothing (its list entry is a stale but
+// valid table offset, its value is discarded). The offsets of the tile after
+// next are requested once the next tile's rows are (nt_next2 tokens).
+template <int G, int T, int SMODE, bool LOAD_V, bool LIST_READY, bool RG = false>
 __device__ __forceinline__ void fast_tile(const DecodeArgs& a, int bh, const unsigned char* tab, uint8_t* lst,
                                           float* ptab, const uint16_t* vbh, const float (&cq)[G], int t0, int nt,
-                                          int nt_next, int L, uint4& mw, uint32_t (&kr)[(T + 1) / 2],
-                                          uint4 (&vr)[16], float (&m_run)[G], float (&l_run)[G],
-                                          f32x4 (&accm)[8], const float* qn) {
+                                          int nt_next, int L, uint4& mw,
+                                          uint32_t (&kr)[RG ? RAGGED_KR : (T + 1) / 2], uint4 (&vr)[16],
+                                          float (&m_run)[G], float (&l_run)[G], f32x4 (&accm)[8], const float* qn,
+                                          RaggedRows& rr, int nt_next2) {
     const int tau = L >> 4, oct = L & 15;
     const int t1 = t0 + (DECODE_FAST_THREADS / 64) * DECODE_TILE;
     if constexpr (!LIST_READY) build_list<T>(mw, lst, L);
@@ -1004,6 +1051,9 @@ __device__ __forceinline__ void fast_tile(const DecodeArgs& a, int bh, const uns
     float s[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) s[g] = cq[g];
+    // ragged rows: slots up to the wave's longest row (a wave-uniform bound)
+    const int nmax = RG ? (int)wave_max_dpp((float)rr.c) : T;
+    const uint32_t sh16 = RG ? 16u * (uint32_t)rr.sh : 0u;
     constexpr int NB = 8;
     // the list entries of each batch are requested one batch ahead, so their
     // LDS round trip overlaps the previous batch's gathers
@@ -1013,6 +1063,8 @@ __device__ __forceinline__ void fast_tile(const DecodeArgs& a, int bh, const uns
         if (k < T) off_next[k] = lrow16[k];
 #pragma unroll
     for (int r0 = 0; r0 < T; r0 += NB) {
+        // (ragged rows: batches past the longest row are skipped, uniformly)
+        if (RG && r0 >= nmax) continue;
         // keep each batch's loads inside the batch: unbounded hoisting across
         // the fully unrolled slot loop would need registers for every slot
         __builtin_amdgcn_sched_barrier(0);
@@ -1035,8 +1087,16 @@ __device__ __forceinline__ void fast_tile(const DecodeArgs& a, int bh, const uns
         for (int k = 0; k < NB; ++k) {
             if (r0 + k < T) {
                 const int rho = r0 + k;
-                const float kv = (rho & 1) ? bf16_hi(kr[rho >> 1]) : bf16_lo(kr[rho >> 1]);
-                const float e = kv - rv[k];
+                float kv;
+                if constexpr (RG) {
+                    // slots rho & ~1 and rho | 1 of the row, whatever its shift
+                    const uint32_t w = __builtin_amdgcn_alignbit(kr[(rho >> 1) + 1], kr[rho >> 1], sh16);
+                    kv = (rho & 1) ? bf16_hi(w) : bf16_lo(w);
+                } else {
+                    kv = (rho & 1) ? bf16_hi(kr[rho >> 1]) : bf16_lo(kr[rho >> 1]);
+                }
+                float e = kv - rv[k];
+                if (RG) e = rho < rr.c ? e : 0.0f;
                 s[0] = fmaf(qv[k].x, e, s[0]);
                 s[1] = fmaf(qv[k].y, e, s[1]);
                 s[2] = fmaf(qv[k].z, e, s[2]);
@@ -1056,7 +1116,16 @@ __device__ __forceinline__ void fast_tile(const DecodeArgs& a, int bh, const uns
         for (int g = 0; g < G; ++g) s[g] = -INFINITY;
     }
     // the packed rows are consumed: request the next tile's into them
-    if (nt_next > 0) load_row<T>(a, bh, t1, nt_next, L, mw, kr);
+    if constexpr (RG) {
+        if (nt_next > 0) {
+            load_row_ragged(a, bh, t1 + min(L, nt_next - 1), rr.o_nx, rr.oe_nx, mw, kr, rr);
+            if (nt_next2 > 0)
+                ragged_offsets(a, bh, t1 + (DECODE_FAST_THREADS / 64) * DECODE_TILE + min(L, nt_next2 - 1), rr.o_nx,
+                               rr.oe_nx);
+        }
+    } else {
+        if (nt_next > 0) load_row<T>(a, bh, t1, nt_next, L, mw, kr);
+    }
     softmax_tile_mf<G>(s, m_run, l_run, accm, ptab, L);
     wave_lds_sync();
     pv_tile_mf(vr, ptab, accm, L);
@@ -1071,13 +1140,17 @@ __device__ __forceinline__ void fast_tile(const DecodeArgs& a, int bh, const uns
 //
 // SMODE 4 / 5: the sampled F (Gaussian / Exponential); the r table then holds
 // mu / a_j, and a q' ns table of 2 KiB follows the other LDS.
-template <int G, int T, int SMODE>
+//
+// RG: ragged rows (SparK-p, T = 128 slots): row offsets are read a tile
+// ahead, each lane's row goes into 65 registers (load_row_ragged).
+template <int G, int T, int SMODE, bool RG = false>
 __global__ void __launch_bounds__(DECODE_FAST_THREADS)
 decode_fast_kernel(const DecodeArgs a) {
     // statically sized LDS: its base address is a compile-time constant, so
     // table offsets fold into the LDS instructions' offset fields
-    __shared__ __align__(16) unsigned char smem[DECODE_FAST_LDS_BYTES + (SMODE ? 128 * G * 4 : 0)];
-    float* qn = reinterpret_cast<float*>(smem + DECODE_FAST_LDS_BYTES);   // [128][G], sampled F only
+    constexpr uint32_t LDS = RG ? DECODE_FAST_RAGGED_LDS_BYTES : DECODE_FAST_LDS_BYTES;
+    __shared__ __align__(16) unsigned char smem[LDS + (SMODE ? 128 * G * 4 : 0)];
+    float* qn = reinterpret_cast<float*>(smem + LDS);   // [128][G], sampled F only
     // tables: q'_0..q'_3 of the group as a float4 per channel (2 KiB), then
     // r as one float per channel (512 bytes)
     constexpr uint32_t TAB = 16u;
@@ -1086,7 +1159,9 @@ decode_fast_kernel(const DecodeArgs a) {
     constexpr uint32_t LIST = list_bytes_of(T);
     constexpr uint32_t WAVE = LIST + 64u * G * 4u;
     constexpr int NW = DECODE_FAST_THREADS / 64;
-    static_assert(T % 2 == 0 && T > 0 && T < 128, "fast path needs an even 0 < T < 128");
+    static_assert(RG ? (T == 128 && SMODE == 0) : (T % 2 == 0 && T > 0 && T < 128),
+                  "fast path needs an even 0 < T < 128, or 128 slots for ragged rows");
+    constexpr int KR = RG ? RAGGED_KR : (T + 1) / 2;
     unsigned char* tab = smem;
     unsigned char* wbase = smem + TABLES + 16;
 
@@ -1127,20 +1202,40 @@ decode_fast_kernel(const DecodeArgs a) {
         rv = mu * inv_a;
         ns = (SMODE == 4 ? sigma : mu) * inv_a;
     }
+    // ragged rows: the first tile's row offsets are requested with q and r,
+    // the second tile's right after them
+    RaggedRows rr{};
+    int o0 = 0, oe0 = 0;
+    if constexpr (RG) {
+        const int tr0 = min(blk_begin + wave * DECODE_TILE, S - 1);
+        ragged_offsets(a, bh, tr0 + min(L, max(1, min(DECODE_TILE, blk_end - tr0)) - 1), o0, oe0);
+        const int t1 = blk_begin + (wave + NW) * DECODE_TILE;
+        if (t1 < blk_end) ragged_offsets(a, bh, t1 + min(L, min(DECODE_TILE, blk_end - t1) - 1), rr.o_nx, rr.oe_nx);
+    }
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
     uint4 mw;
-    uint32_t kr[(T + 1) / 2];
+    uint32_t kr[KR];
+    if constexpr (RG) {
+#pragma unroll
+        for (int i = 0; i < KR; ++i) kr[i] = 0u;
+    }
     uint4 vr[16];
     const uint16_t* vbh = a.v + (size_t)bh * a.S_cap * 128;
     // a wave without a tile (or an empty block) reads row min(t0, S-1)
     const int tf0 = min(blk_begin + wave * DECODE_TILE, S - 1);
     const int ntf0 = max(1, min(DECODE_TILE, blk_end - tf0));
-    load_row<T>(a, bh, tf0, ntf0, L, mw, kr);
+    if constexpr (RG) load_row_ragged(a, bh, tf0 + min(L, ntf0 - 1), o0, oe0, mw, kr, rr);
+    else load_row<T>(a, bh, tf0, ntf0, L, mw, kr);
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_sched_barrier(0);
     uint8_t* lst = wbase + (size_t)wave * WAVE;
     float* ptab = reinterpret_cast<float*>(wbase + (size_t)wave * WAVE + LIST);
+    if constexpr (RG) {
+        // slots past a row read whatever entry they find: start every entry
+        // at a valid table offset (channel 0)
+        for (uint32_t i = (uint32_t)L; i < LIST / 16u; i += 64u) reinterpret_cast<uint4*>(lst)[i] = make_uint4(0, 0, 0, 0);
+    }
     // the first tile's slot list needs only its masks: build it before
     // waiting for the table, then request the tile's V rows
     build_list<T>(mw, lst, L);
@@ -1184,18 +1279,20 @@ decode_fast_kernel(const DecodeArgs a) {
     // tiles request theirs at the start of the tile
     if (wave < ntiles) {
         const int t0 = blk_begin + wave * DECODE_TILE;
-        const int t1 = t0 + NW * DECODE_TILE;
-        fast_tile<G, T, SMODE, false, true>(a, bh, tab, lst, ptab, vbh, cq, t0, min(DECODE_TILE, blk_end - t0),
-                                            t1 < blk_end ? min(DECODE_TILE, blk_end - t1) : 0, L, mw, kr, vr, m_run,
-                                            l_run, accm, qn);
+        const int t1 = t0 + NW * DECODE_TILE, t2 = t1 + NW * DECODE_TILE;
+        fast_tile<G, T, SMODE, false, true, RG>(a, bh, tab, lst, ptab, vbh, cq, t0, min(DECODE_TILE, blk_end - t0),
+                                                t1 < blk_end ? min(DECODE_TILE, blk_end - t1) : 0, L, mw, kr, vr,
+                                                m_run, l_run, accm, qn, rr,
+                                                t2 < blk_end ? min(DECODE_TILE, blk_end - t2) : 0);
     }
     for (int tile = wave + NW; tile < ntiles; tile += NW) {
         const int t0 = blk_begin + tile * DECODE_TILE;
-        const int t1 = t0 + NW * DECODE_TILE;     // this wave's next tile, if any
+        const int t1 = t0 + NW * DECODE_TILE, t2 = t1 + NW * DECODE_TILE;   // this wave's next two tiles, if any
         uint4 vt[16];
-        fast_tile<G, T, SMODE, true, false>(a, bh, tab, lst, ptab, vbh, cq, t0, min(DECODE_TILE, blk_end - t0),
-                                            t1 < blk_end ? min(DECODE_TILE, blk_end - t1) : 0, L, mw, kr, vt, m_run,
-                                            l_run, accm, qn);
+        fast_tile<G, T, SMODE, true, false, RG>(a, bh, tab, lst, ptab, vbh, cq, t0, min(DECODE_TILE, blk_end - t0),
+                                                t1 < blk_end ? min(DECODE_TILE, blk_end - t1) : 0, L, mw, kr, vt,
+                                                m_run, l_run, accm, qn, rr,
+                                                t2 < blk_end ? min(DECODE_TILE, blk_end - t2) : 0);
     }
 
     float acc[G][8];
@@ -1221,6 +1318,7 @@ uint32_t decode_fast_lds_bytes(int G, int T, int nsplit) {
 }
 
 bool decode_fast_supported(int G, int T) { return G == 4 && (T == 26 || T == 38 || T == 48 || T == 64); }
+bool decode_fast_ragged_supported(int G) { return G == 4; }
 
 
 template <int SMODE, bool VP, bool RG>
@@ -1263,7 +1361,12 @@ hipError_t launch_fast(const DecodeArgs& a, dim3 grid, dim3 block, hipStream_t s
 // The sampled F always takes the generic kernel.
 hipError_t launch_decode(const DecodeArgs& a, int G, int BH, hipStream_t stream) {
     const dim3 grid(a.nsplit, BH), block(DECODE_THREADS);
-    if (a.row_off) return launch_generic<0, false, true>(a, G, grid, block, stream);
+    if (a.row_off) {
+        if (!decode_fast_ragged_supported(G)) return launch_generic<0, false, true>(a, G, grid, block, stream);
+        if (decode_fast_lds_bytes(G, 128, a.nsplit) > (uint32_t)DECODE_FAST_RAGGED_LDS_BYTES) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((decode_fast_kernel<4, 128, 0, true>), grid, dim3(DECODE_FAST_THREADS), 0, stream, a);
+        return hipGetLastError();
+    }
     if (a.v_packed_mode) return launch_generic<0, true, false>(a, G, grid, block, stream);
     if (decode_fast_supported(G, a.T)) {
         const dim3 fblock(DECODE_FAST_THREADS);

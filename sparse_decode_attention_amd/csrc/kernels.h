@@ -11,6 +11,8 @@
 // LDS of the fast decode kernel: q' and r tables with a flag slot (2576 B),
 // then per wave the slot list of the largest T (64 lanes x 68 u16) and 1 KiB of p
 #define DECODE_FAST_LDS_BYTES (2576 + (DECODE_FAST_THREADS / 64) * (8704 + 1024))
+// the ragged-row variant: a slot list of 128 slots (64 lanes x 132 u16)
+#define DECODE_FAST_RAGGED_LDS_BYTES (2576 + (DECODE_FAST_THREADS / 64) * (16896 + 1024))
 #define DECODE_TILE 64
 #define DECODE_MAX_SPLITS 256
 #define DECODE_RAGGED_CHUNKS (DECODE_TILE * 128 * 2 / 16 + 1)   // 16-byte chunks of a tile of full rows, + misalignment
@@ -121,6 +123,8 @@ hipError_t launch_read_stream(const void* src, size_t bytes, uint32_t* sink, int
 // Launch the decode kernel for group size G; returns a hipError_t.
 hipError_t launch_decode(const DecodeArgs& a, int G, int BH, hipStream_t stream);
 bool decode_fast_supported(int G, int T);
+// ragged rows (SparK-p) on the fast kernel
+bool decode_fast_ragged_supported(int G);
 DecodeLayout decode_layout(int G, int T, int nsplit, bool sampled, int Tv, bool ragged = false);
 
 }  // namespace spark
