@@ -938,12 +938,13 @@ __device__ __forceinline__ void load_row(const DecodeArgs& a, int bh, int t0, in
 
 // Ragged rows (SparK-p): the row of lane L's token starts at element o of the
 // head's packed region (S * 128 elements) and holds c = oe - o values. The
-// lane requests the dwords that cover the row, from the one holding element o:
-// whole 16-byte requests where all four dwords belong to the row, single
-// dwords at its end, so no request leaves the row's dwords (the region may end
-// right after the head's last row). Then kr[i] holds slots 2 i - sh and
-// 2 i - sh + 1 (sh = o & 1); registers past the row keep older values, which
-// the score loop never uses.
+// lane requests the 65 dwords from the one holding element o on (sixteen
+// 16-byte requests and one dword, no branches), so kr[i] holds slots 2 i - sh
+// and 2 i - sh + 1 (sh = o & 1); what lies past the row is never used. A lane
+// whose 65 dwords would leave the region (a row near the end of a nearly full
+// region, which may end the allocation) requests the region's first 65
+// instead and then, in a branch taken only when the wave has such a lane,
+// exactly its row's dwords, one by one.
 constexpr int RAGGED_KR = 65;
 struct RaggedRows {
     int sh, c;        // this tile's row: element shift and count
@@ -962,19 +963,24 @@ __device__ __forceinline__ void load_row_ragged(const DecodeArgs& a, int bh, int
     rr.sh = o & 1;
     rr.c = c;
     const int ndw = (rr.sh + c + 1) >> 1;
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(a.packed + (size_t)bh * a.S * 128) + (o >> 1);
+    const int o_dw = o >> 1;
+    const bool near_end = o_dw + RAGGED_KR > a.S * 64;
+    const uint32_t* head = reinterpret_cast<const uint32_t*>(a.packed + (size_t)bh * a.S * 128);
+    const uint32_t* src = head + (near_end ? 0 : o_dw);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-        if (4 * i + 3 < ndw) {
-            const u32x4_a4 x = *reinterpret_cast<const u32x4_a4*>(src + 4 * i);
-            kr[4 * i] = x.x; kr[4 * i + 1] = x.y; kr[4 * i + 2] = x.z; kr[4 * i + 3] = x.w;
-        } else {
-            if (4 * i < ndw) kr[4 * i] = src[4 * i];
-            if (4 * i + 1 < ndw) kr[4 * i + 1] = src[4 * i + 1];
-            if (4 * i + 2 < ndw) kr[4 * i + 2] = src[4 * i + 2];
+        const u32x4_a4 x = *reinterpret_cast<const u32x4_a4*>(src + 4 * i);
+        kr[4 * i] = x.x; kr[4 * i + 1] = x.y; kr[4 * i + 2] = x.z; kr[4 * i + 3] = x.w;
+    }
+    kr[64] = src[64];
+    if (ballot(near_end) != 0) {
+        if (near_end) {
+            const uint32_t* row = head + o_dw;
+#pragma unroll
+            for (int i = 0; i < RAGGED_KR; ++i)
+                if (i < ndw) kr[i] = row[i];
         }
     }
-    if (64 < ndw) kr[64] = src[64];
 }
 
 // Row stride (u16 elements) of the lane-major slot list: room for T slots and
@@ -1318,7 +1324,8 @@ uint32_t decode_fast_lds_bytes(int G, int T, int nsplit) {
 }
 
 bool decode_fast_supported(int G, int T) { return G == 4 && (T == 26 || T == 38 || T == 48 || T == 64); }
-bool decode_fast_ragged_supported(int G) { return G == 4; }
+// (the ragged rows' loads assume a region of at least 65 dwords: S >= 2)
+bool decode_fast_ragged_supported(int G, int S) { return G == 4 && S >= 2; }
 
 
 template <int SMODE, bool VP, bool RG>
@@ -1362,7 +1369,7 @@ hipError_t launch_fast(const DecodeArgs& a, dim3 grid, dim3 block, hipStream_t s
 hipError_t launch_decode(const DecodeArgs& a, int G, int BH, hipStream_t stream) {
     const dim3 grid(a.nsplit, BH), block(DECODE_THREADS);
     if (a.row_off) {
-        if (!decode_fast_ragged_supported(G)) return launch_generic<0, false, true>(a, G, grid, block, stream);
+        if (!decode_fast_ragged_supported(G, a.S)) return launch_generic<0, false, true>(a, G, grid, block, stream);
         if (decode_fast_lds_bytes(G, 128, a.nsplit) > (uint32_t)DECODE_FAST_RAGGED_LDS_BYTES) return hipErrorInvalidValue;
         hipLaunchKernelGGL((decode_fast_kernel<4, 128, 0, true>), grid, dim3(DECODE_FAST_THREADS), 0, stream, a);
         return hipGetLastError();

@@ -124,7 +124,7 @@ hipError_t launch_read_stream(const void* src, size_t bytes, uint32_t* sink, int
 hipError_t launch_decode(const DecodeArgs& a, int G, int BH, hipStream_t stream);
 bool decode_fast_supported(int G, int T);
 // ragged rows (SparK-p) on the fast kernel
-bool decode_fast_ragged_supported(int G);
+bool decode_fast_ragged_supported(int G, int S);
 DecodeLayout decode_layout(int G, int T, int nsplit, bool sampled, int Tv, bool ragged = false);
 
 }  // namespace spark

@@ -353,7 +353,7 @@ int decode_call(const void* q, const void* k_packed, const uint32_t* mask, const
     // the fast kernel (8 waves, one block per CU) aims for 256 blocks; the
     // generic kernel (4 waves) for 512, two per CU, when two fit in LDS
     const bool ragged = row_off != nullptr;
-    const bool generic = vp || (ragged ? !decode_fast_ragged_supported(G) : !decode_fast_supported(G, T));
+    const bool generic = vp || (ragged ? !decode_fast_ragged_supported(G, S) : !decode_fast_supported(G, T));
     const int waves = generic ? DECODE_THREADS / 64 : DECODE_FAST_THREADS / 64;
     decode_plan(BH, S, splits, &nsplit, &chunk, generic ? DECODE_GENERIC_BLOCKS : 256, waves);
     if (generic && splits == 0 &&

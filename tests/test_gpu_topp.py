@@ -116,3 +116,65 @@ def test_topp_decode_ignores_unwritten_capacity():
     r_ref, _ = oracle.stats(f["k"], ref["mask"], ref["A"])
     assert_tol(out.cpu().numpy(), oracle.decode_attn(f["q_dec"][0], ref["packed"], ref["mask"], f["v"], r_ref),
                "NaN-filled capacity")
+
+
+def hand_built_ragged(counts, seed, n_q_per_kv=4):
+    """A ragged cache built directly from per-token counts (0..128): random
+    kept channels per token, rows packed back to back from element 0 of each
+    head's region, NaN in the capacity past the last row."""
+    rng = np.random.default_rng(seed)
+    B, H, S = counts.shape
+    D = 128
+    ranks = rng.random((B, H, S, D)).argsort(-1).argsort(-1)
+    mask = ranks < counts[..., None]
+    kbits = gen.f32_to_bf16_bits(rng.standard_normal((B, H, S, D)).astype(np.float32))
+    vbits = gen.f32_to_bf16_bits(rng.standard_normal((B, H, S, D)).astype(np.float32))
+    qbits = gen.f32_to_bf16_bits(rng.standard_normal((B, H * n_q_per_kv, D)).astype(np.float32))
+    r = (0.3 * rng.standard_normal((B, H, D))).astype(np.float32)
+    kp = torch.full((B, H, S * D), float("nan"), dtype=torch.bfloat16, device="cuda:0")
+    for b in range(B):
+        for h in range(H):
+            rows = kbits[b, h][mask[b, h]]
+            if rows.size:
+                kp[b, h, :rows.size] = dev_bf16(rows)
+    row_off = np.zeros((B, H, S + 1), np.int32)
+    row_off[..., 1:] = np.cumsum(counts, axis=-1)
+    words = np.packbits(mask, axis=-1, bitorder="little").view(np.uint32)   # bit b of word w: channel 32 w + b
+    dev = {"q": dev_bf16(qbits), "k_packed": kp, "row_off": torch.from_numpy(row_off).to("cuda:0"),
+           "mask": torch.from_numpy(words.view(np.int32).copy()).to("cuda:0"), "v": dev_bf16(vbits),
+           "r": torch.from_numpy(r).to("cuda:0")}
+    kf = gen.bf16_bits_to_f32(kbits)
+    want = oracle.decode_attn(gen.bf16_bits_to_f32(qbits), kf[mask], mask, gen.bf16_bits_to_f32(vbits), r)
+    return dev, want
+
+
+@pytest.mark.parametrize("splits", [0, 3])
+def test_ragged_decode_full_region_and_every_count(splits):
+    """Head 0 keeps all 128 channels of every token, so its region is full to
+    the last element and the rows of its final tiles take the kernel's
+    near-end path; head 1 mixes every count from 0 to 128 (odd and even row
+    starts); head 2 keeps nothing (scores reduce to q . r). S spans several
+    tiles and a ragged tail."""
+    S = 600
+    rng = np.random.default_rng(87)
+    counts = np.stack([np.full(S, 128), rng.permutation(np.arange(S) % 129), np.zeros(S, int),
+                       rng.integers(60, 120, S)])[None].astype(np.int64)
+    d, want = hand_built_ragged(counts, 88)
+    out = ops.decode_attn_ragged(d["q"], d["k_packed"], d["row_off"], d["mask"], d["v"], d["r"], splits=splits)
+    torch.cuda.synchronize()
+    assert_tol(out.cpu().numpy(), want, "hand-built ragged cache")
+
+
+def test_ragged_decode_rows_at_the_end_of_full_regions_batch2():
+    """B = 2, every head full to its last element but one short row near its
+    end, so the last rows start at odd and even elements within the last 65
+    dwords of the allocation."""
+    S = 130
+    counts = np.full((2, 2, S), 128, np.int64)
+    counts[0, 1, -3] = 77
+    counts[1, 0, -1] = 1
+    counts[1, 1, -2] = 0
+    d, want = hand_built_ragged(counts, 89)
+    out = ops.decode_attn_ragged(d["q"], d["k_packed"], d["row_off"], d["mask"], d["v"], d["r"])
+    torch.cuda.synchronize()
+    assert_tol(out.cpu().numpy(), want, "full regions, short rows at the end")
