@@ -5,7 +5,11 @@
 
 #define PRUNE_TOKENS_PER_BLOCK 64
 #define CHAN_ENERGY_ROWS 128
-#define STATS_PARTS 8
+// stats reduction: per (b, kv head) STATS_CH_BLOCKS blocks of 128 / STATS_CH_BLOCKS channels,
+// each channel summed over STATS_PARTS ranges of block partials
+#define STATS_CH_BLOCKS 4
+#define STATS_PARTS 32
+#define STATS_THREADS 1024
 #define DECODE_THREADS 256
 #define DECODE_FAST_THREADS 512
 // LDS of the fast decode kernel: q' and r tables with a flag slot (2576 B),

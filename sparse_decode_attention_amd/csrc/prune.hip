@@ -31,11 +31,29 @@ chan_energy_kernel(const uint16_t* __restrict__ q_win, float* __restrict__ A,
     for (int r0 = 0; r0 < R; r0 += CHAN_ENERGY_ROWS) {
         const int nr = min(CHAN_ENERGY_ROWS, R - r0);
         __syncthreads();
-        for (int i = threadIdx.x; i < nr * 16; i += blockDim.x) rows[i] = src[(size_t)r0 * 16 + i];
+        // every load of the batch in flight before the first LDS write (no
+        // conditions, which would let each load sink to its write: threads
+        // past the end rewrite the last chunk with the same value)
+        constexpr int PER = CHAN_ENERGY_ROWS * 16 / 256;
+        uint4 tmp[PER];
+#pragma unroll
+        for (int u = 0; u < PER; ++u) tmp[u] = src[(size_t)r0 * 16 + min((int)threadIdx.x + u * 256, nr * 16 - 1)];
+#pragma unroll
+        for (int u = 0; u < PER; ++u) rows[min((int)threadIdx.x + u * 256, nr * 16 - 1)] = tmp[u];
         __syncthreads();
         if (j < 128) {
             const uint16_t* rr = reinterpret_cast<const uint16_t*>(rows);
-            for (int i = 0; i < nr; ++i) {
+            // rows in batches of 16: the LDS reads of a batch are all in
+            // flight before its (sequential) additions
+            int i = 0;
+            for (; i + 16 <= nr; i += 16) {
+                float x[16];
+#pragma unroll
+                for (int u = 0; u < 16; ++u) x[u] = bf16_to_f32(rr[(i + u) * 128 + j]);
+#pragma unroll
+                for (int u = 0; u < 16; ++u) acc = (qagg == 0) ? __fadd_rn(acc, __fmul_rn(x[u], x[u])) : __fadd_rn(acc, x[u]);
+            }
+            for (; i < nr; ++i) {
                 const float x = bf16_to_f32(rr[i * 128 + j]);
                 acc = (qagg == 0) ? __fadd_rn(acc, __fmul_rn(x, x)) : __fadd_rn(acc, x);
             }
@@ -466,47 +484,85 @@ stats_partial_kernel(const uint16_t* __restrict__ k_packed, const uint32_t* __re
 }
 
 // ---------------------------------------------------------------- partials -> r
-// One block per (b, kv head): thread (part, j) sums a contiguous range of the
-// block partials of channel j, then the STATS_PARTS ranges are added in
-// order, so the result is the same on every run.
-__global__ void __launch_bounds__(128 * STATS_PARTS)
+// Grid (b * N_kv, STATS_CH_BLOCKS): block y takes channels 32 y .. 32 y + 31
+// of one (b, kv head), so the partials are read by that many CUs per head.
+// Thread (part, jl) sums a contiguous range of the block partials of its
+// channel, then the STATS_PARTS ranges are added in order, so the result is
+// the same on every run.
+__global__ void __launch_bounds__(STATS_THREADS)
 stats_reduce_kernel(const double* __restrict__ part_sum, const int32_t* __restrict__ part_cnt,
                     const double* __restrict__ part_pruned, const float* __restrict__ A,
                     float* __restrict__ r, int32_t* __restrict__ cnt,
                     int S, int T, int nblk, int recovery, float f_const) {
-    __shared__ double sh_s[STATS_PARTS][128];
-    __shared__ long long sh_c[STATS_PARTS][128];
+    constexpr int NCH = 128 / STATS_CH_BLOCKS;
+    static_assert(NCH * STATS_PARTS == STATS_THREADS, "one thread per (part, channel)");
+    __shared__ double sh_s[STATS_PARTS][NCH];
+    __shared__ long long sh_c[STATS_PARTS][NCH];
     __shared__ double sh_p[STATS_PARTS][2];
-    __shared__ long long sh_tot[128];
-    const int bh = blockIdx.x, j = threadIdx.x & 127, part = threadIdx.x >> 7;
+    __shared__ long long sh_k[STATS_THREADS / 64];
+    const int bh = blockIdx.x, tid = threadIdx.x;
+    const int jl = tid % NCH, part = tid / NCH;
+    const int j = blockIdx.y * NCH + jl;
     const int per = (nblk + STATS_PARTS - 1) / STATS_PARTS;
-    const int lo = part * per, hi = min(nblk, lo + per);
+    const int lo = min(nblk, part * per), hi = min(nblk, lo + per);
     double s = 0.0, p = 0.0;
     long long c = 0;
-#pragma unroll 8
-    for (int blk = lo; blk < hi; ++blk) {
-        s += part_sum[((size_t)bh * nblk + blk) * 128 + j];
-        c += part_cnt[((size_t)bh * nblk + blk) * 128 + j];
+    // batches of 16 partials: their loads are all in flight before the
+    // (sequential) additions
+    constexpr int NBAT = 16;
+    for (int b0 = lo; b0 < hi; b0 += NBAT) {
+        double xs[NBAT];
+        int32_t xc[NBAT];
+#pragma unroll
+        for (int u = 0; u < NBAT; ++u) {
+            const int blk = min(b0 + u, hi - 1);
+            xs[u] = part_sum[((size_t)bh * nblk + blk) * 128 + j];
+            xc[u] = part_cnt[((size_t)bh * nblk + blk) * 128 + j];
+        }
+#pragma unroll
+        for (int u = 0; u < NBAT; ++u) {
+            if (b0 + u < hi) {
+                s += xs[u];
+                c += xc[u];
+            }
+        }
     }
-    if (recovery >= 3 && j < 2) {
-        for (int blk = lo; blk < hi; ++blk) p += part_pruned[((size_t)bh * nblk + blk) * 2 + j];
-        sh_p[part][j] = p;
+    if (recovery >= 3 && jl < 2) {
+        constexpr int NBP = 8;
+        for (int b0 = lo; b0 < hi; b0 += NBP) {
+            double xp[NBP];
+#pragma unroll
+            for (int u = 0; u < NBP; ++u) xp[u] = part_pruned[((size_t)bh * nblk + min(b0 + u, hi - 1)) * 2 + jl];
+#pragma unroll
+            for (int u = 0; u < NBP; ++u)
+                if (b0 + u < hi) p += xp[u];
+        }
+        sh_p[part][jl] = p;
     }
-    sh_s[part][j] = s;
-    sh_c[part][j] = c;
-    __syncthreads();
-    s = 0.0;
-    c = 0;
-    for (int q = 0; q < STATS_PARTS; ++q) { s += sh_s[q][j]; c += sh_c[q][j]; }
-    // ragged rows (T < 0): the pruned count is S * 128 minus all kept entries
-    if (part == 0) sh_tot[j] = c;
+    sh_s[part][jl] = s;
+    sh_c[part][jl] = c;
+    // ragged rows (T < 0) with a pruned-saliency F: the pruned count is
+    // S * 128 minus every kept entry of the head, all channels (an integer
+    // sum, so its order does not matter)
+    long long kept_all = (long long)S * (T < 0 ? 0 : T);
+    if (T < 0 && recovery >= 3) {
+        long long k = 0;
+        const int32_t* pc = part_cnt + (size_t)bh * nblk * 128;
+        for (size_t e = tid; e < (size_t)nblk * 128; e += STATS_THREADS) k += pc[e];
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) k += __shfl_xor(k, o, 64);
+        if ((tid & 63) == 0) sh_k[tid >> 6] = k;
+    }
     __syncthreads();
     if (part != 0) return;
-    long long kept_all = (long long)S * (T < 0 ? 0 : T);
-    if (T < 0) {
+    if (T < 0 && recovery >= 3) {
         kept_all = 0;
-        for (int q = 0; q < 128; ++q) kept_all += sh_tot[q];
+        for (int q = 0; q < STATS_THREADS / 64; ++q) kept_all += sh_k[q];
     }
+    s = 0.0;
+    c = 0;
+#pragma unroll 8
+    for (int q = 0; q < STATS_PARTS; ++q) { s += sh_s[q][jl]; c += sh_c[q][jl]; }
     float out = 0.f;
     if (recovery == 0) {
         out = c > 0 ? (float)(s / (double)c) : 0.f;
@@ -515,6 +571,7 @@ stats_reduce_kernel(const double* __restrict__ part_sum, const int32_t* __restri
     } else if (recovery >= 3) {
         double p2 = 0.0;
         p = 0.0;
+#pragma unroll 8
         for (int q = 0; q < STATS_PARTS; ++q) { p += sh_p[q][0]; p2 += sh_p[q][1]; }
         const double npruned = (double)S * 128.0 - (double)kept_all;
         const double mu = npruned > 0 ? p / npruned : 0.0;

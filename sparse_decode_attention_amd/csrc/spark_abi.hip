@@ -158,7 +158,7 @@ int spark_prefill_prune_cap(const void* q_win, const void* k, int B, int S, int 
                        static_cast<const uint16_t*>(k), chan_energy, static_cast<uint16_t*>(k_packed), mask,
                        w.sum, w.cnt, w.pruned, S, T, w.nblk, recovery, static_cast<const uint8_t*>(nullptr),
                        GroupSpec{}, 0.0f, static_cast<int32_t*>(nullptr), static_cast<int32_t*>(nullptr), S_cap);
-    hipLaunchKernelGGL(stats_reduce_kernel, dim3(BH), dim3(128 * STATS_PARTS), 0, st,
+    hipLaunchKernelGGL(stats_reduce_kernel, dim3(BH, STATS_CH_BLOCKS), dim3(STATS_THREADS), 0, st,
                        w.sum, w.cnt, w.pruned, chan_energy, r, cnt, S, T, w.nblk, recovery, f_const);
     return hip_status(hipGetLastError());
 }
@@ -206,7 +206,7 @@ int spark_prefill_prune_v(const void* v, int B, int S, int N_kv, int D, float la
                        static_cast<uint16_t*>(v_packed), v_mask, w.sum, w.cnt, w.pruned, S, T, w.nblk,
                        (int)SPARK_F_MEAN_RETAINED, static_cast<const uint8_t*>(nullptr), GroupSpec{}, 0.0f,
                        static_cast<int32_t*>(nullptr), static_cast<int32_t*>(nullptr), S);
-    hipLaunchKernelGGL(stats_reduce_kernel, dim3(BH), dim3(128 * STATS_PARTS), 0, st, w.sum, w.cnt, w.pruned,
+    hipLaunchKernelGGL(stats_reduce_kernel, dim3(BH, STATS_CH_BLOCKS), dim3(STATS_THREADS), 0, st, w.sum, w.cnt, w.pruned,
                        static_cast<const float*>(nullptr), r_v, cnt, S, T, w.nblk, (int)SPARK_F_MEAN_RETAINED, 0.0f);
     return hip_status(hipGetLastError());
 }
@@ -244,7 +244,7 @@ int spark_prefill_prune_grouped(const void* q_win, const void* k, int B, int S, 
                        static_cast<uint16_t*>(k_packed), mask, w.sum, w.cnt, w.pruned, S, T, w.nblk, recovery,
                        static_cast<const uint8_t*>(w.gid), grp, 0.0f, static_cast<int32_t*>(nullptr),
                        static_cast<int32_t*>(nullptr), S);
-    hipLaunchKernelGGL(stats_reduce_kernel, dim3(BH), dim3(128 * STATS_PARTS), 0, st,
+    hipLaunchKernelGGL(stats_reduce_kernel, dim3(BH, STATS_CH_BLOCKS), dim3(STATS_THREADS), 0, st,
                        w.sum, w.cnt, w.pruned, chan_energy, r, cnt, S, T, w.nblk, recovery, f_const);
     return hip_status(hipGetLastError());
 }
@@ -280,7 +280,7 @@ int spark_prefill_prune_topp(const void* q_win, const void* k, int B, int S, int
     hipLaunchKernelGGL(topp_pack_kernel, dim3(w.nblk, BH), dim3(256), 0, st, static_cast<const uint16_t*>(k),
                        static_cast<const uint32_t*>(mask), static_cast<uint16_t*>(k_packed), row_off,
                        static_cast<const int32_t*>(w.blk), S, w.nblk);
-    hipLaunchKernelGGL(stats_reduce_kernel, dim3(BH), dim3(128 * STATS_PARTS), 0, st,
+    hipLaunchKernelGGL(stats_reduce_kernel, dim3(BH, STATS_CH_BLOCKS), dim3(STATS_THREADS), 0, st,
                        w.sum, w.cnt, w.pruned, chan_energy, r, cnt, S, -1, w.nblk, recovery, f_const);
     return hip_status(hipGetLastError());
 }
@@ -306,7 +306,7 @@ int spark_stats(const void* k_packed, const uint32_t* mask, const float* chan_en
     hipLaunchKernelGGL(stats_partial_kernel, dim3(w.nblk, BH), dim3(256), 0, st,
                        static_cast<const uint16_t*>(k_packed), mask, static_cast<const uint16_t*>(k_dense),
                        chan_energy, w.sum, w.cnt, w.pruned, S, T, w.nblk, recovery);
-    hipLaunchKernelGGL(stats_reduce_kernel, dim3(BH), dim3(128 * STATS_PARTS), 0, st,
+    hipLaunchKernelGGL(stats_reduce_kernel, dim3(BH, STATS_CH_BLOCKS), dim3(STATS_THREADS), 0, st,
                        w.sum, w.cnt, w.pruned, chan_energy, r, cnt, S, T, w.nblk, recovery, f_const);
     return hip_status(hipGetLastError());
 }
