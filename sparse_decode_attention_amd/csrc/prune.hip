@@ -88,14 +88,17 @@ template <bool MASKED>
 __device__ __forceinline__ void select_top(uint32_t key0, uint32_t key1, bool in0, bool in1, int Tg, bool& kept0,
                                            bool& kept1) {
     uint32_t v = 0;
-    bool exact = false;
 #pragma unroll
     for (int bit = 30; bit >= 0; --bit) {
         const uint32_t c = __builtin_amdgcn_readfirstlane(v | (1u << bit));
         const int n = __popcll(ballot((!MASKED || in0) && key0 >= c)) + __popcll(ballot((!MASKED || in1) && key1 >= c));
         v = n >= Tg ? c : v;
-        if (n == Tg) { exact = true; break; }
+        if (n == Tg) break;
     }
+    // whether exactly Tg keys are >= v, counted once here rather than
+    // carried through every step of the search
+    const bool exact = __popcll(ballot((!MASKED || in0) && key0 >= v)) +
+                       __popcll(ballot((!MASKED || in1) && key1 >= v)) == Tg;
     if (exact) {
         kept0 = (!MASKED || in0) && key0 >= v;
         kept1 = (!MASKED || in1) && key1 >= v;
