@@ -188,9 +188,11 @@ __global__ void __launch_bounds__(NWV * 64) evict_stats_kernel(const EvictArgs a
                     float mn = m[mb][e];
 #pragma unroll
                     for (int n = 0; n < NB; ++n) mn = fmaxf(mn, s[n][mb][e]);
-                    float acc = l[mb][e] * exp2f(m[mb][e] - mn);
+                    // the hardware exp2 (v_exp_f32, about 1 ulp, no denormal
+                    // rescaling): every term is at most 1 and the sum at least 1
+                    float acc = l[mb][e] * __builtin_amdgcn_exp2f(m[mb][e] - mn);
 #pragma unroll
-                    for (int n = 0; n < NB; ++n) acc += exp2f(s[n][mb][e] - mn);
+                    for (int n = 0; n < NB; ++n) acc += __builtin_amdgcn_exp2f(s[n][mb][e] - mn);
                     l[mb][e] = acc;
                     m[mb][e] = mn;
                 }
@@ -279,7 +281,7 @@ __global__ void __launch_bounds__(NWV * 64) evict_score_kernel(const EvictArgs a
 #pragma unroll
                 for (int mb = 0; mb < MBW; ++mb)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) acc = fmaf(exp2f(s[mb][e] - M[mb][e]), iL[mb][e], acc);
+                    for (int e = 0; e < 4; ++e) acc = fmaf(__builtin_amdgcn_exp2f(s[mb][e] - M[mb][e]), iL[mb][e], acc);
                 // rows 4 (lane >> 4) + e of every block: add the four lane quarters
                 acc = xor32_sum(xor16_sum(acc));
                 if (L < 16) out[t0 + 16 * n - tb + L] = acc;
