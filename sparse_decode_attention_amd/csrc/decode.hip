@@ -315,8 +315,10 @@ __device__ __forceinline__ void softmax_tile(const float (&s)[G], float (&m_run)
     for (int g = 0; g < G; ++g) {
         const float mt = wave_max_dpp(s[g]);
         const float mn = fmaxf(m_run[g], mt);
-        alpha[g] = exp2f(m_run[g] - mn);
-        const float p = exp2f(s[g] - mn);
+        // hardware exp2 (v_exp_f32, about 1 ulp, no denormal rescaling):
+        // both arguments are <= 0, so every value is at most 1
+        alpha[g] = __builtin_amdgcn_exp2f(m_run[g] - mn);
+        const float p = __builtin_amdgcn_exp2f(s[g] - mn);
         l_run[g] = l_run[g] * alpha[g] + p;
         m_run[g] = mn;
         ptab[L * G + g] = p;
@@ -869,8 +871,10 @@ __device__ __forceinline__ void softmax_tile_mf(const float (&s)[G], float (&m_r
     for (int g = 0; g < G; ++g) {
         const float mt = wave_max_dpp(s[g]);
         const float mn = fmaxf(m_run[g], mt);
-        alpha[g] = exp2f(m_run[g] - mn);
-        const float p = exp2f(s[g] - mn);
+        // hardware exp2 (v_exp_f32, about 1 ulp, no denormal rescaling):
+        // both arguments are <= 0, so every value is at most 1
+        alpha[g] = __builtin_amdgcn_exp2f(m_run[g] - mn);
+        const float p = __builtin_amdgcn_exp2f(s[g] - mn);
         l_run[g] = l_run[g] * alpha[g] + p;
         m_run[g] = mn;
         ptab[g * 64 + ptab_slot((uint32_t)L)] = p;
