@@ -1064,7 +1064,9 @@ __device__ __forceinline__ void fast_tile(const DecodeArgs& a, int bh, const uns
     // ragged rows: slots up to the wave's longest row (a wave-uniform bound)
     const int nmax = RG ? (int)wave_max_dpp((float)rr.c) : T;
     const uint32_t sh16 = RG ? 16u * (uint32_t)rr.sh : 0u;
-    constexpr int NB = 8;
+    // (batches of 4 for ragged rows: that variant holds 65 row registers and
+    // otherwise spills)
+    constexpr int NB = RG ? 4 : 8;
     // the list entries of each batch are requested one batch ahead, so their
     // LDS round trip overlaps the previous batch's gathers
     uint32_t off_next[NB];
