@@ -244,9 +244,13 @@ __global__ void evict_combine_kernel(const EvictArgs a, int nchunk) {
 
 // Pass 2: score[t] = sum over rows of exp2(s - M) / L for the chunk's tokens;
 // each wave sums its rows, the waves' sums meet in LDS.
-__global__ void __launch_bounds__(NWV * 64) evict_score_kernel(const EvictArgs a) {
+__global__ void __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(4))) evict_score_kernel(const EvictArgs a) {
     __shared__ __align__(16) unsigned char lds[2 * TILE_BYTES];
-    __shared__ float part[NWV][EVICT_CHUNK];
+    // per tile, each wave's row sums of its 64 tokens, in two buffers by tile
+    // parity: a tile's sums are added over the waves (and stored) after the
+    // barrier that precedes the next tile, so 2 KiB of LDS suffice and four
+    // blocks fit on a CU
+    __shared__ float part[2][NWV][EVICT_TILE];
     const int bh = blockIdx.y, chunk = blockIdx.x;
     const int b = bh / a.N_kv, h = bh % a.N_kv;
     const int L = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -264,14 +268,30 @@ __global__ void __launch_bounds__(NWV * 64) evict_score_kernel(const EvictArgs a
         }
     const uint16_t* kbh = a.k + (size_t)bh * a.S * 128;
     const int tb = chunk * EVICT_CHUNK, te = min(a.S, tb + EVICT_CHUNK);
+    float* sc = a.scores + (size_t)bh * a.S;
     struct Score {
         const EvictArgs& a;
         const bf16x8 (&q)[MBW][4];
         const float (&M)[MBW][4];
         const float (&iL)[MBW][4];
-        float* out;                 // this wave's row of part, indexed from tb
-        int r0, L, tb, te;
+        float (*part)[NWV][EVICT_TILE];
+        float* sc;
+        int r0, L, wave, tb, te;
+        // the previous tile's scores: its sums are complete after the barrier
+        // that precedes this tile
+        __device__ __forceinline__ void flush(int tp0) {
+            const int i = threadIdx.x;
+            if (i < EVICT_TILE && tp0 + i < te) {
+                const int k = ((tp0 - tb) / EVICT_TILE) & 1;
+                float v = 0.f;
+#pragma unroll
+                for (int w = 0; w < NWV; ++w) v += part[k][w][i];
+                sc[tp0 + i] = v;
+            }
+        }
         __device__ __forceinline__ void tile(const unsigned char* buf, int t0) {
+            if (t0 > tb) flush(t0 - EVICT_TILE);
+            float* out = part[((t0 - tb) / EVICT_TILE) & 1][wave];
 #pragma unroll
             for (int n = 0; n < EVICT_TILE / 16; ++n) {
                 if (t0 + 16 * n >= te) break;
@@ -284,19 +304,13 @@ __global__ void __launch_bounds__(NWV * 64) evict_score_kernel(const EvictArgs a
                     for (int e = 0; e < 4; ++e) acc = fmaf(__builtin_amdgcn_exp2f(s[mb][e] - M[mb][e]), iL[mb][e], acc);
                 // rows 4 (lane >> 4) + e of every block: add the four lane quarters
                 acc = xor32_sum(xor16_sum(acc));
-                if (L < 16) out[t0 + 16 * n - tb + L] = acc;
+                if (L < 16) out[16 * n + L] = acc;
             }
         }
-    } f{a, q, M, iL, part[wave], r0, L, tb, te};
+    } f{a, q, M, iL, part, sc, r0, L, wave, tb, te};
     walk_tiles(a, kbh, tb, te, lds, f);
     __syncthreads();
-    float* sc = a.scores + (size_t)bh * a.S;
-    for (int i = threadIdx.x; i < te - tb; i += blockDim.x) {
-        float v = 0.f;
-#pragma unroll
-        for (int w = 0; w < NWV; ++w) v += part[w][i];
-        sc[tb + i] = v;
-    }
+    if (te > tb) f.flush(tb + (te - tb - 1) / EVICT_TILE * EVICT_TILE);
 }
 
 // Exclusive prefix sum of v over the block (thread order), and the block
