@@ -1053,8 +1053,8 @@ __device__ __forceinline__ void fast_tile(const DecodeArgs& a, int bh, const uns
     wave_lds_sync();
     // scores: s_g = q'_g . r + sum over kept c of q'_g(c) (k_c - r_c), with
     // q' = q * scale * log2(e) as fp32 float4 per channel (tab) and r as fp32
-    // per channel (rtab, 2 KiB after tab); slots in groups of 4: four list
-    // entries, then four q' rows and four r values
+    // per channel (rtab, 2 KiB after tab); slots in batches of NB: the
+    // batch's q' rows and r values, then its FMAs
     static_assert(G == 4, "table row holds four heads");
     const uint16_t* lrow16 = reinterpret_cast<const uint16_t*>(lst) + (uint32_t)L * list_stride<T>();
     const unsigned char* rtab = tab + 128 * 16;
@@ -1318,7 +1318,8 @@ decode_fast_kernel(const DecodeArgs a) {
 
 // LDS bytes the fast kernel needs: tables and flag, then per wave the slot
 // list and p, or the block / split merge scratch (reused after the tile
-// loop). Must not exceed its static DECODE_FAST_LDS_BYTES.
+// loop). Must not exceed its static size: DECODE_FAST_LDS_BYTES, or
+// DECODE_FAST_RAGGED_LDS_BYTES for ragged rows (T = 128).
 uint32_t decode_fast_lds_bytes(int G, int T, int nsplit) {
     const uint32_t tab = 128u * 16u + 128u * 4u + 16u;   // q' float4 and r per channel, flag
     const uint32_t list = list_bytes_of(T);
@@ -1371,7 +1372,9 @@ hipError_t launch_fast(const DecodeArgs& a, dim3 grid, dim3 block, hipStream_t s
 }
 
 // One launch: the split blocks, the last of which per (b, KV head) merges.
-// The sampled F always takes the generic kernel.
+// G = 4 takes the matrix-core kernel for ragged rows (S >= 2), for the fixed
+// T it is specialised for (fixed or sampled F), and the generic kernel
+// otherwise; packed V always takes the generic kernel.
 hipError_t launch_decode(const DecodeArgs& a, int G, int BH, hipStream_t stream) {
     const dim3 grid(a.nsplit, BH), block(DECODE_THREADS);
     if (a.row_off) {
