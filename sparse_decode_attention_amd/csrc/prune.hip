@@ -78,38 +78,35 @@ chan_energy_kernel(const uint16_t* __restrict__ q_win, float* __restrict__ A,
 // >= the candidate: those T are the answer and no tie straddles it.
 // Otherwise theta is exact and the channels equal to theta are taken in
 // ascending channel order until T are kept.
-// The T keys at or above the T-th largest among the lanes' candidates (two
-// per lane; with MASKED, only members in0 / in1 take part and Tg counts
-// members), ties to the lower channel. v, n and the loop state are
+// The Tg keys at or above the Tg-th largest of the wave's 128 keys (two per
+// lane), ties to the lower channel. (SparK-g runs it per group on keys + 1 of
+// the group's members and 0 elsewhere.) v, n and the loop state are
 // wave-uniform (scalar registers); each unrolled step costs two compares, two
 // scalar popcounts and a scalar select, and the search leaves at the first
 // count of exactly Tg.
-template <bool MASKED>
-__device__ __forceinline__ void select_top(uint32_t key0, uint32_t key1, bool in0, bool in1, int Tg, bool& kept0,
-                                           bool& kept1) {
+__device__ __forceinline__ void select_top(uint32_t key0, uint32_t key1, int Tg, bool& kept0, bool& kept1) {
     uint32_t v = 0;
 #pragma unroll
     for (int bit = 30; bit >= 0; --bit) {
         const uint32_t c = __builtin_amdgcn_readfirstlane(v | (1u << bit));
-        const int n = __popcll(ballot((!MASKED || in0) && key0 >= c)) + __popcll(ballot((!MASKED || in1) && key1 >= c));
+        const int n = __popcll(ballot(key0 >= c)) + __popcll(ballot(key1 >= c));
         v = n >= Tg ? c : v;
         if (n == Tg) break;
     }
     // whether exactly Tg keys are >= v, counted once here rather than
     // carried through every step of the search
-    const bool exact = __popcll(ballot((!MASKED || in0) && key0 >= v)) +
-                       __popcll(ballot((!MASKED || in1) && key1 >= v)) == Tg;
+    const bool exact = __popcll(ballot(key0 >= v)) + __popcll(ballot(key1 >= v)) == Tg;
     if (exact) {
-        kept0 = (!MASKED || in0) && key0 >= v;
-        kept1 = (!MASKED || in1) && key1 >= v;
+        kept0 = key0 >= v;
+        kept1 = key1 >= v;
     } else {
-        const bool gt0 = (!MASKED || in0) && key0 > v, gt1 = (!MASKED || in1) && key1 > v;
+        const bool gt0 = key0 > v, gt1 = key1 > v;
         const int need = Tg - (__popcll(ballot(gt0)) + __popcll(ballot(gt1)));
-        const uint64_t eq0 = ballot((!MASKED || in0) && key0 == v), eq1 = ballot((!MASKED || in1) && key1 == v);
+        const uint64_t eq0 = ballot(key0 == v), eq1 = ballot(key1 == v);
         const int r0 = (int)mbcnt(eq0);
         const int r1 = __popcll(eq0) + (int)mbcnt(eq1);
-        kept0 = gt0 || ((!MASKED || in0) && key0 == v && r0 < need);
-        kept1 = gt1 || ((!MASKED || in1) && key1 == v && r1 < need);
+        kept0 = gt0 || (key0 == v && r0 < need);
+        kept1 = gt1 || (key1 == v && r1 < need);
     }
 }
 
@@ -233,7 +230,7 @@ select_pack_kernel(const uint16_t* __restrict__ k, const float* __restrict__ A,
                 if (T >= 128) {
                     kept0 = kept1 = true;
                 } else if (T > 0) {
-                    select_top<false>(key0, key1, true, true, T, kept0, kept1);
+                    select_top(key0, key1, T, kept0, kept1);
                 }
             } else {
                 for (int i = 0; i < grp.n; ++i) {
@@ -243,8 +240,12 @@ select_pack_kernel(const uint16_t* __restrict__ k, const float* __restrict__ A,
                         kept0 |= in0;
                         kept1 |= in1;
                     } else if (Ti > 0) {
+                        // members' keys + 1 (order and ties unchanged; keys are
+                        // below 2^31), others 0: every candidate and the found
+                        // threshold are >= 1, so the plain search over all 128
+                        // counts members only, with no membership masks
                         bool k0, k1;
-                        select_top<true>(key0, key1, in0, in1, Ti, k0, k1);
+                        select_top(in0 ? key0 + 1u : 0u, in1 ? key1 + 1u : 0u, Ti, k0, k1);
                         kept0 |= k0;
                         kept1 |= k1;
                     }
@@ -335,7 +336,7 @@ append_token_kernel(const uint16_t* __restrict__ k_new, const uint16_t* __restri
     if (T >= 128) {
         kept0 = kept1 = true;
     } else if (T > 0) {
-        select_top<false>(key0, key1, true, true, T, kept0, kept1);
+        select_top(key0, key1, T, kept0, kept1);
     }
     const uint64_t m0 = ballot(kept0), m1 = ballot(kept1);
     const size_t row = (size_t)bh * S_cap + pos;
