@@ -128,8 +128,9 @@ __device__ __forceinline__ float tree_sum_wave(float x) {
 // that set at the last accepted threshold v (whose sum reaches the target)
 // and at the last rejected one (whose sum does not); a candidate whose set
 // equals either of them takes its decision without a tree sum, so sums run
-// only where a candidate splits the keys between the two. Once the two sets
-// are equal, no later candidate can be taken and the search stops.
+// only where a candidate splits the keys between the two. Once the accepted
+// set holds a single key more than the rejected one, no later candidate can
+// change the outcome and the search stops.
 __device__ __forceinline__ void select_top_p(uint32_t key0, uint32_t key1, float p, bool& kept0, bool& kept1) {
     const float w0 = sqrtf(__uint_as_float(key0)), w1 = sqrtf(__uint_as_float(key1));
     const float target = __fmul_rn(p, tree_sum_wave(__fadd_rn(w0, w1)));
@@ -154,10 +155,10 @@ __device__ __forceinline__ void select_top_p(uint32_t key0, uint32_t key1, float
         } else {
             n_rej = n;
         }
-        // every later candidate lies between v and the last rejected one; if
-        // both sets have the same count (no key between them), all of those
-        // candidates select the rejected set and fail too: v is final
-        if (n_acc == n_rej) break;
+        // every later candidate lies between v and the last rejected one, so
+        // its set lies between theirs: with one key between them it is one of
+        // the two, and the accepted set is final
+        if (n_acc - n_rej <= 1) break;
     }
     kept0 = key0 >= v;
     kept1 = key1 >= v;
