@@ -17,7 +17,7 @@ bit:
     bf16 values) over the window rows, group head outer, window position inner;
   * saliency key: fl32(A_j * fl32(k^2)), one IEEE multiply.
 
-Readings of points the pages leave open (each is listed in the design doc):
+Readings of points the pages leave open:
   * ||q^j||_2 is the L2 norm of channel j over the stacked window queries of
     all G query heads that share the KV head ("l2"); the walkthrough's
     mean-query proxy of section 3.2 is mode "mean" (A_j = m_j^2 with m_j the
