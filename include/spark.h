@@ -276,7 +276,7 @@ int spark_decode_attn_ragged(const void* q, const void* k_packed, const int32_t*
 
 /*
  * V-channel pruning (walkthrough section 4.4: V channels are pruned together
- * with K by a norm-based heuristic, which the page does not spell out; read
+ * with K by a norm-based rule that the page does not spell out; read
  * here as per-token top-T_v of |v_tj|). Same selection, packing and retained-
  * mean statistics as the keys' with every channel energy equal to 1.
  *  v            bf16 [B][N_kv][S][D]

@@ -390,8 +390,8 @@ def grow_cache(packed, mask, v, k_new, v_new, A, T: int):
 
 # ---------------------------------------------------------------- SparK-p (top-p)
 #
-# Walkthrough section 5.2: per token, the fewest channels whose cumulative
-# saliency reaches p = 99% of the token's total. Reading taken here, chosen
+# Walkthrough section 5.2: per token, the smallest channel set whose summed
+# saliency is at least p = 99% of the token's total. Reading taken here, chosen
 # so that the integer decision is made in one defined fp32 arithmetic:
 #   w_tj = fl32(sqrt(key_tj)) (correctly rounded), the saliency a_j |k_tj|;
 #   every sum over a token's channels is the pairwise tree that folds the
@@ -502,8 +502,8 @@ def prune_grouped(q_win: np.ndarray, k: np.ndarray, n_kv: int, ratios, qagg: str
 
 # ---------------------------------------------------------------- V-channel pruning
 #
-# Walkthrough section 4.4 prunes the V cache too, with a norm-based heuristic
-# that the page does not spell out. Reading taken here: per token, keep the
+# Walkthrough section 4.4 prunes the V cache too, by a norm-based rule that
+# the page does not spell out. Reading taken here: per token, keep the
 # T_v channels of largest |v_tj| (the norm of the single entry), ties to the
 # lower channel, T_v = num_kept(D, lambda_v); a pruned entry is recovered by
 # the channel's mean over the tokens that retain it (the retained-mean F of
