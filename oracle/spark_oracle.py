@@ -398,10 +398,12 @@ def grow_cache(packed, mask, v, k_new, v_new, A, T: int):
 #   upper half onto the lower half (channel j with j + 64, then + 32, ...,
 #   + 1), in fp32;
 #   target = fl32(p * total), total the tree sum of all w;
-#   theta* = the largest key value theta with tree_sum(w [key >= theta]) >=
-#   target (the sum cannot fall as theta falls); the token keeps the channels
-#   with key >= theta*. Channels tied at theta* are kept together; a token
-#   whose saliency is all zero keeps none.
+#   sort the token's channels by key, largest first, and take prefixes of
+#   that order, each one extended over the channels tied with its last key;
+#   the token keeps the first (shortest) such prefix whose tree sum of w
+#   reaches the target. Channels tied at the cut are kept together; a token
+#   whose saliency is all zero has a zero target, which the empty set already
+#   reaches, so it keeps none.
 # The kept count T_t varies per token, so the packed store is ragged: token
 # t's values sit at [row_off[t], row_off[t + 1]) of its head's region.
 
@@ -419,18 +421,35 @@ def tree_sum32(v: np.ndarray) -> np.ndarray:
     return x[..., 0]
 
 
-def select_top_p(keys: np.ndarray, p: float) -> np.ndarray:
-    """SparK-p kept set per token (see the section comment)."""
+def select_top_p(keys: np.ndarray, p: float, chunk: int = 512) -> np.ndarray:
+    """SparK-p kept set per token (see the section comment), in its plain form.
+
+    The candidate sets are the prefixes of the token's channels in descending
+    key order, each prefix extended over every channel tied with its last key
+    (so a candidate is {key >= theta} for one of the token's key values
+    theta), preceded by the empty set. The token keeps the first candidate,
+    scanning from the empty set towards the whole row, whose fp32 tree sum of
+    w reaches the target fl32(p * total). The empty set's sum is 0, so it is
+    kept only when the target is 0 (an all-zero row).
+    """
     k32 = _f32(keys)
-    w = np.sqrt(k32).astype(np.float32)
-    target = (np.float32(p) * tree_sum32(w)).astype(np.float32)
-    bits = k32.view(np.uint32)
-    v = np.zeros(keys.shape[:-1], dtype=np.uint32)
-    for bit in range(30, -1, -1):
-        c = v | np.uint32(1 << bit)
-        s = tree_sum32(np.where(bits >= c[..., None], w, np.float32(0)))
-        v = np.where(s >= target, c, v)
-    return bits >= v[..., None]
+    shape = k32.shape
+    D = shape[-1]
+    rows = k32.reshape(-1, D)
+    out = np.zeros(rows.shape, dtype=bool)
+    for lo in range(0, rows.shape[0], chunk):
+        kk = rows[lo:lo + chunk]                                   # [n][D]
+        w = np.sqrt(kk).astype(np.float32)
+        target = (np.float32(p) * tree_sum32(w)).astype(np.float32)  # [n]
+        theta = -np.sort(-kk, axis=-1)                             # key values, descending
+        cand = kk[:, None, :] >= theta[:, :, None]                 # [n][candidate i][channel]: {key >= theta_i}
+        sums = tree_sum32(np.where(cand, w[:, None, :], np.float32(0)))   # [n][D]
+        reach = sums >= target[:, None]
+        first = np.argmax(reach, axis=-1)                          # the total always reaches fl32(p * total)
+        kept = np.take_along_axis(cand, first[:, None, None], axis=1)[:, 0, :]
+        kept[target == 0] = False                                  # the empty set reaches a zero target
+        out[lo:lo + chunk] = kept
+    return out.reshape(shape)
 
 
 def prune_topp(q_win: np.ndarray, k: np.ndarray, n_kv: int, p: float, qagg: str = QAGG_L2) -> dict:
