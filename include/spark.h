@@ -12,7 +12,9 @@
  *  - Tensors are dense, row-major, in device memory, and owned by the caller.
  *    The library never allocates, frees or caches device memory; scratch
  *    space comes from the caller's workspace `ws` of `ws_bytes` bytes, sized
- *    by the matching *_workspace_bytes() call. Workspaces must be 256-byte
+ *    by the matching *_workspace_bytes() call (the one exception is the fixed
+ *    per-device array of spark_decode_attn_noalloc, part of the library's
+ *    code object). Workspaces must be 256-byte
  *    aligned; every tensor pointer must be 16-byte aligned.
  *  - bf16 tensors are passed as `const void*` holding IEEE bfloat16 values.
  *  - `stream` is a hipStream_t (NULL = the legacy default stream). Calls are
@@ -42,7 +44,8 @@ typedef enum {
     SPARK_EUNSUPPORTED = -2,  /* valid but not implemented (D != 128, G not in {1,2,4,8}) */
     SPARK_EALIGN = -3,        /* pointer misaligned */
     SPARK_ENOSPACE = -4,      /* workspace too small */
-    SPARK_EHIP = -5           /* HIP runtime error at launch */
+    SPARK_EHIP = -5,          /* HIP runtime error at launch */
+    SPARK_ESCRATCH = -6       /* problem too large for the fixed scratch of spark_decode_attn_noalloc */
 } spark_status;
 
 /* Recovery function F for pruned channels (walkthrough section 3.3, F table,
@@ -314,6 +317,30 @@ int spark_decode_attn_kv(const void* q, const void* k_packed, const uint32_t* k_
 /* Zero the decode completion counters of a workspace (a fill kernel on
  * `stream`; safe to record in a HIP graph). */
 int spark_decode_ws_init(void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * spark_decode_attn without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). The completion counters and split
+ * partials live in a fixed device array of SPARK_NOALLOC_SCRATCH_BYTES that
+ * the library holds on every GPU it runs on until the process ends; the call
+ * itself allocates nothing and calls no allocating routine.
+ *  Arguments, layouts and results as for spark_decode_attn (same kernels, same
+ *  split plan, so the output is bit-identical to spark_decode_attn with the
+ *  same splits).
+ *  Returns SPARK_ESCRATCH if the problem needs more scratch than the array
+ *  holds: spark_decode_workspace_bytes(B, S, N_q, N_kv, D, splits) must not
+ *  exceed SPARK_NOALLOC_SCRATCH_BYTES.
+ *  The first call on a device resolves the array's address and zeroes its
+ *  counters with a fill kernel on `stream`; every completed call leaves them
+ *  zero again. All calls on one GPU share the array: calls that overlap in
+ *  time on one GPU (different streams, or host threads) race and give
+ *  undefined results; serialise them.
+ */
+#define SPARK_NOALLOC_SCRATCH_BYTES (8u << 20)
+int spark_decode_attn_noalloc(const void* q, const void* k_packed, const uint32_t* mask, const void* v,
+                              const float* r, int B, int S, int N_q, int N_kv, int D, float lambda, float scale,
+                              int splits, float* out, void* stream);
 
 /*
  * Observation-window token eviction (SnapKV style), the stage SparK is

@@ -3,6 +3,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/spark.h"
 #include "kernels.h"
 
@@ -115,6 +117,7 @@ const char* spark_strerror(int status) {
         case SPARK_EALIGN: return "misaligned pointer (tensors 16 B, workspace 256 B)";
         case SPARK_ENOSPACE: return "workspace too small";
         case SPARK_EHIP: return "HIP runtime error";
+        case SPARK_ESCRATCH: return "problem needs more than the fixed scratch of spark_decode_attn_noalloc";
         default: return "unknown status";
     }
 }
@@ -455,6 +458,57 @@ int spark_decode_ws_init(void* ws, size_t ws_bytes, void* stream) {
     hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
                        static_cast<hipStream_t>(stream), static_cast<uint32_t*>(ws), 0u, n);
     return hip_status(hipGetLastError());
+}
+
+}  // extern "C"
+
+namespace {
+
+// Fixed scratch of the allocation-free decode: completion counters, then the
+// split partials, laid out as a decode workspace. In host code `scratch` is
+// only a symbol: its device address is resolved once per device with
+// hipGetSymbolAddress, and only that address is ever passed to kernels.
+static __device__ __align__(256) unsigned char scratch[SPARK_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of this device's scratch; on the first call on a
+// device, also zero its counters with a fill kernel on `stream`.
+int scratch_for_current_device(hipStream_t stream, void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SPARK_EHIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SPARK_EHIP;
+        const size_t n = SPARK_DECODE_COUNTER_BYTES / 4;
+        hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                           static_cast<uint32_t*>(p), 0u, n);
+        if (hipGetLastError() != hipSuccess) return SPARK_EHIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return SPARK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int spark_decode_attn_noalloc(const void* q, const void* k_packed, const uint32_t* mask, const void* v,
+                              const float* r, int B, int S, int N_q, int N_kv, int D, float lambda, float scale,
+                              int splits, float* out, void* stream) {
+    // size check first: nothing is touched for a problem that does not fit
+    const size_t need = spark_decode_workspace_bytes(B, S, N_q, N_kv, D, splits);
+    if (need == 0) return SPARK_EINVAL;
+    if (need > (size_t)SPARK_NOALLOC_SCRATCH_BYTES) return SPARK_ESCRATCH;
+    void* ws = nullptr;
+    if (int e = scratch_for_current_device(static_cast<hipStream_t>(stream), &ws)) return e;
+    const int st = decode_call(q, k_packed, mask, v, r, nullptr, 0, 0, B, S, N_q, N_kv, D, lambda, scale, splits,
+                               out, ws, SPARK_NOALLOC_SCRATCH_BYTES, stream);
+    return st == SPARK_ENOSPACE ? SPARK_ESCRATCH : st;
 }
 
 // window eviction workspace: chunk (m, l) partials, per-row (M, 1/L), scores

@@ -18,7 +18,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libspark.so")
 HEADER = os.path.join(os.path.dirname(_PKG), "include", "spark.h")
 
-OK, EINVAL, EUNSUPPORTED, EALIGN, ENOSPACE, EHIP = 0, -1, -2, -3, -4, -5
+OK, EINVAL, EUNSUPPORTED, EALIGN, ENOSPACE, EHIP, ESCRATCH = 0, -1, -2, -3, -4, -5, -6
+NOALLOC_SCRATCH_BYTES = 8 << 20
 RECOVERY = {"mean_retained": 0, "zero": 1, "const": 2, "score_mean_pruned": 3, "gaussian": 4, "exponential": 5}
 QAGG = {"l2": 0, "mean": 1}
 DECODE_COUNTER_BYTES = 4096
@@ -52,6 +53,7 @@ _SIGS = {
     "spark_decode_attn_kv": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _f, _f, _i,
                                   _vp, _vp, _sz, _vp]),
     "spark_decode_ws_init": (_i, [_vp, _sz, _vp]),
+    "spark_decode_attn_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _f, _i, _vp, _vp]),
     "spark_read_stream": (_i, [_vp, _sz, _vp, _i, _vp]),
     "spark_window_evict_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "spark_window_evict": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -287,6 +289,24 @@ def decode_attn(q, k_packed, mask, v, r, lam: float, scale: float = 0.0, splits:
                                  B, S, N_q, n_kv, D, float(lam), float(scale), int(splits), _ptr(out),
                                  _ptr(ws), ws.numel(), _stream(dev))
     _check("spark_decode_attn", st)
+    return out
+
+
+def decode_attn_noalloc(q, k_packed, mask, v, r, lam: float, scale: float = 0.0, splits: int = 0, out=None):
+    """spark_decode_attn_noalloc: spark_decode_attn with the library's fixed
+    per-device scratch instead of a workspace (no device allocation by the
+    library; `out` is allocated here only when not given)."""
+    B, N_q, D = q.shape
+    n_kv, S = v.shape[1], v.shape[2]
+    _need(q, "q", torch.bfloat16)
+    _need(v, "v", torch.bfloat16, (B, n_kv, S, D))
+    dev = q.device
+    out = torch.empty((B, N_q, D), dtype=torch.float32, device=dev) if out is None else out
+    T = num_kept(D, lam)
+    st = lib().spark_decode_attn_noalloc(_ptr(q), _ptr(k_packed) if T > 0 else None, _ptr(mask), _ptr(v), _ptr(r),
+                                         B, S, N_q, n_kv, D, float(lam), float(scale), int(splits), _ptr(out),
+                                         _stream(dev))
+    _check("spark_decode_attn_noalloc", st)
     return out
 
 

@@ -32,7 +32,7 @@ def test_num_kept_matches_oracle_rule():
 
 
 def test_strerror_names_every_status():
-    for st in (0, -1, -2, -3, -4, -5):
+    for st in (0, -1, -2, -3, -4, -5, -6):
         assert ops.strerror(st) and ops.strerror(st) != "unknown status"
     assert ops.strerror(7) == "unknown status"
 
@@ -308,3 +308,16 @@ def test_window_evict_checks():
     assert call(k=MIS) == ops.EALIGN
     assert call(ws=FAKE + 16) == ops.EALIGN
     assert call() == ops.ENOSPACE
+
+
+def test_noalloc_decode_rejects_sizes_beyond_its_scratch():
+    """The size check of the allocation-free decode runs before anything
+    touches a device: a problem whose workspace would exceed the fixed
+    scratch returns SPARK_ESCRATCH, invalid sizes SPARK_EINVAL."""
+    l = ops.lib()
+    B, S, N_q, N_kv = 64, 1 << 20, 32, 8
+    assert l.spark_decode_workspace_bytes(B, S, N_q, N_kv, 128, 64) > ops.NOALLOC_SCRATCH_BYTES
+    assert l.spark_decode_attn_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, B, S, N_q, N_kv, 128, 0.5, 0.0, 64, FAKE,
+                                       None) == ops.ESCRATCH
+    assert l.spark_decode_attn_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, 30, 8, 128, 0.5, 0.0, 0, FAKE,
+                                       None) == ops.EINVAL
