@@ -300,6 +300,36 @@ def growth_leg(w, steps, warmup, x):
                     "the appended row"}
 
 
+def sweep_leg(base, lams=(0.5, 0.8), lengths=(4096, 8192, 16384, 32768, 65536, 131072), steps=5, warmup=2):
+    """Decode time against input length (the walkthrough's section 4.3
+    throughput-vs-length curve, Fig. 4(b)) at fixed launch rules, with replica
+    rotation: per lambda, t(S) at each S and the least-squares line
+    t = fixed + bytes / rate over the points, which separates the per-launch
+    fixed cost (start-up, split merge) from the streaming rate."""
+    out = {}
+    for lam in lams:
+        pts = []
+        for S in lengths:
+            w = base.with_(S=S, lam=lam, steps=64)
+            r = run_leg(w, steps, warmup, verbose=False)
+            pts.append((S, r["decode_bytes_per_step"], r["decode_us_per_launch"]))
+            del r
+        n = len(pts)
+        mx = sum(p[1] for p in pts) / n
+        my = sum(p[2] for p in pts) / n
+        sxx = sum((p[1] - mx) ** 2 for p in pts)
+        sxy = sum((p[1] - mx) * (p[2] - my) for p in pts)
+        slope = sxy / sxx                   # us per byte
+        fixed = my - slope * mx
+        out[f"lambda={lam}"] = {
+            "points": [{"S": S, "bytes": b, "us_per_launch": round(t, 3), "GBps": round(b / (t * 1e-6) / 1e9, 1)}
+                       for S, b, t in pts],
+            "fit_fixed_us": round(fixed, 3),
+            "fit_marginal_GBps": round(1e-3 / slope, 1),
+        }
+    return out
+
+
 def stream_ceiling(nbytes: int, reps: int = 7, block_counts=(512, 1024, 2048, 4096)):
     """GB/s of a plain streaming read (spark_read_stream) of `nbytes`, rotated
     over >= 768 MB of buffers like the decode replicas: the practical HBM read
@@ -568,6 +598,7 @@ def main():
     ap.add_argument("--no-topp", action="store_true", help="skip the SparK-p leg")
     ap.add_argument("--no-growth", action="store_true", help="skip the growing-cache serving loop")
     ap.add_argument("--no-shard", action="store_true", help="skip the TP-8 shard-shape leg")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the decode time vs input length sweep")
     ap.add_argument("--warm", action="store_true", help="also report a run without replica rotation")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="run a plain device copy of this size after the legs (counter calibration)")
@@ -730,6 +761,10 @@ def main():
         print("bench: 32-layer stack", file=sys.stderr, flush=True)
         line["layer_stack"] = stack_leg(WORKLOADS["llama8b_32L_b4_s64k_l08"], min(args.steps, 5),
                                         min(args.warmup, 2))
+        torch.cuda.empty_cache()
+    if not args.no_sweep:
+        print("bench: decode time vs input length", file=sys.stderr, flush=True)
+        line["length_sweep"] = sweep_leg(w, steps=min(args.steps, 5), warmup=min(args.warmup, 2))
         torch.cuda.empty_cache()
     if args.warm:
         wl = run_leg(w, args.steps, args.warmup, rotate=False)
