@@ -96,6 +96,11 @@ def effective_prefill_bytes(w, T):
     return w.B * w.n_kv * w.S * (2 * w.D + 2 * T + 16)
 
 
+def decode_bucket(T: int) -> int:
+    """Largest row length of the runtime-T decode variant that serves T."""
+    return 32 if T <= 32 else 64 if T <= 64 else 96 if T <= 96 else 128
+
+
 def run_leg(w, steps, warmup, rotate=True, seed=0, verbose=True, x=None, recovery="mean_retained",
             rng_seed=SAMPLE_SEED, lam_v=None, ratios=None, top_p=None):
     import torch
@@ -599,6 +604,8 @@ def main():
     ap.add_argument("--no-growth", action="store_true", help="skip the growing-cache serving loop")
     ap.add_argument("--no-shard", action="store_true", help="skip the TP-8 shard-shape leg")
     ap.add_argument("--no-sweep", action="store_true", help="skip the decode time vs input length sweep")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the other pruning ratios and group sizes (lambda 0.3 and 0.6; G = 8 and 1)")
     ap.add_argument("--warm", action="store_true", help="also report a run without replica rotation")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="run a plain device copy of this size after the legs (counter calibration)")
@@ -686,6 +693,33 @@ def main():
                              "ops_per_token_head": sampled_alu_ops_per_token(w.G, T, rec)},
                 "x_fixed_r_time": round(lg["decode_us_per_launch"] / main_leg["decode_us_per_launch"], 3),
                 "prefill_us": round(lg["prefill_us"], 2), "seed": hex(SAMPLE_SEED)}
+            del lg
+        torch.cuda.empty_cache()
+    if not args.no_variants:
+        # the runtime-T variants of the matrix-core kernel: other pruning
+        # ratios (G = 4) and other group sizes (G = 8: 64 query heads over 8
+        # KV heads; G = 1: as many query as KV heads), same S and B
+        line["variants"] = []
+        main_us, main_bytes = main_leg["decode_us_per_launch"], main_leg["decode_bytes_per_step"]
+        for name, wv, xv in (("lambda=0.3", w.with_(name=w.name + "_lam03", lam=0.3), main_leg["x"]),
+                             ("lambda=0.6", w.with_(name=w.name + "_lam06", lam=0.6), main_leg["x"]),
+                             ("G=8", w.with_(name=w.name + "_g8", n_q=8 * w.n_kv), None),
+                             ("G=1", w.with_(name=w.name + "_g1", n_q=w.n_kv), None)):
+            print(f"bench: variant {name} ({wv.name})", file=sys.stderr, flush=True)
+            lg = run_leg(wv, min(args.steps, 5), min(args.warmup, 2), x=xv)
+            Tv = lg["T"]
+            exact = wv.G == 4 and Tv in (26, 38, 48, 64)
+            kern = (f"decode_fast_kernel<4, {Tv}>" if exact else
+                    f"decode_fast_kernel<G={wv.G}, T<={decode_bucket(Tv)}, {'odd' if Tv & 1 else 'even'} T>")
+            line["variants"].append({
+                "variant": name, "workload": wv.name, "G": wv.G, "lambda": wv.lam, "T": Tv, "kernel": kern,
+                "decode_us_per_launch": round(lg["decode_us_per_launch"], 3),
+                "bytes_per_launch": lg["decode_bytes_per_step"], "GBps": round(lg["decode_GBps"], 2),
+                "pct_hbm_peak": round(100 * lg["decode_GBps"] / HBM_PEAK_GBS, 2),
+                # time relative to the headline leg over bytes relative to it: 1.0 is byte-proportional
+                "time_over_bytes_vs_headline": round((lg["decode_us_per_launch"] / main_us) /
+                                                     (lg["decode_bytes_per_step"] / main_bytes), 3),
+                "replicas": lg["replicas"]})
             del lg
         torch.cuda.empty_cache()
     if not args.no_vprune:

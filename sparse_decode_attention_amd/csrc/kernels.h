@@ -15,8 +15,6 @@
 // LDS of the fast decode kernel: q' and r tables with a flag slot (2576 B),
 // then per wave the slot list of the largest T (64 lanes x 68 u16) and 1 KiB of p
 #define DECODE_FAST_LDS_BYTES (2576 + (DECODE_FAST_THREADS / 64) * (8704 + 1024))
-// the ragged-row variant: a slot list of 128 slots (64 lanes x 132 u16)
-#define DECODE_FAST_RAGGED_LDS_BYTES (2576 + (DECODE_FAST_THREADS / 64) * (16896 + 1024))
 #define DECODE_TILE 64
 #define DECODE_MAX_SPLITS 256
 #define DECODE_RAGGED_CHUNKS (DECODE_TILE * 128 * 2 / 16 + 1)   // 16-byte chunks of a tile of full rows, + misalignment
@@ -126,9 +124,23 @@ hipError_t launch_read_stream(const void* src, size_t bytes, uint32_t* sink, int
 
 // Launch the decode kernel for group size G; returns a hipError_t.
 hipError_t launch_decode(const DecodeArgs& a, int G, int BH, hipStream_t stream);
-bool decode_fast_supported(int G, int T);
-// ragged rows (SparK-p) on the fast kernel
+// whether the matrix-core decode kernel takes fixed rows of T for group size
+// G (sampled: the sampled F), the packed buffer holding packed_elems values
+bool decode_fast_supported(int G, int T, int sampled, size_t packed_elems);
+// ragged rows (SparK-p) on the matrix-core kernel
 bool decode_fast_ragged_supported(int G, int S);
+// Runtime-T variants of the matrix-core kernel: the largest row length of
+// T's variant, and the dwords each lane requests for a row (the row's dwords
+// plus one when odd rows start mid-dword, in whole 16-byte requests).
+constexpr int decode_fast_bucket(int T) { return T <= 32 ? 32 : T <= 64 ? 64 : T <= 96 ? 96 : 128; }
+constexpr int decode_fast_kr(int TB, bool odd) { return 4 * ((TB / 2 + (odd ? 1 : 0) + 3) / 4); }
+// matrix-core launchers: exact-T variants (G = 4, T in {26, 38, 48, 64},
+// fixed or sampled F) and the runtime-T / ragged variants per group size
+hipError_t launch_fast_fixed(const DecodeArgs& a, dim3 grid, hipStream_t stream);
+hipError_t launch_fast_g1(const DecodeArgs& a, dim3 grid, hipStream_t stream);
+hipError_t launch_fast_g2(const DecodeArgs& a, dim3 grid, hipStream_t stream);
+hipError_t launch_fast_g4(const DecodeArgs& a, dim3 grid, hipStream_t stream);
+hipError_t launch_fast_g8(const DecodeArgs& a, dim3 grid, hipStream_t stream);
 DecodeLayout decode_layout(int G, int T, int nsplit, bool sampled, int Tv, bool ragged = false);
 
 }  // namespace spark
