@@ -46,16 +46,16 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 // that one lane of the matrix-core P.V needs are adjacent.
 __device__ __forceinline__ uint32_t ptab_slot(uint32_t t) { return (t & 48u) | ((t & 3u) << 2) | ((t >> 2) & 3u); }
 
-// ---- q' and r tables in LDS. Channel c's q' of heads 0-3 (min(G, 4) fp32
-// side by side), heads 4-7 of G = 8 in a second table 2 KiB further on; r as
-// one fp32 per channel after the q' tables. A slot-list entry u = 4 c is the
-// byte offset of c's r and a 1/G of the offset of its q' row.
-__host__ __device__ constexpr uint32_t fast_qcols(int G) { return G < 4 ? (uint32_t)G : 4u; }
-__host__ __device__ constexpr uint32_t fast_rtab(int G) { return 128u * 4u * (uint32_t)G; }
-__host__ __device__ constexpr uint32_t fast_tables_bytes(int G) { return fast_rtab(G) + 128u * 4u; }
+// ---- q' and r tables in LDS, 16 bytes per channel: channel c's q' of heads
+// 0-3 (min(G, 4) fp32) at byte 16 c, heads 4-7 of G = 8 in a second table
+// 2 KiB further on, r at byte 16 c of the table after those. A slot-list
+// entry is u = 16 c, so one address register serves every read of a slot
+// (the table distances go into the LDS instructions' offset fields).
+__host__ __device__ constexpr uint32_t fast_rtab(int G) { return G == 8 ? 4096u : 2048u; }
+__host__ __device__ constexpr uint32_t fast_tables_bytes(int G) { return fast_rtab(G) + 2048u; }
 template <int G>
 __device__ __forceinline__ uint32_t qtab_offset(uint32_t c, uint32_t g) {
-    return (g >> 2) * 2048u + (c * fast_qcols(G) + (g & 3u)) * 4u;
+    return (g >> 2) * 2048u + c * 16u + (g & 3u) * 4u;
 }
 
 template <int G>
@@ -66,13 +66,13 @@ __device__ __forceinline__ QV<G> load_qrow(const unsigned char* tab, uint32_t u)
     if constexpr (G == 1) {
         r.v[0] = *reinterpret_cast<const float*>(tab + u);
     } else if constexpr (G == 2) {
-        const float2 x = *reinterpret_cast<const float2*>(__builtin_assume_aligned(tab + 2u * u, 8));
+        const float2 x = *reinterpret_cast<const float2*>(__builtin_assume_aligned(tab + u, 16));
         r.v[0] = x.x; r.v[1] = x.y;
     } else {
-        const float4 x = *reinterpret_cast<const float4*>(__builtin_assume_aligned(tab + 4u * u, 16));
+        const float4 x = *reinterpret_cast<const float4*>(__builtin_assume_aligned(tab + u, 16));
         r.v[0] = x.x; r.v[1] = x.y; r.v[2] = x.z; r.v[3] = x.w;
         if constexpr (G == 8) {
-            const float4 y = *reinterpret_cast<const float4*>(__builtin_assume_aligned(tab + 4u * u + 2048u, 16));
+            const float4 y = *reinterpret_cast<const float4*>(__builtin_assume_aligned(tab + u + 2048u, 16));
             r.v[4] = y.x; r.v[5] = y.y; r.v[6] = y.z; r.v[7] = y.w;
         }
     }
@@ -226,15 +226,22 @@ __device__ __forceinline__ void load_row_rt(const DecodeArgs& a, int T, int bh, 
                                             uint32_t (&kr)[KR], RowState& rs) {
     static_assert(KR % 4 == 0, "whole 16-byte requests");
     typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
-    const size_t row = (size_t)bh * a.S_cap + t0 + min(L, nt - 1);
-    mw = *reinterpret_cast<const uint4*>(a.mask + row * 4);
-    const size_t o = row * (size_t)T;
-    const size_t o_dw = o >> 1;
-    const size_t e_dw = a.packed_elems >> 1;           // whole dwords of the packed buffer
-    const bool near_end = o_dw + KR > e_dw;
-    rs.sh = ODD ? (int)(o & 1) : 0;
+    // wave-uniform: the tile's first row, its first element, the dword
+    // holding it, and the whole dwords from there to the buffer's end
+    const size_t row0 = (size_t)bh * a.S_cap + t0;
+    const size_t o0 = row0 * (size_t)T;
     const uint32_t* base = reinterpret_cast<const uint32_t*>(a.packed);
-    const uint32_t* src = base + (near_end ? 0 : o_dw);
+    const uint32_t* wbase = base + (o0 >> 1);
+    const size_t e_dw = a.packed_elems >> 1;
+    const uint32_t room = (uint32_t)min(e_dw - (o0 >> 1), (size_t)0x40000000u);
+    // per lane, 32-bit: its row's first element and dword from wbase
+    const uint32_t l = (uint32_t)min(L, nt - 1);
+    mw = *reinterpret_cast<const uint4*>(a.mask + row0 * 4 + l * 4u);
+    const uint32_t le = l * (uint32_t)T + (uint32_t)(o0 & 1);
+    const uint32_t ldw = le >> 1;
+    rs.sh = ODD ? (int)(le & 1u) : 0;
+    const bool near_end = ldw + (uint32_t)KR > room;
+    const uint32_t* src = near_end ? base : wbase + ldw;
 #pragma unroll
     for (int i = 0; i < KR / 4; ++i) {
         const u32x4_a4 x = *reinterpret_cast<const u32x4_a4*>(src + 4 * i);
@@ -242,7 +249,8 @@ __device__ __forceinline__ void load_row_rt(const DecodeArgs& a, int T, int bh, 
     }
     if (ballot(near_end) != 0) {
         if (near_end) {
-            const int ndw = ((int)(o & 1) + T + 1) >> 1;
+            const int ndw = ((int)(le & 1u) + T + 1) >> 1;
+            const size_t o_dw = (o0 >> 1) + ldw;
             // the buffer's last element, when it ends mid-dword
             const uint32_t last = (a.packed_elems & 1) != 0 ? (uint32_t)a.packed[a.packed_elems - 1] : 0u;
             // whole dwords from the row's first to the buffer's end (0 when a
@@ -301,21 +309,19 @@ __device__ __forceinline__ void load_row_ragged(const DecodeArgs& a, int bh, int
 }
 
 // ---- slot list. Row stride (u16 elements) of the lane-major list: room for
-// T slots and a spare one, rounded so that the stride in dwords is odd, which
-// puts the 64 lanes of a dword read on distinct bank pairs.
-__host__ __device__ constexpr uint32_t list_stride_of(int T) {
-    return ((T / 2) % 2 == 1) ? (uint32_t)T + 2u : (uint32_t)T + 4u;
-}
+// T slots and a spare one, rounded up to a multiple of 4 so that every row
+// starts 8-byte aligned (the list writes combine into 8-byte stores).
+__host__ __device__ constexpr uint32_t list_stride_of(int T) { return ((uint32_t)T + 5u) & ~3u; }
 // LDS bytes of one wave's slot list, in whole 16-byte units
 __host__ __device__ constexpr uint32_t list_bytes_of(int T) { return (64u * list_stride_of(T) * 2u + 15u) & ~15u; }
-// the list of a runtime T <= TB: the stride of any such T, and 8 spare
-// entries after the last lane's row (the score loop's last batch reads up to
-// 6 entries past a row: the next lane's, or these)
+// the list of a runtime T <= TB: the stride of any such T, and 16 spare
+// entries after the last lane's row (the score loop reads up to 2 NB - 2 <= 14
+// entries past a row, which it never uses: the next lane's, or these)
 __host__ __device__ constexpr uint32_t list_bytes_rt(int TB) {
-    return ((64u * ((uint32_t)TB + 4u) + 8u) * 2u + 15u) & ~15u;
+    return ((64u * ((uint32_t)TB + 4u) + 16u) * 2u + 15u) & ~15u;
 }
 
-// Slot list of one tile, lane-major: lst[lane * stride + rho] = 4 * c for the
+// Slot list of one tile, lane-major: lst[lane * stride + rho] = 16 c for the
 // lane's rho-th kept channel c (ascending). One bit-clearing loop per mask
 // word; lanes leave it as their word empties.
 __device__ __forceinline__ void build_list(const uint4& mw, uint8_t* lst, int L, uint32_t stride) {
@@ -330,12 +336,12 @@ __device__ __forceinline__ void build_list(const uint4& mw, uint8_t* lst, int L,
         for (; i + 4 <= pc; i += 4) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                p[i + u] = (uint16_t)(((uint32_t)__builtin_ctz(m) << 2) | (128u * w));
+                p[i + u] = (uint16_t)(((uint32_t)__builtin_ctz(m) << 4) | (512u * w));
                 m &= m - 1;
             }
         }
         for (; i < pc; ++i) {
-            p[i] = (uint16_t)(((uint32_t)__builtin_ctz(m) << 2) | (128u * w));
+            p[i] = (uint16_t)(((uint32_t)__builtin_ctz(m) << 4) | (512u * w));
             m &= m - 1;
         }
         p += pc;
@@ -355,14 +361,19 @@ struct FastCfg {
     static constexpr int KR = RG ? RAGGED_KR : TFIX ? TFIX / 2 : decode_fast_kr(TB, ODD);
     // slots per batch of the score loop (4 where the row registers or the
     // q' rows of eight heads would otherwise crowd out the rest)
-    static constexpr int NB = G == 8 ? (LOOP >= 128 ? 4 : 2) : (RG || KR > 40) ? 4 : 8;
+    static constexpr int NB = (G == 8 || RG || KR > 40) ? 4 : 8;
+    // the smallest row length the variant serves (the previous bucket's
+    // largest plus one): batches below it are always full
+    static constexpr int TMIN = RG ? 0 : TFIX ? TFIX : (TB == 32 ? 1 : TB - 31);
     static constexpr uint32_t LIST = RG ? list_bytes_of(128) : TFIX ? list_bytes_of(TFIX) : list_bytes_rt(TB);
     static constexpr uint32_t WAVE = LIST + 64u * (uint32_t)G * 4u;
-    // static LDS: the tables and a 16-byte flag slot, then the waves' regions
-    // (the exact-T variants keep the size of the largest of them, 64)
-    static constexpr uint32_t LDS = TFIX ? DECODE_FAST_LDS_BYTES
-                                         : fast_tables_bytes(G) + 16u + (uint32_t)FAST_NW * WAVE;
-    static_assert(fast_tables_bytes(G) + 16u + (uint32_t)FAST_NW * WAVE <= LDS, "LDS");
+    // static LDS: the tables and a 16-byte flag slot, then the waves'
+    // regions (the exact-T variants keep the size of the largest of them,
+    // 64); at least 72 KiB, so that any u16 list entry (even one a mask with
+    // fewer than T bits left unwritten) addresses LDS inside the block's
+    static constexpr uint32_t LDS_NEED = fast_tables_bytes(G) + 16u + (uint32_t)FAST_NW * WAVE;
+    static constexpr uint32_t LDS = TFIX ? DECODE_FAST_LDS_BYTES : (LDS_NEED > 73728u ? LDS_NEED : 73728u);
+    static_assert(LDS_NEED <= LDS && 65535u + fast_rtab(G) + 4u <= LDS, "LDS");
 };
 
 // One 64-token tile. The slot list is built from the tile's mask (before the
@@ -378,7 +389,8 @@ struct FastCfg {
 // gathers. Exact T: every batch full. Runtime T: batches up to T, the slots
 // of the last one past T adding nothing (their list entries are valid
 // offsets, their values are replaced by 0). Ragged rows: batches up to the
-// wave's longest row, each slot past its lane's row adding nothing.
+// wave's longest row, each slot past its lane's row adding nothing (its
+// list entry is a stale but valid table offset, its value is discarded).
 template <int G, int TB, int TFIX, bool ODD, int SMODE, bool LOAD_V, bool LIST_READY, bool RG>
 __device__ __forceinline__ void fast_tile(const DecodeArgs& a, int T, uint32_t lstride, int bh,
                                           const unsigned char* tab, uint8_t* lst, float* ptab, const uint16_t* vbh,
@@ -412,17 +424,12 @@ __device__ __forceinline__ void fast_tile(const DecodeArgs& a, int T, uint32_t l
         uint32_t off[NB];
 #pragma unroll
         for (int k = 0; k < NB; ++k) off[k] = off_next[k];
-        if constexpr (TFIX != 0 || RG) {
+        // (runtime T: the next batch's entries are read even past T, from
+        // the next lane's row or the list's spare entries: unconditional
+        // reads let the compiler rotate registers instead of copying them)
 #pragma unroll
-            for (int k = 0; k < NB; ++k)
-                if (r0 + NB + k < LOOP) off_next[k] = lrow16[r0 + NB + k];
-        } else {
-            if (r0 + NB < nmax) {
-#pragma unroll
-                for (int k = 0; k < NB; ++k)
-                    if (r0 + NB + k < LOOP) off_next[k] = lrow16[r0 + NB + k];
-            }
-        }
+        for (int k = 0; k < NB; ++k)
+            if (r0 + NB + k < LOOP) off_next[k] = lrow16[r0 + NB + k];
         QV<G> qv[NB];
         float rv[NB];
 #pragma unroll
@@ -432,6 +439,7 @@ __device__ __forceinline__ void fast_tile(const DecodeArgs& a, int T, uint32_t l
                 rv[k] = *reinterpret_cast<const float*>(rtab + off[k]);
             }
         }
+        float e[NB];
 #pragma unroll
         for (int k = 0; k < NB; ++k) {
             if (r0 + k < LOOP) {
@@ -440,11 +448,25 @@ __device__ __forceinline__ void fast_tile(const DecodeArgs& a, int T, uint32_t l
                 if constexpr (RG || ODD) w = __builtin_amdgcn_alignbit(kr[(rho >> 1) + 1], kr[rho >> 1], sh16);
                 else w = kr[rho >> 1];
                 const float kv = (rho & 1) ? bf16_hi(w) : bf16_lo(w);
-                float e = kv - rv[k];
-                if constexpr (RG) e = rho < rs.c ? e : 0.0f;
-                else if constexpr (TFIX == 0) e = rho < nmax ? e : 0.0f;
+                e[k] = kv - rv[k];
+                if constexpr (RG) e[k] = rho < rs.c ? e[k] : 0.0f;
+            }
+        }
+        if constexpr (TFIX == 0 && !RG) {
+            // runtime T: only the last batch has slots past T; it clears them
+            // in a branch of its own (the empty asm keeps the compiler from
+            // turning the branch into selects that every batch would pay)
+            if (r0 + NB > C::TMIN && r0 + NB > nmax) {
+                asm volatile("");
 #pragma unroll
-                for (int g = 0; g < G; ++g) s[g] = fmaf(qv[k].v[g], e, s[g]);
+                for (int k = 0; k < NB; ++k) e[k] = r0 + k < nmax ? e[k] : 0.0f;
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < NB; ++k) {
+            if (r0 + k < LOOP) {
+#pragma unroll
+                for (int g = 0; g < G; ++g) s[g] = fmaf(qv[k].v[g], e[k], s[g]);
             }
         }
         // consume the partial sums here: otherwise the compiler sinks the
@@ -453,10 +475,11 @@ __device__ __forceinline__ void fast_tile(const DecodeArgs& a, int T, uint32_t l
         for (int g = 0; g < G; ++g) asm volatile("" : "+v"(s[g]));
     };
     // (batches past the last are skipped one by one, uniformly: a loop with
-    // an early exit would not be unrolled)
+    // an early exit would not be unrolled; batches that every T of the
+    // variant fills need no test)
 #pragma unroll
     for (int r0 = 0; r0 < LOOP; r0 += NB) {
-        if (TFIX != 0 || r0 < nmax) batch(r0);
+        if (r0 + NB <= C::TMIN || r0 < nmax) batch(r0);
     }
     // sampled F: the sample term needs this tile's mask, so it runs before
     // the next tile's masks are requested into mw
@@ -573,10 +596,18 @@ decode_fast_kernel(const DecodeArgs a) {
     __builtin_amdgcn_sched_barrier(0);
     uint8_t* lst = wbase + (size_t)wave * WAVE;
     float* ptab = reinterpret_cast<float*>(wbase + (size_t)wave * WAVE + LIST);
-    if constexpr (TFIX == 0) {
-        // slots past a row (and the last batch's spare reads) find a valid
-        // table offset (channel 0) in every entry no mask has written
+    if constexpr (RG) {
+        // slots past a row find a valid table offset (channel 0) in every
+        // entry no mask has written
         for (uint32_t i = (uint32_t)L; i < LIST / 16u; i += 64u) reinterpret_cast<uint4*>(lst)[i] = make_uint4(0, 0, 0, 0);
+    } else if constexpr (TFIX == 0) {
+        // the entries the score loop reads past a row that no mask writes:
+        // the row's slack (from the 8-byte group holding entry T on; the
+        // masks rewrite those below T) and the spare entries after the last
+        // row; all start at a valid table offset (channel 0)
+        for (uint32_t e = (uint32_t)T & ~3u; e < lstride; e += 4u)
+            reinterpret_cast<uint2*>(lst)[((uint32_t)L * lstride + e) >> 2] = make_uint2(0, 0);
+        if (L < 4) reinterpret_cast<uint2*>(lst)[16u * lstride + (uint32_t)L] = make_uint2(0, 0);
     }
     // the first tile's slot list needs only its masks: build it before
     // waiting for the table, then request the tile's V rows
@@ -593,16 +624,16 @@ decode_fast_kernel(const DecodeArgs a) {
             if (SMODE) qn[(j & 127) * G + (j >> 7)] = qv * ns;     // ns belongs to channel tid & 127 == j & 127
         }
     }
-    if (tid < 128) reinterpret_cast<float*>(tab + fast_rtab(G))[tid] = rv;
+    if (tid < 128) *reinterpret_cast<float*>(tab + fast_rtab(G) + 16u * (uint32_t)tid) = rv;
     __syncthreads();
 
     // q' . r per head
     float cq[G];
     {
-        const QV<G> e0 = load_qrow<G>(tab, 4u * (uint32_t)L);
-        const QV<G> e1 = load_qrow<G>(tab, 4u * (uint32_t)(L + 64));
-        const float r0 = reinterpret_cast<const float*>(tab + fast_rtab(G))[L];
-        const float r1 = reinterpret_cast<const float*>(tab + fast_rtab(G))[L + 64];
+        const QV<G> e0 = load_qrow<G>(tab, 16u * (uint32_t)L);
+        const QV<G> e1 = load_qrow<G>(tab, 16u * (uint32_t)(L + 64));
+        const float r0 = *reinterpret_cast<const float*>(tab + fast_rtab(G) + 16u * (uint32_t)L);
+        const float r1 = *reinterpret_cast<const float*>(tab + fast_rtab(G) + 16u * (uint32_t)(L + 64));
 #pragma unroll
         for (int g = 0; g < G; ++g) cq[g] = wave_sum_dpp(e0.v[g] * r0 + e1.v[g] * r1);
     }

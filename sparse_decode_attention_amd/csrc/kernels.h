@@ -12,9 +12,10 @@
 #define STATS_THREADS 1024
 #define DECODE_THREADS 256
 #define DECODE_FAST_THREADS 512
-// LDS of the fast decode kernel: q' and r tables with a flag slot (2576 B),
-// then per wave the slot list of the largest T (64 lanes x 68 u16) and 1 KiB of p
-#define DECODE_FAST_LDS_BYTES (2576 + (DECODE_FAST_THREADS / 64) * (8704 + 1024))
+// LDS of the exact-T matrix-core decode kernels: q' and r tables with a flag
+// slot (4112 B), then per wave the slot list of the largest T (64 lanes x 68
+// u16) and 1 KiB of p
+#define DECODE_FAST_LDS_BYTES (4112 + (DECODE_FAST_THREADS / 64) * (8704 + 1024))
 #define DECODE_TILE 64
 #define DECODE_MAX_SPLITS 256
 #define DECODE_RAGGED_CHUNKS (DECODE_TILE * 128 * 2 / 16 + 1)   // 16-byte chunks of a tile of full rows, + misalignment
