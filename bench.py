@@ -36,8 +36,10 @@ METRIC = "SparK decode attn effective KV GB/s & %HBM peak, S=32K, λ=0.5/0.8"
 HBM_PEAK_GBS = 8000.0
 MALL_DEFEAT_BYTES = 768e6
 SAMPLE_SEED = 0x5EED5A3B1E0F2C47   # Philox key of the sampled-F legs
-DECODE_SOURCES = ["sparse_decode_attention_amd/csrc/decode.hip", "sparse_decode_attention_amd/csrc/kernels.h",
-                  "sparse_decode_attention_amd/csrc/common.h", "sparse_decode_attention_amd/csrc/spark_abi.hip"]
+DECODE_SOURCES = ["sparse_decode_attention_amd/csrc/decode.hip", "sparse_decode_attention_amd/csrc/decode_common.h",
+                  "sparse_decode_attention_amd/csrc/decode_fast.h", "sparse_decode_attention_amd/csrc/decode_fast_fixed.hip",
+                  "sparse_decode_attention_amd/csrc/kernels.h", "sparse_decode_attention_amd/csrc/common.h",
+                  "sparse_decode_attention_amd/csrc/spark_abi.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_kernel_llama8b_s32k_traffic.md")
 
 
@@ -49,21 +51,22 @@ def decode_source_sha() -> str:
 
 
 def read_traffic(workload: str):
-    """Per-launch HBM bytes of the decode kernel from the committed rocprofv3
-    counter summary, if it was taken on the current kernel source."""
+    """(per-launch HBM bytes, profiled average duration in ns) of the decode
+    kernel from the committed rocprofv3 summary, if it was taken on the
+    current kernel source and this workload; (None, None) otherwise."""
     if not os.path.exists(TRAFFIC_FILE):
-        return None
+        return None, None
     kv = {}
     for line in open(TRAFFIC_FILE):
         if ":" in line and line.strip().startswith("- "):
             k, v = line.strip()[2:].split(":", 1)
             kv[k.strip()] = v.strip()
     if kv.get("source_sha256") != decode_source_sha() or kv.get("workload") != workload:
-        return None
+        return None, None
     try:
-        return float(kv["hbm_bytes_per_launch"])
+        return float(kv["hbm_bytes_per_launch"]), float(kv["avg_duration_ns"])
     except (KeyError, ValueError):
-        return None
+        return None, None
 
 
 # 32-bit VALU lane operations per second: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
@@ -99,6 +102,18 @@ def effective_prefill_bytes(w, T):
 def decode_bucket(T: int) -> int:
     """Largest row length of the runtime-T decode variant that serves T."""
     return 32 if T <= 32 else 64 if T <= 64 else 96 if T <= 96 else 128
+
+
+def decode_kernel_name(G: int, T: int, smode: int = 0, ragged: bool = False) -> str:
+    """The matrix-core decode kernel the library launches, as
+    decode_fast_kernel<G, TB, TFIX, ODD, SMODE, RG>."""
+    if ragged:
+        return f"decode_fast_kernel<{G}, 128, 0, true, 0, true>"
+    if G == 4 and T in (26, 38, 48, 64):
+        return f"decode_fast_kernel<4, {T}, {T}, false, {smode}, false>"
+    if smode:
+        return f"decode_kernel<{G}, {smode}, false, false>"
+    return f"decode_fast_kernel<{G}, {decode_bucket(T)}, 0, {'true' if T & 1 else 'false'}, 0, false>"
 
 
 def run_leg(w, steps, warmup, rotate=True, seed=0, verbose=True, x=None, recovery="mean_retained",
@@ -531,13 +546,18 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def summarize(kt_dir: str, fetch_dir: str, write_dir: str, workload: str, command: str) -> str:
-    """Write profiles/decode_kernel_llama8b_s32k_traffic.md from rocprofv3
-    output: kernel-trace stats (average duration of the decode kernel) and the
-    FETCH_SIZE / WRITE_SIZE passes (KiB per dispatch), scaled by what the same
-    counters read for the plain 256 MiB device copy the run also performs."""
+def summarize(kt_dir: str, fetch_dir: str, write_dir: str, bench_log: str, workload: str, command: str) -> str:
+    """Render profiles/decode_kernel_llama8b_s32k_traffic.md from three
+    rocprofv3 runs of the same bench command (kernel trace, FETCH_SIZE pass,
+    WRITE_SIZE pass) and the bench JSON line the kernel-trace run printed:
+    per kernel of the library its profiled duration and HBM bytes per
+    dispatch, the counters scaled by what they read for the plain 256 MiB
+    device copy the run also performs."""
     import csv
     import glob
+
+    if not command.strip():
+        raise SystemExit("--summary-command must give the rocprofv3 command lines the summary is made from")
 
     def rows(d, name):
         out = []
@@ -545,41 +565,81 @@ def summarize(kt_dir: str, fetch_dir: str, write_dir: str, workload: str, comman
             out += list(csv.DictReader(open(f)))
         return out
 
-    stats = rows(kt_dir, "*kernel_stats.csv")
+    def short(name):
+        return name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
+
+    stats = [r for r in rows(kt_dir, "*kernel_stats.csv") if "spark::" in r["Name"]]
+    stats.sort(key=lambda r: -float(r["TotalDurationNs"]))
     dec = [r for r in stats if "decode_fast_kernel" in r["Name"] or "decode_kernel" in r["Name"]]
-    dec.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    kname = short(dec[0]["Name"])
     avg_ns = float(dec[0]["AverageNs"])
-    kname = dec[0]["Name"]
 
     def per_dispatch(d, counter):
-        vals, calib = [], []
+        """KiB per dispatch of every library kernel (dimension entries of one
+        dispatch summed, then averaged over dispatches), and the copy's."""
+        per, calib = {}, []
         for r in rows(d, "*counter_collection.csv"):
             if r["Counter_Name"] != counter:
                 continue
-            if r["Kernel_Name"] == kname:
-                vals.append(float(r["Counter_Value"]))
             if "copyBuffer" in r["Kernel_Name"] and int(r["Grid_Size"]) >= 131072:
                 calib.append(float(r["Counter_Value"]))
-        return sum(vals) / len(vals), max(calib)
+            if "spark::" in r["Kernel_Name"]:
+                k = per.setdefault(short(r["Kernel_Name"]), {})
+                k[r["Dispatch_Id"]] = k.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+        return {n: sum(v.values()) / len(v) for n, v in per.items()}, max(calib)
 
-    f_kib, f_cal = per_dispatch(fetch_dir, "FETCH_SIZE")
-    w_kib, w_cal = per_dispatch(write_dir, "WRITE_SIZE")
+    fetch, f_cal = per_dispatch(fetch_dir, "FETCH_SIZE")
+    write, w_cal = per_dispatch(write_dir, "WRITE_SIZE")
     copy_bytes = 256 << 20
     f_scale, w_scale = copy_bytes / (f_cal * 1024), copy_bytes / (w_cal * 1024)
-    fetch_b, write_b = f_kib * 1024 * f_scale, w_kib * 1024 * w_scale
-    text = f"""# Decode kernel: time and HBM traffic, {workload}
+    line = None
+    for ln in open(bench_log):
+        if ln.startswith("{"):
+            line = json.loads(ln)
+    ev_us = line["decode_us_per_launch"]
+    alg = line["roofline"]["algorithmic_bytes_per_launch"]
+    fetch_b, write_b = fetch[kname] * 1024 * f_scale, write[kname] * 1024 * w_scale
+    cmds = "\n".join("    " + c.strip() for c in command.split(";;"))
+    table = ["| kernel | calls | profiled avg us | HBM read MB / dispatch | HBM write MB / dispatch |",
+             "|---|---|---|---|---|"]
+    for r in stats:
+        n = short(r["Name"])
+        fr = f"{fetch[n] * 1024 * f_scale / 1e6:.2f}" if n in fetch else "-"
+        wr = f"{write[n] * 1024 * w_scale / 1e6:.2f}" if n in write else "-"
+        table.append(f"| {n} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {fr} | {wr} |")
+    text = f"""# Library kernels: time and HBM traffic, {workload}
 
-Command (rocprofv3, three runs; the GPU-side numbers below come from it):
+Commands (three rocprofv3 runs of the same bench command: kernel trace,
+FETCH_SIZE pass, WRITE_SIZE pass; then this summary):
 
-    {command}
+{cmds}
+
+{chr(10).join(table)}
+
+Counter scale: a 256 MiB device copy (__amd_rocclr_copyBuffer, run by the
+bench's --calib-copy-mb 256) reads FETCH_SIZE {f_cal:.0f} KiB and WRITE_SIZE
+{w_cal:.0f} KiB, so fetch counts are multiplied by {f_scale:.3f} and write
+counts by {w_scale:.3f}. (The derived FETCH_SIZE weighs every read request
+that is not 32 bytes as 64 bytes; the L2's fills from HBM on this chip are
+128-byte requests, so the raw counter shows half the bytes a copy of known
+size reads.)
+
+Decode: the profiled average duration against the HIP-event time per
+launch that the same (profiled) bench run printed, over its graph of 64
+launches; the profiler slows every dispatch, so both read above the
+unprofiled bench's time.
 
 - kernel: {kname}
 - workload: {workload}
 - source_sha256: {decode_source_sha()}
 - avg_duration_ns: {avg_ns:.0f}
-- fetch_kib_per_dispatch_raw: {f_kib:.1f}
-- write_kib_per_dispatch_raw: {w_kib:.1f}
-- calibration: a 256 MiB device copy (__amd_rocclr_copyBuffer) reads FETCH_SIZE {f_cal:.0f} KiB and WRITE_SIZE {w_cal:.0f} KiB, so the scale factors are fetch x{f_scale:.3f}, write x{w_scale:.3f}
+- hipevent_us_per_launch: {ev_us:.3f}
+- profiler_overhead_us: {avg_ns / 1e3 - ev_us:.3f}
+- algorithmic_bytes_per_launch: {alg}
+- frac_hipevent: {alg / (ev_us * 1e-6) / 1e9 / HBM_PEAK_GBS:.4f}
+- frac_profiled: {alg / (avg_ns * 1e-9) / 1e9 / HBM_PEAK_GBS:.4f}
+- fetch_kib_per_dispatch_raw: {fetch[kname]:.1f}
+- write_kib_per_dispatch_raw: {write[kname]:.1f}
 - fetch_bytes_per_launch: {fetch_b:.0f}
 - write_bytes_per_launch: {write_b:.0f}
 - hbm_bytes_per_launch: {fetch_b + write_b:.0f}
@@ -609,9 +669,10 @@ def main():
     ap.add_argument("--warm", action="store_true", help="also report a run without replica rotation")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="run a plain device copy of this size after the legs (counter calibration)")
-    ap.add_argument("--summarize", nargs=3, metavar=("KT_DIR", "FETCH_DIR", "WRITE_DIR"),
+    ap.add_argument("--summarize", nargs=4, metavar=("KT_DIR", "FETCH_DIR", "WRITE_DIR", "BENCH_LOG"),
                     help="write the rocprofv3 traffic summary under profiles/ and exit")
-    ap.add_argument("--summary-command", default="", help="command line recorded in the summary")
+    ap.add_argument("--summary-command", default="",
+                    help="the rocprofv3 command lines the summary is made from, separated by ';;' (required)")
     args = ap.parse_args()
     if args.summarize:
         txt = summarize(*args.summarize, args.workload, args.summary_command)
@@ -656,12 +717,17 @@ def main():
                     "bytes": effective_prefill_bytes(w, T),
                     "tokens_kv_heads_per_s": w.B * w.S * w.n_kv / (main_leg["prefill_us"] * 1e-6)},
     }
-    traffic = read_traffic(w.name)
+    traffic, prof_ns = read_traffic(w.name)
     dec_bytes = main_leg["decode_bytes_per_step"]
     line["roofline"] = {"bound": "hbm", "achieved": round(main_leg["decode_GBps"], 2), "peak": HBM_PEAK_GBS,
                         "unit": "GB/s", "frac": round(main_leg["decode_GBps"] / HBM_PEAK_GBS, 4),
-                        "traffic": traffic, "kernel": f"decode_fast_kernel<4, {T}>",
-                        "algorithmic_bytes_per_launch": dec_bytes}
+                        "traffic": traffic, "kernel": decode_kernel_name(w.G, T),
+                        "algorithmic_bytes_per_launch": dec_bytes,
+                        # the committed rocprofv3 summary's average duration (it includes the
+                        # profiler's per-dispatch overhead) and the fraction it gives
+                        "profiled_us": None if prof_ns is None else round(prof_ns / 1e3, 3),
+                        "frac_profiled": None if prof_ns is None else
+                        round(dec_bytes / (prof_ns * 1e-9) / 1e9 / HBM_PEAK_GBS, 4)}
     ceil, ceil_blocks = stream_ceiling(dec_bytes)
     line["stream_ceiling"] = {"GBps": round(ceil, 1), "bytes": dec_bytes,
                               "frac_of_ceiling": round(main_leg["decode_GBps"] / ceil, 4), "blocks": ceil_blocks,
@@ -685,7 +751,7 @@ def main():
             alu_ops = w.B * w.n_kv * w.S * sampled_alu_ops_per_token(w.G, T, rec)
             alu_gops = alu_ops / (lg["decode_us_per_launch"] * 1e-6) / 1e9
             line["sampled_f"][rec] = {
-                "workload": w.name, "kernel": (f"decode_fast_kernel<4, {T}, {ops.RECOVERY[rec]}>" if w.G == 4 and T in (26, 38, 48, 64) else f"decode_kernel<{w.G}, {ops.RECOVERY[rec]}, false, false>"),
+                "workload": w.name, "kernel": decode_kernel_name(w.G, T, ops.RECOVERY[rec]),
                 "decode_us_per_launch": round(lg["decode_us_per_launch"], 3),
                 "GBps": round(lg["decode_GBps"], 2),
                 "roofline": {"bound": "alu", "achieved": round(alu_gops, 1), "peak": VALU_PEAK_GOPS, "unit": "Gop/s",
@@ -708,9 +774,7 @@ def main():
             print(f"bench: variant {name} ({wv.name})", file=sys.stderr, flush=True)
             lg = run_leg(wv, min(args.steps, 5), min(args.warmup, 2), x=xv)
             Tv = lg["T"]
-            exact = wv.G == 4 and Tv in (26, 38, 48, 64)
-            kern = (f"decode_fast_kernel<4, {Tv}>" if exact else
-                    f"decode_fast_kernel<G={wv.G}, T<={decode_bucket(Tv)}, {'odd' if Tv & 1 else 'even'} T>")
+            kern = decode_kernel_name(wv.G, Tv)
             line["variants"].append({
                 "variant": name, "workload": wv.name, "G": wv.G, "lambda": wv.lam, "T": Tv, "kernel": kern,
                 "decode_us_per_launch": round(lg["decode_us_per_launch"], 3),
@@ -759,7 +823,7 @@ def main():
         lg = run_leg(w, min(args.steps, 5), min(args.warmup, 2), x=main_leg["x"], top_p=0.99)
         line["top_p"] = {
             "workload": w.name, "p": 0.99, "mean_kept": round(lg["T"], 2),
-            "pruning_ratio": round(1 - lg["T"] / w.D, 4), "kernel": ("decode_fast_kernel<4, 128, 0, true>" if w.G == 4 else f"decode_kernel<{w.G}, 0, false, true>"),
+            "pruning_ratio": round(1 - lg["T"] / w.D, 4), "kernel": decode_kernel_name(w.G, w.D, ragged=True),
             "decode_us_per_launch": round(lg["decode_us_per_launch"], 3), "bytes_per_launch": lg["decode_bytes_per_step"],
             "GBps": round(lg["decode_GBps"], 2), "pct_hbm_peak": round(100 * lg["decode_GBps"] / HBM_PEAK_GBS, 2),
             "prefill_us": round(lg["prefill_us"], 2), "replicas": lg["replicas"]}
@@ -770,7 +834,7 @@ def main():
         print(f"bench: SparK-g {ratios} on {w.name}", file=sys.stderr, flush=True)
         lg = run_leg(w, min(args.steps, 5), min(args.warmup, 2), x=main_leg["x"], ratios=ratios)
         line["grouped"] = {
-            "workload": w.name, "ratios": ratios, "T": lg["T"], "kernel": f"decode_fast_kernel<4, {lg['T']}>",
+            "workload": w.name, "ratios": ratios, "T": lg["T"], "kernel": decode_kernel_name(w.G, lg["T"]),
             "decode_us_per_launch": round(lg["decode_us_per_launch"], 3), "GBps": round(lg["decode_GBps"], 2),
             "pct_hbm_peak": round(100 * lg["decode_GBps"] / HBM_PEAK_GBS, 2), "prefill_us": round(lg["prefill_us"], 2),
             "prefill_GBps": round(lg["prefill_GBps"], 1), "replicas": lg["replicas"]}

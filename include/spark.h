@@ -213,17 +213,22 @@ int spark_stats(const void* k_packed, const uint32_t* mask, const float* chan_en
  *  v        bf16 [B][N_kv][S][D]
  *  scale    softmax scale; <= 0 selects 1/sqrt(D)
  *  splits   sequence splits per (b, KV head); 0 lets the library choose
- *           (about 256 blocks in all for the G = 4, T in {26, 38, 48, 64}
- *           kernel, 512 otherwise when two blocks fit in one CU's LDS, and
- *           never fewer 64-token tiles per block than its 8 or 4 waves);
- *           larger values are clamped to min(256, ceil(S / 64))
+ *           (about 256 blocks in all for the matrix-core kernel, which takes
+ *           every T from 1 to D and every group size; 512 for the generic
+ *           one, used for packed V, the sampled F outside G = 4 with T in
+ *           {26, 38, 48, 64}, T = 0 and packed caches shorter than one
+ *           lane's row request (at most 68 dwords in all), when two blocks
+ *           fit in one CU's LDS; never fewer 64-token tiles
+ *           per block than its 8 or 4 waves); larger values are clamped to
+ *           min(256, ceil(S / 64))
  *  out      fp32 [B][N_q][D]
  * No causal mask: the query attends to every cached token. fp32 arithmetic
  * on bf16 inputs. The first SPARK_DECODE_COUNTER_BYTES of ws hold completion
- * counters that must be zero before the first call (spark_decode_ws_init);
- * every call that completes leaves them zero again.
+ * counters, one per (b, KV head), that must be zero before the first call
+ * (spark_decode_ws_init); every call that completes leaves them zero again.
+ * B * N_kv above SPARK_DECODE_COUNTER_BYTES / 4 (65536) is SPARK_EUNSUPPORTED.
  */
-#define SPARK_DECODE_COUNTER_BYTES 4096
+#define SPARK_DECODE_COUNTER_BYTES (256u << 10)
 int spark_decode_attn(const void* q, const void* k_packed, const uint32_t* mask, const void* v,
                       const float* r, int B, int S, int N_q, int N_kv, int D, float lambda,
                       float scale, int splits, float* out, void* ws, size_t ws_bytes, void* stream);

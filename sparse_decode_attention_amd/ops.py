@@ -22,7 +22,7 @@ OK, EINVAL, EUNSUPPORTED, EALIGN, ENOSPACE, EHIP, ESCRATCH = 0, -1, -2, -3, -4, 
 NOALLOC_SCRATCH_BYTES = 8 << 20
 RECOVERY = {"mean_retained": 0, "zero": 1, "const": 2, "score_mean_pruned": 3, "gaussian": 4, "exponential": 5}
 QAGG = {"l2": 0, "mean": 1}
-DECODE_COUNTER_BYTES = 4096
+DECODE_COUNTER_BYTES = 256 << 10
 
 _lib = None
 _lock = threading.Lock()

@@ -20,7 +20,7 @@ def kernel_table(stats_dir: str, title: str, command: str, note: str = "", match
         out += [note, ""]
     out += ["| kernel | calls | avg us | min us | max us | share % |", "|---|---|---|---|---|---|"]
     for r in keep:
-        name = r["Name"].split("(")[0].replace("void ", "")
+        name = r["Name"].replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
         out.append(f"| {name} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
                    f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |")
     return "\n".join(out) + "\n"
@@ -34,7 +34,7 @@ def counter_means(pmc_dir: str, match: str) -> dict:
         for r in csv.DictReader(open(f)):
             if match not in r["Kernel_Name"]:
                 continue
-            name = r["Kernel_Name"].split("(")[0].replace("void ", "")
+            name = r["Kernel_Name"].replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
             key = (r["Dispatch_Id"], r["Counter_Name"])
             per.setdefault(name, {}).setdefault(key, 0.0)
             per[name][key] += float(r["Counter_Value"])

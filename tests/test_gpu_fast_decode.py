@@ -110,3 +110,15 @@ def test_runtime_variants_repeatable_and_split_invariant(G, T):
     np.testing.assert_array_equal(outs[0], outs[1])
     for o in outs:
         assert_tol(o, want, f"G={G} T={T} splits")
+
+
+def test_more_heads_than_1024_counters():
+    """B * N_kv = 1040 (b, KV head) pairs, each with its own completion
+    counter, over two calls in a row (every counter back at zero after the
+    first); G = 4, T = 26 (exact-T kernel) and G = 2, T = 33 (runtime T)."""
+    for G, T in ((4, 26), (2, 33)):
+        d, want = hand_built_fixed(130, 8, 70, T, G, seed=5000 + T)
+        for _ in range(2):
+            out = ops.decode_attn(d["q"], d["k_packed"], d["mask"], d["v"], d["r"], lam_of(T), splits=2)
+            torch.cuda.synchronize()
+            assert_tol(out.cpu().numpy(), want, f"B*N_kv=1040 G={G} T={T}")
