@@ -109,8 +109,10 @@ def decode_kernel_name(G: int, T: int, smode: int = 0, ragged: bool = False) -> 
     decode_fast_kernel<G, TB, TFIX, ODD, SMODE, RG>."""
     if ragged:
         return f"decode_fast_kernel<{G}, 128, 0, true, 0, true>"
-    if G == 4 and T in (26, 38, 48, 64):
-        return f"decode_fast_kernel<4, {T}, {T}, false, {smode}, false>"
+    exact = (G == 4 and T in (26, 38, 48, 64)) or (not smode and (
+        (G == 4 and T in (13, 51, 77, 90, 102, 115)) or (G in (1, 2, 8) and T in (26, 64))))
+    if exact:
+        return f"decode_fast_kernel<{G}, {T}, {T}, {'true' if T & 1 else 'false'}, {smode}, false>"
     if smode:
         return f"decode_kernel<{G}, {smode}, false, false>"
     return f"decode_fast_kernel<{G}, {decode_bucket(T)}, 0, {'true' if T & 1 else 'false'}, 0, false>"

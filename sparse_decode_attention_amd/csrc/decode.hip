@@ -504,15 +504,24 @@ decode_kernel(const DecodeArgs a) {
     finish_block<G, DECODE_THREADS, false>(a, m_run, l_run, acc, wbase, &s_last, bh, b, h, split);
 }
 
-bool decode_fast_exact_T(int T) { return T == 26 || T == 38 || T == 48 || T == 64; }
+// the exact-T variants: G = 4 at T in {26, 38, 48, 64} with every F, at the
+// other tenths of lambda with the fixed F, and G = 1, 2, 8 at T in {26, 64}
+bool decode_fast_exact(int G, int T, int sampled) {
+    const bool base = G == 4 && (T == 26 || T == 38 || T == 48 || T == 64);
+    if (sampled) return base;
+    if (G == 4) return base || T == 13 || T == 51 || T == 77 || T == 90 || T == 102 || T == 115;
+    return (G == 1 || G == 2 || G == 8) && (T == 26 || T == 64);
+}
 
 bool decode_fast_supported(int G, int T, int sampled, size_t packed_elems) {
     if (G != 1 && G != 2 && G != 4 && G != 8) return false;
-    if (sampled) return G == 4 && decode_fast_exact_T(T);
-    if (G == 4 && decode_fast_exact_T(T)) return true;
-    // runtime T: each lane's 16-byte requests start inside the packed buffer
-    // and must fit in it when they start at its first dword
-    return T >= 1 && T <= 128 && packed_elems / 2 >= (size_t)decode_fast_kr(decode_fast_bucket(T), (T & 1) != 0);
+    if (sampled) return decode_fast_exact(G, T, sampled);
+    if (T < 1 || T > 128) return false;
+    // rows that are not exact 16-byte multiples: each lane's 16-byte requests
+    // start inside the packed buffer and must fit in it when they start at
+    // its first dword
+    const int kr = decode_fast_exact(G, T, 0) ? decode_fast_kr_exact(T) : decode_fast_kr(decode_fast_bucket(T), (T & 1) != 0);
+    return T % 2 == 0 && decode_fast_exact(G, T, 0) ? true : packed_elems / 2 >= (size_t)kr;
 }
 // (the ragged rows' loads assume a region of at least 65 dwords: S >= 2)
 bool decode_fast_ragged_supported(int G, int S) { return (G == 1 || G == 2 || G == 4 || G == 8) && S >= 2; }
@@ -554,9 +563,9 @@ hipError_t launch_fast_g(const DecodeArgs& a, int G, dim3 grid, hipStream_t stre
 
 // One launch: the split blocks, the last of which per (b, KV head) merges.
 // The matrix-core kernel takes ragged rows (S >= 2) and, for fixed or
-// sampled F, the shapes decode_fast_supported admits (its exact-T variants
-// for G = 4 and the pruning ratios in common use); packed V and everything
-// else take the generic kernel.
+// sampled F, the shapes decode_fast_supported admits (an exact-T variant
+// where one exists, else the runtime-T variant of T's bucket); packed V and
+// everything else take the generic kernel.
 hipError_t launch_decode(const DecodeArgs& a, int G, int BH, hipStream_t stream) {
     const dim3 grid(a.nsplit, BH), block(DECODE_THREADS);
     if (a.row_off) {
@@ -565,7 +574,8 @@ hipError_t launch_decode(const DecodeArgs& a, int G, int BH, hipStream_t stream)
     }
     if (a.v_packed_mode) return launch_generic<0, true, false>(a, G, grid, block, stream);
     if (decode_fast_supported(G, a.T, a.sampled, a.packed_elems)) {
-        if (G == 4 && decode_fast_exact_T(a.T)) return launch_fast_fixed(a, grid, stream);
+        if (G == 4 && (a.T == 26 || a.T == 38 || a.T == 48 || a.T == 64)) return launch_fast_fixed(a, grid, stream);
+        if (decode_fast_exact(G, a.T, a.sampled)) return launch_fast_fixed2(a, G, grid, stream);
         return launch_fast_g(a, G, grid, stream);
     }
     switch (a.sampled) {

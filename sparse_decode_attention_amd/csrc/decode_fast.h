@@ -13,12 +13,15 @@
 //     a bf16 hi and lo part, V taken from the registers it was loaded into.
 //
 // Variants (template parameters):
-//   TFIX > 0  exact row length TFIX (G = 4, the pruning ratios in common
-//             use; rows read with exact loads);
-//   TB        otherwise: any T with T <= TB (buckets 32, 64, 96, 128); each
-//             lane reads its row as 16-byte loads from the dword holding its
-//             first element, and ODD T rows (2-byte aligned) are realigned
-//             with a funnel shift;
+//   TFIX > 0  exact row length TFIX (the pruning ratios in common use): the
+//             slot loop runs exactly T slots;
+//   TB        otherwise: any T with T <= TB (buckets 32, 64, 96, 128), the
+//             slot loop unrolled for TB with a wave-uniform exit at T;
+//   ODD       odd T: rows start mid-dword on every other token and are
+//             realigned with a funnel shift.
+//   Rows whose length is a multiple of 8 (exact T) are read with exact
+//   16-byte loads; every other lane reads its row as 16-byte loads from the
+//   dword holding its first element;
 //   RG        ragged rows (SparK-p): per-lane row offsets and lengths;
 //   SMODE     sampled recovery F (4 Gaussian, 5 Exponential), TFIX only.
 #pragma once
@@ -191,28 +194,32 @@ struct RowState {
     int o_nx, oe_nx;  // ragged rows: offsets of the next tile's row (requested a tile ahead)
 };
 
-// Exact rows of a compile-time even T.
+// Exact rows of a compile-time even T: T / 16 16-byte loads per lane when
+// T is a multiple of 8 (rows 16-byte aligned), else T / 2 dword loads (rows
+// 4-byte aligned; measured faster here than 16-byte loads at 4-byte
+// alignment: T = 26: 22.6 against 24.5 us at S = 32K).
 template <int T>
 __device__ __forceinline__ void load_row_fixed(const DecodeArgs& a, int bh, int t0, int nt, int L,
                                                uint4& mw, uint32_t (&kr)[T / 2]) {
-    constexpr int NDW = T / 2;
+    static_assert(T % 2 == 0, "even rows");
     const size_t row = (size_t)bh * a.S_cap + t0 + min(L, nt - 1);
     mw = *reinterpret_cast<const uint4*>(a.mask + row * 4);
     if constexpr (T % 8 == 0) {
-        const uint4* src = reinterpret_cast<const uint4*>(a.packed + row * T);   // 16-byte aligned rows
+        const uint4* src = reinterpret_cast<const uint4*>(a.packed + row * T);
 #pragma unroll
-        for (int i = 0; i < NDW / 4; ++i) {
+        for (int i = 0; i < T / 8; ++i) {
             const uint4 x = src[i];
             kr[4 * i] = x.x; kr[4 * i + 1] = x.y; kr[4 * i + 2] = x.z; kr[4 * i + 3] = x.w;
         }
     } else {
-        const uint32_t* src = reinterpret_cast<const uint32_t*>(a.packed + row * T);  // 4-byte aligned rows
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(a.packed + row * T);
 #pragma unroll
-        for (int i = 0; i < NDW; ++i) kr[i] = src[i];
+        for (int i = 0; i < T / 2; ++i) kr[i] = src[i];
     }
 }
 
-// Rows of a runtime T <= TB: the lane requests KR dwords (KR / 4 16-byte
+// Rows of any other T (a runtime T <= TB, or an exact T that is not a
+// multiple of 8): the lane requests KR dwords (KR / 4 16-byte
 // requests, no branches) from the one holding its row's first element, so
 // kr[i] holds slots 2 i - sh and 2 i - sh + 1 (sh = 1 when the row starts in
 // the middle of a dword: odd T only). What lies past the row belongs to the
@@ -352,13 +359,15 @@ __device__ __forceinline__ void build_list(const uint4& mw, uint8_t* lst, int L,
 template <int G, int TB, int TFIX, bool ODD, bool RG>
 struct FastCfg {
     static_assert(G == 1 || G == 2 || G == 4 || G == 8, "group size");
-    static_assert(RG ? (TFIX == 0 && TB == 128) : TFIX ? (TB == TFIX && !ODD && TFIX % 2 == 0 && TFIX < 128)
+    static_assert(RG ? (TFIX == 0 && TB == 128) : TFIX ? (TB == TFIX && ODD == ((TFIX & 1) != 0) && TFIX < 128)
                                                        : (TB == 32 || TB == 64 || TB == 96 || TB == 128),
                   "variant");
+    // exact rows of an even length: loaded exactly (load_row_fixed)
+    static constexpr bool XLOAD = TFIX != 0 && TFIX % 2 == 0;
     // slots the score loop is unrolled for
     static constexpr int LOOP = RG ? 128 : TB;
     // row registers per lane
-    static constexpr int KR = RG ? RAGGED_KR : TFIX ? TFIX / 2 : decode_fast_kr(TB, ODD);
+    static constexpr int KR = RG ? RAGGED_KR : TFIX ? decode_fast_kr_exact(TFIX) : decode_fast_kr(TB, ODD);
     // slots per batch of the score loop (4 where the row registers or the
     // q' rows of eight heads would otherwise crowd out the rest)
     static constexpr int NB = (G == 8 || RG || KR > 40) ? 4 : 8;
@@ -372,7 +381,8 @@ struct FastCfg {
     // 64); at least 72 KiB, so that any u16 list entry (even one a mask with
     // fewer than T bits left unwritten) addresses LDS inside the block's
     static constexpr uint32_t LDS_NEED = fast_tables_bytes(G) + 16u + (uint32_t)FAST_NW * WAVE;
-    static constexpr uint32_t LDS = TFIX ? DECODE_FAST_LDS_BYTES : (LDS_NEED > 73728u ? LDS_NEED : 73728u);
+    static constexpr uint32_t LDS = (TFIX && LDS_NEED <= DECODE_FAST_LDS_BYTES) ? DECODE_FAST_LDS_BYTES
+                                                                                : (LDS_NEED > 73728u ? LDS_NEED : 73728u);
     static_assert(LDS_NEED <= LDS && 65535u + fast_rtab(G) + 4u <= LDS, "LDS");
 };
 
@@ -495,7 +505,7 @@ __device__ __forceinline__ void fast_tile(const DecodeArgs& a, int T, uint32_t l
             if (nt_next2 > 0)
                 ragged_offsets(a, bh, t1 + FAST_NW * DECODE_TILE + min(L, nt_next2 - 1), rs.o_nx, rs.oe_nx);
         }
-    } else if constexpr (TFIX != 0) {
+    } else if constexpr (C::XLOAD) {
         if (nt_next > 0) load_row_fixed<TFIX>(a, bh, t1, nt_next, L, mw, kr);
     } else {
         if (nt_next > 0) load_row_rt<C::KR, ODD>(a, T, bh, t1, nt_next, L, mw, kr, rs);
@@ -591,7 +601,7 @@ decode_fast_kernel(const DecodeArgs a) {
     const int tf0 = min(blk_begin + wave * DECODE_TILE, S - 1);
     const int ntf0 = max(1, min(DECODE_TILE, blk_end - tf0));
     if constexpr (RG) load_row_ragged(a, bh, tf0 + min(L, ntf0 - 1), o0, oe0, mw, kr, rs);
-    else if constexpr (TFIX != 0) load_row_fixed<TFIX>(a, bh, tf0, ntf0, L, mw, kr);
+    else if constexpr (C::XLOAD) load_row_fixed<TFIX>(a, bh, tf0, ntf0, L, mw, kr);
     else load_row_rt<KR, ODD>(a, T, bh, tf0, ntf0, L, mw, kr, rs);
     __builtin_amdgcn_sched_barrier(0);
     uint8_t* lst = wbase + (size_t)wave * WAVE;

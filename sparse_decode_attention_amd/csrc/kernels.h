@@ -135,9 +135,17 @@ bool decode_fast_ragged_supported(int G, int S);
 // plus one when odd rows start mid-dword, in whole 16-byte requests).
 constexpr int decode_fast_bucket(int T) { return T <= 32 ? 32 : T <= 64 ? 64 : T <= 96 ? 96 : 128; }
 constexpr int decode_fast_kr(int TB, bool odd) { return 4 * ((TB / 2 + (odd ? 1 : 0) + 3) / 4); }
+// the same for the exact-T variants: T / 2 for even T (exact loads), else
+// whole 16-byte requests covering the row and the dword after it (the funnel
+// shift's upper operand for the last slot)
+constexpr int decode_fast_kr_exact(int T) { return T % 2 == 0 ? T / 2 : 4 * ((T / 2 + 2 + 3) / 4); }
+// whether an exact-T variant exists for (G, T) (sampled: the sampled F)
+bool decode_fast_exact(int G, int T, int sampled);
 // matrix-core launchers: exact-T variants (G = 4, T in {26, 38, 48, 64},
-// fixed or sampled F) and the runtime-T / ragged variants per group size
+// fixed or sampled F; more pruning ratios and group sizes with the fixed F)
+// and the runtime-T / ragged variants per group size
 hipError_t launch_fast_fixed(const DecodeArgs& a, dim3 grid, hipStream_t stream);
+hipError_t launch_fast_fixed2(const DecodeArgs& a, int G, dim3 grid, hipStream_t stream);
 hipError_t launch_fast_g1(const DecodeArgs& a, dim3 grid, hipStream_t stream);
 hipError_t launch_fast_g2(const DecodeArgs& a, dim3 grid, hipStream_t stream);
 hipError_t launch_fast_g4(const DecodeArgs& a, dim3 grid, hipStream_t stream);

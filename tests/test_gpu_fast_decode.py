@@ -50,9 +50,10 @@ def lam_of(T):
     return lam
 
 
-# T = 26, 64 at G = 4 take the exact-T variants; every other (G, T) the
-# runtime-T ones (buckets 32, 64, 96, 128; odd T realigned per row)
-@pytest.mark.parametrize("T", [1, 7, 26, 33, 51, 64, 77, 90, 101, 127, 128])
+# exact-T variants: G = 4 at T = 13, 26, 51, 64, 77, 90, 102, 115 and
+# G = 1, 2, 8 at T = 26, 64; every other (G, T) takes the runtime-T variant of
+# its bucket (32, 64, 96, 128); odd T realigned per row in both
+@pytest.mark.parametrize("T", [1, 7, 13, 26, 33, 51, 64, 77, 90, 101, 102, 115, 127, 128])
 @pytest.mark.parametrize("G", [1, 2, 4, 8])
 def test_fixed_rows_every_group_and_length(G, T):
     lam = lam_of(T)
