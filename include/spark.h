@@ -226,7 +226,8 @@ int spark_stats(const void* k_packed, const uint32_t* mask, const float* chan_en
  * on bf16 inputs. The first SPARK_DECODE_COUNTER_BYTES of ws hold completion
  * counters, one per (b, KV head), that must be zero before the first call
  * (spark_decode_ws_init); every call that completes leaves them zero again.
- * B * N_kv above SPARK_DECODE_COUNTER_BYTES / 4 (65536) is SPARK_EUNSUPPORTED.
+ * B * N_kv above SPARK_DECODE_COUNTER_BYTES / 4 (65536), and 2^24 or more
+ * cached tokens per head (the head stride, S or S_cap), are SPARK_EUNSUPPORTED.
  */
 #define SPARK_DECODE_COUNTER_BYTES (256u << 10)
 int spark_decode_attn(const void* q, const void* k_packed, const uint32_t* mask, const void* v,

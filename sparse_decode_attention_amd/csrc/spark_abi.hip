@@ -335,6 +335,8 @@ int decode_call(const void* q, const void* k_packed, const uint32_t* mask, const
                 const PackedV* vp = nullptr, const int32_t* row_off = nullptr, int S_cap = 0) {
     if (S_cap == 0) S_cap = S;
     if (B < 1 || S < 1 || D < 1 || splits < 0 || S_cap < S) return SPARK_EINVAL;
+    // V rows are addressed with 32-bit byte offsets within a head
+    if (S_cap >= (1 << 24)) return SPARK_EUNSUPPORTED;
     const int T = kept_or_neg(D, lambda);
     if (T < 0) return SPARK_EINVAL;
     const int Tv = vp ? kept_or_neg(D, vp->lambda) : -1;

@@ -94,6 +94,7 @@ def test_decode_rejects_bad_arguments():
     assert _decode(D=256) == ops.EUNSUPPORTED
     assert _decode(B=200, N_kv=8) == ops.ENOSPACE        # 1600 (b, kv head) pairs: counters enough, workspace not
     assert _decode(B=8193, N_kv=8) == ops.EUNSUPPORTED   # more (b, kv head) pairs than counters (65536)
+    assert _decode(S=1 << 24) == ops.EUNSUPPORTED         # V rows addressed with 32-bit offsets per head
     assert _decode(v=None) == ops.EINVAL
     assert _decode(out=None) == ops.EINVAL
     assert _decode(q=MIS) == ops.EALIGN
