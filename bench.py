@@ -731,10 +731,12 @@ def main():
                         "frac_profiled": None if prof_ns is None else
                         round(dec_bytes / (prof_ns * 1e-9) / 1e9 / HBM_PEAK_GBS, 4)}
     ceil, ceil_blocks = stream_ceiling(dec_bytes)
+    ceil_1g, ceil_1g_blocks = stream_ceiling(1 << 30)
     line["stream_ceiling"] = {"GBps": round(ceil, 1), "bytes": dec_bytes,
                               "frac_of_ceiling": round(main_leg["decode_GBps"] / ceil, 4), "blocks": ceil_blocks,
-                              "what": "spark_read_stream of the same bytes, rotated like the decode replicas; "
-                                      "best over launch sizes of the median replay"}
+                              "GBps_1GiB": round(ceil_1g, 1), "blocks_1GiB": ceil_1g_blocks,
+                              "what": "spark_read_stream (nontemporal 16-byte requests) of the same bytes, rotated "
+                                      "like the decode replicas, and of 1 GiB; best over launch sizes of the median replay"}
     if args.second:
         w2 = WORKLOADS[args.second]
         print(f"bench: {w2.name}", file=sys.stderr, flush=True)
