@@ -123,3 +123,14 @@ def test_more_heads_than_1024_counters():
             out = ops.decode_attn(d["q"], d["k_packed"], d["mask"], d["v"], d["r"], lam_of(T), splits=2)
             torch.cuda.synchronize()
             assert_tol(out.cpu().numpy(), want, f"B*N_kv=1040 G={G} T={T}")
+
+
+@pytest.mark.parametrize("G,T", [(4, 90), (4, 51), (8, 64), (1, 64)])
+def test_full_size_variants_s32k(G, T):
+    """The bench's other pruning ratios and group sizes at their full shape
+    (B = 1, 8 KV heads, S = 32768, the default split plan the bench times):
+    every output against the oracle."""
+    d, want = hand_built_fixed(1, 8, 32768, T, G, seed=6000 + 10 * G + T)
+    out = ops.decode_attn(d["q"], d["k_packed"], d["mask"], d["v"], d["r"], lam_of(T))
+    torch.cuda.synchronize()
+    assert_tol(out.cpu().numpy(), want, f"S=32K G={G} T={T}")
