@@ -295,7 +295,9 @@ int spark_decode_attn_ragged(const void* q, const void* k_packed, const int32_t*
  *  v_mask       uint32 [B][N_kv][S][D/32]  exactly T_v bits per token; order |v| descending
  *               (key fl32(v^2)), ties to the lower channel
  *  r_v          fp32 [B][N_kv][D]  mean of the retained v_tj over the tokens keeping
- *               channel j (0 if none): the value a pruned V entry takes
+ *               channel j (0 if none), rounded to the nearest bfloat16 (ties to
+ *               even), the precision of the cached entries it stands in for: the
+ *               value a pruned V entry takes
  *  cnt          int32 [B][N_kv][D]  tokens keeping channel j (may be NULL)
  * Workspace: spark_prefill_workspace_bytes(B, S, N_kv, D).
  */

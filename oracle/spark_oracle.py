@@ -534,14 +534,28 @@ def value_keys(v: np.ndarray) -> np.ndarray:
     return v * v
 
 
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Finite fp32 values to the nearest bfloat16 (8 significand bits, ties
+    to even), returned as fp32: add half a bf16 unit (minus one, plus the
+    kept part's lowest bit for the tie) to the bit pattern, then drop the low
+    16 bits."""
+    u = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32)
+
+
 def prune_v(v: np.ndarray, lam_v: float) -> dict:
     """V-channel pruning of one cache: {"T", "mask", "words", "packed", "r",
-    "cnt"} with r the retained-mean recovery of the pruned entries."""
+    "cnt"} with r the retained-mean recovery of the pruned entries, rounded
+    to bfloat16, the precision of the cached V entries it stands in for
+    (walkthrough section 4.4 prunes V with K but does not spell the rule out;
+    this is the reading taken)."""
     D = v.shape[-1]
     T = num_kept(D, lam_v)
     mask = select_top_t(value_keys(v), T)
     r, cnt = stats(v, mask, None, F_MEAN_RETAINED)
-    return {"T": T, "mask": mask, "words": mask_words(mask), "packed": pack_kept(v, mask), "r": r, "cnt": cnt}
+    return {"T": T, "mask": mask, "words": mask_words(mask), "packed": pack_kept(v, mask), "r": round_bf16(r),
+            "cnt": cnt}
 
 
 def decode_attn_kv(q, k_packed, k_mask, r, v_packed, v_mask, rv, scale: float | None = None) -> np.ndarray:

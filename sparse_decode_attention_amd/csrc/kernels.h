@@ -55,7 +55,7 @@ __global__ void stats_partial_kernel(const uint16_t* k_packed, const uint32_t* m
                                      int S, int T, int nblk, int recovery);
 __global__ void stats_reduce_kernel(const double* part_sum, const int32_t* part_cnt, const double* part_pruned,
                                     const float* A, float* r, int32_t* cnt, int S, int T, int nblk,
-                                    int recovery, float f_const);
+                                    int recovery, float f_const, int round_bf16);
 __global__ void fill_u32_kernel(uint32_t* p, uint32_t value, size_t n);
 
 // LDS layout of the decode kernel (computed on the host for T and G).

@@ -503,7 +503,7 @@ __global__ void __launch_bounds__(STATS_THREADS)
 stats_reduce_kernel(const double* __restrict__ part_sum, const int32_t* __restrict__ part_cnt,
                     const double* __restrict__ part_pruned, const float* __restrict__ A,
                     float* __restrict__ r, int32_t* __restrict__ cnt,
-                    int S, int T, int nblk, int recovery, float f_const) {
+                    int S, int T, int nblk, int recovery, float f_const, int round_bf16) {
     constexpr int NCH = 128 / STATS_CH_BLOCKS;
     static_assert(NCH * STATS_PARTS == STATS_THREADS, "one thread per (part, channel)");
     __shared__ double sh_s[STATS_PARTS][NCH];
@@ -593,6 +593,13 @@ stats_reduce_kernel(const double* __restrict__ part_sum, const int32_t* __restri
             const double m2 = npruned > 0 ? p2 / npruned : 0.0;
             out = j == 0 ? (float)mu : j == 1 ? (float)sqrt(fmax(m2 - mu * mu, 0.0)) : 0.f;
         }
+    }
+    if (round_bf16) {
+        // to the nearest bfloat16, ties to even (the recovery of pruned V
+        // entries is kept in the cache's own precision)
+        uint32_t u = __float_as_uint(out);
+        u = (u + 0x7FFFu + ((u >> 16) & 1u)) & 0xFFFF0000u;
+        out = __uint_as_float(u);
     }
     r[(size_t)bh * 128 + j] = out;
     if (cnt) cnt[(size_t)bh * 128 + j] = (int32_t)c;

@@ -162,7 +162,7 @@ int spark_prefill_prune_cap(const void* q_win, const void* k, int B, int S, int 
                        w.sum, w.cnt, w.pruned, S, T, w.nblk, recovery, static_cast<const uint8_t*>(nullptr),
                        GroupSpec{}, 0.0f, static_cast<int32_t*>(nullptr), static_cast<int32_t*>(nullptr), S_cap);
     hipLaunchKernelGGL(stats_reduce_kernel, dim3(BH, STATS_CH_BLOCKS), dim3(STATS_THREADS), 0, st,
-                       w.sum, w.cnt, w.pruned, chan_energy, r, cnt, S, T, w.nblk, recovery, f_const);
+                       w.sum, w.cnt, w.pruned, chan_energy, r, cnt, S, T, w.nblk, recovery, f_const, 0);
     return hip_status(hipGetLastError());
 }
 
@@ -210,7 +210,7 @@ int spark_prefill_prune_v(const void* v, int B, int S, int N_kv, int D, float la
                        (int)SPARK_F_MEAN_RETAINED, static_cast<const uint8_t*>(nullptr), GroupSpec{}, 0.0f,
                        static_cast<int32_t*>(nullptr), static_cast<int32_t*>(nullptr), S);
     hipLaunchKernelGGL(stats_reduce_kernel, dim3(BH, STATS_CH_BLOCKS), dim3(STATS_THREADS), 0, st, w.sum, w.cnt, w.pruned,
-                       static_cast<const float*>(nullptr), r_v, cnt, S, T, w.nblk, (int)SPARK_F_MEAN_RETAINED, 0.0f);
+                       static_cast<const float*>(nullptr), r_v, cnt, S, T, w.nblk, (int)SPARK_F_MEAN_RETAINED, 0.0f, 1);
     return hip_status(hipGetLastError());
 }
 
@@ -248,7 +248,7 @@ int spark_prefill_prune_grouped(const void* q_win, const void* k, int B, int S, 
                        static_cast<const uint8_t*>(w.gid), grp, 0.0f, static_cast<int32_t*>(nullptr),
                        static_cast<int32_t*>(nullptr), S);
     hipLaunchKernelGGL(stats_reduce_kernel, dim3(BH, STATS_CH_BLOCKS), dim3(STATS_THREADS), 0, st,
-                       w.sum, w.cnt, w.pruned, chan_energy, r, cnt, S, T, w.nblk, recovery, f_const);
+                       w.sum, w.cnt, w.pruned, chan_energy, r, cnt, S, T, w.nblk, recovery, f_const, 0);
     return hip_status(hipGetLastError());
 }
 
@@ -284,7 +284,7 @@ int spark_prefill_prune_topp(const void* q_win, const void* k, int B, int S, int
                        static_cast<const uint32_t*>(mask), static_cast<uint16_t*>(k_packed), row_off,
                        static_cast<const int32_t*>(w.blk), S, w.nblk);
     hipLaunchKernelGGL(stats_reduce_kernel, dim3(BH, STATS_CH_BLOCKS), dim3(STATS_THREADS), 0, st,
-                       w.sum, w.cnt, w.pruned, chan_energy, r, cnt, S, -1, w.nblk, recovery, f_const);
+                       w.sum, w.cnt, w.pruned, chan_energy, r, cnt, S, -1, w.nblk, recovery, f_const, 0);
     return hip_status(hipGetLastError());
 }
 
@@ -310,7 +310,7 @@ int spark_stats(const void* k_packed, const uint32_t* mask, const float* chan_en
                        static_cast<const uint16_t*>(k_packed), mask, static_cast<const uint16_t*>(k_dense),
                        chan_energy, w.sum, w.cnt, w.pruned, S, T, w.nblk, recovery);
     hipLaunchKernelGGL(stats_reduce_kernel, dim3(BH, STATS_CH_BLOCKS), dim3(STATS_THREADS), 0, st,
-                       w.sum, w.cnt, w.pruned, chan_energy, r, cnt, S, T, w.nblk, recovery, f_const);
+                       w.sum, w.cnt, w.pruned, chan_energy, r, cnt, S, T, w.nblk, recovery, f_const, 0);
     return hip_status(hipGetLastError());
 }
 

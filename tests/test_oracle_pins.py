@@ -591,17 +591,41 @@ def test_v_selection_matches_brute_force_with_ties():
     assert n_tied > 500
 
 
+def _bf16_neighbours(x: float):
+    """The bfloat16 values just below and above the finite value x (exact
+    Fractions from the definition: 8 significand bits)."""
+    if x == 0:
+        return Fraction(0), Fraction(0)
+    m, e = math.frexp(abs(x))                     # |x| = m 2^e, 0.5 <= m < 1
+    ulp = Fraction(2) ** (e - 8)
+    lo = (Fraction(abs(x)) // ulp) * ulp
+    hi = lo if lo == Fraction(abs(x)) else lo + ulp
+    return (lo, hi) if x > 0 else (-hi, -lo)
+
+
 def test_v_retained_mean_brute_force():
+    """The recovery of a pruned V entry is the channel's retained mean
+    rounded to the nearest bfloat16 (ties to the even significand): checked
+    against the exact mean with Fractions, not against a rounding routine."""
     rng = np.random.default_rng(32)
-    v = rng.standard_normal((2, 3, 40, 16)).astype(np.float32)
+    v = gen.bf16_bits_to_f32(gen.f32_to_bf16_bits(rng.standard_normal((2, 3, 40, 16)).astype(np.float32)))
     pv = oracle.prune_v(v, 0.7)
+    n_rounded = 0
     for b in range(2):
         for h in range(3):
             for j in range(16):
-                vals = [float(v[b, h, t, j]) for t in range(40) if pv["mask"][b, h, t, j]]
-                want = sum(vals) / len(vals) if vals else 0.0
-                assert abs(float(pv["r"][b, h, j]) - want) <= 1e-6 * max(1.0, abs(want))
+                vals = [Fraction(float(v[b, h, t, j])) for t in range(40) if pv["mask"][b, h, t, j]]
+                want = sum(vals) / len(vals) if vals else Fraction(0)
+                got = Fraction(float(pv["r"][b, h, j]))
+                lo, hi = _bf16_neighbours(float(want))
+                assert got in (lo, hi), (b, h, j)
+                if lo != hi:
+                    n_rounded += 1
+                    d_lo, d_hi = want - lo, hi - want
+                    if d_lo != d_hi:
+                        assert got == (lo if d_lo < d_hi else hi)
                 assert pv["cnt"][b, h, j] == len(vals)
+    assert n_rounded > 50
 
 
 def test_v_lambda0_is_the_dense_v_decode():
