@@ -42,6 +42,10 @@ Readings of points the pages leave open:
     groups, most important first), per-group top-T_i by saliency key.
   * V-channel pruning (section 4.4, "norm-based"): per-token top-T_v of
     |v_tj|, ties to the lower channel, retained-mean recovery of V.
+    Second reading of the same rule, the block mode: the channels fall into
+    D/8 blocks of 8 consecutive channels, and per token the n_b blocks of
+    largest squared L2 norm (fp32, summed in channel order) are kept, ties to
+    the lower block; recovery as in the first reading.
   * Sampled F ("gaussian", "exponential", the other rows of the section 3.3 F
     table): mu and sigma are the mean and population standard deviation of
     the pruned saliency a_j |k_tj| per (batch, KV head); each pruned (t, j)
@@ -556,6 +560,46 @@ def prune_v(v: np.ndarray, lam_v: float) -> dict:
     r, cnt = stats(v, mask, None, F_MEAN_RETAINED)
     return {"T": T, "mask": mask, "words": mask_words(mask), "packed": pack_kept(v, mask), "r": round_bf16(r),
             "cnt": cnt}
+
+
+# Block reading of the same section's norm-based V rule: a token keeps whole
+# blocks of 8 consecutive channels, the n_b = num_kept(D / 8, lambda_v) blocks
+# whose V entries have the largest L2 norm, ties to the lower block. The norm
+# is compared squared, as an fp32 sum of the block's 8 squares (exact for bf16
+# v) added in channel order. Kept blocks are packed in ascending block order;
+# a pruned entry is recovered as in prune_v.
+
+V_BLOCK = 8
+
+
+def value_block_keys(v: np.ndarray) -> np.ndarray:
+    """Squared L2 norm of each block of V_BLOCK consecutive channels, fp32:
+    [..., D] -> [..., D / V_BLOCK], the squares added one at a time in
+    channel order, each sum rounded to fp32."""
+    v = _f32(v)
+    D = v.shape[-1]
+    if D % V_BLOCK:
+        raise ValueError("D must be a multiple of the block size")
+    sq = (v * v).reshape(*v.shape[:-1], D // V_BLOCK, V_BLOCK)
+    acc = np.zeros(sq.shape[:-1], dtype=np.float32)
+    for c in range(V_BLOCK):
+        acc = (acc + sq[..., c]).astype(np.float32)
+    return acc
+
+
+def prune_v_blocks(v: np.ndarray, lam_v: float) -> dict:
+    """Block-mode V pruning of one cache: {"nb", "T", "block_mask", "mask",
+    "packed", "r", "cnt"}. block_mask [..., S, D / 8] holds the kept blocks,
+    mask the same per channel; packed holds each token's kept blocks back to
+    back in ascending block order (T = 8 nb values); r is the retained-mean
+    recovery rounded to bfloat16, as in prune_v."""
+    D = v.shape[-1]
+    nb = num_kept(D // V_BLOCK, lam_v)
+    block_mask = select_top_t(value_block_keys(v), nb)
+    mask = np.repeat(block_mask, V_BLOCK, axis=-1)
+    r, cnt = stats(v, mask, None, F_MEAN_RETAINED)
+    return {"nb": nb, "T": V_BLOCK * nb, "block_mask": block_mask, "mask": mask, "packed": pack_kept(v, mask),
+            "r": round_bf16(r), "cnt": cnt}
 
 
 def decode_attn_kv(q, k_packed, k_mask, r, v_packed, v_mask, rv, scale: float | None = None) -> np.ndarray:

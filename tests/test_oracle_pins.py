@@ -670,6 +670,111 @@ def test_v_constant_channels_closed_form():
     np.testing.assert_allclose(out[0], np.broadcast_to(want, (3, D)), rtol=1e-12, atol=1e-12)
 
 
+# ------------------------------------------------------------------ V pruned in 8-channel blocks
+
+def test_v_block_norm_is_summed_in_channel_order():
+    """Hand case where the fp32 order of the block sum decides the ranking.
+    Block 0 holds squares (2^24, 1, 1): in channel order 2^24 + 1 rounds back
+    to 2^24 (ties to even) and so does + 1, giving 2^24. Block 1 holds
+    (1, 1, 2^24): 1 + 1 = 2, then 2^24 + 2 is exact. Exact sums are equal,
+    so any other order or an exact sum would tie and keep block 0; channel
+    order keeps block 1."""
+    v = np.zeros((1, 1, 1, 16), dtype=np.float32)
+    v[0, 0, 0, 0:3] = (4096.0, 1.0, -1.0)
+    v[0, 0, 0, 8:11] = (1.0, -1.0, 4096.0)
+    keys = oracle.value_block_keys(v)
+    assert keys[0, 0, 0].tolist() == [2.0 ** 24, 2.0 ** 24 + 2]
+    pv = oracle.prune_v_blocks(v, 0.5)
+    assert pv["nb"] == 1 and pv["block_mask"][0, 0, 0].tolist() == [False, True]
+    np.testing.assert_array_equal(pv["packed"][0, 0, 0], v[0, 0, 0, 8:16])
+
+
+def test_v_block_selection_matches_brute_force_with_ties():
+    """Few-valued entries (exact fp32 block sums, many ties): the kept blocks
+    are the first subset, in lexicographic order, of largest summed squared
+    norm; packed rows are the kept blocks back to back in ascending order."""
+    rng = np.random.default_rng(36)
+    D, S = 32, 120
+    v = rng.choice([0.0, 1.0, -1.0, 2.0, -2.0, 0.5], size=(1, 1, S, D))
+    n_tied = 0
+    for nb in range(D // 8 + 1):
+        got = oracle.prune_v_blocks(v, _lam_for(nb, D // 8))
+        assert got["nb"] == nb and got["T"] == 8 * nb
+        for t in range(S):
+            w = [sum(Fraction(float(x)) ** 2 for x in v[0, 0, t, 8 * i:8 * i + 8]) for i in range(D // 8)]
+            want = _brute_reduced(w, nb)
+            assert tuple(np.flatnonzero(got["block_mask"][0, 0, t]).tolist()) == want, (nb, t)
+            assert got["mask"][0, 0, t].tolist() == [(j // 8) in want for j in range(D)]
+            row = [float(x) for i in want for x in v[0, 0, t, 8 * i:8 * i + 8]]
+            assert got["packed"][0, 0, t].tolist() == row
+            n_tied += len(set(w)) < len(w)
+    assert n_tied > 50
+
+
+def test_v_block_retained_mean_brute_force():
+    """Recovery per channel: the mean over the tokens keeping the channel's
+    block, rounded to the nearest bfloat16 (checked with Fractions); every
+    channel of a block has the block's retention count."""
+    rng = np.random.default_rng(37)
+    v = gen.bf16_bits_to_f32(gen.f32_to_bf16_bits(rng.standard_normal((2, 2, 40, 32)).astype(np.float32)))
+    pv = oracle.prune_v_blocks(v, 0.5)
+    n_rounded = 0
+    for b in range(2):
+        for h in range(2):
+            for j in range(32):
+                keep = [t for t in range(40) if pv["block_mask"][b, h, t, j // 8]]
+                vals = [Fraction(float(v[b, h, t, j])) for t in keep]
+                want = sum(vals) / len(vals) if vals else Fraction(0)
+                got = Fraction(float(pv["r"][b, h, j]))
+                lo, hi = _bf16_neighbours(float(want))
+                assert got in (lo, hi), (b, h, j)
+                if lo != hi:
+                    n_rounded += 1
+                    d_lo, d_hi = want - lo, hi - want
+                    if d_lo != d_hi:
+                        assert got == (lo if d_lo < d_hi else hi)
+                assert pv["cnt"][b, h, j] == len(keep)
+    assert n_rounded > 50
+
+
+def test_v_block_extremes():
+    """lambda_v = 0 keeps every block (the dense-V decode, bit for bit);
+    lambda_v = 1 keeps none (every recovery 0, output 0)."""
+    w = WORKLOADS["tiny_s1k"].with_(S=300, n_q=8, n_kv=2)
+    x = gen.numpy_layer(w, seed=38, steps=1)
+    f = {n: gen.bf16_bits_to_f32(a) for n, a in x.items()}
+    pk = oracle.prune(f["q_win"], f["k"], w.n_kv, 0.5)
+    r, _ = oracle.stats(f["k"], pk["mask"], pk["A"])
+    pv = oracle.prune_v_blocks(f["v"], 0.0)
+    assert pv["nb"] == 16 and pv["mask"].all()
+    got = oracle.decode_attn_kv(f["q_dec"][0], pk["packed"], pk["mask"], r, pv["packed"], pv["mask"], pv["r"])
+    np.testing.assert_array_equal(got, oracle.decode_attn(f["q_dec"][0], pk["packed"], pk["mask"], f["v"], r))
+    pv = oracle.prune_v_blocks(f["v"], 1.0)
+    assert pv["nb"] == 0 and not pv["mask"].any() and (pv["r"] == 0).all()
+    out = oracle.decode_attn_kv(f["q_dec"][0], pk["packed"], pk["mask"], r, pv["packed"], pv["mask"], pv["r"])
+    assert (out == 0).all()
+
+
+def test_v_block_constant_rows_closed_form():
+    """v_t = c for every token, with distinct block norms: every token keeps
+    the same n_b blocks (largest sum of c_j^2), which recover exactly; the
+    other blocks are never retained and recover to 0. So out_j = c_j on the
+    kept blocks and 0 elsewhere, for any attention weights."""
+    rng = np.random.default_rng(39)
+    D, S, nb = 32, 64, 3
+    c = rng.permutation(np.arange(1, D + 1)) * rng.choice([-1.0, 1.0], size=D) * 0.25
+    norms = [float(np.sum(c[8 * i:8 * i + 8] ** 2)) for i in range(4)]
+    assert len(set(norms)) == 4
+    top = set(np.argsort(-np.asarray(norms))[:nb].tolist())
+    v = np.broadcast_to(c, (1, 1, S, D)).copy()
+    pv = oracle.prune_v_blocks(v, _lam_for(nb, D // 8))
+    want = np.array([c[j] if j // 8 in top else 0.0 for j in range(D)])
+    q = rng.standard_normal((1, 2, D))
+    k = rng.standard_normal((1, 1, S, D))
+    out = oracle.decode_attn_kv(q, k, np.ones(k.shape, bool), np.zeros((1, 1, D)), pv["packed"], pv["mask"], pv["r"])
+    np.testing.assert_allclose(out[0], np.broadcast_to(want, (2, D)), rtol=1e-12, atol=1e-12)
+
+
 # ------------------------------------------------------------------ SparK-g
 
 def test_grouped_one_group_is_plain_top_t():
