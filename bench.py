@@ -89,9 +89,13 @@ def sampled_alu_ops_per_token(G, T, rec, valu_pv=None):
     return 32 * per_group + G * T + T + (G * 128 if valu_pv else 0)
 
 
-def effective_decode_bytes(w, T, Tv=None):
-    """Packed K and its mask, then dense V (Tv None) or packed V and its mask."""
+def effective_decode_bytes(w, T, Tv=None, nbv=None):
+    """Packed K and its mask, then dense V (Tv and nbv None), packed V and
+    its mask, or V pruned in 8-channel blocks (nbv blocks of 16 bytes and a
+    2-byte block mask)."""
     v_bytes = 2 * w.D if Tv is None else 2 * Tv + 16
+    if nbv is not None:
+        v_bytes = 16 * nbv + 2
     return w.B * w.n_kv * w.S * (2 * T + 16 + v_bytes)
 
 
@@ -104,22 +108,28 @@ def decode_bucket(T: int) -> int:
     return 32 if T <= 32 else 64 if T <= 64 else 96 if T <= 96 else 128
 
 
-def decode_kernel_name(G: int, T: int, smode: int = 0, ragged: bool = False) -> str:
+def decode_kernel_name(G: int, T: int, smode: int = 0, ragged: bool = False, vblocks: bool = False) -> str:
     """The matrix-core decode kernel the library launches, as
-    decode_fast_kernel<G, TB, TFIX, ODD, SMODE, RG>."""
+    decode_fast_kernel<G, TB, TFIX, ODD, SMODE, RG, VB> (VB: V pruned in
+    8-channel blocks)."""
     if ragged:
-        return f"decode_fast_kernel<{G}, 128, 0, true, 0, true>"
+        return f"decode_fast_kernel<{G}, 128, 0, true, 0, true, false>"
+    odd = "true" if T & 1 else "false"
+    if vblocks:
+        if G == 4 and T in (26, 64):
+            return f"decode_fast_kernel<4, {T}, {T}, false, 0, false, true>"
+        return f"decode_fast_kernel<{G}, {decode_bucket(T)}, 0, {odd}, 0, false, true>"
     exact = (G == 4 and T in (26, 38, 48, 64)) or (not smode and (
         (G == 4 and T in (13, 51, 77, 90, 102, 115)) or (G in (1, 2, 8) and T in (26, 64))))
     if exact:
-        return f"decode_fast_kernel<{G}, {T}, {T}, {'true' if T & 1 else 'false'}, {smode}, false>"
+        return f"decode_fast_kernel<{G}, {T}, {T}, {odd}, {smode}, false, false>"
     if smode:
-        return f"decode_kernel<{G}, {smode}, false, false>"
-    return f"decode_fast_kernel<{G}, {decode_bucket(T)}, 0, {'true' if T & 1 else 'false'}, 0, false>"
+        return f"decode_kernel<{G}, {smode}, 0, false>"
+    return f"decode_fast_kernel<{G}, {decode_bucket(T)}, 0, {odd}, 0, false, false>"
 
 
 def run_leg(w, steps, warmup, rotate=True, seed=0, verbose=True, x=None, recovery="mean_retained",
-            rng_seed=SAMPLE_SEED, lam_v=None, ratios=None, top_p=None):
+            rng_seed=SAMPLE_SEED, lam_v=None, ratios=None, top_p=None, lam_vb=None):
     import torch
     from sparse_decode_attention_amd import gen, ops
 
@@ -131,7 +141,8 @@ def run_leg(w, steps, warmup, rotate=True, seed=0, verbose=True, x=None, recover
     if x is None:
         x = gen.torch_layer(w, dev, seed=seed, steps=w.steps)
     Tv = None if lam_v is None else ops.num_kept(w.D, lam_v)
-    dec_bytes = effective_decode_bytes(w, T, Tv)
+    nbv = None if lam_vb is None else ops.num_kept_vblocks(w.D, lam_vb)
+    dec_bytes = effective_decode_bytes(w, T, Tv, nbv)
     R = max(1, int(-(-MALL_DEFEAT_BYTES // dec_bytes))) if rotate else 1
     # replica 0 is written by the prefill every step; replicas 1..R-1 hold copies of it
     reps = []
@@ -143,8 +154,15 @@ def run_leg(w, steps, warmup, rotate=True, seed=0, verbose=True, x=None, recover
             "chan_energy": torch.empty((w.B, w.n_kv, w.D), dtype=torch.float32, device=dev),
             "r": torch.empty((w.B, w.n_kv, w.D), dtype=torch.float32, device=dev),
             "cnt": torch.empty((w.B, w.n_kv, w.D), dtype=torch.int32, device=dev),
-            "v": x["v"] if (i == 0 or Tv is not None) else x["v"].clone(),
+            "v": x["v"] if (i == 0 or Tv is not None or nbv is not None) else x["v"].clone(),
         })
+        if nbv is not None:
+            reps[-1].update({
+                "v_packed": torch.empty((w.B, w.n_kv, w.S, 8 * nbv), dtype=torch.bfloat16, device=dev),
+                "v_bmask": torch.empty((w.B, w.n_kv, ops.vblock_mask_stride(w.S)), dtype=torch.int16, device=dev),
+                "r_v": torch.empty((w.B, w.n_kv, w.D), dtype=torch.float32, device=dev),
+                "cnt_v": torch.empty((w.B, w.n_kv, w.D), dtype=torch.int32, device=dev),
+            })
         if Tv is not None:
             reps[-1].update({
                 "v_packed": torch.empty((w.B, w.n_kv, w.S, Tv), dtype=torch.bfloat16, device=dev),
@@ -169,6 +187,10 @@ def run_leg(w, steps, warmup, rotate=True, seed=0, verbose=True, x=None, recover
             r0 = reps[0]
             ops.prefill_prune_v(x["v"], lam_v, out={"v_packed": r0["v_packed"], "v_mask": r0["v_mask"],
                                                     "r_v": r0["r_v"], "cnt": r0["cnt_v"]})
+        if nbv is not None:
+            r0 = reps[0]
+            ops.prefill_prune_vblocks(x["v"], lam_vb, out={"v_packed": r0["v_packed"], "v_bmask": r0["v_bmask"],
+                                                           "r_v": r0["r_v"], "cnt": r0["cnt_v"]})
 
     def decode_all():
         for s in range(w.steps):
@@ -176,6 +198,9 @@ def run_leg(w, steps, warmup, rotate=True, seed=0, verbose=True, x=None, recover
             if top_p is not None:
                 ops.decode_attn_ragged(x["q_dec"][s], rp["k_packed"].view(w.B, w.n_kv, w.S * w.D), rp["row_off"],
                                        rp["mask"], rp["v"], rp["r"], out=outs[s])
+            elif nbv is not None:
+                ops.decode_attn_kvb(x["q_dec"][s], rp["k_packed"], rp["mask"], rp["r"], rp["v_packed"],
+                                    rp["v_bmask"], rp["r_v"], lam, lam_vb, out=outs[s])
             elif Tv is not None:
                 ops.decode_attn_kv(x["q_dec"][s], rp["k_packed"], rp["mask"], rp["r"], rp["v_packed"], rp["v_mask"],
                                    rp["r_v"], lam, lam_v, out=outs[s])
@@ -189,7 +214,7 @@ def run_leg(w, steps, warmup, rotate=True, seed=0, verbose=True, x=None, recover
     prefill()
     for rp in reps[1:]:
         for n in ("k_packed", "mask", "chan_energy", "r", "cnt") + (("v_packed", "v_mask", "r_v") if Tv else ()) + \
-                (("row_off",) if top_p is not None else ()):
+                (("v_packed", "v_bmask", "r_v") if nbv else ()) + (("row_off",) if top_p is not None else ()):
             rp[n].copy_(reps[0][n])
     if top_p is not None:
         # the bytes a ragged decode reads: kept values, masks and row offsets, dense V
@@ -251,7 +276,7 @@ def run_leg(w, steps, warmup, rotate=True, seed=0, verbose=True, x=None, recover
         "decode_GBps": dec_bytes / (dec_launch_us * 1e-6) / 1e9,
         "prefill_us": med(pre_ms) * 1e3,
         "prefill_GBps": effective_prefill_bytes(w, T) / (med(pre_ms) * 1e-3) / 1e9,
-        "Tv": Tv,
+        "Tv": Tv, "nbv": nbv,
         "step_ms_median": med(step_ms),
         "step_ms_mean": sum(step_ms) / len(step_ms),
         "wall_s": wall,
@@ -796,7 +821,22 @@ def main():
             print(f"bench: K and V pruned, lambda_v={lam_v}, on {w.name}", file=sys.stderr, flush=True)
             lg = run_leg(w, min(args.steps, 5), min(args.warmup, 2), x=main_leg["x"], lam_v=lam_v)
             line["v_pruned"][f"lambda_v={lam_v}"] = {
-                "workload": w.name, "kernel": f"decode_kernel<{w.G}, 0, true>", "T_v": lg["Tv"],
+                "workload": w.name, "kernel": f"decode_kernel<{w.G}, 0, 1, false>", "T_v": lg["Tv"],
+                "decode_us_per_launch": round(lg["decode_us_per_launch"], 3),
+                "bytes_per_launch": lg["decode_bytes_per_step"],
+                "GBps": round(lg["decode_GBps"], 2), "pct_hbm_peak": round(100 * lg["decode_GBps"] / HBM_PEAK_GBS, 2),
+                "x_dense_v_time": round(lg["decode_us_per_launch"] / main_leg["decode_us_per_launch"], 3),
+                "prefill_us_k_and_v": round(lg["prefill_us"], 2), "replicas": lg["replicas"]}
+            del lg
+        torch.cuda.empty_cache()
+        # V pruned in 8-channel blocks: the matrix-core kernel reads packed V
+        # blocks with the dense V requests
+        line["v_block_pruned"] = {}
+        for lam_v in (0.5, 0.8):
+            print(f"bench: K pruned, V pruned in blocks, lambda_v={lam_v}, on {w.name}", file=sys.stderr, flush=True)
+            lg = run_leg(w, min(args.steps, 5), min(args.warmup, 2), x=main_leg["x"], lam_vb=lam_v)
+            line["v_block_pruned"][f"lambda_v={lam_v}"] = {
+                "workload": w.name, "kernel": decode_kernel_name(w.G, lg["T"], vblocks=True), "n_b": lg["nbv"],
                 "decode_us_per_launch": round(lg["decode_us_per_launch"], 3),
                 "bytes_per_launch": lg["decode_bytes_per_step"],
                 "GBps": round(lg["decode_GBps"], 2), "pct_hbm_peak": round(100 * lg["decode_GBps"] / HBM_PEAK_GBS, 2),

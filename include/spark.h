@@ -322,6 +322,68 @@ int spark_decode_attn_kv(const void* q, const void* k_packed, const uint32_t* k_
                          int N_kv, int D, float lambda, float lambda_v, float scale, int splits, float* out, void* ws,
                          size_t ws_bytes, void* stream);
 
+/*
+ * V pruned in blocks of 8 consecutive channels: a second reading of the
+ * norm-based V rule of walkthrough section 4.4, under which a token keeps
+ * whole blocks: the n_b blocks whose entries have the largest L2 norm,
+ * compared squared as an fp32 sum of the block's 8 squares (exact for bf16)
+ * added in channel order, ties to the lower block. A block is the 16-byte
+ * unit in which decode reads V, so the pruned cache is read with the same
+ * requests as a dense one (2 * 8 n_b + 2 bytes per token and KV head
+ * instead of 2 D).
+ */
+#define SPARK_VBLOCK 8
+
+/* n_b = floor((1 - lambda_v) * D / 8 + 0.5) (lambda_v as an IEEE fp32 value)
+ * blocks kept per token; -1 if D is not a positive multiple of 8 or lambda_v
+ * lies outside [0, 1]. */
+int spark_num_kept_vblocks(int D, float lambda_v);
+
+/* Block masks per head for a cache of S (or capacity S_cap) tokens: S
+ * rounded up to a multiple of 64 (0 for S < 1). */
+size_t spark_vblock_mask_stride(int S);
+
+/*
+ * Block-mode V pruning of a V cache.
+ *  v            bf16 [B][N_kv][S][D]
+ *  lambda_v     pruned fraction of V blocks; n_b = spark_num_kept_vblocks(D, lambda_v)
+ * Outputs (caller-allocated, fully overwritten):
+ *  v_packed     bf16 [B][N_kv][S][8 n_b]  each token's kept blocks back to back in
+ *               ascending block order (NULL only if n_b = 0)
+ *  v_bmask      uint16 [B][N_kv][spark_vblock_mask_stride(S)]  per token a 16-bit mask, bit i
+ *               for block i (channels 8i .. 8i + 7), exactly n_b bits set. Stored
+ *               tile-interleaved: token t of a head at entry
+ *               64 floor(t / 64) + 16 (t mod 4) + floor((t mod 64) / 4); the entries
+ *               of the last tile past S are written as 0
+ *  r_v          fp32 [B][N_kv][D]  mean of v_tj over the tokens keeping channel j's block
+ *               (0 if none), rounded to the nearest bfloat16 (ties to even): the value a
+ *               pruned V entry takes
+ *  cnt          int32 [B][N_kv][D]  tokens keeping channel j's block (may be NULL)
+ * Workspace: spark_prefill_workspace_bytes(B, S, N_kv, D).
+ * SPARK_EUNSUPPORTED for D != 128 or B * N_kv > 65535.
+ */
+int spark_prefill_prune_vblocks(const void* v, int B, int S, int N_kv, int D, float lambda_v, void* v_packed,
+                                uint16_t* v_bmask, float* r_v, int32_t* cnt, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * One decode step over a cache whose K channels are pruned and whose V is
+ * pruned in 8-channel blocks (walkthrough sections 3.3 and 4.4): K_hat as in
+ * spark_decode_attn, V_hat = the token's block if kept, else r_v of its
+ * channels, then softmax attention.
+ *  k_packed, k_mask, r          the K cache, as for spark_decode_attn
+ *  v_packed, v_bmask, r_v       the V cache, as written by spark_prefill_prune_vblocks
+ *                               (r_v is read as bfloat16: other values are rounded to
+ *                               the nearest)
+ *  lambda, lambda_v             pruned fractions of K channels and V blocks
+ * Other arguments, the workspace and the return codes as for
+ * spark_decode_attn (SPARK_EINVAL also for a NULL v_bmask or r_v, or a NULL
+ * v_packed with n_b > 0).
+ */
+int spark_decode_attn_kvb(const void* q, const void* k_packed, const uint32_t* k_mask, const float* r,
+                          const void* v_packed, const uint16_t* v_bmask, const float* r_v, int B, int S, int N_q,
+                          int N_kv, int D, float lambda, float lambda_v, float scale, int splits, float* out, void* ws,
+                          size_t ws_bytes, void* stream);
+
 /* Zero the decode completion counters of a workspace (a fill kernel on
  * `stream`; safe to record in a HIP graph). */
 int spark_decode_ws_init(void* ws, size_t ws_bytes, void* stream);

@@ -263,16 +263,19 @@ __device__ __forceinline__ void pv_tile_vpacked(const uint16_t* vst, const uint4
 // spills), so the Philox and sample arithmetic of one wave covers the
 // latency of the other.
 //
-// VP: the V cache is packed too (V channels pruned): its rows and masks are
-// loaded one tile ahead like the keys', staged in LDS, and expanded in P.V.
+// VM 1: the V cache is packed too (V channels pruned): its rows and masks
+// are loaded one tile ahead like the keys', staged in LDS, and expanded in
+// P.V. VM 2: V pruned in 8-channel blocks, read straight into the P.V
+// registers (load_v_tile_blocks), its tile's masks just before.
 //
 // RG: ragged packed rows (SparK-p): per-lane row starts and counts; the score
 // loop runs to the wave's longest row, shorter rows pointing their surplus
 // slots at a zero table entry and reading 0 for their values.
-template <int G, int SMODE, bool VP, bool RG>
+template <int G, int SMODE, int VM, bool RG>
 __global__ void __launch_bounds__(DECODE_THREADS) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 2 : 1)))
 decode_kernel(const DecodeArgs a) {
     constexpr bool SAMPLED = SMODE != 0;
+    constexpr bool VP = VM == 1;
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr int NW = DECODE_THREADS / 64;
     const DecodeLayout& lay = a.lay;
@@ -345,7 +348,14 @@ decode_kernel(const DecodeArgs a) {
         for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
     }
 
-    const uint16_t* vbh = VP ? nullptr : a.v + (size_t)bh * a.S_cap * 128;
+    const uint16_t* vbh = VP ? nullptr
+                             : VM == 2 ? a.v_packed + (size_t)bh * a.S_cap * a.nbv * 8 : a.v + (size_t)bh * a.S_cap * 128;
+    const uint16_t* vmh = VM == 2 ? a.v_bmask + (size_t)bh * vblock_mask_stride(a.S_cap) : nullptr;
+    uint4 rvo = make_uint4(0, 0, 0, 0);     // VM 2: this lane's recovery block in bf16
+    if (VM == 2) {
+        const float4* rq = reinterpret_cast<const float4*>(a.rv + (size_t)bh * 128 + 8 * oct);
+        rvo = vblock_recovery(rq[0], rq[1]);
+    }
     float rvl[8];          // VP: recovery values of this lane's 8 V channels
     if (VP) {
 #pragma unroll
@@ -381,7 +391,13 @@ decode_kernel(const DecodeArgs a) {
 
         // -- V of this tile (dense V), then the next tile's packed keys and mask
         uint4 vr[16];
-        if (!VP) load_v_tile(vbh, t0, nt, tau, oct, vr);
+        if (VM == 0) load_v_tile(vbh, t0, nt, tau, oct, vr);
+        uint32_t vkept = 0u;    // VM 2: which of vr hold kept blocks
+        if (VM == 2) {
+            uint4 vm[2];
+            load_vblock_masks(vmh, t0, tau, vm);
+            vkept = load_v_tile_blocks(vbh, vm, a.nbv, t0, nt, tau, oct, vr);
+        }
         if (tile + NW < ntiles) {
             const int t1 = t0 + NW * DECODE_TILE;
             if (RG) issue_meta_ragged(a, bh, t1, min(DECODE_TILE, blk_end - t1), L, meta);
@@ -495,8 +511,10 @@ decode_kernel(const DecodeArgs a) {
         if (VP)
             pv_tile_vpacked<G>(reinterpret_cast<const uint16_t*>(vstage) + vshift, vmask, a.Tv, ptab, rvl, acc, tau,
                                oct);
-        else
+        else {
+            if (VM == 2) vblock_fill(vr, vkept, rvo);
             pv_tile<G>(vr, ptab, acc, tau);
+        }
         wave_lds_sync();
     }
 
@@ -526,15 +544,15 @@ bool decode_fast_supported(int G, int T, int sampled, size_t packed_elems) {
 // (the ragged rows' loads assume a region of at least 65 dwords: S >= 2)
 bool decode_fast_ragged_supported(int G, int S) { return (G == 1 || G == 2 || G == 4 || G == 8) && S >= 2; }
 
-template <int SMODE, bool VP, bool RG>
+template <int SMODE, int VM, bool RG>
 hipError_t launch_generic(const DecodeArgs& a, int G, dim3 grid, dim3 block, hipStream_t stream) {
     const size_t lds = a.lay.lds_bytes;
     const void* fn = nullptr;
     switch (G) {
-        case 1: fn = reinterpret_cast<const void*>(&decode_kernel<1, SMODE, VP, RG>); break;
-        case 2: fn = reinterpret_cast<const void*>(&decode_kernel<2, SMODE, VP, RG>); break;
-        case 4: fn = reinterpret_cast<const void*>(&decode_kernel<4, SMODE, VP, RG>); break;
-        case 8: fn = reinterpret_cast<const void*>(&decode_kernel<8, SMODE, VP, RG>); break;
+        case 1: fn = reinterpret_cast<const void*>(&decode_kernel<1, SMODE, VM, RG>); break;
+        case 2: fn = reinterpret_cast<const void*>(&decode_kernel<2, SMODE, VM, RG>); break;
+        case 4: fn = reinterpret_cast<const void*>(&decode_kernel<4, SMODE, VM, RG>); break;
+        case 8: fn = reinterpret_cast<const void*>(&decode_kernel<8, SMODE, VM, RG>); break;
         default: return hipErrorInvalidValue;
     }
     if (lds > 65536) {
@@ -543,10 +561,10 @@ hipError_t launch_generic(const DecodeArgs& a, int G, dim3 grid, dim3 block, hip
         if (e != hipSuccess) return e;
     }
     switch (G) {
-        case 1: hipLaunchKernelGGL((decode_kernel<1, SMODE, VP, RG>), grid, block, lds, stream, a); break;
-        case 2: hipLaunchKernelGGL((decode_kernel<2, SMODE, VP, RG>), grid, block, lds, stream, a); break;
-        case 4: hipLaunchKernelGGL((decode_kernel<4, SMODE, VP, RG>), grid, block, lds, stream, a); break;
-        default: hipLaunchKernelGGL((decode_kernel<8, SMODE, VP, RG>), grid, block, lds, stream, a); break;
+        case 1: hipLaunchKernelGGL((decode_kernel<1, SMODE, VM, RG>), grid, block, lds, stream, a); break;
+        case 2: hipLaunchKernelGGL((decode_kernel<2, SMODE, VM, RG>), grid, block, lds, stream, a); break;
+        case 4: hipLaunchKernelGGL((decode_kernel<4, SMODE, VM, RG>), grid, block, lds, stream, a); break;
+        default: hipLaunchKernelGGL((decode_kernel<8, SMODE, VM, RG>), grid, block, lds, stream, a); break;
     }
     return hipGetLastError();
 }
@@ -569,19 +587,29 @@ hipError_t launch_fast_g(const DecodeArgs& a, int G, dim3 grid, hipStream_t stre
 hipError_t launch_decode(const DecodeArgs& a, int G, int BH, hipStream_t stream) {
     const dim3 grid(a.nsplit, BH), block(DECODE_THREADS);
     if (a.row_off) {
-        if (!decode_fast_ragged_supported(G, a.S)) return launch_generic<0, false, true>(a, G, grid, block, stream);
+        if (!decode_fast_ragged_supported(G, a.S)) return launch_generic<0, 0, true>(a, G, grid, block, stream);
         return launch_fast_g(a, G, grid, stream);
     }
-    if (a.v_packed_mode) return launch_generic<0, true, false>(a, G, grid, block, stream);
+    if (a.v_packed_mode == 1) return launch_generic<0, 1, false>(a, G, grid, block, stream);
+    if (a.v_packed_mode == 2) {
+        if (!decode_fast_supported(G, a.T, 0, a.packed_elems)) return launch_generic<0, 2, false>(a, G, grid, block, stream);
+        switch (G) {
+            case 1: return launch_fast_vb_g1(a, grid, stream);
+            case 2: return launch_fast_vb_g2(a, grid, stream);
+            case 4: return launch_fast_vb_g4(a, grid, stream);
+            case 8: return launch_fast_vb_g8(a, grid, stream);
+            default: return hipErrorInvalidValue;
+        }
+    }
     if (decode_fast_supported(G, a.T, a.sampled, a.packed_elems)) {
         if (G == 4 && (a.T == 26 || a.T == 38 || a.T == 48 || a.T == 64)) return launch_fast_fixed(a, grid, stream);
         if (decode_fast_exact(G, a.T, a.sampled)) return launch_fast_fixed2(a, G, grid, stream);
         return launch_fast_g(a, G, grid, stream);
     }
     switch (a.sampled) {
-        case 0: return launch_generic<0, false, false>(a, G, grid, block, stream);
-        case 4: return launch_generic<4, false, false>(a, G, grid, block, stream);
-        case 5: return launch_generic<5, false, false>(a, G, grid, block, stream);
+        case 0: return launch_generic<0, 0, false>(a, G, grid, block, stream);
+        case 4: return launch_generic<4, 0, false>(a, G, grid, block, stream);
+        case 5: return launch_generic<5, 0, false>(a, G, grid, block, stream);
         default: return hipErrorInvalidValue;
     }
 }

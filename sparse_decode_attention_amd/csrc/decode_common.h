@@ -171,6 +171,81 @@ __device__ __forceinline__ void load_v_tile(const uint16_t* vbh, int t0, int nt,
     }
 }
 
+// ---- V pruned in 8-channel blocks. The 8 channels a lane (tau, oct) holds
+// in the P.V layout are one block, so a pruned V cache is read with the same
+// 16-byte requests as a dense one: the block from its slot in the token's
+// packed row when kept, else the block's recovery values.
+
+// The tile's block masks for rows 4i + tau (i = 0..15): entries 16 tau ..
+// 16 tau + 15 of the tile's 64 interleaved masks, 32 contiguous bytes (the 16
+// lanes of one tau read the same two requests). t0 is rounded down to its
+// tile, so that a wave without a tile (t0 clamped to S - 1) reads in bounds.
+__device__ __forceinline__ void load_vblock_masks(const uint16_t* vmh, int t0, int tau, uint4 (&vm)[2]) {
+    const uint4* p = reinterpret_cast<const uint4*>(vmh + (t0 & ~(DECODE_TILE - 1)) + 16 * tau);
+    vm[0] = p[0];
+    vm[1] = p[1];
+}
+
+// This lane's 8 recovery values (channels 8 oct .. 8 oct + 7) as bf16 bits,
+// rounded to nearest even (the prefill writes them already rounded to bf16,
+// which this leaves unchanged). Taken as the two fp32 quads loaded, so that
+// the loads can be issued early and converted where first needed.
+__device__ __forceinline__ uint4 vblock_recovery(const float4& lo, const float4& hi) {
+    const float f[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    uint32_t h[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const uint32_t u = __float_as_uint(f[e]);
+        h[e] = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+    }
+    return make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+}
+
+// V rows of one tile from a block-pruned cache, in load_v_tile's layout: row
+// 4i + tau takes its kept block oct from slot popcount(mask below oct) of the
+// packed row (nb blocks of 16 bytes); bit i of the returned mask says whether
+// it was kept. A lane whose block is pruned (or whose row lies past the
+// tile's end) requests slot 0 of its row, a line the row's kept blocks bring
+// in anyway, so that no request is conditional; vblock_fill later puts the
+// recovery block in its place. The choice is made there, where P.V needs
+// the values, and not here: a select right after the requests would wait
+// for them before the scores. With nb = 0 there is nothing to read. Slots
+// are clamped to the row, so a mask with more than nb bits set reads wrong
+// values but stays in bounds. Row offsets are 32-bit (heads of fewer than
+// 2^24 tokens of at most 256 B).
+__device__ __forceinline__ uint32_t load_v_tile_blocks(const uint16_t* vpbh, const uint4 (&vm)[2], int nb, int t0,
+                                                       int nt, int tau, int oct, uint4 (&vr)[16]) {
+    typedef uint32_t u32x4_nt __attribute__((ext_vector_type(4)));
+    if (nb == 0) return 0u;
+    const unsigned char* vb = reinterpret_cast<const unsigned char*>(vpbh);
+    const uint32_t below = (1u << oct) - 1u;
+    const uint32_t row_bytes = 16u * (uint32_t)nb;
+    uint32_t kbits = 0u;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const uint4& q = vm[i >> 3];
+        const int d = (i >> 1) & 3;
+        const uint32_t w = d == 0 ? q.x : d == 1 ? q.y : d == 2 ? q.z : q.w;
+        const uint32_t m = (i & 1) ? (w >> 16) : (w & 0xFFFFu);
+        const bool kept = 4 * i + tau < nt && ((m >> oct) & 1u) != 0u;
+        const uint32_t row = (uint32_t)(t0 + min(4 * i + tau, nt - 1));
+        const uint32_t slot = kept ? min((uint32_t)__popc(m & below), (uint32_t)nb - 1u) : 0u;
+        const u32x4_nt x =
+            __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt*>(vb + (row * row_bytes + 16u * slot)));
+        vr[i] = make_uint4(x.x, x.y, x.z, x.w);
+        kbits |= kept ? (1u << i) : 0u;
+    }
+    return kbits;
+}
+
+// The recovery block in every slot of vr that load_v_tile_blocks did not
+// fill with a kept block.
+__device__ __forceinline__ void vblock_fill(uint4 (&vr)[16], uint32_t kbits, const uint4& rvo) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        if (((kbits >> i) & 1u) == 0u) vr[i] = rvo;
+}
+
 // ---- sampled recovery F (walkthrough section 3.3, F table, Gaussian and
 // Exponential rows): every pruned (t, j) draws its own sample.
 //

@@ -386,6 +386,16 @@ struct FastCfg {
     static_assert(LDS_NEED <= LDS && 65535u + fast_rtab(G) + 4u <= LDS, "LDS");
 };
 
+// Block-pruned V (VB): the head's block masks, the tile's masks of this
+// lane's rows (requested one tile ahead, before the tile's packed rows) and
+// this lane's recovery block in bf16.
+struct VBlockState {
+    const uint16_t* vmh = nullptr;
+    uint4 vm[2] = {};
+    uint4 rvo = {};
+    uint32_t kbits = 0u;     // which V registers of the tile hold kept blocks
+};
+
 // One 64-token tile. The slot list is built from the tile's mask (before the
 // call when LIST_READY); then the tile's V rows are requested (unless LOAD_V
 // is false: then the prologue did), so they arrive during the score loop and
@@ -401,19 +411,22 @@ struct FastCfg {
 // offsets, their values are replaced by 0). Ragged rows: batches up to the
 // wave's longest row, each slot past its lane's row adding nothing (its
 // list entry is a stale but valid table offset, its value is discarded).
-template <int G, int TB, int TFIX, bool ODD, int SMODE, bool LOAD_V, bool LIST_READY, bool RG>
+template <int G, int TB, int TFIX, bool ODD, int SMODE, bool LOAD_V, bool LIST_READY, bool RG, bool VB>
 __device__ __forceinline__ void fast_tile(const DecodeArgs& a, int T, uint32_t lstride, int bh,
                                           const unsigned char* tab, uint8_t* lst, float* ptab, const uint16_t* vbh,
                                           const float (&cq)[G], int t0, int nt, int nt_next, int L, uint4& mw,
                                           uint32_t (&kr)[FastCfg<G, TB, TFIX, ODD, RG>::KR], uint4 (&vr)[16],
                                           float (&m_run)[G], float (&l_run)[G], f32x4 (&accm)[8], const float* qn,
-                                          RowState& rs, int nt_next2) {
+                                          RowState& rs, int nt_next2, VBlockState& vbs) {
     using C = FastCfg<G, TB, TFIX, ODD, RG>;
     constexpr int NB = C::NB, LOOP = C::LOOP;
     const int tau = L >> 4, oct = L & 15;
     const int t1 = t0 + FAST_NW * DECODE_TILE;
     if constexpr (!LIST_READY) build_list(mw, lst, L, lstride);
-    if constexpr (LOAD_V) load_v_tile(vbh, t0, nt, tau, oct, vr);
+    if constexpr (LOAD_V) {
+        if constexpr (VB) vbs.kbits = load_v_tile_blocks(vbh, vbs.vm, a.nbv, t0, nt, tau, oct, vr);
+        else load_v_tile(vbh, t0, nt, tau, oct, vr);
+    }
     wave_lds_sync();
     const uint16_t* lrow16 = reinterpret_cast<const uint16_t*>(lst) + (uint32_t)L * lstride;
     const unsigned char* rtab = tab + fast_rtab(G);
@@ -505,13 +518,21 @@ __device__ __forceinline__ void fast_tile(const DecodeArgs& a, int T, uint32_t l
             if (nt_next2 > 0)
                 ragged_offsets(a, bh, t1 + FAST_NW * DECODE_TILE + min(L, nt_next2 - 1), rs.o_nx, rs.oe_nx);
         }
-    } else if constexpr (C::XLOAD) {
-        if (nt_next > 0) load_row_fixed<TFIX>(a, bh, t1, nt_next, L, mw, kr);
     } else {
-        if (nt_next > 0) load_row_rt<C::KR, ODD>(a, T, bh, t1, nt_next, L, mw, kr, rs);
+        // block-pruned V: the next tile's block masks go first, so that
+        // waiting for them does not wait for its packed rows
+        if constexpr (VB) {
+            if (nt_next > 0) load_vblock_masks(vbs.vmh, t1, tau, vbs.vm);
+        }
+        if constexpr (C::XLOAD) {
+            if (nt_next > 0) load_row_fixed<TFIX>(a, bh, t1, nt_next, L, mw, kr);
+        } else {
+            if (nt_next > 0) load_row_rt<C::KR, ODD>(a, T, bh, t1, nt_next, L, mw, kr, rs);
+        }
     }
     softmax_tile_mf<G>(s, m_run, l_run, accm, ptab, L);
     wave_lds_sync();
+    if constexpr (VB) vblock_fill(vr, vbs.kbits, vbs.rvo);
     pv_tile_mf<G>(vr, ptab, accm, L);
     wave_lds_sync();
 }
@@ -523,11 +544,12 @@ __device__ __forceinline__ void fast_tile(const DecodeArgs& a, int T, uint32_t l
 //
 // SMODE 4 / 5: the sampled F (Gaussian / Exponential); the r table then holds
 // mu / a_j, and a q' ns table of 128 G fp32 follows the other LDS.
-template <int G, int TB, int TFIX, bool ODD, int SMODE, bool RG>
+template <int G, int TB, int TFIX, bool ODD, int SMODE, bool RG, bool VB>
 __global__ void __launch_bounds__(DECODE_FAST_THREADS)
 decode_fast_kernel(const DecodeArgs a) {
     using C = FastCfg<G, TB, TFIX, ODD, RG>;
     static_assert(SMODE == 0 || TFIX != 0, "sampled F on the exact-T variants only");
+    static_assert(!VB || (SMODE == 0 && !RG), "block-pruned V with fixed rows and the fixed F");
     // statically sized LDS: its base address is a compile-time constant, so
     // table offsets fold into the LDS instructions' offset fields
     __shared__ __align__(16) unsigned char smem[C::LDS + (SMODE ? 128 * G * 4 : 0)];
@@ -568,6 +590,13 @@ decode_fast_kernel(const DecodeArgs a) {
         if (j < 128 * G) qb[i] = a.q[((size_t)b * a.N_q + (size_t)h * G + (j >> 7)) * 128 + (j & 127)];
     }
     float rv = a.r[(size_t)bh * 128 + (tid & 127)];
+    VBlockState vbs{};
+    float4 rvq[2];       // block-pruned V: this lane's recovery block, converted once it has arrived
+    if constexpr (VB) {
+        const float4* rq = reinterpret_cast<const float4*>(a.rv + (size_t)bh * 128 + 8 * (L & 15));
+        rvq[0] = rq[0];
+        rvq[1] = rq[1];
+    }
     float ns = 0.0f;     // sampled F: the noise scale of channel tid & 127 back-solved
     if (SMODE) {
         // r holds (mu, sigma); a pruned key is (mu + ns n) / a_j, a_j = sqrt(A_j)
@@ -596,10 +625,14 @@ decode_fast_kernel(const DecodeArgs a) {
         for (int i = 0; i < KR; ++i) kr[i] = 0u;
     }
     uint4 vr[16];
-    const uint16_t* vbh = a.v + (size_t)bh * a.S_cap * 128;
+    const uint16_t* vbh = VB ? a.v_packed + (size_t)bh * a.S_cap * a.nbv * 8 : a.v + (size_t)bh * a.S_cap * 128;
     // a wave without a tile (or an empty block) reads row min(t0, S-1)
     const int tf0 = min(blk_begin + wave * DECODE_TILE, S - 1);
     const int ntf0 = max(1, min(DECODE_TILE, blk_end - tf0));
+    if constexpr (VB) {
+        vbs.vmh = a.v_bmask + (size_t)bh * vblock_mask_stride(a.S_cap);
+        load_vblock_masks(vbs.vmh, tf0, L >> 4, vbs.vm);
+    }
     if constexpr (RG) load_row_ragged(a, bh, tf0 + min(L, ntf0 - 1), o0, oe0, mw, kr, rs);
     else if constexpr (C::XLOAD) load_row_fixed<TFIX>(a, bh, tf0, ntf0, L, mw, kr);
     else load_row_rt<KR, ODD>(a, T, bh, tf0, ntf0, L, mw, kr, rs);
@@ -623,7 +656,12 @@ decode_fast_kernel(const DecodeArgs a) {
     // waiting for the table, then request the tile's V rows
     build_list(mw, lst, L, lstride);
     __builtin_amdgcn_sched_barrier(0);
-    load_v_tile(vbh, tf0, ntf0, L >> 4, L & 15, vr);
+    if constexpr (VB) {
+        vbs.rvo = vblock_recovery(rvq[0], rvq[1]);
+        vbs.kbits = load_v_tile_blocks(vbh, vbs.vm, a.nbv, tf0, ntf0, L >> 4, L & 15, vr);
+    } else {
+        load_v_tile(vbh, tf0, ntf0, L >> 4, L & 15, vr);
+    }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < QPT; ++i) {
@@ -663,19 +701,19 @@ decode_fast_kernel(const DecodeArgs a) {
     if (wave < ntiles) {
         const int t0 = blk_begin + wave * DECODE_TILE;
         const int t1 = t0 + FAST_NW * DECODE_TILE, t2 = t1 + FAST_NW * DECODE_TILE;
-        fast_tile<G, TB, TFIX, ODD, SMODE, false, true, RG>(
+        fast_tile<G, TB, TFIX, ODD, SMODE, false, true, RG, VB>(
             a, T, lstride, bh, tab, lst, ptab, vbh, cq, t0, min(DECODE_TILE, blk_end - t0),
             t1 < blk_end ? min(DECODE_TILE, blk_end - t1) : 0, L, mw, kr, vr, m_run, l_run, accm, qn, rs,
-            t2 < blk_end ? min(DECODE_TILE, blk_end - t2) : 0);
+            t2 < blk_end ? min(DECODE_TILE, blk_end - t2) : 0, vbs);
     }
     for (int tile = wave + FAST_NW; tile < ntiles; tile += FAST_NW) {
         const int t0 = blk_begin + tile * DECODE_TILE;
         const int t1 = t0 + FAST_NW * DECODE_TILE, t2 = t1 + FAST_NW * DECODE_TILE;   // this wave's next two tiles
         uint4 vt[16];
-        fast_tile<G, TB, TFIX, ODD, SMODE, true, false, RG>(
+        fast_tile<G, TB, TFIX, ODD, SMODE, true, false, RG, VB>(
             a, T, lstride, bh, tab, lst, ptab, vbh, cq, t0, min(DECODE_TILE, blk_end - t0),
             t1 < blk_end ? min(DECODE_TILE, blk_end - t1) : 0, L, mw, kr, vt, m_run, l_run, accm, qn, rs,
-            t2 < blk_end ? min(DECODE_TILE, blk_end - t2) : 0);
+            t2 < blk_end ? min(DECODE_TILE, blk_end - t2) : 0, vbs);
     }
 
     float acc[G][8];
@@ -686,33 +724,39 @@ decode_fast_kernel(const DecodeArgs a) {
 
 // Launch one variant, after checking that the block and split merge scratch
 // (reused from the waves' regions after the tile loop) fits.
-template <int G, int TB, int TFIX, bool ODD, int SMODE, bool RG>
+template <int G, int TB, int TFIX, bool ODD, int SMODE, bool RG, bool VB = false>
 hipError_t launch_fast_variant(const DecodeArgs& a, dim3 grid, hipStream_t stream) {
     using C = FastCfg<G, TB, TFIX, ODD, RG>;
     if (finish_scratch_bytes(G, DECODE_FAST_THREADS, a.nsplit) > (uint32_t)FAST_NW * C::WAVE)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL((decode_fast_kernel<G, TB, TFIX, ODD, SMODE, RG>), grid, dim3(DECODE_FAST_THREADS), 0, stream,
-                       a);
+    hipLaunchKernelGGL((decode_fast_kernel<G, TB, TFIX, ODD, SMODE, RG, VB>), grid, dim3(DECODE_FAST_THREADS), 0,
+                       stream, a);
     return hipGetLastError();
+}
+
+// Runtime-T variants of one group size (VB: block-pruned V).
+template <int G, bool VB>
+hipError_t launch_fast_rt_v(const DecodeArgs& a, dim3 grid, hipStream_t stream) {
+    const bool odd = (a.T & 1) != 0;
+    const int tb = decode_fast_bucket(a.T);
+    switch (tb) {
+        case 32: return odd ? launch_fast_variant<G, 32, 0, true, 0, false, VB>(a, grid, stream)
+                            : launch_fast_variant<G, 32, 0, false, 0, false, VB>(a, grid, stream);
+        case 64: return odd ? launch_fast_variant<G, 64, 0, true, 0, false, VB>(a, grid, stream)
+                            : launch_fast_variant<G, 64, 0, false, 0, false, VB>(a, grid, stream);
+        case 96: return odd ? launch_fast_variant<G, 96, 0, true, 0, false, VB>(a, grid, stream)
+                            : launch_fast_variant<G, 96, 0, false, 0, false, VB>(a, grid, stream);
+        case 128: return odd ? launch_fast_variant<G, 128, 0, true, 0, false, VB>(a, grid, stream)
+                             : launch_fast_variant<G, 128, 0, false, 0, false, VB>(a, grid, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 // Runtime-T and ragged variants of one group size.
 template <int G>
 hipError_t launch_fast_rt(const DecodeArgs& a, dim3 grid, hipStream_t stream) {
     if (a.row_off) return launch_fast_variant<G, 128, 0, true, 0, true>(a, grid, stream);
-    const bool odd = (a.T & 1) != 0;
-    const int tb = decode_fast_bucket(a.T);
-    switch (tb) {
-        case 32: return odd ? launch_fast_variant<G, 32, 0, true, 0, false>(a, grid, stream)
-                            : launch_fast_variant<G, 32, 0, false, 0, false>(a, grid, stream);
-        case 64: return odd ? launch_fast_variant<G, 64, 0, true, 0, false>(a, grid, stream)
-                            : launch_fast_variant<G, 64, 0, false, 0, false>(a, grid, stream);
-        case 96: return odd ? launch_fast_variant<G, 96, 0, true, 0, false>(a, grid, stream)
-                            : launch_fast_variant<G, 96, 0, false, 0, false>(a, grid, stream);
-        case 128: return odd ? launch_fast_variant<G, 128, 0, true, 0, false>(a, grid, stream)
-                             : launch_fast_variant<G, 128, 0, false, 0, false>(a, grid, stream);
-        default: return hipErrorInvalidValue;
-    }
+    return launch_fast_rt_v<G, false>(a, grid, stream);
 }
 
 }  // namespace

@@ -57,6 +57,18 @@ __global__ void stats_reduce_kernel(const double* part_sum, const int32_t* part_
                                     const float* A, float* r, int32_t* cnt, int S, int T, int nblk,
                                     int recovery, float f_const, int round_bf16);
 __global__ void fill_u32_kernel(uint32_t* p, uint32_t value, size_t n);
+// V pruned in 8-channel blocks: 16-bit block masks per token, stored
+// tile-interleaved so that a decode lane reading rows 4i + tau of a 64-token
+// tile finds its 16 masks in 32 contiguous bytes; a head holds its capacity
+// rounded up to whole tiles
+__host__ __device__ constexpr size_t vblock_mask_stride(int S_cap) {
+    return ((size_t)S_cap + DECODE_TILE - 1) / DECODE_TILE * DECODE_TILE;
+}
+__host__ __device__ constexpr uint32_t vblock_mask_index(int t) {
+    return (uint32_t)(t & ~(DECODE_TILE - 1)) + 16u * (uint32_t)(t & 3) + (uint32_t)((t & (DECODE_TILE - 1)) >> 2);
+}
+__global__ void vblock_select_kernel(const uint16_t* v, uint16_t* v_packed, uint16_t* bmask, double* part_sum,
+                                     int32_t* part_cnt, int S, int nb, int nblk, int S_cap);
 
 // LDS layout of the decode kernel (computed on the host for T and G).
 struct DecodeLayout {
@@ -86,6 +98,7 @@ struct DecodeArgs {
     const uint16_t* v_packed; // [B][N_kv][S][Tv] (V channels pruned only)
     const uint32_t* v_mask;   // [B][N_kv][S][4]
     const float* rv;          // [B][N_kv][128] recovery of pruned V entries
+    const uint16_t* v_bmask;  // V pruned in 8-channel blocks: [B][N_kv][vblock_mask_stride(S_cap)] block masks
     const int32_t* row_off;   // ragged packed rows (SparK-p): [B][N_kv][S + 1] offsets within a head's
                               // region of S * 128 elements of `packed`; null otherwise
     float* out;               // [B][N_q][128]
@@ -98,8 +111,10 @@ struct DecodeArgs {
     int S_cap;                // head stride of packed, mask and v in tokens (>= S; S unless a cache grows)
     float qscale;             // softmax scale * log2(e)
     int sampled;              // 0, or the sampled F (4 Gaussian, 5 Exponential)
-    int v_packed_mode;        // 1: V channels pruned (v_packed, v_mask, rv; v unused)
-    int Tv;                   // V channels kept per token (v_packed_mode)
+    int v_packed_mode;        // 1: V channels pruned (v_packed, v_mask, rv; v unused); 2: V pruned in
+                              // 8-channel blocks (v_packed [B][N_kv][S_cap][8 nbv], v_bmask, rv)
+    int Tv;                   // V channels kept per token (v_packed_mode 1)
+    int nbv;                  // V blocks kept per token (v_packed_mode 2)
     uint32_t seed_lo, seed_hi;  // Philox key of the sampled F
     DecodeLayout lay;
 };
@@ -150,6 +165,12 @@ hipError_t launch_fast_g1(const DecodeArgs& a, dim3 grid, hipStream_t stream);
 hipError_t launch_fast_g2(const DecodeArgs& a, dim3 grid, hipStream_t stream);
 hipError_t launch_fast_g4(const DecodeArgs& a, dim3 grid, hipStream_t stream);
 hipError_t launch_fast_g8(const DecodeArgs& a, dim3 grid, hipStream_t stream);
+// block-pruned V: per group size, the runtime-T variants (and at G = 4 the
+// exact T = 64 and 26)
+hipError_t launch_fast_vb_g1(const DecodeArgs& a, dim3 grid, hipStream_t stream);
+hipError_t launch_fast_vb_g2(const DecodeArgs& a, dim3 grid, hipStream_t stream);
+hipError_t launch_fast_vb_g4(const DecodeArgs& a, dim3 grid, hipStream_t stream);
+hipError_t launch_fast_vb_g8(const DecodeArgs& a, dim3 grid, hipStream_t stream);
 DecodeLayout decode_layout(int G, int T, int nsplit, bool sampled, int Tv, bool ragged = false);
 
 }  // namespace spark

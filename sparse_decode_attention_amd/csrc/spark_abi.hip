@@ -109,6 +109,13 @@ int spark_num_kept_grouped(int D, int ngroups, const float* ratios) {
     return T;
 }
 
+int spark_num_kept_vblocks(int D, float lambda_v) {
+    if (D < SPARK_VBLOCK || D % SPARK_VBLOCK) return -1;
+    return kept_or_neg(D / SPARK_VBLOCK, lambda_v);
+}
+
+size_t spark_vblock_mask_stride(int S) { return S < 1 ? 0 : vblock_mask_stride(S); }
+
 const char* spark_strerror(int status) {
     switch (status) {
         case SPARK_OK: return "ok";
@@ -211,6 +218,29 @@ int spark_prefill_prune_v(const void* v, int B, int S, int N_kv, int D, float la
                        static_cast<int32_t*>(nullptr), static_cast<int32_t*>(nullptr), S);
     hipLaunchKernelGGL(stats_reduce_kernel, dim3(BH, STATS_CH_BLOCKS), dim3(STATS_THREADS), 0, st, w.sum, w.cnt, w.pruned,
                        static_cast<const float*>(nullptr), r_v, cnt, S, T, w.nblk, (int)SPARK_F_MEAN_RETAINED, 0.0f, 1);
+    return hip_status(hipGetLastError());
+}
+
+int spark_prefill_prune_vblocks(const void* v, int B, int S, int N_kv, int D, float lambda_v, void* v_packed,
+                                uint16_t* v_bmask, float* r_v, int32_t* cnt, void* ws, size_t ws_bytes, void* stream) {
+    if (B < 1 || S < 1 || N_kv < 1 || D < 1) return SPARK_EINVAL;
+    const int nb = spark_num_kept_vblocks(D, lambda_v);
+    if (nb < 0) return SPARK_EINVAL;
+    if (D != 128) return SPARK_EUNSUPPORTED;
+    if ((size_t)B * N_kv > 65535) return SPARK_EUNSUPPORTED;
+    if (!v || !v_bmask || !r_v || !ws || (nb > 0 && !v_packed)) return SPARK_EINVAL;
+    if (!aligned(v, 16) || !aligned(v_bmask, 16) || !aligned(r_v, 16) || (v_packed && !aligned(v_packed, 16)) ||
+        (cnt && !aligned(cnt, 16)) || !aligned(ws, 256))
+        return SPARK_EALIGN;
+    const PrefillWs w = prefill_layout(ws, B, S, N_kv);
+    if (ws_bytes < w.bytes) return SPARK_ENOSPACE;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int BH = B * N_kv;
+    hipLaunchKernelGGL(vblock_select_kernel, dim3(w.nblk, BH), dim3(256), 0, st, static_cast<const uint16_t*>(v),
+                       static_cast<uint16_t*>(v_packed), v_bmask, w.sum, w.cnt, S, nb, w.nblk, S);
+    hipLaunchKernelGGL(stats_reduce_kernel, dim3(BH, STATS_CH_BLOCKS), dim3(STATS_THREADS), 0, st, w.sum, w.cnt, w.pruned,
+                       static_cast<const float*>(nullptr), r_v, cnt, S, SPARK_VBLOCK * nb, w.nblk,
+                       (int)SPARK_F_MEAN_RETAINED, 0.0f, 1);
     return hip_status(hipGetLastError());
 }
 
@@ -324,9 +354,10 @@ namespace {
 // Packed V (V channels pruned): vp.mask != nullptr.
 struct PackedV {
     const void* packed;
-    const uint32_t* mask;
+    const uint32_t* mask;     // per-entry V pruning
     const float* r;
     float lambda;
+    const uint16_t* bmask;    // V pruned in 8-channel blocks (mask unused)
 };
 
 int decode_call(const void* q, const void* k_packed, const uint32_t* mask, const void* v, const float* r,
@@ -339,7 +370,8 @@ int decode_call(const void* q, const void* k_packed, const uint32_t* mask, const
     if (S_cap >= (1 << 24)) return SPARK_EUNSUPPORTED;
     const int T = kept_or_neg(D, lambda);
     if (T < 0) return SPARK_EINVAL;
-    const int Tv = vp ? kept_or_neg(D, vp->lambda) : -1;
+    const bool vblocks = vp && vp->bmask;
+    const int Tv = vp ? (vblocks ? spark_num_kept_vblocks(D, vp->lambda) : kept_or_neg(D, vp->lambda)) : -1;
     if (vp && Tv < 0) return SPARK_EINVAL;
     if (!(scale == scale)) return SPARK_EINVAL;
     if (int e = check_group(N_q, N_kv)) return e;
@@ -347,23 +379,24 @@ int decode_call(const void* q, const void* k_packed, const uint32_t* mask, const
     const int BH = B * N_kv;
     if ((size_t)BH > (SPARK_DECODE_COUNTER_BYTES / 4)) return SPARK_EUNSUPPORTED;
     if (!q || !mask || !r || !out || !ws || (T > 0 && !k_packed) || (sampled && !A)) return SPARK_EINVAL;
-    if (vp ? (!vp->mask || !vp->r || (Tv > 0 && !vp->packed)) : !v) return SPARK_EINVAL;
+    if (vp ? ((!vp->mask && !vblocks) || !vp->r || (Tv > 0 && !vp->packed)) : !v) return SPARK_EINVAL;
     if (!aligned(q, 16) || !aligned(mask, 16) || (v && !aligned(v, 16)) || !aligned(r, 16) || !aligned(out, 16) ||
         (k_packed && !aligned(k_packed, 16)) || (A && !aligned(A, 16)) || !aligned(ws, 256))
         return SPARK_EALIGN;
-    if (vp && (!aligned(vp->mask, 16) || !aligned(vp->r, 16) || (vp->packed && !aligned(vp->packed, 16))))
+    if (vp && ((vp->mask && !aligned(vp->mask, 16)) || (vblocks && !aligned(vp->bmask, 16)) || !aligned(vp->r, 16) ||
+               (vp->packed && !aligned(vp->packed, 16))))
         return SPARK_EALIGN;
     const int G = N_q / N_kv;
     int nsplit, chunk;
     // the fast kernel (8 waves, one block per CU) aims for 256 blocks; the
     // generic kernel (4 waves) for 512, two per CU, when two fit in LDS
     const bool ragged = row_off != nullptr;
-    const bool generic = vp || (ragged ? !decode_fast_ragged_supported(G, S)
-                                        : !decode_fast_supported(G, T, sampled, (size_t)BH * S_cap * T));
+    const bool generic = (vp && !vblocks) || (ragged ? !decode_fast_ragged_supported(G, S)
+                                                      : !decode_fast_supported(G, T, sampled, (size_t)BH * S_cap * T));
     const int waves = generic ? DECODE_THREADS / 64 : DECODE_FAST_THREADS / 64;
     decode_plan(BH, S, splits, &nsplit, &chunk, generic ? DECODE_GENERIC_BLOCKS : 256, waves);
     if (generic && splits == 0 &&
-        decode_layout(G, T, nsplit, sampled != 0, Tv, ragged).lds_bytes > DECODE_LDS_PER_CU / 2)
+        decode_layout(G, T, nsplit, sampled != 0, vblocks ? -1 : Tv, ragged).lds_bytes > DECODE_LDS_PER_CU / 2)
         decode_plan(BH, S, splits, &nsplit, &chunk, 256, waves);
     if (ws_bytes < decode_ws_bytes(BH, G, nsplit)) return SPARK_ENOSPACE;
 
@@ -375,7 +408,13 @@ int decode_call(const void* q, const void* k_packed, const uint32_t* mask, const
     a.v = static_cast<const uint16_t*>(v);
     a.r = r;
     a.A = A;
-    if (vp) {
+    if (vblocks) {
+        a.v_packed = static_cast<const uint16_t*>(vp->packed);
+        a.v_bmask = vp->bmask;
+        a.rv = vp->r;
+        a.v_packed_mode = 2;
+        a.nbv = Tv;
+    } else if (vp) {
         a.v_packed = static_cast<const uint16_t*>(vp->packed);
         a.v_mask = vp->mask;
         a.rv = vp->r;
@@ -402,7 +441,7 @@ int decode_call(const void* q, const void* k_packed, const uint32_t* mask, const
     a.sampled = sampled;
     a.seed_lo = (uint32_t)seed;
     a.seed_hi = (uint32_t)(seed >> 32);
-    a.lay = decode_layout(G, T, nsplit, sampled != 0, Tv, ragged);
+    a.lay = decode_layout(G, T, nsplit, sampled != 0, vblocks ? -1 : Tv, ragged);
     return hip_status(launch_decode(a, G, BH, static_cast<hipStream_t>(stream)));
 }
 
@@ -438,7 +477,18 @@ int spark_decode_attn_kv(const void* q, const void* k_packed, const uint32_t* k_
                          const void* v_packed, const uint32_t* v_mask, const float* r_v, int B, int S, int N_q,
                          int N_kv, int D, float lambda, float lambda_v, float scale, int splits, float* out, void* ws,
                          size_t ws_bytes, void* stream) {
-    const PackedV vp{v_packed, v_mask, r_v, lambda_v};
+    if (!v_mask) return SPARK_EINVAL;
+    const PackedV vp{v_packed, v_mask, r_v, lambda_v, nullptr};
+    return decode_call(q, k_packed, k_mask, nullptr, r, nullptr, 0, 0, B, S, N_q, N_kv, D, lambda, scale, splits, out,
+                       ws, ws_bytes, stream, &vp);
+}
+
+int spark_decode_attn_kvb(const void* q, const void* k_packed, const uint32_t* k_mask, const float* r,
+                          const void* v_packed, const uint16_t* v_bmask, const float* r_v, int B, int S, int N_q,
+                          int N_kv, int D, float lambda, float lambda_v, float scale, int splits, float* out, void* ws,
+                          size_t ws_bytes, void* stream) {
+    if (!v_bmask) return SPARK_EINVAL;
+    const PackedV vp{v_packed, nullptr, r_v, lambda_v, v_bmask};
     return decode_call(q, k_packed, k_mask, nullptr, r, nullptr, 0, 0, B, S, N_q, N_kv, D, lambda, scale, splits, out,
                        ws, ws_bytes, stream, &vp);
 }

@@ -52,6 +52,11 @@ _SIGS = {
                                          _i, _f, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "spark_decode_attn_kv": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _f, _f, _i,
                                   _vp, _vp, _sz, _vp]),
+    "spark_num_kept_vblocks": (_i, [_i, _f]),
+    "spark_vblock_mask_stride": (_sz, [_i]),
+    "spark_prefill_prune_vblocks": (_i, [_vp, _i, _i, _i, _i, _f, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "spark_decode_attn_kvb": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _f, _f, _i,
+                                   _vp, _vp, _sz, _vp]),
     "spark_decode_ws_init": (_i, [_vp, _sz, _vp]),
     "spark_decode_attn_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _f, _i, _vp, _vp]),
     "spark_read_stream": (_i, [_vp, _sz, _vp, _i, _vp]),
@@ -376,6 +381,65 @@ def decode_attn_kv(q, k_packed, k_mask, r, v_packed, v_mask, r_v, lam: float, la
                                     float(lam), float(lam_v), float(scale), int(splits), _ptr(out), _ptr(ws),
                                     ws.numel(), _stream(dev))
     _check("spark_decode_attn_kv", st)
+    return out
+
+
+VBLOCK = 8
+
+
+def num_kept_vblocks(D: int, lam_v: float) -> int:
+    """spark_num_kept_vblocks: V blocks of 8 channels kept per token."""
+    return lib().spark_num_kept_vblocks(D, float(lam_v))
+
+
+def vblock_mask_stride(S: int) -> int:
+    """spark_vblock_mask_stride: block-mask entries per head (S rounded up to 64)."""
+    return lib().spark_vblock_mask_stride(S)
+
+
+def prefill_prune_vblocks(v: torch.Tensor, lam_v: float, out: dict | None = None) -> dict:
+    """spark_prefill_prune_vblocks: v bf16 [B][N_kv][S][D] -> {"nb",
+    "v_packed" [B][N_kv][S][8 nb], "v_bmask" int16 [B][N_kv][stride]
+    (tile-interleaved), "r_v", "cnt"} (new tensors unless `out` supplies them)."""
+    B, n_kv, S, D = v.shape
+    _need(v, "v", torch.bfloat16)
+    nb = num_kept_vblocks(D, lam_v)
+    if nb < 0:
+        raise SparkError("spark_num_kept_vblocks", EINVAL)
+    dev = v.device
+    o = dict(out or {})
+    o.setdefault("v_packed", torch.empty((B, n_kv, S, VBLOCK * nb), dtype=torch.bfloat16, device=dev))
+    o.setdefault("v_bmask", torch.empty((B, n_kv, vblock_mask_stride(S)), dtype=torch.int16, device=dev))
+    o.setdefault("r_v", torch.empty((B, n_kv, D), dtype=torch.float32, device=dev))
+    o.setdefault("cnt", torch.empty((B, n_kv, D), dtype=torch.int32, device=dev))
+    ws = workspace(dev, "prefill", lib().spark_prefill_workspace_bytes(B, S, n_kv, D))
+    st = lib().spark_prefill_prune_vblocks(_ptr(v), B, S, n_kv, D, float(lam_v),
+                                           _ptr(o["v_packed"]) if nb > 0 else None, _ptr(o["v_bmask"]),
+                                           _ptr(o["r_v"]), _ptr(o["cnt"]), _ptr(ws), ws.numel(), _stream(dev))
+    _check("spark_prefill_prune_vblocks", st)
+    o["nb"] = nb
+    return o
+
+
+def decode_attn_kvb(q, k_packed, k_mask, r, v_packed, v_bmask, r_v, lam: float, lam_v: float, scale: float = 0.0,
+                    splits: int = 0, out=None, ws=None):
+    """spark_decode_attn_kvb: decode over a cache with K channels pruned and V
+    pruned in 8-channel blocks."""
+    B, N_q, D = q.shape
+    n_kv, S = k_mask.shape[1], k_mask.shape[2]
+    _need(q, "q", torch.bfloat16)
+    _need(v_bmask, "v_bmask", torch.int16, (B, n_kv, vblock_mask_stride(S)))
+    _need(r_v, "r_v", torch.float32, (B, n_kv, D))
+    dev = q.device
+    out = torch.empty((B, N_q, D), dtype=torch.float32, device=dev) if out is None else out
+    if ws is None:
+        ws = workspace(dev, "decode", decode_ws_bytes(B, S, N_q, n_kv, D, splits))
+    T, nb = num_kept(D, lam), num_kept_vblocks(D, lam_v)
+    st = lib().spark_decode_attn_kvb(_ptr(q), _ptr(k_packed) if T > 0 else None, _ptr(k_mask), _ptr(r),
+                                     _ptr(v_packed) if nb > 0 else None, _ptr(v_bmask), _ptr(r_v), B, S, N_q, n_kv,
+                                     D, float(lam), float(lam_v), float(scale), int(splits), _ptr(out), _ptr(ws),
+                                     ws.numel(), _stream(dev))
+    _check("spark_decode_attn_kvb", st)
     return out
 
 

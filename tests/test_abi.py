@@ -160,6 +160,55 @@ def test_decode_kv_rejects_bad_arguments():
     assert call() == ops.ENOSPACE
 
 
+def test_num_kept_vblocks_and_mask_stride():
+    assert ops.num_kept_vblocks(128, 0.5) == 8
+    assert ops.num_kept_vblocks(128, 0.8) == 3          # floor(3.2 + 0.5)
+    assert ops.num_kept_vblocks(128, 0.3) == 11         # floor(11.2 + 0.5)
+    assert ops.num_kept_vblocks(128, 0.0) == 16 and ops.num_kept_vblocks(128, 1.0) == 0
+    assert ops.num_kept_vblocks(132, 0.5) == -1         # not a multiple of 8
+    assert ops.num_kept_vblocks(128, 1.5) == -1
+    assert [ops.vblock_mask_stride(S) for S in (0, 1, 64, 65, 4096)] == [0, 64, 64, 128, 4096]
+
+
+def test_prefill_prune_vblocks_rejects_bad_arguments():
+    def call(**kw):
+        a = dict(v=FAKE, B=1, S=64, N_kv=8, D=128, lam=0.5, vp=FAKE, vm=FAKE, rv=FAKE, cnt=None, ws=FAKE, nws=0)
+        a.update(kw)
+        return ops.lib().spark_prefill_prune_vblocks(a["v"], a["B"], a["S"], a["N_kv"], a["D"], a["lam"], a["vp"],
+                                                     a["vm"], a["rv"], a["cnt"], a["ws"], a["nws"], None)
+    assert call(S=0) == ops.EINVAL
+    assert call(lam=1.5) == ops.EINVAL
+    assert call(D=64) == ops.EUNSUPPORTED
+    assert call(D=60) == ops.EINVAL                      # no whole blocks
+    assert call(B=65536, N_kv=1) == ops.EUNSUPPORTED
+    assert call(v=None) == ops.EINVAL
+    assert call(vm=None) == ops.EINVAL
+    assert call(vp=None) == ops.EINVAL                   # n_b > 0 needs the packed store
+    assert call(vp=None, lam=1.0) == ops.ENOSPACE        # n_b = 0 does not
+    assert call(vm=MIS) == ops.EALIGN
+    assert call() == ops.ENOSPACE
+
+
+def test_decode_kvb_rejects_bad_arguments():
+    def call(**kw):
+        a = dict(q=FAKE, kp=FAKE, km=FAKE, r=FAKE, vp=FAKE, vm=FAKE, rv=FAKE, B=1, S=64, N_q=32, N_kv=8, D=128,
+                 lam=0.5, lam_v=0.5, scale=0.0, splits=0, out=FAKE, ws=FAKE, nws=0)
+        a.update(kw)
+        return ops.lib().spark_decode_attn_kvb(a["q"], a["kp"], a["km"], a["r"], a["vp"], a["vm"], a["rv"], a["B"],
+                                               a["S"], a["N_q"], a["N_kv"], a["D"], a["lam"], a["lam_v"], a["scale"],
+                                               a["splits"], a["out"], a["ws"], a["nws"], None)
+    assert call(lam_v=-0.1) == ops.EINVAL
+    assert call(vm=None) == ops.EINVAL
+    assert call(rv=None) == ops.EINVAL
+    assert call(vp=None) == ops.EINVAL
+    assert call(vp=None, lam_v=1.0) == ops.ENOSPACE
+    assert call(vm=MIS) == ops.EALIGN
+    assert call(vp=MIS) == ops.EALIGN
+    assert call(N_q=24) == ops.EUNSUPPORTED
+    assert call(S=1 << 24) == ops.EUNSUPPORTED
+    assert call() == ops.ENOSPACE
+
+
 def test_num_kept_grouped():
     assert ops.num_kept_grouped(128, [0.25, 0.5, 0.75, 1.0]) == 48
     assert ops.num_kept_grouped(128, [0.5]) == ops.num_kept(128, 0.5)
