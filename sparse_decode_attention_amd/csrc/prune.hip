@@ -113,9 +113,22 @@ __device__ __forceinline__ void select_top(uint32_t key0, uint32_t key1, int Tg,
 // fp32 sum over the wave of each lane's x (= w_L + w_{L+64}): the pairwise
 // tree that folds lanes L + 32 onto L, then L + 16, ..., L + 1. Lane L and its
 // partner add the same two values, so every lane ends with the same sum.
+//
+// No step goes through LDS: the 32 and 16 steps are gfx950 permlane swaps,
+// the others DPP moves inside each 16-lane row. After the 8 step, lanes L
+// and L ^ 8 hold the same value, so the row rotation by 4 (lane (L + 4) mod
+// 16) delivers lane L ^ 4's value; the last two steps are quad permutes.
 __device__ __forceinline__ float tree_sum_wave(float x) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) x = __fadd_rn(x, __shfl_xor(x, m, 64));
+    x = xor32_sum(x);
+    x = xor16_sum(x);
+    int v = __float_as_int(x);
+    x = __fadd_rn(x, __int_as_float(__builtin_amdgcn_update_dpp(v, v, 0x128, 0xF, 0xF, false)));   // row_ror:8
+    v = __float_as_int(x);
+    x = __fadd_rn(x, __int_as_float(__builtin_amdgcn_update_dpp(v, v, 0x124, 0xF, 0xF, false)));   // row_ror:4
+    v = __float_as_int(x);
+    x = __fadd_rn(x, __int_as_float(__builtin_amdgcn_update_dpp(v, v, 0x4E, 0xF, 0xF, false)));    // quad_perm 2,3,0,1
+    v = __float_as_int(x);
+    x = __fadd_rn(x, __int_as_float(__builtin_amdgcn_update_dpp(v, v, 0xB1, 0xF, 0xF, false)));    // quad_perm 1,0,3,2
     return x;
 }
 
