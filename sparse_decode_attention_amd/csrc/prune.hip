@@ -390,6 +390,12 @@ topp_scan_kernel(int32_t* __restrict__ blk_cnt, int nblk) {
 // row_off[t + 1] = blk_base + inclusive prefix, and packs each token's kept
 // values (ascending channel) at row_off[t] of the head's region (S * 128
 // elements per head).
+//
+// Wave w packs tokens 16 w .. 16 w + 15 of the block; in round q lane L takes
+// channels 8 (L & 15) .. + 7 of token 16 w + 4 q + (L >> 4), so each request
+// reads four rows whole and all four rounds' rows and masks are requested
+// before any is used. A kept channel goes to the token's offset plus the
+// mask bits below it.
 __global__ void __launch_bounds__(256)
 topp_pack_kernel(const uint16_t* __restrict__ k, const uint32_t* __restrict__ mask, uint16_t* __restrict__ k_packed,
                  int32_t* __restrict__ row_off, const int32_t* __restrict__ blk_base, int S, int nblk) {
@@ -398,8 +404,18 @@ topp_pack_kernel(const uint16_t* __restrict__ k, const uint32_t* __restrict__ ma
     const int t_begin = blk * PRUNE_TOKENS_PER_BLOCK;
     const int nt = min(PRUNE_TOKENS_PER_BLOCK, S - t_begin);
     int32_t* ro = row_off + (size_t)bh * (S + 1);
+    const int wave = threadIdx.x >> 6, L = threadIdx.x & 63;
+    const int cb = L & 15;
+    const uint16_t* kbh = k + (size_t)bh * S * 128;
+    uint4 x[4], mw[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int i = 16 * wave + 4 * q + (L >> 4);
+        const int t = t_begin + min(i, nt - 1);
+        mw[q] = *reinterpret_cast<const uint4*>(mask + ((size_t)bh * S + t) * 4);
+        x[q] = *reinterpret_cast<const uint4*>(kbh + (size_t)t * 128 + 8 * cb);
+    }
     if (threadIdx.x < 64) {
-        const int L = threadIdx.x;
         const int n = L < nt ? ro[t_begin + L + 1] : 0;
         int incl = n;
         for (int o = 1; o < 64; o <<= 1) {
@@ -413,18 +429,28 @@ topp_pack_kernel(const uint16_t* __restrict__ k, const uint32_t* __restrict__ ma
     __syncthreads();
     if (threadIdx.x < nt) ro[t_begin + threadIdx.x + 1] = off[threadIdx.x + 1];
     if (blk == 0 && threadIdx.x == 0) ro[0] = 0;
-    const int wave = threadIdx.x >> 6, L = threadIdx.x & 63;
-    const uint16_t* kbh = k + (size_t)bh * S * 128;
     uint16_t* pbh = k_packed + (size_t)bh * S * 128;
-    for (int i = wave; i < nt; i += 4) {
-        const int t = t_begin + i;
-        const uint4 mw = *reinterpret_cast<const uint4*>(mask + ((size_t)bh * S + t) * 4);
-        const uint64_t m0 = ((uint64_t)mw.y << 32) | mw.x, m1 = ((uint64_t)mw.w << 32) | mw.z;
-        const bool kept0 = (m0 >> L) & 1, kept1 = (m1 >> L) & 1;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int i = 16 * wave + 4 * q + (L >> 4);
+        if (i >= nt) continue;
+        const uint32_t words[4] = {mw[q].x, mw[q].y, mw[q].z, mw[q].w};
+        const int wi = cb >> 2, sh = 8 * (cb & 3);
+        int below = __popc(words[wi] & ((1u << sh) - 1u));
+#pragma unroll
+        for (int w = 0; w < 3; ++w) below += w < wi ? __popc(words[w]) : 0;
+        const uint32_t byte = (words[wi] >> sh) & 0xFFu;
         // ranks are bounded by the row's count (the mask's popcount), so the
         // writes stay in [row_off[t], row_off[t + 1])
-        if (kept0) pbh[off[i] + (int)mbcnt(m0)] = kbh[(size_t)t * 128 + L];
-        if (kept1) pbh[off[i] + __popcll(m0) + (int)mbcnt(m1)] = kbh[(size_t)t * 128 + 64 + L];
+        const int base = off[i] + below;
+        const uint32_t e2[4] = {x[q].x, x[q].y, x[q].z, x[q].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            if ((byte >> e) & 1u) {
+                const uint16_t val = (uint16_t)((e & 1) ? (e2[e >> 1] >> 16) : (e2[e >> 1] & 0xFFFFu));
+                pbh[base + __popc(byte & ((1u << e) - 1u))] = val;
+            }
+        }
     }
 }
 
