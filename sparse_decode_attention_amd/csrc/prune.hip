@@ -182,6 +182,56 @@ __device__ __forceinline__ void select_top_p(uint32_t key0, uint32_t key1, float
 // threshold fraction top_p: nothing is packed here (the rows are ragged); the
 // token counts go to tok_cnt[bh * (S + 1) + t] (row_off + 1: its count slots)
 // and the block totals to blk_cnt[bh][blk].
+// SparK-g with groups of SZ = 16 or 32 channels: a key's rank in its group
+// is the number of members with a larger key, so the member is kept when its
+// rank is below the group's T_i. One pass over the group's keys in LDS (the
+// lanes of a group read the same words) replaces a bit search per group.
+// Equal keys get the same rank, so a tie that straddles T_i keeps too many;
+// the group's kept count shows it, and only then is that group decided again
+// by the exact bit search (ties to the lower channel).
+template <int SZ>
+__device__ __forceinline__ void group_ranks(const uint32_t* row, uint32_t key0, uint32_t key1, int base0, int base1,
+                                            int& r0, int& r1) {
+    r0 = 0;
+    r1 = 0;
+    const uint4* q0 = reinterpret_cast<const uint4*>(row + base0);
+    const uint4* q1 = reinterpret_cast<const uint4*>(row + base1);
+#pragma unroll
+    for (int j = 0; j < SZ / 4; ++j) {
+        const uint4 a = q0[j], b = q1[j];
+        r0 += (a.x > key0) + (a.y > key0) + (a.z > key0) + (a.w > key0);
+        r1 += (b.x > key1) + (b.y > key1) + (b.z > key1) + (b.w > key1);
+    }
+}
+
+__device__ __forceinline__ void select_grouped_rank(uint32_t key0, uint32_t key1, int g0, int g1, int slot0,
+                                                    int slot1, int T0, int T1, const GroupSpec& grp, uint32_t* row,
+                                                    bool& kept0, bool& kept1) {
+    row[slot0] = key0;
+    row[slot1] = key1;
+    wave_lds_sync();
+    int r0, r1;
+    if (grp.size == 32) group_ranks<32>(row, key0, key1, g0 * 32, g1 * 32, r0, r1);
+    else group_ranks<16>(row, key0, key1, g0 * 16, g1 * 16, r0, r1);
+    wave_lds_sync();      // every lane has read the row before the next token's keys overwrite it
+    kept0 = r0 < T0;
+    kept1 = r1 < T1;
+    for (int i = 0; i < grp.n; ++i) {       // uniform
+        const int Ti = grp.T[i];
+        if (Ti <= 0 || Ti >= grp.size) continue;
+        const bool in0 = g0 == i, in1 = g1 == i;
+        const int n = __popcll(ballot(kept0 && in0)) + __popcll(ballot(kept1 && in1));
+        if (n != Ti) {
+            // members' keys + 1 (order and ties unchanged; keys are below
+            // 2^31), others 0: the plain search counts members only
+            bool k0, k1;
+            select_top(in0 ? key0 + 1u : 0u, in1 ? key1 + 1u : 0u, Ti, k0, k1);
+            if (in0) kept0 = k0;
+            if (in1) kept1 = k1;
+        }
+    }
+}
+
 template <int SEL>
 __global__ void __launch_bounds__(256)
 select_pack_kernel(const uint16_t* __restrict__ k, const float* __restrict__ A,
@@ -210,6 +260,25 @@ select_pack_kernel(const uint16_t* __restrict__ k, const float* __restrict__ A,
     const double a0 = sqrt((double)A0), a1 = sqrt((double)A1);
     const int g0 = GROUPED ? gid[(size_t)bh * 128 + L] : 0;
     const int g1 = GROUPED ? gid[(size_t)bh * 128 + 64 + L] : 0;
+    // SparK-g with groups of 16 or 32 channels: each token's keys go to a
+    // per-wave LDS row, group i's members at [i size, (i + 1) size) in
+    // channel order; slot, group base and the group's kept count per lane
+    __shared__ __align__(16) uint32_t gkeys[GROUPED ? 4 : 1][GROUPED ? 128 : 1];
+    const bool rank_path = GROUPED && (grp.size == 16 || grp.size == 32);
+    int slot0 = 0, slot1 = 0, T0 = 0, T1 = 0;
+    if (rank_path) {
+        for (int i = 0; i < grp.n; ++i) {       // uniform
+            const uint64_t m0 = ballot(g0 == i), m1 = ballot(g1 == i);
+            if (g0 == i) {
+                slot0 = i * grp.size + (int)mbcnt(m0);
+                T0 = grp.T[i];
+            }
+            if (g1 == i) {
+                slot1 = i * grp.size + __popcll(m0) + (int)mbcnt(m1);
+                T1 = grp.T[i];
+            }
+        }
+    }
 
     double sum0 = 0.0, sum1 = 0.0, pruned = 0.0, pruned2 = 0.0;
     int cnt0 = 0, cnt1 = 0;
@@ -246,6 +315,8 @@ select_pack_kernel(const uint16_t* __restrict__ k, const float* __restrict__ A,
                 } else if (T > 0) {
                     select_top(key0, key1, T, kept0, kept1);
                 }
+            } else if (rank_path) {
+                select_grouped_rank(key0, key1, g0, g1, slot0, slot1, T0, T1, grp, gkeys[wave], kept0, kept1);
             } else {
                 for (int i = 0; i < grp.n; ++i) {
                     const bool in0 = g0 == i, in1 = g1 == i;
