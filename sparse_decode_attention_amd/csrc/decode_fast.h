@@ -19,11 +19,13 @@
 //             slot loop unrolled for TB with a wave-uniform exit at T;
 //   ODD       odd T: rows start mid-dword on every other token and are
 //             realigned with a funnel shift.
-//   Rows whose length is a multiple of 8 (exact T) are read with exact
-//   16-byte loads; every other lane reads its row as 16-byte loads from the
-//   dword holding its first element;
+//   Rows of an even exact T are read exactly (16-byte loads when T is a
+//   multiple of 8, single dwords otherwise); every other row as 16-byte
+//   loads from the dword holding its first element;
 //   RG        ragged rows (SparK-p): per-lane row offsets and lengths;
-//   SMODE     sampled recovery F (4 Gaussian, 5 Exponential), TFIX only.
+//   SMODE     sampled recovery F (4 Gaussian, 5 Exponential), TFIX only;
+//   VB        V pruned in 8-channel blocks: each lane's 16-byte V block read
+//             from its slot in the packed V row, or the recovery block.
 #pragma once
 #include "decode_common.h"
 
