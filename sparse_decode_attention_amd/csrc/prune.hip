@@ -78,36 +78,106 @@ chan_energy_kernel(const uint16_t* __restrict__ q_win, float* __restrict__ A,
 // >= the candidate: those T are the answer and no tie straddles it.
 // Otherwise theta is exact and the channels equal to theta are taken in
 // ascending channel order until T are kept.
-// The Tg keys at or above the Tg-th largest of the wave's 128 keys (two per
-// lane), ties to the lower channel. (SparK-g runs it per group on keys + 1 of
-// the group's members and 0 elsewhere.) v, n and the loop state are
-// wave-uniform (scalar registers); each unrolled step costs two compares, two
-// scalar popcounts and a scalar select, and the search leaves at the first
-// count of exactly Tg.
+
+// One step of the bit search below: candidate c = v | BIT, n = #keys >= c
+// (two compares into separate scalar masks, two scalar popcounts), v = c when
+// n >= Tg, and a jump to the exit when n == Tg. The exit test runs on the
+// vector ALU (every lane compares the scalar n with Tg; the branch reads VCC):
+// the search is bound by scalar issue (one scalar instruction per SIMD every
+// four cycles), and this leaves six scalar and three vector instructions a
+// step.
+#define SPARK_SEL_STEP(BIT)                          \
+    "s_or_b32 %[c], %[v], " BIT "\n\t"              \
+    "v_cmp_le_u32_e64 %[m0], %[c], %[k0]\n\t"       \
+    "v_cmp_le_u32_e64 %[m1], %[c], %[k1]\n\t"       \
+    "s_bcnt1_i32_b64 %[x], %[m0]\n\t"               \
+    "s_bcnt1_i32_b64 %[y], %[m1]\n\t"               \
+    "s_add_u32 %[n], %[x], %[y]\n\t"                \
+    "s_cmp_lt_u32 %[n], %[T]\n\t"                   \
+    "s_cselect_b32 %[v], %[v], %[c]\n\t"            \
+    "v_cmp_eq_u32 vcc, %[n], %[Tv]\n\t"             \
+    "s_cbranch_vccnz 1f\n\t"
+
+// Threshold of the Tg largest of the wave's 128 keys (two per lane; every
+// lane of the wave active): v, and whether exactly Tg keys are >= v. v, n and
+// the step state are wave-uniform (scalar registers); the 31 steps are
+// unrolled, and the search leaves at the first count of exactly Tg. A search
+// that never meets that count leaves v at 0 or at an accepted candidate, and
+// more than Tg keys are >= v in both cases (0 < Tg < 128).
+__device__ __forceinline__ bool search_threshold(uint32_t key0, uint32_t key1, int Tg, uint32_t& v) {
+    uint32_t c, x, y, n, ex;
+    uint64_t m0, m1;
+    const int Tv = Tg;
+    asm volatile(
+        "s_mov_b32 %[v], 0\n\t"
+        SPARK_SEL_STEP("0x40000000") SPARK_SEL_STEP("0x20000000") SPARK_SEL_STEP("0x10000000")
+        SPARK_SEL_STEP("0x8000000") SPARK_SEL_STEP("0x4000000") SPARK_SEL_STEP("0x2000000")
+        SPARK_SEL_STEP("0x1000000") SPARK_SEL_STEP("0x800000") SPARK_SEL_STEP("0x400000")
+        SPARK_SEL_STEP("0x200000") SPARK_SEL_STEP("0x100000") SPARK_SEL_STEP("0x80000")
+        SPARK_SEL_STEP("0x40000") SPARK_SEL_STEP("0x20000") SPARK_SEL_STEP("0x10000")
+        SPARK_SEL_STEP("0x8000") SPARK_SEL_STEP("0x4000") SPARK_SEL_STEP("0x2000")
+        SPARK_SEL_STEP("0x1000") SPARK_SEL_STEP("0x800") SPARK_SEL_STEP("0x400")
+        SPARK_SEL_STEP("0x200") SPARK_SEL_STEP("0x100") SPARK_SEL_STEP("0x80")
+        SPARK_SEL_STEP("0x40") SPARK_SEL_STEP("0x20") SPARK_SEL_STEP("0x10")
+        SPARK_SEL_STEP("0x8") SPARK_SEL_STEP("0x4") SPARK_SEL_STEP("0x2")
+        SPARK_SEL_STEP("0x1")
+        "s_mov_b32 %[ex], 0\n\t"
+        "s_branch 2f\n"
+        "1:\n\t"
+        "s_mov_b32 %[ex], 1\n"
+        "2:"
+        : [v] "=&s"(v), [c] "=&s"(c), [x] "=&s"(x), [y] "=&s"(y), [n] "=&s"(n), [ex] "=&s"(ex), [m0] "=&s"(m0),
+          [m1] "=&s"(m1)
+        : [k0] "v"(key0), [k1] "v"(key1), [T] "s"(Tg), [Tv] "v"(Tv)
+        : "vcc", "scc");
+    return ex != 0;
+}
+
+// More than Tg keys are >= v: all keys > v, then the keys equal to v in
+// ascending channel order until Tg are kept.
+__device__ __forceinline__ void take_ties(uint32_t key0, uint32_t key1, int Tg, uint32_t v, bool& kept0, bool& kept1) {
+    const bool gt0 = key0 > v, gt1 = key1 > v;
+    const int need = Tg - (__popcll(ballot(gt0)) + __popcll(ballot(gt1)));
+    const uint64_t eq0 = ballot(key0 == v), eq1 = ballot(key1 == v);
+    const int r0 = (int)mbcnt(eq0);
+    const int r1 = __popcll(eq0) + (int)mbcnt(eq1);
+    kept0 = gt0 || (key0 == v && r0 < need);
+    kept1 = gt1 || (key1 == v && r1 < need);
+}
+
+// The Tg keys at or above the Tg-th largest of the wave's 128 keys, ties to
+// the lower channel, as per-lane flags. (SparK-g runs it per group on keys + 1
+// of the group's members and 0 elsewhere.)
 __device__ __forceinline__ void select_top(uint32_t key0, uint32_t key1, int Tg, bool& kept0, bool& kept1) {
-    uint32_t v = 0;
-#pragma unroll
-    for (int bit = 30; bit >= 0; --bit) {
-        const uint32_t c = __builtin_amdgcn_readfirstlane(v | (1u << bit));
-        const int n = __popcll(ballot(key0 >= c)) + __popcll(ballot(key1 >= c));
-        v = n >= Tg ? c : v;
-        if (n == Tg) break;
-    }
-    // whether exactly Tg keys are >= v, counted once here rather than
-    // carried through every step of the search
-    const bool exact = __popcll(ballot(key0 >= v)) + __popcll(ballot(key1 >= v)) == Tg;
-    if (exact) {
+    uint32_t v;
+    if (search_threshold(key0, key1, Tg, v)) {
         kept0 = key0 >= v;
         kept1 = key1 >= v;
     } else {
-        const bool gt0 = key0 > v, gt1 = key1 > v;
-        const int need = Tg - (__popcll(ballot(gt0)) + __popcll(ballot(gt1)));
-        const uint64_t eq0 = ballot(key0 == v), eq1 = ballot(key1 == v);
-        const int r0 = (int)mbcnt(eq0);
-        const int r1 = __popcll(eq0) + (int)mbcnt(eq1);
-        kept0 = gt0 || (key0 == v && r0 < need);
-        kept1 = gt1 || (key1 == v && r1 < need);
+        take_ties(key0, key1, Tg, v, kept0, kept1);
     }
+}
+
+// The same selection as the two 64-lane masks (channels 0-63, 64-127).
+__device__ __forceinline__ void select_top_masks(uint32_t key0, uint32_t key1, int Tg, uint64_t& m0, uint64_t& m1) {
+    uint32_t v;
+    if (search_threshold(key0, key1, Tg, v)) {
+        m0 = ballot(key0 >= v);
+        m1 = ballot(key1 >= v);
+    } else {
+        bool k0, k1;
+        take_ties(key0, key1, Tg, v, k0, k1);
+        m0 = ballot(k0);
+        m1 = ballot(k1);
+    }
+}
+
+// Lane L's bit of the wave mask m picks b (set) or a (clear): one vector
+// select with the mask as its condition operand.
+__device__ __forceinline__ uint32_t lane_pick(uint64_t m, uint32_t a, uint32_t b) {
+    uint32_t r;
+    asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "s"(m));
+    return r;
 }
 
 // fp32 sum over the wave of each lane's x (= w_L + w_{L+64}): the pairwise
@@ -232,6 +302,142 @@ __device__ __forceinline__ void select_grouped_rank(uint32_t key0, uint32_t key1
     }
 }
 
+// Per-wave state of the token loop of select_pack_kernel.
+struct SelectLoop {
+    const uint16_t* kbh;        // this (b, kv head)'s K rows
+    uint16_t* st;               // the wave's 4-row LDS stage
+    uint32_t* gkeys;            // the wave's SparK-g LDS row
+    int L, t_first, t_end, T;
+    float A0, A1;
+    double a0, a1;
+    int g0, g1, slot0, slot1, T0, T1;
+    bool rank_path, squares;
+    float top_p;
+    int32_t* tok_row;           // SparK-p: row_off + 1 of this (b, kv head)
+    __amdgpu_buffer_rsrc_t mrsrc, prsrc;
+    int t_begin;
+};
+
+// Accumulators of one wave: kept values (REC 0), kept counts, pruned |w|
+// and |w|^2 (REC 2), channels kept (SparK-p).
+struct SelectAcc {
+    double sum0 = 0.0, sum1 = 0.0, pruned = 0.0, pruned2 = 0.0;
+    int cnt0 = 0, cnt1 = 0, kept_tokens = 0;
+};
+
+// The token loop. REC: 0 sums of the kept values (mean-retained recovery);
+// 1 counts only; 2 counts and the pruned saliency sums (squares too when
+// squares is set). SEARCH (SEL 0): 0 < T < 128; otherwise every channel is
+// kept or none.
+template <int SEL, int REC, bool SEARCH>
+__device__ __forceinline__ void select_tokens(const SelectLoop& p, const GroupSpec& grp, SelectAcc& acc) {
+    constexpr uint32_t kDropped = 0x7FFFFFFFu;    // a buffer offset past every resource's end
+    const int L = p.L;
+    // the next 4 rows are loaded while the current 4 are searched
+    uint4 xn = make_uint4(0, 0, 0, 0);
+    if (p.t_first + (L >> 4) < p.t_end)
+        xn = *reinterpret_cast<const uint4*>(p.kbh + (size_t)(p.t_first + (L >> 4)) * 128 + (L & 15) * 8);
+    for (int t4 = p.t_first; t4 < p.t_end; t4 += 16) {
+        const int n4 = min(4, p.t_end - t4);
+        reinterpret_cast<uint4*>(p.st)[L] = xn;
+        {
+            const int tn = t4 + 16 + (L >> 4);
+            xn = make_uint4(0, 0, 0, 0);
+            if (tn < p.t_end) xn = *reinterpret_cast<const uint4*>(p.kbh + (size_t)tn * 128 + (L & 15) * 8);
+        }
+        wave_lds_sync();
+        // one token: i-th row of the stage
+        auto token = [&](const int i) {
+            const int t = t4 + i;
+            const uint16_t kb0 = p.st[i * 128 + L], kb1 = p.st[i * 128 + 64 + L];
+            const float k0 = bf16_to_f32(kb0), k1 = bf16_to_f32(kb1);
+            const uint32_t key0 = __float_as_uint(__fmul_rn(p.A0, __fmul_rn(k0, k0)));
+            const uint32_t key1 = __float_as_uint(__fmul_rn(p.A1, __fmul_rn(k1, k1)));
+            uint64_t m0, m1;
+            if (SEL == 0) {
+                if (SEARCH) {
+                    select_top_masks(key0, key1, p.T, m0, m1);
+                } else {
+                    m0 = m1 = ballot(p.T >= 128);      // every channel or none
+                }
+            } else {
+                bool kept0 = false, kept1 = false;
+                if (SEL == 2) {
+                    select_top_p(key0, key1, p.top_p, kept0, kept1);
+                } else if (p.rank_path) {
+                    select_grouped_rank(key0, key1, p.g0, p.g1, p.slot0, p.slot1, p.T0, p.T1, grp, p.gkeys, kept0,
+                                        kept1);
+                } else {
+                    for (int g = 0; g < grp.n; ++g) {
+                        const bool in0 = p.g0 == g, in1 = p.g1 == g;
+                        const int Ti = grp.T[g];
+                        if (Ti >= grp.size) {
+                            kept0 |= in0;
+                            kept1 |= in1;
+                        } else if (Ti > 0) {
+                            // members' keys + 1 (order and ties unchanged; keys
+                            // are below 2^31), others 0: every candidate and the
+                            // found threshold are >= 1, so the plain search over
+                            // all 128 counts members only, with no membership
+                            // masks
+                            bool k0s, k1s;
+                            select_top(in0 ? key0 + 1u : 0u, in1 ? key1 + 1u : 0u, Ti, k0s, k1s);
+                            kept0 |= k0s;
+                            kept1 |= k1s;
+                        }
+                    }
+                }
+                m0 = ballot(kept0);
+                m1 = ballot(kept1);
+            }
+            // stores through buffer resources of this block's rows: a lane
+            // that must not store gives an offset past the resource's end,
+            // which the hardware drops, so no lane mask is switched
+            {
+                typedef uint32_t u32x4_b __attribute__((ext_vector_type(4)));
+                const u32x4_b mw = {(uint32_t)m0, (uint32_t)(m0 >> 32), (uint32_t)m1, (uint32_t)(m1 >> 32)};
+                __builtin_amdgcn_raw_buffer_store_b128(mw, p.mrsrc, L == 0 ? 16 * (t - p.t_begin) : (int)kDropped,
+                                                       0, 0);
+            }
+            if (SEL == 2) {
+                const int n = __popcll(m0) + __popcll(m1);
+                if (L == 0) p.tok_row[t] = n;
+                acc.kept_tokens += n;
+            } else if (p.T > 0) {
+                const int row = (t - p.t_begin) * p.T;
+                const uint32_t o0 = 2u * (uint32_t)(row + (int)mbcnt(m0));
+                const uint32_t o1 = 2u * (uint32_t)(row + __popcll(m0) + (int)mbcnt(m1));
+                __builtin_amdgcn_raw_buffer_store_b16(kb0, p.prsrc, (int)lane_pick(m0, kDropped, o0), 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b16(kb1, p.prsrc, (int)lane_pick(m1, kDropped, o1), 0, 0);
+            }
+            acc.cnt0 += (int)lane_pick(m0, 0u, 1u);
+            acc.cnt1 += (int)lane_pick(m1, 0u, 1u);
+            if (REC == 0) {
+                // a pruned entry adds +0, which leaves a sum that starts at +0
+                // unchanged bit for bit (it is never -0)
+                acc.sum0 += (double)__uint_as_float(lane_pick(m0, 0u, __float_as_uint(k0)));
+                acc.sum1 += (double)__uint_as_float(lane_pick(m1, 0u, __float_as_uint(k1)));
+            } else if (REC == 2) {
+                const double p0 = p.a0 * (double)fabsf(k0), p1 = p.a1 * (double)fabsf(k1);
+                const uint64_t b0 = __double_as_longlong(p0), b1 = __double_as_longlong(p1);
+                const double w0 = __longlong_as_double((long long)(((uint64_t)lane_pick(m0, (uint32_t)(b0 >> 32), 0u) << 32) |
+                                                                   lane_pick(m0, (uint32_t)b0, 0u)));
+                const double w1 = __longlong_as_double((long long)(((uint64_t)lane_pick(m1, (uint32_t)(b1 >> 32), 0u) << 32) |
+                                                                   lane_pick(m1, (uint32_t)b1, 0u)));
+                acc.pruned += w0 + w1;
+                if (p.squares) acc.pruned2 += w0 * w0 + w1 * w1;
+            }
+        };
+        if (SEL == 0 && n4 == 4) {      // full groups of the plain select unrolled
+#pragma unroll
+            for (int i = 0; i < 4; ++i) token(i);
+        } else {
+            for (int i = 0; i < n4; ++i) token(i);
+        }
+        wave_lds_sync();
+    }
+}
+
 template <int SEL>
 __global__ void __launch_bounds__(256)
 select_pack_kernel(const uint16_t* __restrict__ k, const float* __restrict__ A,
@@ -249,122 +455,72 @@ select_pack_kernel(const uint16_t* __restrict__ k, const float* __restrict__ A,
 
     const int bh = blockIdx.y;
     const int blk = blockIdx.x;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);     // scalar token loop
     const int L = threadIdx.x & 63;
     const int t_begin = blk * PRUNE_TOKENS_PER_BLOCK;
     const int t_end = min(S, t_begin + PRUNE_TOKENS_PER_BLOCK);
 
+    SelectLoop p;
+    p.L = L;
+    p.t_begin = t_begin;
+    p.t_first = t_begin + 4 * wave;        // wave w takes tokens t_begin + 4 (w + 4 i) .. + 3
+    p.t_end = t_end;
+    p.T = T;
+    p.top_p = top_p;
+    p.squares = recovery >= 4;
     // A == nullptr: unit channel energy, so the key is v^2 (V-channel pruning)
-    const float A0 = A ? A[(size_t)bh * 128 + L] : 1.0f;
-    const float A1 = A ? A[(size_t)bh * 128 + 64 + L] : 1.0f;
-    const double a0 = sqrt((double)A0), a1 = sqrt((double)A1);
-    const int g0 = GROUPED ? gid[(size_t)bh * 128 + L] : 0;
-    const int g1 = GROUPED ? gid[(size_t)bh * 128 + 64 + L] : 0;
+    p.A0 = A ? A[(size_t)bh * 128 + L] : 1.0f;
+    p.A1 = A ? A[(size_t)bh * 128 + 64 + L] : 1.0f;
+    p.a0 = sqrt((double)p.A0);
+    p.a1 = sqrt((double)p.A1);
+    p.g0 = GROUPED ? gid[(size_t)bh * 128 + L] : 0;
+    p.g1 = GROUPED ? gid[(size_t)bh * 128 + 64 + L] : 0;
     // SparK-g with groups of 16 or 32 channels: each token's keys go to a
     // per-wave LDS row, group i's members at [i size, (i + 1) size) in
     // channel order; slot, group base and the group's kept count per lane
     __shared__ __align__(16) uint32_t gkeys[GROUPED ? 4 : 1][GROUPED ? 128 : 1];
-    const bool rank_path = GROUPED && (grp.size == 16 || grp.size == 32);
-    int slot0 = 0, slot1 = 0, T0 = 0, T1 = 0;
-    if (rank_path) {
+    p.gkeys = gkeys[GROUPED ? wave : 0];
+    p.rank_path = GROUPED && (grp.size == 16 || grp.size == 32);
+    p.slot0 = p.slot1 = p.T0 = p.T1 = 0;
+    if (p.rank_path) {
         for (int i = 0; i < grp.n; ++i) {       // uniform
-            const uint64_t m0 = ballot(g0 == i), m1 = ballot(g1 == i);
-            if (g0 == i) {
-                slot0 = i * grp.size + (int)mbcnt(m0);
-                T0 = grp.T[i];
+            const uint64_t m0 = ballot(p.g0 == i), m1 = ballot(p.g1 == i);
+            if (p.g0 == i) {
+                p.slot0 = i * grp.size + (int)mbcnt(m0);
+                p.T0 = grp.T[i];
             }
-            if (g1 == i) {
-                slot1 = i * grp.size + __popcll(m0) + (int)mbcnt(m1);
-                T1 = grp.T[i];
+            if (p.g1 == i) {
+                p.slot1 = i * grp.size + __popcll(m0) + (int)mbcnt(m1);
+                p.T1 = grp.T[i];
             }
         }
     }
 
-    double sum0 = 0.0, sum1 = 0.0, pruned = 0.0, pruned2 = 0.0;
-    int cnt0 = 0, cnt1 = 0;
-
-    const uint16_t* kbh = k + (size_t)bh * S * 128;
+    p.kbh = k + (size_t)bh * S * 128;
     // outputs use the head stride S_out (a cache's capacity, >= S)
     uint16_t* pbh = (SEL != 2 && k_packed) ? k_packed + (size_t)bh * S_out * T : nullptr;
-    int kept_tokens = 0;     // SEL 2: channels kept by this wave's tokens
     uint32_t* mbh = mask + (size_t)bh * S_out * 4;
-    uint16_t* st = reinterpret_cast<uint16_t*>(&stage[wave][0]);
+    p.st = reinterpret_cast<uint16_t*>(&stage[wave][0]);
+    p.tok_row = SEL == 2 ? tok_cnt + (size_t)bh * (S + 1) : nullptr;      // row_off[bh][t + 1]
+    // buffer resources over this block's mask rows and packed rows (word 3:
+    // 32-bit data format, no swizzle)
+    p.mrsrc = __builtin_amdgcn_make_buffer_rsrc(mbh + (size_t)t_begin * 4, (short)0, 16 * (t_end - t_begin),
+                                               0x00020000);
+    p.prsrc = __builtin_amdgcn_make_buffer_rsrc(pbh ? (void*)(pbh + (size_t)t_begin * T) : (void*)mbh, (short)0,
+                                               pbh ? 2 * T * (t_end - t_begin) : 0, 0x00020000);
 
-    // wave w takes tokens t_begin + 4*(w + 4*i) .. +3
-    for (int t4 = t_begin + 4 * wave; t4 < t_end; t4 += 16) {
-        const int n4 = min(4, t_end - t4);
-        {   // coalesced load of up to 4 token rows (16 B per lane)
-            const int tok = L >> 4;
-            uint4 x = make_uint4(0, 0, 0, 0);
-            if (tok < n4) x = *reinterpret_cast<const uint4*>(kbh + (size_t)(t4 + tok) * 128 + (L & 15) * 8);
-            stage[wave][L] = x;
-        }
-        wave_lds_sync();
-        for (int i = 0; i < n4; ++i) {
-            const int t = t4 + i;
-            const uint16_t kb0 = st[i * 128 + L], kb1 = st[i * 128 + 64 + L];
-            const float k0 = bf16_to_f32(kb0), k1 = bf16_to_f32(kb1);
-            const uint32_t key0 = __float_as_uint(__fmul_rn(A0, __fmul_rn(k0, k0)));
-            const uint32_t key1 = __float_as_uint(__fmul_rn(A1, __fmul_rn(k1, k1)));
-            bool kept0 = false, kept1 = false;
-            if (SEL == 2) {
-                select_top_p(key0, key1, top_p, kept0, kept1);
-            } else if (!GROUPED) {
-                if (T >= 128) {
-                    kept0 = kept1 = true;
-                } else if (T > 0) {
-                    select_top(key0, key1, T, kept0, kept1);
-                }
-            } else if (rank_path) {
-                select_grouped_rank(key0, key1, g0, g1, slot0, slot1, T0, T1, grp, gkeys[wave], kept0, kept1);
-            } else {
-                for (int i = 0; i < grp.n; ++i) {
-                    const bool in0 = g0 == i, in1 = g1 == i;
-                    const int Ti = grp.T[i];
-                    if (Ti >= grp.size) {
-                        kept0 |= in0;
-                        kept1 |= in1;
-                    } else if (Ti > 0) {
-                        // members' keys + 1 (order and ties unchanged; keys are
-                        // below 2^31), others 0: every candidate and the found
-                        // threshold are >= 1, so the plain search over all 128
-                        // counts members only, with no membership masks
-                        bool k0, k1;
-                        select_top(in0 ? key0 + 1u : 0u, in1 ? key1 + 1u : 0u, Ti, k0, k1);
-                        kept0 |= k0;
-                        kept1 |= k1;
-                    }
-                }
-            }
-            const uint64_t m0 = ballot(kept0), m1 = ballot(kept1);
-            if (L == 0) {
-                *reinterpret_cast<uint4*>(mbh + (size_t)t * 4) =
-                    make_uint4((uint32_t)m0, (uint32_t)(m0 >> 32), (uint32_t)m1, (uint32_t)(m1 >> 32));
-            }
-            if (SEL == 2) {
-                const int n = __popcll(m0) + __popcll(m1);
-                if (L == 0) tok_cnt[(size_t)bh * (S + 1) + t] = n;    // row_off[bh][t + 1]
-                kept_tokens += n;
-            } else {
-                if (kept0) pbh[(size_t)t * T + mbcnt(m0)] = kb0;
-                if (kept1) pbh[(size_t)t * T + __popcll(m0) + mbcnt(m1)] = kb1;
-            }
-            if (recovery == 0) {
-                if (kept0) { sum0 += (double)k0; ++cnt0; }
-                if (kept1) { sum1 += (double)k1; ++cnt1; }
-            } else {
-                cnt0 += kept0;
-                cnt1 += kept1;
-                if (recovery >= 3) {
-                    const double w0 = kept0 ? 0.0 : a0 * (double)fabsf(k0);
-                    const double w1 = kept1 ? 0.0 : a1 * (double)fabsf(k1);
-                    pruned += w0 + w1;
-                    if (recovery >= 4) pruned2 += w0 * w0 + w1 * w1;
-                }
-            }
-        }
-        wave_lds_sync();
+    SelectAcc acc;
+    if (SEL == 0 && (T <= 0 || T >= 128)) {
+        if (recovery == 0) select_tokens<SEL, 0, false>(p, grp, acc);
+        else if (recovery < 3) select_tokens<SEL, 1, false>(p, grp, acc);
+        else select_tokens<SEL, 2, false>(p, grp, acc);
+    } else {
+        if (recovery == 0) select_tokens<SEL, 0, true>(p, grp, acc);
+        else if (recovery < 3) select_tokens<SEL, 1, true>(p, grp, acc);
+        else select_tokens<SEL, 2, true>(p, grp, acc);
     }
+    const double sum0 = acc.sum0, sum1 = acc.sum1, pruned = acc.pruned, pruned2 = acc.pruned2;
+    const int cnt0 = acc.cnt0, cnt1 = acc.cnt1, kept_tokens = acc.kept_tokens;
 
     // fixed-order combination of the 4 waves, then one partial per block
     if (SEL == 2 && L == 0) red_tok[wave] = kept_tokens;
@@ -373,12 +529,12 @@ select_pack_kernel(const uint16_t* __restrict__ k, const float* __restrict__ A,
     red_cnt[wave][L] = cnt0;
     red_cnt[wave][64 + L] = cnt1;
     if (recovery >= 3) {
-        double p = pruned, p2 = pruned2;
+        double pr = pruned, pr2 = pruned2;
         for (int o = 32; o > 0; o >>= 1) {
-            p += __shfl_xor(p, o, 64);
-            p2 += __shfl_xor(p2, o, 64);
+            pr += __shfl_xor(pr, o, 64);
+            pr2 += __shfl_xor(pr2, o, 64);
         }
-        if (L == 0) { red_pr[wave][0] = p; red_pr[wave][1] = p2; }
+        if (L == 0) { red_pr[wave][0] = pr; red_pr[wave][1] = pr2; }
     }
     __syncthreads();
     if (threadIdx.x < 128) {
@@ -585,12 +741,12 @@ stats_partial_kernel(const uint16_t* __restrict__ k_packed, const uint32_t* __re
     red_cnt[wave][L] = cnt0;
     red_cnt[wave][64 + L] = cnt1;
     if (recovery >= 3) {
-        double p = pruned, p2 = pruned2;
+        double pr = pruned, pr2 = pruned2;
         for (int o = 32; o > 0; o >>= 1) {
-            p += __shfl_xor(p, o, 64);
-            p2 += __shfl_xor(p2, o, 64);
+            pr += __shfl_xor(pr, o, 64);
+            pr2 += __shfl_xor(pr2, o, 64);
         }
-        if (L == 0) { red_pr[wave][0] = p; red_pr[wave][1] = p2; }
+        if (L == 0) { red_pr[wave][0] = pr; red_pr[wave][1] = pr2; }
     }
     __syncthreads();
     if (threadIdx.x < 128) {
