@@ -79,6 +79,15 @@ def test_prefill_modes(recovery, qagg):
     check_prefill(gen.numpy_layer(w, seed=1, steps=0), w.n_kv, 0.8, qagg, recovery)
 
 
+@pytest.mark.parametrize("recovery", ["zero", "const", "score_mean_pruned"])
+@pytest.mark.parametrize("lam", [0.0, 1.0])
+def test_prefill_modes_keep_all_or_none(recovery, lam):
+    """lambda = 0 keeps every channel and lambda = 1 none: the select runs no
+    bit search there, in every recovery mode."""
+    w = WORKLOADS["tiny_s1k"].with_(S=300)
+    check_prefill(gen.numpy_layer(w, seed=3, steps=0), w.n_kv, lam, recovery=recovery)
+
+
 @pytest.mark.parametrize("B,S,n_q,n_kv", [(2, 1, 32, 8), (1, 63, 8, 8), (2, 65, 16, 8), (1, 257, 8, 4),
                                           (3, 1000, 16, 2), (1, 513, 8, 1)])
 def test_prefill_ragged_and_groups(B, S, n_q, n_kv):
