@@ -121,6 +121,23 @@ def test_prefill_embedded_d8_brute_force():
             assert got == best_set, (T, t)
 
 
+@pytest.mark.parametrize("lam", [0.99, 0.985, 0.51, 0.5, 0.49, 0.012, 0.008])
+def test_prefill_extreme_t_with_ties(lam):
+    """T = 1, 2, 63, 64, 65, 126, 127 on keys with many exact ties: equal
+    channel energies (every window row the same) and |k| from four values,
+    plus all-zero tokens, whose kept set is the first T channels."""
+    rng = np.random.default_rng(4)
+    B, N_kv, S = 1, 2, 257
+    q = np.ones((B, 2 * N_kv, 4, 128), np.float32)
+    k = rng.choice([0.0, 1.0, -1.0, 2.0, -0.5, 0.5], size=(B, N_kv, S, 128)).astype(np.float32)
+    k[:, :, ::17] = 0.0
+    x = {"q_win": gen.f32_to_bf16_bits(q), "k": gen.f32_to_bf16_bits(k)}
+    g, ref, _ = check_prefill(x, N_kv, lam)
+    T = ops.num_kept(128, lam)
+    zero = words_u32(g["mask"])[0, 0, 0]
+    assert [(int(zero[j >> 5]) >> (j & 31)) & 1 for j in range(128)] == [1] * T + [0] * (128 - T)
+
+
 def test_chan_energy_hand_cases_through_the_abi():
     """The oracle's hand cases for the window grouping and the fp32 order of
     A, embedded in D = 128 (other channels zero): query heads 0, 1 feed KV
