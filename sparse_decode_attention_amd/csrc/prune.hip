@@ -83,9 +83,9 @@ chan_energy_kernel(const uint16_t* __restrict__ q_win, float* __restrict__ A,
 // (two compares into separate scalar masks, two scalar popcounts), v = c when
 // n >= Tg, and a jump to the exit when n == Tg. The exit test runs on the
 // vector ALU (every lane compares the scalar n with Tg; the branch reads VCC):
-// the search is bound by scalar issue (one scalar instruction per SIMD every
-// four cycles), and this leaves six scalar and three vector instructions a
-// step.
+// scalar issue (one scalar instruction per SIMD every four cycles) is the
+// search's main limit, and this leaves six scalar and three vector
+// instructions a step.
 #define SPARK_SEL_STEP(BIT)                          \
     "s_or_b32 %[c], %[v], " BIT "\n\t"              \
     "v_cmp_le_u32_e64 %[m0], %[c], %[k0]\n\t"       \
