@@ -427,7 +427,7 @@ int spark_decode_attn_noalloc(const void* q, const void* k_packed, const uint32_
  *           the gather
  *  scores   fp32 [B][N_kv][S]  window-summed scores (NULL: kept in ws)
  * Logits run on the matrix cores (bf16 inputs, fp32 accumulation); two
- * passes over K. Requires D = 128, G*W <= 128 and S <= 65536 (else
+ * passes over K. Requires D = 128, G*W <= 128 and S <= 1048576 (else
  * SPARK_EUNSUPPORTED),
  * 1 <= W <= S, 1 <= keep <= S (else SPARK_EINVAL). Scores that tie exactly in
  * fp32 are broken by the lower t; scores are fp32, so tokens whose scores

@@ -423,6 +423,71 @@ __global__ void __launch_bounds__(EVICT_SELECT_THREADS) evict_select_kernel(cons
     }
 }
 
+// Caches longer than the register-held select takes (64 tokens a thread):
+// the same search and compaction, with the scores read again from global
+// memory (4 bytes a token; they stay in L2) at every step. The counts read
+// them thread-interleaved, one request per 64 consecutive tokens of a wave;
+// the ordered compaction reads each thread's contiguous run twice, for its
+// counts and then for its writes.
+__global__ void __launch_bounds__(EVICT_SELECT_THREADS) evict_select_long_kernel(const EvictArgs a) {
+    constexpr int NT = EVICT_SELECT_THREADS;
+    constexpr int NWV = NT / 64;
+    __shared__ uint32_t wsum[2][NWV];
+    __shared__ uint32_t wtot[NWV];
+    const int bh = blockIdx.x;
+    const int tid = threadIdx.x, L = tid & 63, wave = tid >> 6;
+    const uint32_t* u = reinterpret_cast<const uint32_t*>(a.scores) + (size_t)bh * a.S;
+    const int S = a.S;
+    const uint32_t keep = (uint32_t)a.keep;
+    uint32_t v = 0;
+    bool exact = false;
+    for (int bit = 31, par = 0; bit >= 0; --bit, par ^= 1) {
+        const uint32_t c = v | (1u << bit);
+        uint32_t cnt = 0;
+        for (int t = tid; t < S; t += NT) cnt += u[t] >= c ? 1u : 0u;
+        const float cw = wave_sum_dpp((float)cnt);                   // exact: counts < 2^24
+        if (L == 0) wsum[par][wave] = (uint32_t)cw;
+        __syncthreads();
+        uint32_t total = 0;
+#pragma unroll
+        for (int w = 0; w < NWV; ++w) total += wsum[par][w];
+        if (total >= keep) {
+            v = c;
+            if (total == keep) { exact = true; break; }
+        }
+    }
+    const int per = (S + NT - 1) / NT;
+    const int t_begin = min(S, tid * per), t_end = min(S, t_begin + per);
+    uint32_t n_gt = 0, n_eq = 0;
+    for (int t = t_begin; t < t_end; ++t) {
+        const uint32_t x = u[t];
+        n_gt += x > v ? 1u : 0u;
+        n_eq += x == v ? 1u : 0u;
+    }
+    uint32_t eq_before = 0, take_eq = 0;
+    if (!exact) {      // uniform
+        uint32_t gt_total, eq_total;
+        (void)block_excl_scan<NT>(n_gt, wtot, gt_total);
+        eq_before = block_excl_scan<NT>(n_eq, wtot, eq_total);
+        take_eq = keep - gt_total;
+    } else {
+        take_eq = 0xffffffffu;     // every value == v is kept
+    }
+    const uint32_t n_take = n_eq == 0 ? 0u
+                          : eq_before >= take_eq ? 0u
+                          : min(n_eq, take_eq - eq_before);
+    uint32_t kept_total;
+    uint32_t pos = block_excl_scan<NT>(n_gt + n_take, wtot, kept_total);
+    int32_t* idx = a.idx + (size_t)bh * a.keep;
+    uint32_t e = eq_before;
+    for (int t = t_begin; t < t_end; ++t) {
+        const uint32_t x = u[t];
+        bool k = x > v;
+        if (x == v) { k = e < take_eq; ++e; }
+        if (k && pos < keep) idx[pos++] = t;
+    }
+}
+
 // K and V rows of the kept tokens: one 16-byte chunk per thread.
 __global__ void evict_gather_kernel(const EvictArgs a) {
     const size_t n = (size_t)a.BH * a.keep * 16;
@@ -447,6 +512,8 @@ hipError_t launch_evict(const EvictArgs& a, hipStream_t stream) {
     if (per <= 8) hipLaunchKernelGGL(evict_select_kernel<8>, dim3(a.BH), dim3(EVICT_SELECT_THREADS), 0, stream, a);
     else if (per <= 32) hipLaunchKernelGGL(evict_select_kernel<32>, dim3(a.BH), dim3(EVICT_SELECT_THREADS), 0, stream, a);
     else if (per <= 64) hipLaunchKernelGGL(evict_select_kernel<64>, dim3(a.BH), dim3(EVICT_SELECT_THREADS), 0, stream, a);
+    else if (a.S <= EVICT_MAX_S_LONG)
+        hipLaunchKernelGGL(evict_select_long_kernel, dim3(a.BH), dim3(EVICT_SELECT_THREADS), 0, stream, a);
     else return hipErrorInvalidValue;
     if (a.k_out != nullptr) {
         const size_t n = (size_t)a.BH * a.keep * 16;

@@ -27,7 +27,8 @@
 #define EVICT_CHUNK 1024
 #define EVICT_TILE 64
 #define EVICT_SELECT_THREADS 1024
-#define EVICT_MAX_S (EVICT_SELECT_THREADS * 64)   // tokens per (b, KV head) the select handles
+#define EVICT_MAX_S (EVICT_SELECT_THREADS * 64)   // tokens per (b, KV head) the register-held select handles
+#define EVICT_MAX_S_LONG (1 << 20)                 // longer caches: the select that re-reads the scores
 
 namespace spark {
 

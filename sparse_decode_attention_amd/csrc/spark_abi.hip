@@ -582,7 +582,7 @@ int spark_window_evict(const void* q_win, const void* k, const void* v, int B, i
     if (int e = check_group(N_q, N_kv)) return e;
     if (D != 128) return SPARK_EUNSUPPORTED;
     const int G = N_q / N_kv;
-    if ((long)G * window > EVICT_MAX_ROWS || S > EVICT_MAX_S) return SPARK_EUNSUPPORTED;
+    if ((long)G * window > EVICT_MAX_ROWS || S > EVICT_MAX_S_LONG) return SPARK_EUNSUPPORTED;
     if (!q_win || !k || !idx || !ws || ((k_out == nullptr) != (v_out == nullptr)) || (k_out && !v)) return SPARK_EINVAL;
     if (!aligned(q_win, 16) || !aligned(k, 16) || (v && !aligned(v, 16)) || !aligned(idx, 4) ||
         (k_out && (!aligned(k_out, 16) || !aligned(v_out, 16))) || (scores && !aligned(scores, 4)) || !aligned(ws, 256))

@@ -354,6 +354,8 @@ def test_window_evict_checks():
     assert call(N_q=30) == ops.EINVAL
     assert call(D=64) == ops.EUNSUPPORTED
     assert call(N_q=64, W=64) == ops.EUNSUPPORTED          # G * W = 512 window rows
+    assert call(S=(1 << 20) + 1) == ops.EUNSUPPORTED       # longer than the select takes
+    assert call(S=(1 << 20)) == ops.ENOSPACE                # the longest cache passes the size checks
     assert call(ko=None) == ops.EINVAL                      # k_out and v_out go together
     assert call(idx=None) == ops.EINVAL
     assert call(k=MIS) == ops.EALIGN

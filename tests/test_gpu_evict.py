@@ -118,3 +118,11 @@ def test_evict_full_size_sampled():
         sel = torch.from_numpy(idx.astype(np.int64)).to(DEV)
         assert torch.equal(got["k"][b, h], x["k"][b, h].index_select(0, sel))
         assert torch.equal(got["v"][b, h], x["v"][b, h].index_select(0, sel))
+
+
+def test_evict_beyond_64k_tokens():
+    """S = 70000 (more tokens per head than the register-held select takes),
+    so the select that re-reads the scores runs: scores, the certified kept
+    set and the gathered rows of both KV heads."""
+    w = WORKLOADS["snapkv_b8_s32k_keep4k_l07"]
+    check_case(Workload("evict_long", 4, 1, 70000, 8, 2, 128, 8, 0.7, 0, keep=5000), 70000, 5000, seed=2)
