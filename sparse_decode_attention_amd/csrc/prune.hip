@@ -623,10 +623,19 @@ topp_scan_kernel(int32_t* __restrict__ blk_cnt, int nblk) {
 // reads four rows whole and all four rounds' rows and masks are requested
 // before any is used. A kept channel goes to the token's offset plus the
 // mask bits below it.
+//
+// The wave's 16 rows are consecutive, so their packed values fill one
+// contiguous range [off[16 w], off[16 w + 16]) of the head's region. They
+// are first placed in a per-wave LDS stage, shifted so that the stage and the
+// region agree modulo 16 bytes; the range then goes out as whole 16-byte
+// stores, and the (at most two) 16-byte chunks it shares with the
+// neighbouring waves' ranges element by element.
 __global__ void __launch_bounds__(256)
 topp_pack_kernel(const uint16_t* __restrict__ k, const uint32_t* __restrict__ mask, uint16_t* __restrict__ k_packed,
                  int32_t* __restrict__ row_off, const int32_t* __restrict__ blk_base, int S, int nblk) {
     __shared__ int off[PRUNE_TOKENS_PER_BLOCK + 1];
+    // per wave: 16 rows of at most 128 values, plus the alignment shift (< 8)
+    __shared__ __align__(16) uint16_t stage[4][16 * 128 + 8];
     const int bh = blockIdx.y, blk = blockIdx.x;
     const int t_begin = blk * PRUNE_TOKENS_PER_BLOCK;
     const int nt = min(PRUNE_TOKENS_PER_BLOCK, S - t_begin);
@@ -657,6 +666,12 @@ topp_pack_kernel(const uint16_t* __restrict__ k, const uint32_t* __restrict__ ma
     if (threadIdx.x < nt) ro[t_begin + threadIdx.x + 1] = off[threadIdx.x + 1];
     if (blk == 0 && threadIdx.x == 0) ro[0] = 0;
     uint16_t* pbh = k_packed + (size_t)bh * S * 128;
+    // the wave's range: rows 16 w .. min(16 w + 16, nt) - 1 (tokens past nt
+    // have no row: their offsets repeat the last one)
+    const int r_lo = min(16 * wave, nt), r_hi = min(16 * wave + 16, nt);
+    const int g0 = off[r_lo], g1 = off[r_hi];
+    const int shift = g0 & 7;                // stage index shift + j <-> region element g0 + j
+    uint16_t* stw = stage[wave];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int i = 16 * wave + 4 * q + (L >> 4);
@@ -668,15 +683,29 @@ topp_pack_kernel(const uint16_t* __restrict__ k, const uint32_t* __restrict__ ma
         for (int w = 0; w < 3; ++w) below += w < wi ? __popc(words[w]) : 0;
         const uint32_t byte = (words[wi] >> sh) & 0xFFu;
         // ranks are bounded by the row's count (the mask's popcount), so the
-        // writes stay in [row_off[t], row_off[t + 1])
-        const int base = off[i] + below;
+        // entries stay in the row's part of the range
+        const int base = shift + (off[i] - g0) + below;
         const uint32_t e2[4] = {x[q].x, x[q].y, x[q].z, x[q].w};
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             if ((byte >> e) & 1u) {
                 const uint16_t val = (uint16_t)((e & 1) ? (e2[e >> 1] >> 16) : (e2[e >> 1] & 0xFFFFu));
-                pbh[base + __popc(byte & ((1u << e) - 1u))] = val;
+                stw[base + __popc(byte & ((1u << e) - 1u))] = val;
             }
+        }
+    }
+    wave_lds_sync();
+    // 16-byte chunks of the region from element g0 - shift: chunk c holds
+    // region elements g0 - shift + 8 c .. + 7, the stage's entries 8 c .. + 7
+    const int nchunk = (shift + (g1 - g0) + 7) >> 3;
+    for (int c = L; c < nchunk; c += 64) {
+        const int e0 = 8 * c;                                   // stage index of the chunk's first element
+        const int lo = max(e0, shift), hi = min(e0 + 8, shift + (g1 - g0));
+        uint16_t* dst = pbh + (g0 - shift) + e0;
+        if (lo == e0 && hi == e0 + 8) {
+            *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(stw + e0);
+        } else {
+            for (int j = lo; j < hi; ++j) dst[j - e0] = stw[j];
         }
     }
 }
