@@ -188,17 +188,20 @@ __device__ __forceinline__ uint32_t lane_pick(uint64_t m, uint32_t a, uint32_t b
 // the others DPP moves inside each 16-lane row. After the 8 step, lanes L
 // and L ^ 8 hold the same value, so the row rotation by 4 (lane (L + 4) mod
 // 16) delivers lane L ^ 4's value; the last two steps are quad permutes.
+// Each DPP step is written as a move with no old value, which the compiler
+// folds into the add (one v_add_f32_dpp; none of these patterns reads
+// outside its row, so the bound control setting never applies).
 __device__ __forceinline__ float tree_sum_wave(float x) {
     x = xor32_sum(x);
     x = xor16_sum(x);
     int v = __float_as_int(x);
-    x = __fadd_rn(x, __int_as_float(__builtin_amdgcn_update_dpp(v, v, 0x128, 0xF, 0xF, false)));   // row_ror:8
+    x = __fadd_rn(x, __int_as_float(__builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, true)));   // row_ror:8
     v = __float_as_int(x);
-    x = __fadd_rn(x, __int_as_float(__builtin_amdgcn_update_dpp(v, v, 0x124, 0xF, 0xF, false)));   // row_ror:4
+    x = __fadd_rn(x, __int_as_float(__builtin_amdgcn_mov_dpp(v, 0x124, 0xF, 0xF, true)));   // row_ror:4
     v = __float_as_int(x);
-    x = __fadd_rn(x, __int_as_float(__builtin_amdgcn_update_dpp(v, v, 0x4E, 0xF, 0xF, false)));    // quad_perm 2,3,0,1
+    x = __fadd_rn(x, __int_as_float(__builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, true)));    // quad_perm 2,3,0,1
     v = __float_as_int(x);
-    x = __fadd_rn(x, __int_as_float(__builtin_amdgcn_update_dpp(v, v, 0xB1, 0xF, 0xF, false)));    // quad_perm 1,0,3,2
+    x = __fadd_rn(x, __int_as_float(__builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true)));    // quad_perm 1,0,3,2
     return x;
 }
 
