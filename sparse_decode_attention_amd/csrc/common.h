@@ -35,16 +35,19 @@ __device__ __forceinline__ float wave_sum(float x) {
 }
 
 // Wave-wide max through DPP (no LDS traffic): butterfly inside each 16-lane
-// row, then the four row results combined from lanes 0, 16, 32, 48.
+// row, then the four row results combined from lanes 0, 16, 32, 48. The DPP
+// steps are moves with no old value, which the compiler folds into the max
+// or add that uses them; these patterns never read outside a row, so the
+// bound control setting does not apply.
 __device__ __forceinline__ float dpp_row_max(float x) {
     int v = __float_as_int(x);
-    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(v, v, 0xB1, 0xF, 0xF, false)));  // quad_perm 1,0,3,2
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true)));  // quad_perm 1,0,3,2
     v = __float_as_int(x);
-    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(v, v, 0x4E, 0xF, 0xF, false)));  // quad_perm 2,3,0,1
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, true)));  // quad_perm 2,3,0,1
     v = __float_as_int(x);
-    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(v, v, 0x141, 0xF, 0xF, false))); // row_half_mirror
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, true))); // row_half_mirror
     v = __float_as_int(x);
-    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(v, v, 0x140, 0xF, 0xF, false))); // row_mirror
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(v, 0x140, 0xF, 0xF, true))); // row_mirror
     return x;
 }
 __device__ __forceinline__ float wave_max_dpp(float x) {
@@ -72,13 +75,13 @@ __device__ __forceinline__ float xor32_sum(float x) {
 // rows combined with permlane swaps. Every lane gets the total.
 __device__ __forceinline__ float wave_sum_dpp(float x) {
     int v = __float_as_int(x);
-    x += __int_as_float(__builtin_amdgcn_update_dpp(v, v, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true));   // quad_perm 1,0,3,2
     v = __float_as_int(x);
-    x += __int_as_float(__builtin_amdgcn_update_dpp(v, v, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, true));   // quad_perm 2,3,0,1
     v = __float_as_int(x);
-    x += __int_as_float(__builtin_amdgcn_update_dpp(v, v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, true));  // row_half_mirror
     v = __float_as_int(x);
-    x += __int_as_float(__builtin_amdgcn_update_dpp(v, v, 0x140, 0xF, 0xF, false));  // row_mirror
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(v, 0x140, 0xF, 0xF, true));  // row_mirror
     return xor32_sum(xor16_sum(x));
 }
 
